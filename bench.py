@@ -1,0 +1,189 @@
+"""Throughput of the GIFT encode + decode-reduce unit on one MI355X.
+
+Unit of work (one "step"): gift_encode of one replica's 1536 x 6144 fp32
+gradient (rank-32 input-side whitening, E4M3, per-tensor scale) and
+gift_decode_reduce of R = 8 replica payloads into one fp32 gradient, on one
+stream.  The other 7 payloads are encoded during setup.  Statistics
+(T = 16384 bf16 tokens) and the rank-32 refresh run in setup and are timed
+separately.
+
+Timed region: W untimed warmup steps, then K steps bracketed by
+torch.cuda.synchronize(); the input buffers rotate over 4 independent sets
+(W, 8 payloads, output: 604 MB in all, more than twice the 256 MB Infinity
+Cache) so each step reads inputs that are not cache-resident.
+
+Prints one JSON line (the metric, roofline of the dominant kernel, the oracle
+timed on the host cores as a baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFS = 2500.0
+FP64_PEAK_TFS = 78.6
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--scaling", default="tensor", choices=["tensor", "block"])
+    p.add_argument("--sets", type=int, default=4)
+    p.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    p.add_argument("--extra", action="store_true", help="also time statistics / refresh / Euclidean")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (the multi-GPU reduce-scatter / all-gather "
+              "exchange is a design, not built); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import fac_whitening_amd as fw
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    m, d, T, R, k = 1536, 6144, 16384, 8, 32
+    scaling = fw.SCALINGS[args.scaling]
+    nb = fw.nblocks(m, d, scaling)
+
+    # ---- setup: synthetic layer (Llama-600M fc2 shape), statistics, refresh
+    t0 = time.time()
+    case = synth.make_layer(4, device=dev, R=R)
+    print(f"[bench] inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    L = fw.Layer(m, d, "lowrank", rank=k, oversample=16, power_iters=4, ema_decay=0.0, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    L.accumulate_stats(case.a_steps[0], fw.SIDE_A, commit=True)
+    ev[1].record()
+    L.refresh(case.omega)
+    ev[2].record()
+    torch.cuda.synchronize()
+    t_stats_ms = ev[0].elapsed_time(ev[1])
+    t_refresh_ms = ev[1].elapsed_time(ev[2])
+    assert L.flags() == 0, "non-finite factor"
+
+    # ---- payloads: replica 0 is encoded inside each step; 1..R-1 in setup
+    sets = []
+    pay_codes = torch.empty(R, m, d, dtype=torch.uint8, device=dev)
+    pay_scales = torch.empty(R, nb, dtype=torch.float32, device=dev)
+    for r in range(1, R):
+        L.encode(case.W[r], fw.E4M3, scaling, codes=pay_codes[r], scales=pay_scales[r])
+    for s in range(args.sets):
+        W = case.W[0].clone()
+        codes = pay_codes.clone()
+        scales = pay_scales.clone()
+        out = torch.empty(m, d, dtype=torch.float32, device=dev)
+        sets.append((W, codes, scales, out))
+    torch.cuda.synchronize()
+
+    def step(i):
+        W, codes, scales, out = sets[i % len(sets)]
+        L.encode(W, fw.E4M3, scaling, codes=codes[0], scales=scales[0])
+        L.decode_reduce(codes, scales, fw.E4M3, scaling, out=out)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # timed region: events around every call on the stream the kernels use
+    enc_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    dec_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        W, codes, scales, out = sets[i % len(sets)]
+        enc_ev[i][0].record()
+        L.encode(W, fw.E4M3, scaling, codes=codes[0], scales=scales[0])
+        enc_ev[i][1].record()
+        dec_ev[i][0].record()
+        L.decode_reduce(codes, scales, fw.E4M3, scaling, out=out)
+        dec_ev[i][1].record()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(stop)
+    t_enc = float(np.mean([a.elapsed_time(b) for a, b in enc_ev]))
+    t_dec = float(np.mean([a.elapsed_time(b) for a, b in dec_ev]))
+    ms_per_step = total_ms / args.steps
+    grad_bytes = 4.0 * m * d
+    value = grad_bytes / (ms_per_step * 1e-3) / 1e9         # GB/s of fp32 gradient
+
+    # algorithmic bytes per unit: encode reads W and U, writes codes + scales;
+    # decode reads R payloads and U, writes the fp32 gradient
+    u_bytes = d * k * 4 + 68 * 4
+    enc_bytes = 4.0 * m * d + u_bytes + m * d + 4 * nb
+    dec_bytes = R * (m * d + 4 * nb) + u_bytes + 4.0 * m * d
+    dominant = "decode" if t_dec >= t_enc else "encode"
+    dom_bytes = dec_bytes if dominant == "decode" else enc_bytes
+    dom_ms = max(t_dec, t_enc)
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": f"gift_{dominant}" + ("_reduce" if dominant == "decode" else ""),
+                "unit_frac": round((enc_bytes + dec_bytes) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "encode_ms": round(t_enc, 5), "decode_ms": round(t_dec, 5),
+                "alg_bytes_encode": int(enc_bytes), "alg_bytes_decode": int(dec_bytes)}
+
+    result = {
+        "metric": "GIFT encode+decode GB/s of fp32 grad (1536x6144, r=32); % of HBM peak",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded Llama-600M fc2 layer: a ~ N(0, Q diag(i^-1.5) Q^T) bf16, W = delta^T a / T)",
+        "config": {"workload": "fc2 1536x6144 fp32 gradient, rank-32 lowrank whitening, E4M3 "
+                               f"{args.scaling} scale, R=8 replicas", "d_out": m, "d_in": d, "rank": k,
+                   "replicas": R, "tokens": T, "format": "e4m3", "scaling": args.scaling,
+                   "cache": f"cold ({args.sets} rotating buffer sets)"},
+        "roofline": roofline,
+        "setup": {"stats_ms": round(t_stats_ms, 3), "refresh_ms": round(t_refresh_ms, 3),
+                  "stats_tflops_triangle": round(T * d * (d + 1) / (t_stats_ms * 1e-3) / 1e12, 2)},
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(case, L, R, m, d, args.scaling)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(case, L, R, m, d, scaling):
+    """The oracle (numpy fp64) on one unit of the same workload: encode of one
+    replica + decode-reduce of R payloads, with the oracle's own dense T_A
+    (built from the GPU's A outside the timed part)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import gift as G
+    A = L.buffers()["A"].double().cpu().numpy()
+    lam = G.damping(A)
+    T, Tinv = G.transform_lowrank(G.lowrank_factor(A, case.omega.cpu().numpy(), 32, 4, lam))
+    Ws = [w.cpu().numpy() for w in case.W]
+    pre = [G.encode(Ws[r], T, "e4m3", scaling) for r in range(1, R)]
+    t0 = time.perf_counter()
+    e0 = G.encode(Ws[0], T, "e4m3", scaling)
+    G.decode_reduce([e0["codes"]] + [p["codes"] for p in pre], [e0["scales"]] + [p["scales"] for p in pre], Tinv,
+                    "e4m3", scaling)
+    t = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(4.0 * m * d / t / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": "one full unit (encode 1 replica + decode-reduce 8) at 1536x6144, numpy fp64 with dense T_A",
+            "seconds": round(t, 3), "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()

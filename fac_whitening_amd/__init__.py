@@ -1,0 +1,294 @@
+"""Python binding of libgift (GIFT encode/decode on MI355X).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``libgift.so`` (built from ``csrc/`` by ``build.py``).  PyTorch provides the
+device memory and the current stream; nothing here computes on the data.
+Importing this module raises if the library has not been built: there is no
+fallback.
+
+Function names follow the C ABI in ``include/gift.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgift.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libgift.so not built ({LIB_PATH}); run `python -m fac_whitening_amd.build` "
+                      "or __graft_entry__.build()")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# enums (include/gift.h)
+EUCLID, DIAG, LOWRANK, CHOL_INPUT, CHOL_TWOSIDED = range(5)
+E4M3, E5M2 = 0, 1
+SCALE_TENSOR, SCALE_BLOCK128 = 0, 1
+BF16, FP32 = 0, 1
+SIDE_A, SIDE_G = 0, 1
+FLAG_NONFINITE, FLAG_SPIN_TIMEOUT = 1, 2
+TRANSFORMS = {"euclid": EUCLID, "diag": DIAG, "lowrank": LOWRANK, "chol": CHOL_INPUT, "twosided": CHOL_TWOSIDED}
+FORMATS = {"e4m3": E4M3, "e5m2": E5M2}
+SCALINGS = {"tensor": SCALE_TENSOR, "block": SCALE_BLOCK128}
+STATUS = {0: "GIFT_OK", 1: "GIFT_ERR_INVALID_ARG", 2: "GIFT_ERR_WORKSPACE", 3: "GIFT_ERR_NOT_READY",
+          4: "GIFT_ERR_NUMERICAL", 5: "GIFT_ERR_UNSUPPORTED", 6: "GIFT_ERR_HIP"}
+
+EXPORTS = [
+    "gift_layer_state_bytes", "gift_layer_create", "gift_layer_destroy", "gift_layer_get_counters",
+    "gift_layer_set_counters", "gift_layer_flags", "gift_layer_buffers", "gift_layer_mark_ready",
+    "gift_accumulate_stats", "gift_commit_stats", "gift_refresh_factors", "gift_encode",
+    "gift_decode_reduce", "gift_payload_bytes", "gift_profiler_create", "gift_profiler_destroy",
+    "gift_profiler_workspace_bytes", "gift_profile_step", "gift_select_layers", "gift_status_string",
+    "gift_last_hip_error",
+]
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("d_out", ctypes.c_int32), ("d_in", ctypes.c_int32), ("transform", ctypes.c_int32),
+                ("rank", ctypes.c_int32), ("oversample", ctypes.c_int32), ("power_iters", ctypes.c_int32),
+                ("ema_decay", ctypes.c_float), ("damping_rel", ctypes.c_float)]
+
+
+_vp, _sz, _i32, _i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+_P = ctypes.POINTER
+
+
+def _sig(name, res, *args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = list(args)
+    return f
+
+
+_sig("gift_layer_state_bytes", _i32, _P(LayerDesc), _P(_sz), _P(_sz))
+_sig("gift_layer_create", _i32, _P(LayerDesc), _vp, _sz, _vp, _P(_vp))
+_sig("gift_layer_destroy", _i32, _vp)
+_sig("gift_layer_get_counters", _i32, _vp, _P(_i64))
+_sig("gift_layer_set_counters", _i32, _vp, _P(_i64))
+_sig("gift_layer_flags", _i32, _vp, _vp, _P(ctypes.c_uint32))
+_sig("gift_layer_buffers", _i32, _vp, *[_P(_vp)] * 8)
+_sig("gift_layer_mark_ready", _i32, _vp)
+_sig("gift_accumulate_stats", _i32, _vp, _i32, _vp, _i32, _i64, _i64, _i32, _vp)
+_sig("gift_commit_stats", _i32, _vp, _i32, _vp)
+_sig("gift_refresh_factors", _i32, _vp, _vp, _vp, _sz, _vp)
+_sig("gift_encode", _i32, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp)
+_sig("gift_decode_reduce", _i32, _vp, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _vp, _i64, _vp, _sz, _vp)
+_sig("gift_payload_bytes", _sz, _i32, _i32, _i32)
+_sig("gift_profiler_create", _i32, _i32, _i32, _i32, _vp, _vp, _P(_vp))
+_sig("gift_profiler_destroy", _i32, _vp)
+_sig("gift_profiler_workspace_bytes", _sz, _i32, _i32, _i64)
+_sig("gift_profile_step", _i32, _vp, _i32, _P(_vp), _P(_i64), _vp, _sz, _vp)
+_sig("gift_select_layers", _i32, _vp, _i32, _P(ctypes.c_double), _P(_i32), _P(_i32), _P(_i32), _vp)
+_sig("gift_status_string", ctypes.c_char_p, _i32)
+_sig("gift_last_hip_error", _i32)
+
+
+class GiftError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = f"{where}: {STATUS.get(status, status)} ({_lib.gift_status_string(status).decode()})"
+        if status == 6:
+            msg += f", hipError {_lib.gift_last_hip_error()}"
+        super().__init__(msg)
+        self.status = status
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise GiftError(status, where)
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def nblocks(m: int, d: int, scaling: int) -> int:
+    return 1 if scaling == SCALE_TENSOR else -(-m // 128) * -(-d // 128)
+
+
+def payload_bytes(d_out: int, d_in: int, scaling: int) -> int:
+    return int(_lib.gift_payload_bytes(d_out, d_in, scaling))
+
+
+def _alloc(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+class Layer:
+    """One layer's state and calls (gift_layer_*)."""
+
+    def __init__(self, d_out: int, d_in: int, transform="lowrank", rank: int = 32, oversample: int = 16,
+                 power_iters: int = 4, ema_decay: float = 0.0, damping_rel: float = 1e-3, device="cuda",
+                 stream=None, workspace=None):
+        tr = TRANSFORMS[transform] if isinstance(transform, str) else int(transform)
+        self.desc = LayerDesc(d_out, d_in, tr, rank, oversample, power_iters, ema_decay, damping_rel)
+        sb, wb = _sz(), _sz()
+        _check(_lib.gift_layer_state_bytes(ctypes.byref(self.desc), ctypes.byref(sb), ctypes.byref(wb)),
+               "gift_layer_state_bytes")
+        self.device = torch.device(device)
+        self.state = _alloc(sb.value, self.device)
+        self.work_bytes = wb.value
+        self.work = workspace if workspace is not None else _alloc(wb.value, self.device)
+        h = _vp()
+        _check(_lib.gift_layer_create(ctypes.byref(self.desc), _ptr(self.state), sb.value, _stream(stream),
+                                      ctypes.byref(h)), "gift_layer_create")
+        self._h = h
+        self.m, self.d, self.k = d_out, d_in, rank
+
+    # -- lifecycle ---------------------------------------------------------
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.gift_layer_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def handle(self):
+        return self._h
+
+    def counters(self):
+        arr = (_i64 * 5)()
+        _check(_lib.gift_layer_get_counters(self._h, arr), "gift_layer_get_counters")
+        return list(arr)
+
+    def set_counters(self, vals):
+        arr = (_i64 * 5)(*vals)
+        _check(_lib.gift_layer_set_counters(self._h, arr), "gift_layer_set_counters")
+
+    def flags(self, stream=None) -> int:
+        f = ctypes.c_uint32()
+        _check(_lib.gift_layer_flags(self._h, _stream(stream), ctypes.byref(f)), "gift_layer_flags")
+        return f.value
+
+    def buffers(self) -> dict:
+        """Views into the state buffer (device tensors), by name."""
+        ptrs = [_vp() for _ in range(8)]
+        _check(_lib.gift_layer_buffers(self._h, *[ctypes.byref(p) for p in ptrs]), "gift_layer_buffers")
+        names = ["A", "G", "U", "coef", "tinv_a", "t_a", "lg_inv", "lg"]
+        m, d = self.m, self.d
+        shapes = {"A": (d, d), "G": (m, m), "U": (d, 32), "tinv_a": (d, d), "t_a": (d, d), "lg_inv": (m, m),
+                  "lg": (m, m), "coef": (68,) if self.desc.transform == LOWRANK else (2 * d,)}
+        base = self.state.data_ptr()
+        out = {}
+        for n, p in zip(names, ptrs):
+            if not p.value:
+                continue
+            off = p.value - base
+            cnt = 1
+            for s in shapes[n]:
+                cnt *= s
+            out[n] = self.state[off:off + 4 * cnt].view(torch.float32).view(*shapes[n])
+        return out
+
+    def mark_ready(self):
+        _check(_lib.gift_layer_mark_ready(self._h), "gift_layer_mark_ready")
+
+    # -- statistics / refresh --------------------------------------------
+    def accumulate_stats(self, x: torch.Tensor, side: int = SIDE_A, commit: bool = False, stream=None):
+        dtype = BF16 if x.dtype == torch.bfloat16 else FP32
+        if x.dtype not in (torch.bfloat16, torch.float32) or x.dim() != 2 or x.stride(1) != 1:
+            raise ValueError("x must be a row-major [T][n] bf16 or fp32 tensor")
+        _check(_lib.gift_accumulate_stats(self._h, side, _ptr(x), dtype, x.shape[0], x.stride(0), int(commit),
+                                          _stream(stream)), "gift_accumulate_stats")
+
+    def commit_stats(self, side: int = SIDE_A, stream=None):
+        _check(_lib.gift_commit_stats(self._h, side, _stream(stream)), "gift_commit_stats")
+
+    def refresh(self, omega=None, stream=None):
+        _check(_lib.gift_refresh_factors(self._h, _ptr(omega), _ptr(self.work), self.work_bytes, _stream(stream)),
+               "gift_refresh_factors")
+
+    # -- encode / decode --------------------------------------------------
+    def encode(self, W: torch.Tensor, fmt=E4M3, scaling=SCALE_TENSOR, amax_in=None, codes=None, scales=None,
+               amax_out=None, whitened=None, want_codes=True, stream=None):
+        fmt = FORMATS.get(fmt, fmt)
+        scaling = SCALINGS.get(scaling, scaling)
+        m, d = self.m, self.d
+        nb = nblocks(m, d, scaling)
+        if W.dtype != torch.float32 or W.shape != (m, d) or W.stride(1) != 1:
+            raise ValueError("W must be fp32 [d_out][d_in] with unit column stride")
+        if want_codes:
+            if codes is None:
+                codes = torch.empty(m, d, dtype=torch.uint8, device=W.device)
+            if scales is None:
+                scales = torch.empty(nb, dtype=torch.float32, device=W.device)
+        _check(_lib.gift_encode(self._h, _ptr(W), W.stride(0), fmt, scaling, _ptr(amax_in), _ptr(amax_out),
+                                _ptr(codes) if want_codes else None, _ptr(scales) if want_codes else None,
+                                _ptr(whitened), _ptr(self.work), self.work_bytes, _stream(stream)), "gift_encode")
+        return codes, scales
+
+    def decode_reduce(self, codes: torch.Tensor, scales: torch.Tensor, fmt=E4M3, scaling=SCALE_TENSOR, out=None,
+                      R=None, stream=None):
+        """codes [R][m][d] uint8, scales [R][nblk] fp32 (contiguous replicas)."""
+        fmt = FORMATS.get(fmt, fmt)
+        scaling = SCALINGS.get(scaling, scaling)
+        m, d = self.m, self.d
+        if codes.dim() == 2:
+            codes = codes.unsqueeze(0)
+            scales = scales.reshape(1, -1)
+        R = codes.shape[0] if R is None else R
+        if out is None:
+            out = torch.empty(m, d, dtype=torch.float32, device=codes.device)
+        cs = codes.stride(0) if R > 1 else m * d
+        ss = scales.stride(0) if R > 1 else scales.shape[-1]
+        _check(_lib.gift_decode_reduce(self._h, _ptr(codes), cs, _ptr(scales), ss, R, fmt, scaling, _ptr(out),
+                                       out.stride(0), _ptr(self.work), self.work_bytes, _stream(stream)),
+               "gift_decode_reduce")
+        return out
+
+
+class Profiler:
+    """FP8 boundary-hit profiler over a list of layers (gift_profiler_*)."""
+
+    def __init__(self, n_layers: int, fmt=E4M3, scaling=SCALE_TENSOR, device="cuda", stream=None):
+        self.n = n_layers
+        self.counts = torch.zeros(n_layers, 2, dtype=torch.int64, device=device)
+        self.work_bytes = int(_lib.gift_profiler_workspace_bytes(n_layers, scaling, 0))
+        self.work = _alloc(self.work_bytes, device)
+        h = _vp()
+        _check(_lib.gift_profiler_create(n_layers, FORMATS.get(fmt, fmt), SCALINGS.get(scaling, scaling),
+                                         _ptr(self.counts), _stream(stream), ctypes.byref(h)), "gift_profiler_create")
+        self._h = h
+
+    def step(self, grads, stream=None):
+        ptrs = (_vp * self.n)(*[g.data_ptr() for g in grads])
+        numel = (_i64 * self.n)(*[g.numel() for g in grads])
+        for g in grads:
+            if g.dtype != torch.float32 or not g.is_contiguous():
+                raise ValueError("gradients must be contiguous fp32")
+        _check(_lib.gift_profile_step(self._h, self.n, ptrs, numel, _ptr(self.work), self.work_bytes,
+                                      _stream(stream)), "gift_profile_step")
+
+    def select(self, max_select: int, stream=None):
+        sc = (ctypes.c_double * self.n)()
+        order = (_i32 * self.n)()
+        sel = (_i32 * self.n)()
+        nsel = _i32()
+        _check(_lib.gift_select_layers(self._h, max_select, sc, order, sel, ctypes.byref(nsel), _stream(stream)),
+               "gift_select_layers")
+        return list(sc), list(order), list(sel[:nsel.value])
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.gift_profiler_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,69 @@
+"""Build libgift.so (HIP, gfx950) in-tree with hipcc.
+
+Every HIP source under csrc/ is compiled for gfx950 and linked into one shared
+library next to this file.  Packed-fp32 instructions are disabled for all GPU
+code (``-Xclang -target-feature -Xclang -packed-fp32-ops``).
+"""
+from __future__ import annotations
+
+import glob
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libgift.so")
+ARCH = "gfx950"
+
+FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-fno-gpu-flush-denormals-to-zero", "-ffp-contract=fast",
+    "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
+]
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    """Compile each source to an object in parallel, then link libgift.so."""
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    procs, objs = [], []
+    for src in sources():
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        objs.append(obj)
+        cmd = ["hipcc", *[f for f in FLAGS if f != "-shared"], "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        if len(procs) >= jobs:
+            _wait(procs.pop(0))
+    for p in procs:
+        _wait(p)
+    tmp = LIB + ".tmp"
+    cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    out = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if out.returncode != 0:
+        raise RuntimeError(f"link failed:\n{out.stdout}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def _wait(item):
+    src, p = item
+    out, _ = p.communicate()
+    text = out.decode(errors="replace")
+    if p.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {os.path.basename(src)}:\n{text}")
+    if text.strip():
+        sys.stderr.write(f"[{os.path.basename(src)}]\n{text}\n")
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

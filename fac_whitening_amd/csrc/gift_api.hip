@@ -1,0 +1,575 @@
+// Host side of libgift: argument checks, state / workspace layout, and the
+// order in which each C-ABI call enqueues its kernels.  Nothing here touches
+// data on the host; every step of the path runs in the kernels.
+//
+// GIFT 阅读笔记, Algorithm 1: per step and layer, the Euclidean branch
+// (Scale -> AllReduceMax -> Q -> AllReduceSum -> Dequantize / N) or the
+// geometry branch (W L_A^-T -> Scale_loc -> Q -> AllReduceSum -> Dequantize
+// / N -> L_A^T).  On one GPU the collectives become: a shared amax passed in
+// by the caller (AllReduceMax) and a decode that reduces R payloads held in
+// device memory (AllReduceSum).
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "gift_internal.hpp"
+
+struct gift_layer {
+  gift_layer_desc desc;
+  gift::StateLayout sl;
+  gift::WorkLayout wl;
+  char* state;
+  int64_t counters[5];   // tokens A, tokens G, commits A, commits G, refreshes
+  bool ready;
+};
+
+struct gift_profiler {
+  int32_t n_layers, fmt, scaling;
+  uint64_t* counts;
+  int64_t steps;
+  std::vector<int64_t> numel;
+};
+
+namespace {
+
+thread_local int32_t g_last_hip = 0;
+
+gift_status hip_fail(hipError_t e) {
+  g_last_hip = (int32_t)e;
+  return GIFT_ERR_HIP;
+}
+
+#define GIFT_HIP(expr)                                  \
+  do {                                                  \
+    hipError_t _e = (expr);                             \
+    if (_e != hipSuccess) return hip_fail(_e);          \
+  } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int lp_of(int l) { return l <= 48 ? 48 : 64; }
+
+int l_of(const gift_layer_desc& d) { return std::min(d.rank + d.oversample, d.d_in); }
+
+bool desc_ok(const gift_layer_desc* d) {
+  if (!d) return false;
+  if (d->d_out < 1 || d->d_in < 8 || d->d_in % 8 != 0) return false;
+  if (d->transform < GIFT_EUCLID || d->transform > GIFT_CHOL_TWOSIDED) return false;
+  if (!(d->ema_decay >= 0.0f && d->ema_decay < 1.0f)) return false;
+  if (!(d->damping_rel >= 0.0f) || !std::isfinite(d->damping_rel)) return false;
+  if (d->transform == GIFT_LOWRANK) {
+    if (d->rank < 1 || d->rank > 32 || d->rank > d->d_in) return false;
+    if (d->oversample < 0 || d->power_iters < 0 || d->power_iters > 64) return false;
+    if (l_of(*d) > gift::kMaxRank || l_of(*d) < d->rank) return false;
+  }
+  return true;
+}
+
+int64_t nblk(int m, int d, int scaling) {
+  return scaling == GIFT_SCALE_TENSOR ? 1 : gift::cdiv(m, gift::kBlock) * gift::cdiv(d, gift::kBlock);
+}
+
+}  // namespace
+
+namespace gift {
+
+StateLayout state_layout(const gift_layer_desc& g) {
+  StateLayout s;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const size_t d = (size_t)g.d_in, m = (size_t)g.d_out;
+  const bool stats_a = g.transform != GIFT_EUCLID;
+  const bool stats_g = g.transform == GIFT_CHOL_TWOSIDED;
+  s.flags = take(256);
+  if (stats_a) {
+    s.S_A = take(d * d * 4);
+    s.A = take(d * d * 4);
+  }
+  if (stats_g) {
+    s.S_G = take(m * m * 4);
+    s.G = take(m * m * 4);
+  }
+  if (g.transform == GIFT_LOWRANK) {
+    s.U = take(d * 32 * 4);
+    s.coef = take(68 * 4);
+  }
+  if (g.transform == GIFT_DIAG) s.coef = take(2 * d * 4);
+  if (g.transform == GIFT_CHOL_INPUT || g.transform == GIFT_CHOL_TWOSIDED) {
+    s.tinv_a = take(d * d * 4);
+    s.t_a = take(d * d * 4);
+  }
+  if (stats_g) {
+    s.lg_inv = take(m * m * 4);
+    s.lg = take(m * m * 4);
+  }
+  s.total = off;
+  return s;
+}
+
+WorkLayout work_layout(const gift_layer_desc& g) {
+  WorkLayout w;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const size_t d = (size_t)g.d_in, m = (size_t)g.d_out;
+  w.amax = take((size_t)nblk((int)m, (int)d, GIFT_SCALE_BLOCK128) * 4);
+  if (g.transform != GIFT_EUCLID) w.tile = take(m * d * 4);
+  if (g.transform == GIFT_CHOL_TWOSIDED) w.tmp = take(m * d * 4);
+  if (g.transform == GIFT_LOWRANK) {
+    w.ppart = take((size_t)cdiv((int64_t)d, kProjChunk) * m * 32 * 4);
+    const size_t lp = (size_t)lp_of(l_of(g));
+    w.Y = take(d * lp * 8);
+    w.Q = take(d * lp * 8);
+    w.Z = take(d * lp * 8);
+    w.small = take((64 + 64 * 64 + 64) * 8);
+    w.gpart = take((size_t)cdiv((int64_t)d, 256) * lp * lp * 8);
+  }
+  if (g.transform == GIFT_CHOL_INPUT || g.transform == GIFT_CHOL_TWOSIDED) {
+    const size_t n = g.transform == GIFT_CHOL_TWOSIDED ? std::max(d, m) : d;
+    w.chol = take(n * n * 8);
+    w.chol2 = take(n * n * 8 + 256);   // + the damping scalar
+  }
+  w.total = std::max<size_t>(off, 256);
+  return w;
+}
+
+}  // namespace gift
+
+using gift::cdiv;
+
+extern "C" {
+
+const char* gift_status_string(gift_status s) {
+  switch (s) {
+    case GIFT_OK: return "ok";
+    case GIFT_ERR_INVALID_ARG: return "invalid argument";
+    case GIFT_ERR_WORKSPACE: return "state or workspace buffer too small";
+    case GIFT_ERR_NOT_READY: return "not ready (no committed statistics or no factor yet)";
+    case GIFT_ERR_NUMERICAL: return "numerical failure";
+    case GIFT_ERR_UNSUPPORTED: return "unsupported combination";
+    case GIFT_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int32_t gift_last_hip_error(void) { return g_last_hip; }
+
+size_t gift_payload_bytes(int32_t d_out, int32_t d_in, int32_t scaling) {
+  if (d_out < 0 || d_in < 0) return 0;
+  return (size_t)d_out * (size_t)d_in + 4 * (size_t)nblk(d_out, d_in, scaling);
+}
+
+gift_status gift_layer_state_bytes(const gift_layer_desc* desc, size_t* state_bytes, size_t* workspace_bytes) {
+  if (!desc_ok(desc)) return GIFT_ERR_INVALID_ARG;
+  if (state_bytes) *state_bytes = gift::state_layout(*desc).total;
+  if (workspace_bytes) *workspace_bytes = gift::work_layout(*desc).total;
+  return GIFT_OK;
+}
+
+gift_status gift_layer_create(const gift_layer_desc* desc, void* d_state, size_t state_bytes, gift_stream_t stream,
+                              gift_layer_t* out) {
+  if (!desc_ok(desc) || !out || !d_state || (reinterpret_cast<uintptr_t>(d_state) & 255u)) return GIFT_ERR_INVALID_ARG;
+  gift::StateLayout sl = gift::state_layout(*desc);
+  if (state_bytes < sl.total) return GIFT_ERR_WORKSPACE;
+  gift_layer* L = new (std::nothrow) gift_layer;
+  if (!L) return GIFT_ERR_INVALID_ARG;
+  L->desc = *desc;
+  L->sl = sl;
+  L->wl = gift::work_layout(*desc);
+  L->state = static_cast<char*>(d_state);
+  std::memset(L->counters, 0, sizeof(L->counters));
+  L->ready = desc->transform == GIFT_EUCLID;
+  hipError_t e = gift::launch_fill_u32(reinterpret_cast<uint32_t*>(d_state), 0u, sl.total / 4,
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    delete L;
+    return hip_fail(e);
+  }
+  *out = L;
+  return GIFT_OK;
+}
+
+gift_status gift_layer_destroy(gift_layer_t layer) {
+  delete layer;
+  return GIFT_OK;
+}
+
+gift_status gift_layer_get_counters(gift_layer_t L, int64_t h[5]) {
+  if (!L || !h) return GIFT_ERR_INVALID_ARG;
+  std::memcpy(h, L->counters, sizeof(L->counters));
+  return GIFT_OK;
+}
+
+gift_status gift_layer_set_counters(gift_layer_t L, const int64_t h[5]) {
+  if (!L || !h) return GIFT_ERR_INVALID_ARG;
+  for (int i = 0; i < 5; ++i)
+    if (h[i] < 0) return GIFT_ERR_INVALID_ARG;
+  std::memcpy(L->counters, h, sizeof(L->counters));
+  L->ready = L->desc.transform == GIFT_EUCLID || h[4] > 0;
+  return GIFT_OK;
+}
+
+gift_status gift_layer_flags(gift_layer_t L, gift_stream_t stream, uint32_t* h_flags) {
+  if (!L || !h_flags) return GIFT_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  GIFT_HIP(hipMemcpyAsync(h_flags, L->state + L->sl.flags, 4, hipMemcpyDeviceToHost, s));
+  GIFT_HIP(hipStreamSynchronize(s));
+  return GIFT_OK;
+}
+
+gift_status gift_layer_buffers(gift_layer_t L, float** A, float** G, float** U, float** coef, float** tinv_a,
+                               float** t_a, float** lg_inv, float** lg) {
+  if (!L) return GIFT_ERR_INVALID_ARG;
+  const gift_layer_desc& g = L->desc;
+  auto at = [&](size_t off, bool present) -> float* {
+    return present ? reinterpret_cast<float*>(L->state + off) : nullptr;
+  };
+  const bool chol = g.transform == GIFT_CHOL_INPUT || g.transform == GIFT_CHOL_TWOSIDED;
+  if (A) *A = at(L->sl.A, g.transform != GIFT_EUCLID);
+  if (G) *G = at(L->sl.G, g.transform == GIFT_CHOL_TWOSIDED);
+  if (U) *U = at(L->sl.U, g.transform == GIFT_LOWRANK);
+  if (coef) *coef = at(L->sl.coef, g.transform == GIFT_LOWRANK || g.transform == GIFT_DIAG);
+  if (tinv_a) *tinv_a = at(L->sl.tinv_a, chol);
+  if (t_a) *t_a = at(L->sl.t_a, chol);
+  if (lg_inv) *lg_inv = at(L->sl.lg_inv, g.transform == GIFT_CHOL_TWOSIDED);
+  if (lg) *lg = at(L->sl.lg, g.transform == GIFT_CHOL_TWOSIDED);
+  return GIFT_OK;
+}
+
+gift_status gift_layer_mark_ready(gift_layer_t L) {
+  if (!L) return GIFT_ERR_INVALID_ARG;
+  L->ready = true;
+  return GIFT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Statistics
+// ---------------------------------------------------------------------------
+
+gift_status gift_commit_stats(gift_layer_t L, int32_t side, gift_stream_t stream) {
+  if (!L || (side != GIFT_SIDE_A && side != GIFT_SIDE_G)) return GIFT_ERR_INVALID_ARG;
+  const gift_layer_desc& g = L->desc;
+  if (g.transform == GIFT_EUCLID) return GIFT_ERR_INVALID_ARG;
+  if (side == GIFT_SIDE_G && g.transform != GIFT_CHOL_TWOSIDED) return GIFT_ERR_INVALID_ARG;
+  int64_t& tokens = L->counters[side];
+  int64_t& commits = L->counters[2 + side];
+  if (tokens <= 0) return GIFT_ERR_NOT_READY;
+  const int n = side == GIFT_SIDE_A ? g.d_in : g.d_out;
+  float* S = reinterpret_cast<float*>(L->state + (side == GIFT_SIDE_A ? L->sl.S_A : L->sl.S_G));
+  float* A = reinterpret_cast<float*>(L->state + (side == GIFT_SIDE_A ? L->sl.A : L->sl.G));
+  GIFT_HIP(gift::launch_commit(S, A, n, 1.0 / (double)tokens, g.ema_decay, commits == 0 ? 1 : 0,
+                               static_cast<hipStream_t>(stream)));
+  tokens = 0;
+  ++commits;
+  return GIFT_OK;
+}
+
+gift_status gift_accumulate_stats(gift_layer_t L, int32_t side, const void* d_x, int32_t dtype, int64_t T,
+                                  int64_t ld, int32_t commit, gift_stream_t stream) {
+  if (!L || (side != GIFT_SIDE_A && side != GIFT_SIDE_G)) return GIFT_ERR_INVALID_ARG;
+  const gift_layer_desc& g = L->desc;
+  if (g.transform == GIFT_EUCLID) return GIFT_ERR_INVALID_ARG;
+  if (side == GIFT_SIDE_G && g.transform != GIFT_CHOL_TWOSIDED) return GIFT_ERR_INVALID_ARG;
+  if (dtype != GIFT_BF16 && dtype != GIFT_FP32) return GIFT_ERR_INVALID_ARG;
+  const int n = side == GIFT_SIDE_A ? g.d_in : g.d_out;
+  if (T < 0) return GIFT_ERR_INVALID_ARG;
+  if (T > 0) {
+    if (!d_x || !aligned16(d_x) || ld < n) return GIFT_ERR_INVALID_ARG;
+    if (ld % (dtype == GIFT_BF16 ? 8 : 4) != 0) return GIFT_ERR_INVALID_ARG;
+  }
+  if (commit && L->counters[side] + T <= 0) return GIFT_ERR_NOT_READY;
+  float* S = reinterpret_cast<float*>(L->state + (side == GIFT_SIDE_A ? L->sl.S_A : L->sl.S_G));
+  if (T > 0) GIFT_HIP(gift::launch_stats(d_x, dtype, T, ld, n, S, static_cast<hipStream_t>(stream)));
+  L->counters[side] += T;
+  if (commit) return gift_commit_stats(L, side, stream);
+  return GIFT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Refresh
+// ---------------------------------------------------------------------------
+
+gift_status gift_refresh_factors(gift_layer_t L, const float* d_omega, void* d_work, size_t work_bytes,
+                                 gift_stream_t stream) {
+  if (!L) return GIFT_ERR_INVALID_ARG;
+  const gift_layer_desc& g = L->desc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (g.transform == GIFT_EUCLID) return GIFT_OK;
+  if (L->counters[2] == 0) return GIFT_ERR_NOT_READY;
+  if (g.transform == GIFT_CHOL_TWOSIDED && L->counters[3] == 0) return GIFT_ERR_NOT_READY;
+  if (work_bytes < L->wl.total) return GIFT_ERR_WORKSPACE;
+  if (!d_work || (reinterpret_cast<uintptr_t>(d_work) & 255u)) return GIFT_ERR_INVALID_ARG;
+  char* work = static_cast<char*>(d_work);
+  uint32_t* flags = reinterpret_cast<uint32_t*>(L->state + L->sl.flags);
+  const float* A = reinterpret_cast<const float*>(L->state + L->sl.A);
+  switch (g.transform) {
+    case GIFT_DIAG:
+      GIFT_HIP(gift::launch_refresh_diag(A, g.d_in, g.damping_rel, reinterpret_cast<float*>(L->state + L->sl.coef),
+                                         flags, s));
+      break;
+    case GIFT_LOWRANK: {
+      if (!d_omega || !aligned16(d_omega)) return GIFT_ERR_INVALID_ARG;
+      GIFT_HIP(gift::launch_refresh_lowrank(A, g.d_in, g.rank, l_of(g), g.power_iters, g.damping_rel, d_omega,
+                                            reinterpret_cast<float*>(L->state + L->sl.U),
+                                            reinterpret_cast<float*>(L->state + L->sl.coef), L->wl, work, flags, s));
+      break;
+    }
+    case GIFT_CHOL_INPUT:
+    case GIFT_CHOL_TWOSIDED: {
+      double* wa = reinterpret_cast<double*>(work + L->wl.chol);
+      double* wb = reinterpret_cast<double*>(work + L->wl.chol2);
+      GIFT_HIP(gift::launch_refresh_chol(A, g.d_in, g.damping_rel, reinterpret_cast<float*>(L->state + L->sl.tinv_a),
+                                         reinterpret_cast<float*>(L->state + L->sl.t_a), 0, wa, wb, flags, s));
+      if (g.transform == GIFT_CHOL_TWOSIDED) {
+        const float* Gm = reinterpret_cast<const float*>(L->state + L->sl.G);
+        GIFT_HIP(gift::launch_refresh_chol(Gm, g.d_out, g.damping_rel,
+                                           reinterpret_cast<float*>(L->state + L->sl.lg_inv),
+                                           reinterpret_cast<float*>(L->state + L->sl.lg), 1, wa, wb, flags, s));
+      }
+      break;
+    }
+    default:
+      return GIFT_ERR_INVALID_ARG;
+  }
+  L->ready = true;
+  ++L->counters[4];
+  return GIFT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Encode / decode
+// ---------------------------------------------------------------------------
+
+gift_status gift_encode(gift_layer_t L, const float* d_W, int64_t ldw, int32_t fmt, int32_t scaling,
+                        const float* d_amax_in, float* d_amax_out, uint8_t* d_codes, float* d_scales,
+                        float* d_whitened, void* d_work, size_t work_bytes, gift_stream_t stream) {
+  if (!L) return GIFT_ERR_INVALID_ARG;
+  const gift_layer_desc& g = L->desc;
+  const int m = g.d_out, d = g.d_in;
+  if (fmt != GIFT_E4M3 && fmt != GIFT_E5M2) return GIFT_ERR_INVALID_ARG;
+  if (scaling != GIFT_SCALE_TENSOR && scaling != GIFT_SCALE_BLOCK128) return GIFT_ERR_INVALID_ARG;
+  if (!d_W || !aligned16(d_W) || ldw < d || ldw % 4 != 0) return GIFT_ERR_INVALID_ARG;
+  if (d_codes && (!aligned16(d_codes) || !d_scales)) return GIFT_ERR_INVALID_ARG;
+  if (!d_codes && !d_amax_out) return GIFT_ERR_INVALID_ARG;
+  if (d_whitened && !aligned16(d_whitened)) return GIFT_ERR_INVALID_ARG;
+  if (!d_work || (reinterpret_cast<uintptr_t>(d_work) & 255u)) return GIFT_ERR_INVALID_ARG;
+  if (work_bytes < L->wl.total) return GIFT_ERR_WORKSPACE;
+  if (!L->ready) return GIFT_ERR_NOT_READY;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* work = static_cast<char*>(d_work);
+  uint32_t* slots = reinterpret_cast<uint32_t*>(work + L->wl.amax);
+  uint32_t* flags = reinterpret_cast<uint32_t*>(L->state + L->sl.flags);
+  const int64_t nb = nblk(m, d, scaling);
+  GIFT_HIP(gift::launch_fill_u32(slots, 0u, (size_t)nb, s));
+  const float* X = d_W;
+  int64_t ldx = ldw;
+  float* out = d_whitened ? d_whitened : reinterpret_cast<float*>(work + L->wl.tile);
+  switch (g.transform) {
+    case GIFT_EUCLID:
+      GIFT_HIP(gift::launch_amax(d_W, ldw, m, d, scaling, slots, s));
+      if (d_whitened) GIFT_HIP(hipMemcpy2DAsync(d_whitened, (size_t)d * 4, d_W, (size_t)ldw * 4, (size_t)d * 4, m,
+                                                hipMemcpyDeviceToDevice, s));
+      break;
+    case GIFT_DIAG:
+      GIFT_HIP(gift::launch_diag_apply(d_W, ldw, m, d, reinterpret_cast<const float*>(L->state + L->sl.coef), out, d,
+                                       scaling, slots, s));
+      X = out;
+      ldx = d;
+      break;
+    case GIFT_LOWRANK: {
+      float* ppart = reinterpret_cast<float*>(work + L->wl.ppart);
+      const float* U = reinterpret_cast<const float*>(L->state + L->sl.U);
+      const float* coef = reinterpret_cast<const float*>(L->state + L->sl.coef);
+      GIFT_HIP(gift::launch_lr_project(d_W, ldw, m, d, U, g.rank, ppart, s));
+      GIFT_HIP(gift::launch_lr_apply(d_W, ldw, m, d, U, g.rank, ppart, coef, 0, out, d, scaling, slots, s));
+      X = out;
+      ldx = d;
+      break;
+    }
+    case GIFT_CHOL_INPUT:
+    case GIFT_CHOL_TWOSIDED: {
+      const float* src = d_W;
+      int64_t lds = ldw;
+      if (g.transform == GIFT_CHOL_TWOSIDED) {
+        float* tmp = reinterpret_cast<float*>(work + L->wl.tmp);
+        GIFT_HIP(gift::launch_trmm(d_W, ldw, m, d, reinterpret_cast<const float*>(L->state + L->sl.lg_inv), 1, tmp, d,
+                                   s));
+        src = tmp;
+        lds = d;
+      }
+      GIFT_HIP(gift::launch_trmm(src, lds, m, d, reinterpret_cast<const float*>(L->state + L->sl.tinv_a), 0, out, d,
+                                 s));
+      GIFT_HIP(gift::launch_amax(out, d, m, d, scaling, slots, s));
+      X = out;
+      ldx = d;
+      break;
+    }
+    default:
+      return GIFT_ERR_INVALID_ARG;
+  }
+  if (d_codes) {
+    GIFT_HIP(gift::launch_quantize(X, ldx, m, d, fmt, scaling, slots, d_amax_in, d_amax_out, d_codes, d_scales, flags,
+                                   s));
+  } else {
+    GIFT_HIP(gift::launch_amax_out(slots, d_amax_out, nb, s));   // amax only
+  }
+  return GIFT_OK;
+}
+
+gift_status gift_decode_reduce(gift_layer_t L, const uint8_t* d_codes, int64_t code_stride, const float* d_scales,
+                               int64_t scale_stride, int32_t R, int32_t fmt, int32_t scaling, float* d_out,
+                               int64_t ldo, void* d_work, size_t work_bytes, gift_stream_t stream) {
+  if (!L) return GIFT_ERR_INVALID_ARG;
+  const gift_layer_desc& g = L->desc;
+  const int m = g.d_out, d = g.d_in;
+  if (fmt != GIFT_E4M3 && fmt != GIFT_E5M2) return GIFT_ERR_INVALID_ARG;
+  if (scaling != GIFT_SCALE_TENSOR && scaling != GIFT_SCALE_BLOCK128) return GIFT_ERR_INVALID_ARG;
+  if (R < 1 || !d_codes || !d_scales || !d_out) return GIFT_ERR_INVALID_ARG;
+  if (!aligned16(d_codes) || !aligned16(d_out) || ldo < d || ldo % 4 != 0) return GIFT_ERR_INVALID_ARG;
+  if (R > 1 && (code_stride < (int64_t)m * d || code_stride % 16 != 0)) return GIFT_ERR_INVALID_ARG;
+  const int64_t nb = nblk(m, d, scaling);
+  if (R > 1 && scale_stride < nb) return GIFT_ERR_INVALID_ARG;
+  if (!d_work || (reinterpret_cast<uintptr_t>(d_work) & 255u)) return GIFT_ERR_INVALID_ARG;
+  if (work_bytes < L->wl.total) return GIFT_ERR_WORKSPACE;
+  if (!L->ready) return GIFT_ERR_NOT_READY;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* work = static_cast<char*>(d_work);
+  if (g.transform == GIFT_EUCLID) {
+    GIFT_HIP(gift::launch_dequant_sum(d_codes, code_stride, d_scales, scale_stride, R, m, d, fmt, scaling, d_out, ldo,
+                                      s));
+    return GIFT_OK;
+  }
+  float* Ub = reinterpret_cast<float*>(work + L->wl.tile);
+  GIFT_HIP(gift::launch_dequant_sum(d_codes, code_stride, d_scales, scale_stride, R, m, d, fmt, scaling, Ub, d, s));
+  switch (g.transform) {
+    case GIFT_DIAG:
+      GIFT_HIP(gift::launch_diag_apply(Ub, d, m, d, reinterpret_cast<const float*>(L->state + L->sl.coef) + d, d_out,
+                                       ldo, scaling, nullptr, s));
+      break;
+    case GIFT_LOWRANK: {
+      float* ppart = reinterpret_cast<float*>(work + L->wl.ppart);
+      const float* U = reinterpret_cast<const float*>(L->state + L->sl.U);
+      const float* coef = reinterpret_cast<const float*>(L->state + L->sl.coef);
+      GIFT_HIP(gift::launch_lr_project(Ub, d, m, d, U, g.rank, ppart, s));
+      GIFT_HIP(gift::launch_lr_apply(Ub, d, m, d, U, g.rank, ppart, coef, 1, d_out, ldo, scaling, nullptr, s));
+      break;
+    }
+    case GIFT_CHOL_INPUT:
+      GIFT_HIP(gift::launch_trmm(Ub, d, m, d, reinterpret_cast<const float*>(L->state + L->sl.t_a), 0, d_out, ldo, s));
+      break;
+    case GIFT_CHOL_TWOSIDED: {
+      float* tmp = reinterpret_cast<float*>(work + L->wl.tmp);
+      GIFT_HIP(gift::launch_trmm(Ub, d, m, d, reinterpret_cast<const float*>(L->state + L->sl.t_a), 0, tmp, d, s));
+      GIFT_HIP(gift::launch_trmm(tmp, d, m, d, reinterpret_cast<const float*>(L->state + L->sl.lg), 1, d_out, ldo, s));
+      break;
+    }
+    default:
+      return GIFT_ERR_INVALID_ARG;
+  }
+  return GIFT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Profiler
+// ---------------------------------------------------------------------------
+
+size_t gift_profiler_workspace_bytes(int32_t n_layers, int32_t scaling, int64_t max_numel) {
+  (void)scaling;
+  (void)max_numel;
+  if (n_layers < 1) return 0;
+  return gift::align256((size_t)n_layers * 4);
+}
+
+gift_status gift_profiler_create(int32_t n_layers, int32_t fmt, int32_t scaling, uint64_t* d_counts,
+                                 gift_stream_t stream, gift_profiler_t* out) {
+  if (n_layers < 1 || !d_counts || !out || (reinterpret_cast<uintptr_t>(d_counts) & 7u)) return GIFT_ERR_INVALID_ARG;
+  if (fmt != GIFT_E4M3 && fmt != GIFT_E5M2) return GIFT_ERR_INVALID_ARG;
+  if (scaling != GIFT_SCALE_TENSOR) return GIFT_ERR_UNSUPPORTED;
+  gift_profiler* P = new (std::nothrow) gift_profiler;
+  if (!P) return GIFT_ERR_INVALID_ARG;
+  P->n_layers = n_layers;
+  P->fmt = fmt;
+  P->scaling = scaling;
+  P->counts = d_counts;
+  P->steps = 0;
+  P->numel.assign((size_t)n_layers, -1);
+  hipError_t e = gift::launch_fill_u32(reinterpret_cast<uint32_t*>(d_counts), 0u, (size_t)n_layers * 4,
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    delete P;
+    return hip_fail(e);
+  }
+  *out = P;
+  return GIFT_OK;
+}
+
+gift_status gift_profiler_destroy(gift_profiler_t P) {
+  delete P;
+  return GIFT_OK;
+}
+
+gift_status gift_profile_step(gift_profiler_t P, int32_t n_layers, const float* const* h_grads,
+                              const int64_t* h_numel, void* d_work, size_t work_bytes, gift_stream_t stream) {
+  if (!P || n_layers != P->n_layers || !h_grads || !h_numel || !d_work) return GIFT_ERR_INVALID_ARG;
+  if (work_bytes < gift_profiler_workspace_bytes(n_layers, P->scaling, 0)) return GIFT_ERR_WORKSPACE;
+  for (int i = 0; i < n_layers; ++i) {
+    if (h_numel[i] < 0 || (h_numel[i] > 0 && !h_grads[i])) return GIFT_ERR_INVALID_ARG;
+    if (P->numel[(size_t)i] >= 0 && P->numel[(size_t)i] != h_numel[i]) return GIFT_ERR_INVALID_ARG;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t* slots = static_cast<uint32_t*>(d_work);
+  GIFT_HIP(gift::launch_fill_u32(slots, 0u, (size_t)n_layers, s));
+  for (int i = 0; i < n_layers; ++i) {
+    GIFT_HIP(gift::launch_amax_flat(h_grads[i], h_numel[i], slots + i, s));
+    GIFT_HIP(gift::launch_hits(h_grads[i], h_numel[i], P->fmt, slots + i,
+                               reinterpret_cast<unsigned long long*>(P->counts) + 2 * i, s));
+  }
+  for (int i = 0; i < n_layers; ++i) P->numel[(size_t)i] = h_numel[i];
+  ++P->steps;
+  return GIFT_OK;
+}
+
+gift_status gift_select_layers(gift_profiler_t P, int32_t max_select, double* h_scores, int32_t* h_order,
+                               int32_t* h_selected, int32_t* h_n_selected, gift_stream_t stream) {
+  if (!P || max_select < 1 || !h_scores || !h_order || !h_selected || !h_n_selected) return GIFT_ERR_INVALID_ARG;
+  if (P->steps == 0) return GIFT_ERR_NOT_READY;
+  const int n = P->n_layers;
+  std::vector<uint64_t> c((size_t)n * 2);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  GIFT_HIP(hipMemcpyAsync(c.data(), P->counts, c.size() * 8, hipMemcpyDeviceToHost, s));
+  GIFT_HIP(hipStreamSynchronize(s));
+  for (int i = 0; i < n; ++i) {
+    double den = (double)P->numel[(size_t)i] * (double)P->steps;
+    h_scores[i] = den > 0 ? ((double)c[2 * (size_t)i] + (double)c[2 * (size_t)i + 1]) / den : 0.0;
+  }
+  std::vector<int32_t> order((size_t)n);
+  for (int i = 0; i < n; ++i) order[(size_t)i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return h_scores[a] > h_scores[b]; });
+  int best_i = 1;
+  double best = -1.0;
+  for (int i = 1; i <= std::min(n - 1, max_select); ++i) {
+    double a = h_scores[order[(size_t)i - 1]], b = h_scores[order[(size_t)i]];
+    double ratio = b > 0 ? a / b : (a > 0 ? INFINITY : 1.0);
+    if (ratio > best) {
+      best = ratio;
+      best_i = i;
+    }
+  }
+  int nsel = std::min(best_i, max_select);
+  if (n == 1) nsel = 1;
+  for (int i = 0; i < n; ++i) h_order[i] = order[(size_t)i];
+  for (int i = 0; i < nsel; ++i) h_selected[i] = order[(size_t)i];
+  *h_n_selected = nsel;
+  return GIFT_OK;
+}
+
+}  // extern "C"

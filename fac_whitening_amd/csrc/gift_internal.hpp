@@ -1,0 +1,104 @@
+// Internal declarations shared by the host library and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/gift.h"
+
+namespace gift {
+
+constexpr int kBlock = 128;          // per-block scaling tile (128 x 128)
+constexpr int kMaxRank = 64;         // k + p <= 64 for the small dense solvers
+constexpr int kProjChunk = 256;      // columns per partial in the projection X U
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+__host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Offsets (bytes) of the regions of one layer's device state.
+struct StateLayout {
+  size_t S_A = 0, A = 0, S_G = 0, G = 0, U = 0, coef = 0, tinv_a = 0, t_a = 0, lg_inv = 0, lg = 0,
+         flags = 0, total = 0;
+};
+
+// Offsets (bytes) inside the per-call workspace.  Regions overlap between
+// calls of different kinds (encode / decode / refresh never run at once on
+// one workspace).
+struct WorkLayout {
+  // encode / decode
+  size_t tile = 0;      // fp32 [m][d]: whitened tensor (encode) or reduced U (decode)
+  size_t tmp = 0;       // fp32 [m][d]: second buffer (two-sided)
+  size_t ppart = 0;     // fp32 [nchunk][m][k]: projection partials
+  size_t amax = 0;      // uint32 [nblk]
+  // refresh
+  size_t Y = 0, Q = 0, Z = 0;   // fp64 [d][l]
+  size_t small = 0;             // fp64 scratch for the l x l solvers
+  size_t gpart = 0;             // fp64 [nchunk][l][l]
+  size_t chol = 0;              // fp64 [n][n] (Cholesky variants)
+  size_t chol2 = 0;             // fp64 [n][n]
+  size_t total = 0;
+};
+
+struct Dims {
+  int m, d, k, l;
+};
+
+StateLayout state_layout(const gift_layer_desc& desc);
+WorkLayout work_layout(const gift_layer_desc& desc);
+
+// ---- kernel launchers (each returns hipGetLastError() of its launches) ----
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s);
+hipError_t launch_fill_f32(float* p, float v, size_t n, hipStream_t s);
+
+// amax of |x| over a [m][ld] fp32 tensor into uint32 slots (bit patterns).
+hipError_t launch_amax(const float* x, int64_t ld, int m, int d, int scaling, uint32_t* slots,
+                       hipStream_t s);
+// quantise x [m][ld] with amax slots (or amax_in) -> codes, scales, amax_out.
+hipError_t launch_quantize(const float* x, int64_t ld, int m, int d, int fmt, int scaling,
+                           const uint32_t* slots, const float* amax_in, float* amax_out,
+                           uint8_t* codes, float* scales, uint32_t* flags, hipStream_t s);
+// U = (1/R) sum_r s_r dec(q_r) -> fp32 [m][ldo]
+hipError_t launch_dequant_sum(const uint8_t* codes, int64_t code_stride, const float* scales,
+                              int64_t scale_stride, int R, int m, int d, int fmt, int scaling,
+                              float* out, int64_t ldo, hipStream_t s);
+
+// Low-rank transform pieces: partials of X U, then out = alpha X + (P c) U^T.
+hipError_t launch_lr_project(const float* x, int64_t ldx, int m, int d, const float* U, int k,
+                             float* ppart, hipStream_t s);
+hipError_t launch_lr_apply(const float* x, int64_t ldx, int m, int d, const float* U, int k,
+                           const float* ppart, const float* coef, int which, float* out,
+                           int64_t ldo, int scaling, uint32_t* amax_slots, hipStream_t s);
+// Column scaling out = x * v[j] (diagonal transform), with optional amax.
+hipError_t launch_diag_apply(const float* x, int64_t ldx, int m, int d, const float* v, float* out,
+                             int64_t ldo, int scaling, uint32_t* amax_slots, hipStream_t s);
+
+// Statistics.
+hipError_t launch_stats(const void* x, int dtype, int64_t T, int64_t ld, int n, float* S,
+                        hipStream_t s);
+hipError_t launch_commit(float* S, float* A, int n, double inv_count, float beta, int first,
+                         hipStream_t s);
+
+// Refresh (rank-k).
+hipError_t launch_refresh_lowrank(const float* A, int d, int k, int l, int q, float damping_rel,
+                                  const float* omega, float* U, float* coef, const WorkLayout& w,
+                                  char* work, uint32_t* flags, hipStream_t s);
+hipError_t launch_refresh_diag(const float* A, int d, float damping_rel, float* coef,
+                               uint32_t* flags, hipStream_t s);
+hipError_t launch_refresh_chol(const float* A, int n, float damping_rel, float* tinv, float* t,
+                               int lower_out, double* work_a, double* work_b, uint32_t* flags,
+                               hipStream_t s);
+
+// Dense fp32 product with a triangular right/left operand:
+//   out = x * M (M [d][d], upper triangular, right side)   side = 0
+//   out = M * x (M [m][m], lower triangular, left side)    side = 1
+hipError_t launch_trmm(const float* x, int64_t ldx, int m, int d, const float* M, int side,
+                       float* out, int64_t ldo, hipStream_t s);
+
+// Profiler: upper / lower boundary hits of one flattened gradient with its
+// local per-tensor amax (already in slot).
+hipError_t launch_hits(const float* g, int64_t n, int fmt, const uint32_t* slot,
+                       unsigned long long* counts, hipStream_t s);
+hipError_t launch_amax_out(const uint32_t* slots, float* amax_out, int64_t n, hipStream_t s);
+hipError_t launch_amax_flat(const float* g, int64_t n, uint32_t* slot, hipStream_t s);
+
+}  // namespace gift

@@ -1,0 +1,258 @@
+// Scale, quantise and dequantise-reduce kernels (byte-bound passes).
+//
+// GIFT 阅读笔记, §前置知识 FP8: s = amax(X) / FP8_MAX, divide by s,
+// quantise, multiply back; Algorithm 1: Scale, Q, AllReduceSum, Dequantize, /N.
+// Tiling: a workgroup of 256 threads (4 wave64s) covers 256 columns of a
+// 128-row band; each lane owns 4 consecutive columns (one 16-byte fp32 load,
+// one 4-byte code store), so a half-wave spans exactly one 128-column scaling
+// tile and per-tile reductions are half-wave shuffles.
+#include "fp8_codec.hpp"
+#include "gift_internal.hpp"
+
+namespace gift {
+
+__global__ void k_fill_u32(uint32_t* __restrict__ p, uint32_t v, size_t n) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (; i < n; i += stride) p[i] = v;
+}
+
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)blocks), dim3(256), 0, s, p, v, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_f32(float* p, float v, size_t n, hipStream_t s) {
+  union { float f; uint32_t u; } c;
+  c.f = v;
+  return launch_fill_u32(reinterpret_cast<uint32_t*>(p), c.u, n, s);
+}
+
+__device__ __forceinline__ uint32_t absbits(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// Max over the 32 lanes of each half-wave.
+__device__ __forceinline__ uint32_t halfwave_max(uint32_t v) {
+  for (int o = 16; o > 0; o >>= 1) v = umax(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+
+// amax of |x| (as uint32 bit patterns: exact and order-independent) per
+// 128 x 128 tile or for the whole tensor.
+__global__ void __launch_bounds__(256) k_amax(const float* __restrict__ x, int64_t ld, int m, int d,
+                                              int scaling, uint32_t* __restrict__ slots) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = blockIdx.x * 256 + lane * 4;
+  const int r0 = blockIdx.y * kBlock;
+  const int r1 = min(m, r0 + kBlock);
+  uint32_t mx = 0;
+  if (col < d) {
+    for (int r = r0 + wave; r < r1; r += 4) {
+      float4 v = *reinterpret_cast<const float4*>(x + (int64_t)r * ld + col);
+      mx = umax(mx, umax(umax(absbits(v.x), absbits(v.y)), umax(absbits(v.z), absbits(v.w))));
+    }
+  }
+  mx = halfwave_max(mx);
+  __shared__ uint32_t red[4][2];
+  if ((lane & 31) == 0) red[wave][lane >> 5] = mx;
+  __syncthreads();
+  if (threadIdx.x < 2) {
+    int h = threadIdx.x;
+    uint32_t v = umax(umax(red[0][h], red[1][h]), umax(red[2][h], red[3][h]));
+    int cb = (blockIdx.x * 256 + h * 128);
+    if (cb < d) {
+      int slot = scaling == 0 ? 0 : blockIdx.y * (int)cdiv(d, kBlock) + cb / kBlock;
+      if (v) atomicMax(slots + slot, v);
+    }
+  }
+}
+
+hipError_t launch_amax(const float* x, int64_t ld, int m, int d, int scaling, uint32_t* slots,
+                       hipStream_t s) {
+  if (m == 0 || d == 0) return hipSuccess;
+  dim3 grid((unsigned)cdiv(d, 256), (unsigned)cdiv(m, kBlock));
+  hipLaunchKernelGGL(k_amax, grid, dim3(256), 0, s, x, ld, m, d, scaling, slots);
+  return hipGetLastError();
+}
+
+template <int FMT>
+__global__ void __launch_bounds__(256) k_quantize(const float* __restrict__ x, int64_t ld, int m, int d,
+                                                  int scaling, const uint32_t* __restrict__ slots,
+                                                  const float* __restrict__ amax_in,
+                                                  float* __restrict__ amax_out, uint8_t* __restrict__ codes,
+                                                  float* __restrict__ scales, uint32_t* __restrict__ flags) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = blockIdx.x * 256 + lane * 4;
+  const int r0 = blockIdx.y * kBlock;
+  const int r1 = min(m, r0 + kBlock);
+  const int nbd = (int)cdiv(d, kBlock);
+  const float fmax = fp8_fmax(FMT);
+  if (col >= d) return;
+  const int slot = scaling == 0 ? 0 : blockIdx.y * nbd + col / kBlock;
+  uint32_t am = amax_in ? absbits(amax_in[slot]) : slots[slot];
+  float r, sc;
+  scale_pair(am, fmax, r, sc);
+  const bool first_of_tile = scaling == 0 ? (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
+                                          : (wave == 0 && (lane & 31) == 0);
+  if (first_of_tile) {
+    scales[slot] = sc;
+    if (amax_out) amax_out[slot] = __uint_as_float(slots[slot]);   // the local amax
+    if (am >= 0x7F800000u) atomicOr(flags, (uint32_t)GIFT_FLAG_NONFINITE);
+  }
+  const bool bad = am >= 0x7F800000u;
+  for (int rr = r0 + wave; rr < r1; rr += 4) {
+    float4 v = *reinterpret_cast<const float4*>(x + (int64_t)rr * ld + col);
+    uint32_t c0, c1, c2, c3;
+    if (bad) {
+      c0 = c1 = c2 = c3 = 0x7Fu;
+    } else {
+      c0 = enc_fp8<FMT>(v.x * r);
+      c1 = enc_fp8<FMT>(v.y * r);
+      c2 = enc_fp8<FMT>(v.z * r);
+      c3 = enc_fp8<FMT>(v.w * r);
+    }
+    *reinterpret_cast<uint32_t*>(codes + (int64_t)rr * d + col) = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+  }
+}
+
+hipError_t launch_quantize(const float* x, int64_t ld, int m, int d, int fmt, int scaling,
+                           const uint32_t* slots, const float* amax_in, float* amax_out,
+                           uint8_t* codes, float* scales, uint32_t* flags, hipStream_t s) {
+  if (m == 0 || d == 0) return hipSuccess;
+  dim3 grid((unsigned)cdiv(d, 256), (unsigned)cdiv(m, kBlock));
+  if (fmt == 0)
+    hipLaunchKernelGGL(k_quantize<0>, grid, dim3(256), 0, s, x, ld, m, d, scaling, slots, amax_in,
+                       amax_out, codes, scales, flags);
+  else
+    hipLaunchKernelGGL(k_quantize<1>, grid, dim3(256), 0, s, x, ld, m, d, scaling, slots, amax_in,
+                       amax_out, codes, scales, flags);
+  return hipGetLastError();
+}
+
+// U = (1/R) sum_r s_r dec(q_r), replicas summed in increasing r.
+template <int FMT>
+__global__ void __launch_bounds__(256) k_dequant_sum(const uint8_t* __restrict__ codes, int64_t code_stride,
+                                                     const float* __restrict__ scales, int64_t scale_stride,
+                                                     int R, int m, int d, int scaling,
+                                                     float* __restrict__ out, int64_t ldo, float invR) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = blockIdx.x * 256 + lane * 4;
+  const int r0 = blockIdx.y * kBlock;
+  const int r1 = min(m, r0 + kBlock);
+  if (col >= d) return;
+  const int slot = scaling == 0 ? 0 : blockIdx.y * (int)cdiv(d, kBlock) + col / kBlock;
+  for (int rr = r0 + wave; rr < r1; rr += 4) {
+    // the sum starts from replica 0's term (not +0), so a lone -0 stays -0
+    const float s0 = scales[slot];
+    const uint32_t q0 = *reinterpret_cast<const uint32_t*>(codes + (int64_t)rr * d + col);
+    float a0 = s0 * dec_fp8<FMT>(q0 & 0xFFu), a1 = s0 * dec_fp8<FMT>((q0 >> 8) & 0xFFu);
+    float a2 = s0 * dec_fp8<FMT>((q0 >> 16) & 0xFFu), a3 = s0 * dec_fp8<FMT>(q0 >> 24);
+    for (int r = 1; r < R; ++r) {
+      const float sc = scales[(int64_t)r * scale_stride + slot];
+      uint32_t c = *reinterpret_cast<const uint32_t*>(codes + (int64_t)r * code_stride + (int64_t)rr * d + col);
+      a0 += sc * dec_fp8<FMT>(c & 0xFFu);
+      a1 += sc * dec_fp8<FMT>((c >> 8) & 0xFFu);
+      a2 += sc * dec_fp8<FMT>((c >> 16) & 0xFFu);
+      a3 += sc * dec_fp8<FMT>(c >> 24);
+    }
+    *reinterpret_cast<float4*>(out + (int64_t)rr * ldo + col) = make_float4(a0 * invR, a1 * invR, a2 * invR, a3 * invR);
+  }
+}
+
+hipError_t launch_dequant_sum(const uint8_t* codes, int64_t code_stride, const float* scales,
+                              int64_t scale_stride, int R, int m, int d, int fmt, int scaling,
+                              float* out, int64_t ldo, hipStream_t s) {
+  if (m == 0 || d == 0) return hipSuccess;
+  dim3 grid((unsigned)cdiv(d, 256), (unsigned)cdiv(m, kBlock));
+  float invR = 1.0f / (float)R;
+  if (fmt == 0)
+    hipLaunchKernelGGL(k_dequant_sum<0>, grid, dim3(256), 0, s, codes, code_stride, scales, scale_stride,
+                       R, m, d, scaling, out, ldo, invR);
+  else
+    hipLaunchKernelGGL(k_dequant_sum<1>, grid, dim3(256), 0, s, codes, code_stride, scales, scale_stride,
+                       R, m, d, scaling, out, ldo, invR);
+  return hipGetLastError();
+}
+
+__global__ void k_amax_out(const uint32_t* __restrict__ slots, float* __restrict__ out, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) out[i] = __uint_as_float(slots[i]);
+}
+
+hipError_t launch_amax_out(const uint32_t* slots, float* amax_out, int64_t n, hipStream_t s) {
+  hipLaunchKernelGGL(k_amax_out, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, slots, amax_out, n);
+  return hipGetLastError();
+}
+
+// ---- profiler: flat amax and boundary-hit counts ----
+
+__global__ void __launch_bounds__(256) k_amax_flat(const float* __restrict__ g, int64_t n, uint32_t* slot) {
+  uint32_t mx = 0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    mx = umax(mx, absbits(g[i]));
+  for (int o = 32; o > 0; o >>= 1) mx = umax(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+  __shared__ uint32_t red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t v = umax(umax(red[0], red[1]), umax(red[2], red[3]));
+    if (v) atomicMax(slot, v);
+  }
+}
+
+hipError_t launch_amax_flat(const float* g, int64_t n, uint32_t* slot, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  int64_t blocks = cdiv(n, 256 * 8);
+  if (blocks > 2048) blocks = 2048;
+  hipLaunchKernelGGL(k_amax_flat, dim3((unsigned)blocks), dim3(256), 0, s, g, n, slot);
+  return hipGetLastError();
+}
+
+template <int FMT>
+__global__ void __launch_bounds__(256) k_hits(const float* __restrict__ g, int64_t n, const uint32_t* slot,
+                                              unsigned long long* counts) {
+  float r, sc;
+  scale_pair(*slot, fp8_fmax(FMT), r, sc);
+  const uint32_t maxc = FMT == 0 ? 0x7Eu : 0x7Bu;
+  uint32_t up = 0, lo = 0;
+  const bool bad = *slot >= 0x7F800000u;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    float x = g[i];
+    uint32_t c = bad ? 0x7Fu : (enc_fp8<FMT>(x * r) & 0x7Fu);
+    up += c == maxc;
+    lo += (c == 0u) && (x != 0.0f);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    up += (uint32_t)__shfl_xor((int)up, o, 64);
+    lo += (uint32_t)__shfl_xor((int)lo, o, 64);
+  }
+  __shared__ uint32_t red[4][2];
+  if ((threadIdx.x & 63) == 0) {
+    red[threadIdx.x >> 6][0] = up;
+    red[threadIdx.x >> 6][1] = lo;
+  }
+  __syncthreads();
+  if (threadIdx.x < 2) {
+    unsigned long long v = (unsigned long long)red[0][threadIdx.x] + red[1][threadIdx.x] + red[2][threadIdx.x] +
+                           red[3][threadIdx.x];
+    if (v) atomicAdd(counts + threadIdx.x, v);
+  }
+}
+
+hipError_t launch_hits(const float* g, int64_t n, int fmt, const uint32_t* slot,
+                       unsigned long long* counts, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  int64_t blocks = cdiv(n, 256 * 8);
+  if (blocks > 2048) blocks = 2048;
+  if (fmt == 0)
+    hipLaunchKernelGGL(k_hits<0>, dim3((unsigned)blocks), dim3(256), 0, s, g, n, slot, counts);
+  else
+    hipLaunchKernelGGL(k_hits<1>, dim3((unsigned)blocks), dim3(256), 0, s, g, n, slot, counts);
+  return hipGetLastError();
+}
+
+}  // namespace gift

@@ -1,0 +1,236 @@
+/*
+ * gift.h -- C ABI of libgift, an MI355X (gfx950) library for the
+ * data-parallel hot path of GIFT: geometry-aware FP8 encode / decode of one
+ * layer's weight gradient.
+ *
+ * Sources (cited by page title and equation / section):
+ *   [Note] "GIFT 阅读笔记:量化用的坐标系,比量化器本身更重要" (zhongzhuzhou.org)
+ *   [Abs]  "GIFT: Geometry-Informed Low-precision Gradient Communication for
+ *          LLM Pretraining" (shd-paper.top abstract page)
+ *
+ * Conventions for every call:
+ *   - Device pointers ("d_") are allocated and owned by the caller; the
+ *     library never allocates or frees device memory.  Host pointers ("h_")
+ *     are read or written during the call only.
+ *   - Matrices are row-major.  A leading dimension ("ld") is in elements and
+ *     must be >= the row length and a multiple of 4 (fp32) or 8 (bf16);
+ *     device pointers must be 16-byte aligned.  d_in must be a multiple of 8.
+ *   - Device work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream) and the call returns without waiting, except where noted.
+ *   - All argument checks happen before anything is enqueued: on any error
+ *     return nothing has been enqueued.  A HIP launch failure returns
+ *     GIFT_ERR_HIP; gift_last_hip_error() then gives the hipError_t.
+ *   - Non-finite data is not reported synchronously: the affected scale is
+ *     written as NaN, its codes as 0x7F, decode propagates NaN, and the
+ *     layer's sticky device flag GIFT_FLAG_NONFINITE is set
+ *     (gift_layer_flags()).
+ *   - Handles are not thread-safe; distinct handles are independent.
+ *     Calls that share a workspace buffer must be ordered on one stream.
+ */
+#ifndef GIFT_H
+#define GIFT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t gift_status;
+typedef void* gift_stream_t;                 /* a hipStream_t */
+typedef struct gift_layer* gift_layer_t;       /* opaque host handle */
+typedef struct gift_profiler* gift_profiler_t; /* opaque host handle */
+
+enum {
+  GIFT_OK = 0,
+  GIFT_ERR_INVALID_ARG = 1, /* bad pointer, shape, stride, alignment or enum */
+  GIFT_ERR_WORKSPACE = 2,   /* state or workspace buffer smaller than required */
+  GIFT_ERR_NOT_READY = 3,   /* encode/decode of a non-Euclidean layer before its first refresh,
+                               or a refresh before any statistics were committed */
+  GIFT_ERR_NUMERICAL = 4,   /* reserved for host-detected numerical failure */
+  GIFT_ERR_UNSUPPORTED = 5, /* valid but not implemented combination */
+  GIFT_ERR_HIP = 6          /* a HIP runtime call failed */
+};
+
+/* Change of coordinates applied before quantisation ([Note] Algorithm 1). */
+enum gift_transform {
+  GIFT_EUCLID = 0,          /* none: the Euclidean FP8 baseline ([Note] Algorithm 1, lines 3-8) */
+  GIFT_DIAG = 1,            /* T_A = diag((A_ii + lam)^-1/2) ([Note] §简化二, Table II "diagonal") */
+  GIFT_LOWRANK = 2,         /* T_A = U diag((Lt)^-1/2 - rho^-1/2) U^T + rho^-1/2 I, rank k
+                               ([Note] §简化二, Eq. (17); the form is this library's reading) */
+  GIFT_CHOL_INPUT = 3,      /* T_A = L_A^-T, A + lam I = L_A L_A^T ([Note] Eq. (7), (16)) */
+  GIFT_CHOL_TWOSIDED = 4    /* W~ = L_G^-1 W L_A^-T ([Note] Eq. (11)); map back Eq. (14) */
+};
+
+enum gift_format { GIFT_E4M3 = 0, GIFT_E5M2 = 1 };          /* [Note] §前置知识, FP8 */
+enum gift_scaling { GIFT_SCALE_TENSOR = 0, GIFT_SCALE_BLOCK128 = 1 };
+enum gift_dtype { GIFT_BF16 = 0, GIFT_FP32 = 1 };
+enum gift_side { GIFT_SIDE_A = 0, GIFT_SIDE_G = 1 };      /* input / output statistics */
+enum { GIFT_FLAG_NONFINITE = 1u, GIFT_FLAG_SPIN_TIMEOUT = 2u };
+
+/* Description of one layer.  d_out x d_in is the shape of W_g. */
+typedef struct gift_layer_desc {
+  int32_t d_out;       /* m, rows of W_g                                   */
+  int32_t d_in;        /* d, columns of W_g; multiple of 8                 */
+  int32_t transform;   /* enum gift_transform                              */
+  int32_t rank;        /* k for GIFT_LOWRANK (32 on the pages), 1..d_in    */
+  int32_t oversample;  /* p: the test matrix has l = min(k + p, d) columns */
+  int32_t power_iters; /* q: re-orthonormalised products after Y = A Omega */
+  float ema_decay;     /* beta in [0, 1): A <- beta A + (1 - beta) A_batch  */
+  float damping_rel;   /* lam = damping_rel * tr(A) / d (also for G)       */
+} gift_layer_desc;
+
+/* ---------------------------------------------------------------------------
+ * Layer state.
+ * gift_layer_state_bytes: bytes of the caller-owned device state buffer for
+ * this layer (statistics A [and G], their EMA, the factor, flags) and the
+ * largest workspace any call on this layer needs.  Both are multiples of 256.
+ * gift_layer_create: binds `d_state` (>= state_bytes, 256-byte aligned) to a
+ * new host handle; enqueues the zeroing of the state on `stream`.
+ * The state is plain device memory: copying it (and the handle's host
+ * counters, see gift_layer_get_counters/gift_layer_set_counters) is a
+ * checkpoint.
+ * ------------------------------------------------------------------------- */
+gift_status gift_layer_state_bytes(const gift_layer_desc* desc, size_t* state_bytes,
+                                   size_t* workspace_bytes);
+gift_status gift_layer_create(const gift_layer_desc* desc, void* d_state, size_t state_bytes,
+                              gift_stream_t stream, gift_layer_t* out);
+gift_status gift_layer_destroy(gift_layer_t layer);
+/* Host-side counters: [0] tokens pending in the A window, [1] tokens pending
+ * in the G window, [2] commits of A, [3] commits of G, [4] refreshes. */
+gift_status gift_layer_get_counters(gift_layer_t layer, int64_t h_counters[5]);
+gift_status gift_layer_set_counters(gift_layer_t layer, const int64_t h_counters[5]);
+/* Reads the sticky device flags (GIFT_FLAG_*).  Synchronises `stream`. */
+gift_status gift_layer_flags(gift_layer_t layer, gift_stream_t stream, uint32_t* h_flags);
+/* Device addresses inside the state buffer, for inspection and for
+ * stage-isolated tests.  Any pointer argument may be NULL.
+ *   A, G:       fp32 [d][d] / [m][m] committed statistics (EMA)
+ *   U:          fp32 [d][k] rank-k basis (GIFT_LOWRANK)
+ *   coef:       fp32 [2k + 4]: c_enc[k], c_dec[k], rho^-1/2, rho^1/2, lam, rho
+ *               (GIFT_LOWRANK); fp32 [2d]: (A_ii+lam)^-1/2, (A_ii+lam)^1/2 (GIFT_DIAG)
+ *   tinv_a:     fp32 [d][d] T_A (= L_A^-T, upper triangular) (Cholesky variants)
+ *   t_a:        fp32 [d][d] T_A^-1 (= L_A^T, upper triangular)
+ *   lg_inv, lg: fp32 [m][m] L_G^-1 and L_G (lower triangular) (two-sided)   */
+gift_status gift_layer_buffers(gift_layer_t layer, float** A, float** G, float** U, float** coef,
+                               float** tinv_a, float** t_a, float** lg_inv, float** lg);
+/* Marks a factor written directly into the state (through gift_layer_buffers)
+ * as valid, so encode/decode accept the layer without a refresh. */
+gift_status gift_layer_mark_ready(gift_layer_t layer);
+
+/* ---------------------------------------------------------------------------
+ * Statistics.  [Note] §前置知识 Eq. (4): A = E[a a^T] over the layer's input
+ * activations a (d_in), G = E[delta delta^T] over output gradients (d_out).
+ *
+ * gift_accumulate_stats: S_side += x^T x for x = d_x [T][ld] (dtype bf16 or
+ * fp32, the first n columns used, n = d_in for side A, d_out for side G),
+ * and adds T to the side's pending-token count.  If `commit` is nonzero the
+ * window is then committed in the same launch (see gift_commit_stats).
+ * T may be 0 (no-op unless commit).
+ * gift_commit_stats: A_batch = S / count; A = A_batch on the first commit,
+ * else A = beta A + (1 - beta) A_batch; S = 0, count = 0.  GIFT_ERR_NOT_READY
+ * if no tokens are pending.
+ * ------------------------------------------------------------------------- */
+gift_status gift_accumulate_stats(gift_layer_t layer, int32_t side, const void* d_x, int32_t dtype,
+                                  int64_t T, int64_t ld, int32_t commit, gift_stream_t stream);
+gift_status gift_commit_stats(gift_layer_t layer, int32_t side, gift_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Factor refresh ([Note] §简化二 Eq. (17); refreshed every K steps, Algorithm 1
+ * preamble).  From the committed A (and G):
+ *   GIFT_DIAG:     the two diagonal vectors.
+ *   GIFT_LOWRANK:  randomized subspace iteration with the caller's test matrix
+ *                  d_omega (fp32 [d_in][l], l = min(rank + oversample, d_in),
+ *                  row-major): Y = A Omega, q times {Q = orth(Y), Y = A Q},
+ *                  Q = orth(Y), Rayleigh-Ritz B = Q^T A Q = V Theta V^T,
+ *                  U = Q V[:, :k]; Lt = max(Theta_k, 0) + lam,
+ *                  rho = max((tr A - sum Theta_k)/(d - k), 0) + lam.
+ *   GIFT_CHOL_*:   L_A = chol(A + lam I) in fp64, T_A = L_A^-T and L_A^T
+ *                  stored in fp32; two-sided also L_G^-1 and L_G.
+ * d_omega may be NULL for the other transforms.  GIFT_ERR_NOT_READY if A
+ * (or G) was never committed.  A non-positive pivot sets
+ * GIFT_FLAG_NONFINITE and leaves a NaN factor.
+ * ------------------------------------------------------------------------- */
+gift_status gift_refresh_factors(gift_layer_t layer, const float* d_omega, void* d_work,
+                                 size_t work_bytes, gift_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Encode one replica's gradient ([Note] Algorithm 1, lines 10-13 without
+ * error feedback; Euclidean lines 4-6):
+ *   W~ = W T_A (two-sided: L_G^-1 W T_A), amax per tensor or per 128x128
+ *   tile (edge tiles: their valid region), r = fp32(FMAX / amax),
+ *   code = FP8(fp32(w~ * r)) with round-to-nearest-even (ties to the even
+ *   code), saturation at +-FMAX (also for +-Inf), NaN -> 0x7F; scale
+ *   s = fp32(amax / FMAX).  amax = 0 gives r = s = 0.
+ * d_W:          fp32 [d_out][ldw]
+ * d_amax_in:    NULL (use the local amax) or fp32 [nblk] shared amax, e.g. the
+ *               max over replicas (the AllReduceMax of Algorithm 1)
+ * d_amax_out:   NULL or fp32 [nblk]: the local amax of W~
+ * d_codes:      uint8 [d_out][d_in]; NULL = only compute d_amax_out
+ * d_scales:     fp32 [nblk]; nblk = 1 (tensor) or ceil(m/128) * ceil(d/128),
+ *               row-major over tiles
+ * d_whitened:   NULL or fp32 [d_out][d_in]: receives W~ (inspection)
+ * d_work:       workspace of >= the layer's workspace_bytes
+ * ------------------------------------------------------------------------- */
+gift_status gift_encode(gift_layer_t layer, const float* d_W, int64_t ldw, int32_t fmt,
+                        int32_t scaling, const float* d_amax_in, float* d_amax_out,
+                        uint8_t* d_codes, float* d_scales, float* d_whitened, void* d_work,
+                        size_t work_bytes, gift_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Decode-reduce R replica payloads ([Note] Eq. (1) and Algorithm 1, lines
+ * 20-22; the payloads of R workers held in one GPU's memory):
+ *   U = (1/R) sum_{r=0..R-1} s_r dec(q_r) (fp32, r in increasing order),
+ *   W^ = U T_A^-1 (two-sided: L_G U L_A^T), written as fp32.
+ * d_codes:      replica r at d_codes + r * code_stride (bytes), [d_out][d_in]
+ * d_scales:     replica r at d_scales + r * scale_stride (elements), [nblk]
+ * d_out:        fp32 [d_out][ldo]
+ * ------------------------------------------------------------------------- */
+gift_status gift_decode_reduce(gift_layer_t layer, const uint8_t* d_codes, int64_t code_stride,
+                               const float* d_scales, int64_t scale_stride, int32_t R,
+                               int32_t fmt, int32_t scaling, float* d_out, int64_t ldo,
+                               void* d_work, size_t work_bytes, gift_stream_t stream);
+
+/* Payload size of one replica: d_out * d_in code bytes + 4 * nblk scale bytes. */
+size_t gift_payload_bytes(int32_t d_out, int32_t d_in, int32_t scaling);
+
+/* ---------------------------------------------------------------------------
+ * FP8 boundary-hit profiler ([Note] §简化三, Fig. 3): over the first steps of
+ * Euclidean training, count per layer how many FP8 codes hit the upper
+ * boundary (|code| = the largest finite code) or the lower one (a nonzero
+ * gradient element encoded as +-0), with each layer's local scale; rank the
+ * layers by the mean hit rate and keep those before the sharp drop.
+ *
+ * gift_profiler_create: d_counts = caller-owned uint64 [n_layers][2]
+ * (upper, lower); zeroing is enqueued on `stream`.
+ * gift_profile_step: one step over n_layers fp32 gradients (device pointers
+ * given in the host array h_grads, h_numel elements each, contiguous).
+ * d_work: >= gift_profiler_workspace_bytes(n_layers, scaling, max numel).
+ * gift_select_layers: synchronises `stream`, reads the counts, writes
+ * h_scores[n_layers] = (upper + lower) / (numel * steps), h_order[n_layers]
+ * (descending score, ties to the lower index), and the selection: the first
+ * i* layers of h_order where i* maximises s_i / s_{i+1} over
+ * 1 <= i <= min(n_layers - 1, max_select) (s_{i+1} = 0 < s_i counts as
+ * infinite, 0/0 as 1, ties to the smallest i).
+ * ------------------------------------------------------------------------- */
+gift_status gift_profiler_create(int32_t n_layers, int32_t fmt, int32_t scaling, uint64_t* d_counts,
+                                 gift_stream_t stream, gift_profiler_t* out);
+gift_status gift_profiler_destroy(gift_profiler_t prof);
+size_t gift_profiler_workspace_bytes(int32_t n_layers, int32_t scaling, int64_t max_numel);
+gift_status gift_profile_step(gift_profiler_t prof, int32_t n_layers, const float* const* h_grads,
+                              const int64_t* h_numel, void* d_work, size_t work_bytes,
+                              gift_stream_t stream);
+gift_status gift_select_layers(gift_profiler_t prof, int32_t max_select, double* h_scores,
+                               int32_t* h_order, int32_t* h_selected, int32_t* h_n_selected,
+                               gift_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Diagnostics.
+ * ------------------------------------------------------------------------- */
+const char* gift_status_string(gift_status s);
+int32_t gift_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GIFT_H */
