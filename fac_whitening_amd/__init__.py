@@ -43,7 +43,7 @@ EXPORTS = [
     "gift_accumulate_stats", "gift_commit_stats", "gift_refresh_factors", "gift_encode",
     "gift_decode_reduce", "gift_payload_bytes", "gift_profiler_create", "gift_profiler_destroy",
     "gift_profiler_workspace_bytes", "gift_profile_step", "gift_select_layers", "gift_status_string",
-    "gift_last_hip_error",
+    "gift_last_hip_error", "gift_set_fused",
 ]
 
 
@@ -71,7 +71,7 @@ _sig("gift_layer_get_counters", _i32, _vp, _P(_i64))
 _sig("gift_layer_set_counters", _i32, _vp, _P(_i64))
 _sig("gift_layer_flags", _i32, _vp, _vp, _P(ctypes.c_uint32))
 _sig("gift_layer_buffers", _i32, _vp, *[_P(_vp)] * 8)
-_sig("gift_layer_mark_ready", _i32, _vp)
+_sig("gift_layer_mark_ready", _i32, _vp, _vp)
 _sig("gift_accumulate_stats", _i32, _vp, _i32, _vp, _i32, _i64, _i64, _i32, _vp)
 _sig("gift_commit_stats", _i32, _vp, _i32, _vp)
 _sig("gift_refresh_factors", _i32, _vp, _vp, _vp, _sz, _vp)
@@ -85,6 +85,13 @@ _sig("gift_profile_step", _i32, _vp, _i32, _P(_vp), _P(_i64), _vp, _sz, _vp)
 _sig("gift_select_layers", _i32, _vp, _i32, _P(ctypes.c_double), _P(_i32), _P(_i32), _P(_i32), _vp)
 _sig("gift_status_string", ctypes.c_char_p, _i32)
 _sig("gift_last_hip_error", _i32)
+_sig("gift_set_fused", _i32, _i32)
+
+
+def set_fused(enable: bool) -> bool:
+    """Select the persistent single-launch rank-k kernels (True, default) or
+    the multi-kernel path (False); returns the previous setting."""
+    return bool(_lib.gift_set_fused(1 if enable else 0))
 
 
 class GiftError(RuntimeError):
@@ -161,12 +168,12 @@ class Layer:
         return self._h
 
     def counters(self):
-        arr = (_i64 * 5)()
+        arr = (_i64 * 7)()
         _check(_lib.gift_layer_get_counters(self._h, arr), "gift_layer_get_counters")
         return list(arr)
 
     def set_counters(self, vals):
-        arr = (_i64 * 5)(*vals)
+        arr = (_i64 * 7)(*vals)
         _check(_lib.gift_layer_set_counters(self._h, arr), "gift_layer_set_counters")
 
     def flags(self, stream=None) -> int:
@@ -194,8 +201,8 @@ class Layer:
             out[n] = self.state[off:off + 4 * cnt].view(torch.float32).view(*shapes[n])
         return out
 
-    def mark_ready(self):
-        _check(_lib.gift_layer_mark_ready(self._h), "gift_layer_mark_ready")
+    def mark_ready(self, stream=None):
+        _check(_lib.gift_layer_mark_ready(self._h, _stream(stream)), "gift_layer_mark_ready")
 
     # -- statistics / refresh --------------------------------------------
     def accumulate_stats(self, x: torch.Tensor, side: int = SIDE_A, commit: bool = False, stream=None):

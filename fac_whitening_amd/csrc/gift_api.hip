@@ -21,7 +21,9 @@ struct gift_layer {
   gift::StateLayout sl;
   gift::WorkLayout wl;
   char* state;
-  int64_t counters[5];   // tokens A, tokens G, commits A, commits G, refreshes
+  // tokens A, tokens G, commits A, commits G, refreshes, fused encode and
+  // decode barrier epochs (the device counters in the state only grow)
+  int64_t counters[7];
   bool ready;
 };
 
@@ -71,6 +73,34 @@ int64_t nblk(int m, int d, int scaling) {
   return scaling == GIFT_SCALE_TENSOR ? 1 : gift::cdiv(m, gift::kBlock) * gift::cdiv(d, gift::kBlock);
 }
 
+int g_fused_enabled = 1;
+
+// Workgroups of the fused rank-k kernels for this shape.
+int fused_groups(const gift_layer_desc& g) { return (int)gift::cdiv(g.d_out, gift::kFusedTR); }
+int fused_cg(const gift_layer_desc& g) { return (int)gift::cdiv(g.d_in, gift::kFusedTC); }
+
+// Compute units of the current device (cached per device id).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// The fused path keeps every tile resident (one 512-thread workgroup per
+// compute unit at most), so it is taken when the tiles fit on the device.
+bool fused_ok(const gift_layer_desc& g) {
+  if (!g_fused_enabled || g.transform != GIFT_LOWRANK) return false;
+  const int64_t tiles = (int64_t)fused_groups(g) * fused_cg(g);
+  const int cus = device_cus();
+  return cus > 0 && tiles <= cus;
+}
+
 }  // namespace
 
 namespace gift {
@@ -98,6 +128,14 @@ StateLayout state_layout(const gift_layer_desc& g) {
   if (g.transform == GIFT_LOWRANK) {
     s.U = take(d * 32 * 4);
     s.coef = take(68 * 4);
+    const size_t ncb = (size_t)cdiv((int64_t)d, 32);
+    s.ub = take(ncb * 6 * 1024);
+    s.ua = take(ncb * 6 * 1024);
+    const size_t ngr = (size_t)fused_groups(g);
+    s.esync = take(ngr * 64);
+    s.dsync = take(ngr * 64);
+    s.hsync = take(512 * 4);
+    s.amax2 = take(2 * (size_t)nblk((int)m, (int)d, GIFT_SCALE_BLOCK128) * 4);
   }
   if (g.transform == GIFT_DIAG) s.coef = take(2 * d * 4);
   if (g.transform == GIFT_CHOL_INPUT || g.transform == GIFT_CHOL_TWOSIDED) {
@@ -126,6 +164,7 @@ WorkLayout work_layout(const gift_layer_desc& g) {
   if (g.transform == GIFT_CHOL_TWOSIDED) w.tmp = take(m * d * 4);
   if (g.transform == GIFT_LOWRANK) {
     w.ppart = take((size_t)cdiv((int64_t)d, kProjChunk) * m * 32 * 4);
+    w.xch = take((size_t)fused_groups(g) * fused_cg(g) * kFusedTR * 32 * 4);
     const size_t lp = (size_t)lp_of(l_of(g));
     w.Y = take(d * lp * 8);
     w.Q = take(d * lp * 8);
@@ -162,6 +201,12 @@ const char* gift_status_string(gift_status s) {
 }
 
 int32_t gift_last_hip_error(void) { return g_last_hip; }
+
+int32_t gift_set_fused(int32_t enable) {
+  const int32_t old = g_fused_enabled;
+  g_fused_enabled = enable ? 1 : 0;
+  return old;
+}
 
 size_t gift_payload_bytes(int32_t d_out, int32_t d_in, int32_t scaling) {
   if (d_out < 0 || d_in < 0) return 0;
@@ -203,15 +248,15 @@ gift_status gift_layer_destroy(gift_layer_t layer) {
   return GIFT_OK;
 }
 
-gift_status gift_layer_get_counters(gift_layer_t L, int64_t h[5]) {
+gift_status gift_layer_get_counters(gift_layer_t L, int64_t h[7]) {
   if (!L || !h) return GIFT_ERR_INVALID_ARG;
   std::memcpy(h, L->counters, sizeof(L->counters));
   return GIFT_OK;
 }
 
-gift_status gift_layer_set_counters(gift_layer_t L, const int64_t h[5]) {
+gift_status gift_layer_set_counters(gift_layer_t L, const int64_t h[7]) {
   if (!L || !h) return GIFT_ERR_INVALID_ARG;
-  for (int i = 0; i < 5; ++i)
+  for (int i = 0; i < 7; ++i)
     if (h[i] < 0) return GIFT_ERR_INVALID_ARG;
   std::memcpy(L->counters, h, sizeof(L->counters));
   L->ready = L->desc.transform == GIFT_EUCLID || h[4] > 0;
@@ -245,8 +290,11 @@ gift_status gift_layer_buffers(gift_layer_t L, float** A, float** G, float** U, 
   return GIFT_OK;
 }
 
-gift_status gift_layer_mark_ready(gift_layer_t L) {
+gift_status gift_layer_mark_ready(gift_layer_t L, gift_stream_t stream) {
   if (!L) return GIFT_ERR_INVALID_ARG;
+  if (L->desc.transform == GIFT_LOWRANK)
+    GIFT_HIP(gift::launch_pack_u(reinterpret_cast<const float*>(L->state + L->sl.U), L->desc.d_in, L->state + L->sl.ub,
+                                 L->state + L->sl.ua, static_cast<hipStream_t>(stream)));
   L->ready = true;
   return GIFT_OK;
 }
@@ -321,6 +369,8 @@ gift_status gift_refresh_factors(gift_layer_t L, const float* d_omega, void* d_w
       GIFT_HIP(gift::launch_refresh_lowrank(A, g.d_in, g.rank, l_of(g), g.power_iters, g.damping_rel, d_omega,
                                             reinterpret_cast<float*>(L->state + L->sl.U),
                                             reinterpret_cast<float*>(L->state + L->sl.coef), L->wl, work, flags, s));
+      GIFT_HIP(gift::launch_pack_u(reinterpret_cast<const float*>(L->state + L->sl.U), g.d_in, L->state + L->sl.ub,
+                                   L->state + L->sl.ua, s));
       break;
     }
     case GIFT_CHOL_INPUT:
@@ -369,6 +419,39 @@ gift_status gift_encode(gift_layer_t L, const float* d_W, int64_t ldw, int32_t f
   uint32_t* slots = reinterpret_cast<uint32_t*>(work + L->wl.amax);
   uint32_t* flags = reinterpret_cast<uint32_t*>(L->state + L->sl.flags);
   const int64_t nb = nblk(m, d, scaling);
+  if (fused_ok(g)) {
+    gift::FusedArgs a{};
+    a.mode = 0;
+    a.m = m;
+    a.d = d;
+    a.CG = fused_cg(g);
+    a.fmt = fmt;
+    a.scaling = scaling;
+    a.nslots = (int)nblk(m, d, GIFT_SCALE_BLOCK128);
+    a.epoch = (unsigned)(++L->counters[5]);
+    a.W = d_W;
+    a.ldw = ldw;
+    a.ub = reinterpret_cast<const uint4*>(L->state + L->sl.ub);
+    a.ua = reinterpret_cast<const uint4*>(L->state + L->sl.ua);
+    a.coef = reinterpret_cast<const float*>(L->state + L->sl.coef);
+    a.xch = reinterpret_cast<float*>(work + L->wl.xch);
+    a.gsync = reinterpret_cast<unsigned*>(L->state + L->sl.esync);
+    a.hsync = reinterpret_cast<unsigned*>(L->state + L->sl.hsync);
+    a.amax_slots = reinterpret_cast<uint32_t*>(L->state + L->sl.amax2);
+    a.flags = flags;
+    a.amax_in = d_amax_in;
+    a.amax_out = d_amax_out;
+    a.codes = d_codes;
+    a.scales = d_scales;
+    a.whitened = d_whitened;
+    const int grid = fused_groups(g) * a.CG;
+    hipError_t e = gift::launch_fused(a, grid, s);
+    if (e != hipSuccess) {
+      --L->counters[5];
+      return hip_fail(e);
+    }
+    return GIFT_OK;
+  }
   GIFT_HIP(gift::launch_fill_u32(slots, 0u, (size_t)nb, s));
   const float* X = d_W;
   int64_t ldx = ldw;
@@ -446,6 +529,38 @@ gift_status gift_decode_reduce(gift_layer_t L, const uint8_t* d_codes, int64_t c
   if (g.transform == GIFT_EUCLID) {
     GIFT_HIP(gift::launch_dequant_sum(d_codes, code_stride, d_scales, scale_stride, R, m, d, fmt, scaling, d_out, ldo,
                                       s));
+    return GIFT_OK;
+  }
+  if (fused_ok(g)) {
+    gift::FusedArgs a{};
+    a.mode = 1;
+    a.m = m;
+    a.d = d;
+    a.CG = fused_cg(g);
+    a.fmt = fmt;
+    a.scaling = scaling;
+    a.R = R;
+    a.epoch = (unsigned)(++L->counters[6]);
+    a.ub = reinterpret_cast<const uint4*>(L->state + L->sl.ub);
+    a.ua = reinterpret_cast<const uint4*>(L->state + L->sl.ua);
+    a.coef = reinterpret_cast<const float*>(L->state + L->sl.coef);
+    a.xch = reinterpret_cast<float*>(work + L->wl.xch);
+    a.gsync = reinterpret_cast<unsigned*>(L->state + L->sl.dsync);
+    a.hsync = reinterpret_cast<unsigned*>(L->state + L->sl.hsync);
+    a.flags = reinterpret_cast<uint32_t*>(L->state + L->sl.flags);
+    a.qcodes = d_codes;
+    a.code_stride = code_stride;
+    a.qscales = d_scales;
+    a.scale_stride = scale_stride;
+    a.invR = 1.0f / (float)R;
+    a.out = d_out;
+    a.ldo = ldo;
+    const int grid = fused_groups(g) * a.CG;
+    hipError_t e = gift::launch_fused(a, grid, s);
+    if (e != hipSuccess) {
+      --L->counters[6];
+      return hip_fail(e);
+    }
     return GIFT_OK;
   }
   float* Ub = reinterpret_cast<float*>(work + L->wl.tile);

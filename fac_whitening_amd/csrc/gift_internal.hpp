@@ -19,7 +19,42 @@ __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 
 struct StateLayout {
   size_t S_A = 0, A = 0, S_G = 0, G = 0, U = 0, coef = 0, tinv_a = 0, t_a = 0, lg_inv = 0, lg = 0,
          flags = 0, total = 0;
+  // fused rank-k path: packed U operands, barrier counters, amax slots
+  size_t ub = 0, ua = 0, esync = 0, dsync = 0, hsync = 0, amax2 = 0;
 };
+
+// Fused rank-k kernel geometry (48 x 768 tiles, 8 waves).
+constexpr int kFusedTR = 48, kFusedTC = 768;
+
+// Arguments of the fused encode (mode 0) / decode-reduce (mode 1) kernel.
+struct FusedArgs {
+  int mode, m, d, CG, fmt, scaling, R, nslots;
+  unsigned epoch;
+  const float* W;
+  int64_t ldw;
+  const uint4* ub;
+  const uint4* ua;
+  const float* coef;
+  float* xch;
+  unsigned* gsync;
+  unsigned* hsync;
+  uint32_t* amax_slots;
+  unsigned* flags;
+  const float* amax_in;
+  float* amax_out;
+  uint8_t* codes;
+  float* scales;
+  float* whitened;
+  const uint8_t* qcodes;
+  int64_t code_stride;
+  const float* qscales;
+  int64_t scale_stride;
+  float invR;
+  float* out;
+  int64_t ldo;
+};
+hipError_t launch_fused(const FusedArgs& args, int grid, hipStream_t s);
+hipError_t launch_pack_u(const float* U, int d, void* ub, void* ua, hipStream_t s);
 
 // Offsets (bytes) inside the per-call workspace.  Regions overlap between
 // calls of different kinds (encode / decode / refresh never run at once on
@@ -30,6 +65,7 @@ struct WorkLayout {
   size_t tmp = 0;       // fp32 [m][d]: second buffer (two-sided)
   size_t ppart = 0;     // fp32 [nchunk][m][k]: projection partials
   size_t amax = 0;      // uint32 [nblk]
+  size_t xch = 0;       // fp32 [tiles][48][32]: fused-path projection partials
   // refresh
   size_t Y = 0, Q = 0, Z = 0;   // fp64 [d][l]
   size_t small = 0;             // fp64 scratch for the l x l solvers

@@ -98,9 +98,11 @@ gift_status gift_layer_create(const gift_layer_desc* desc, void* d_state, size_t
                               gift_stream_t stream, gift_layer_t* out);
 gift_status gift_layer_destroy(gift_layer_t layer);
 /* Host-side counters: [0] tokens pending in the A window, [1] tokens pending
- * in the G window, [2] commits of A, [3] commits of G, [4] refreshes. */
-gift_status gift_layer_get_counters(gift_layer_t layer, int64_t h_counters[5]);
-gift_status gift_layer_set_counters(gift_layer_t layer, const int64_t h_counters[5]);
+ * in the G window, [2] commits of A, [3] commits of G, [4] refreshes,
+ * [5] / [6] barrier epochs of the fused rank-k encode / decode (they must
+ * travel with a copy of the state: the state's barrier counters only grow). */
+gift_status gift_layer_get_counters(gift_layer_t layer, int64_t h_counters[7]);
+gift_status gift_layer_set_counters(gift_layer_t layer, const int64_t h_counters[7]);
 /* Reads the sticky device flags (GIFT_FLAG_*).  Synchronises `stream`. */
 gift_status gift_layer_flags(gift_layer_t layer, gift_stream_t stream, uint32_t* h_flags);
 /* Device addresses inside the state buffer, for inspection and for
@@ -115,8 +117,10 @@ gift_status gift_layer_flags(gift_layer_t layer, gift_stream_t stream, uint32_t*
 gift_status gift_layer_buffers(gift_layer_t layer, float** A, float** G, float** U, float** coef,
                                float** tinv_a, float** t_a, float** lg_inv, float** lg);
 /* Marks a factor written directly into the state (through gift_layer_buffers)
- * as valid, so encode/decode accept the layer without a refresh. */
-gift_status gift_layer_mark_ready(gift_layer_t layer);
+ * as valid, so encode/decode accept the layer without a refresh; for
+ * GIFT_LOWRANK it enqueues the repacking of U into the kernel operand
+ * order on `stream`. */
+gift_status gift_layer_mark_ready(gift_layer_t layer, gift_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Statistics.  [Note] §前置知识 Eq. (4): A = E[a a^T] over the layer's input
@@ -229,6 +233,16 @@ gift_status gift_select_layers(gift_profiler_t prof, int32_t max_select, double*
  * ------------------------------------------------------------------------- */
 const char* gift_status_string(gift_status s);
 int32_t gift_last_hip_error(void);
+/* Process-wide choice of the GIFT_LOWRANK kernels: nonzero (the default)
+ * uses the single-launch persistent kernels whenever every 48 x 768 tile of
+ * the gradient fits on the device at once (one 512-thread workgroup per
+ * compute unit); zero always uses the multi-kernel path (project, apply,
+ * amax, quantise / dequantise-sum, project, apply).  Both give results
+ * within the same tolerances; the persistent kernels keep the tile in
+ * registers and read the gradient once.  Returns the previous setting.
+ * Calls on one layer must be ordered on one stream (the persistent kernels
+ * synchronise their workgroups through counters in the layer state). */
+int32_t gift_set_fused(int32_t enable);
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,152 @@
+"""The persistent rank-k kernels (one launch per direction) against the oracle
+and against the multi-kernel path, on ragged multi-tile shapes.
+
+Pages: GIFT 阅读笔记 §简化二 Eq. (17) (rank-32 factor), Eq. (16) (input-side
+whitening), Algorithm 1 (scale, quantise, reduce, map back).  The factor is
+the oracle's, written into the layer state (stage isolation), so every
+difference comes from the whitening / quantisation / reduction kernels.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import gift as G
+from tests.helpers import assert_codes, rel_fro
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def fw():
+    import fac_whitening_amd as fw
+    yield fw
+    fw.set_fused(True)
+
+
+def _case(m, d, R, seed):
+    """Power-law activations (rotated), W_r = delta_r^T a_r / T, oracle factor."""
+    rng = np.random.default_rng(seed)
+    big = d > 2000                 # keep the host-side draw cheap: no rotation, T = 2048
+    T = 2048 if big else max(2 * d, 512)
+    Q = np.eye(d) if big else np.linalg.qr(rng.standard_normal((d, d)))[0]
+    sd = np.arange(1, d + 1) ** -0.75
+    a0 = ((rng.standard_normal((T, d)) * sd) @ Q.T).astype(np.float32)
+    A = G.second_moment(a0)
+    om = rng.standard_normal((d, 48)).astype(np.float32)
+    fac = G.lowrank_factor(A, om, 32, 4, G.damping(A))
+    Ws = []
+    for r in range(R):
+        a = a0 if r == 0 else ((rng.standard_normal((T, d)) * sd) @ Q.T).astype(np.float32)
+        dl = (rng.standard_normal((T, m)) * np.arange(1, m + 1) ** -0.5).astype(np.float32)
+        Ws.append((dl.T.astype(np.float64) @ a.astype(np.float64) / T).astype(np.float32))
+    return Ws, fac
+
+
+def _layer_with_factor(fw, m, d, fac):
+    L = fw.Layer(m, d, "lowrank", device=DEV)
+    b = L.buffers()
+    b["U"].copy_(torch.from_numpy(fac["U"].astype(np.float32)))
+    coef = np.zeros(68, np.float32)
+    coef[:32] = fac["c_enc"]
+    coef[32:64] = fac["c_dec"]
+    coef[64], coef[65] = fac["rho"] ** -0.5, fac["rho"] ** 0.5
+    b["coef"].copy_(torch.from_numpy(coef))
+    L.mark_ready()
+    return L
+
+
+SHAPES = [(100, 1000), (200, 1544), (48, 768), (1536, 6144)]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("scaling", ["tensor", "block"])
+@pytest.mark.parametrize("fused", [True, False])
+def test_lowrank_paths_against_oracle(fw, shape, scaling, fused):
+    m, d = shape
+    R = 3
+    print(f"[lowrank {shape} {scaling} fused={fused}]", flush=True)
+    fw.set_fused(fused)
+    Ws, fac = _case(m, d, R, seed=m + d)
+    T, Tinv = G.transform_lowrank(fac)
+    L = _layer_with_factor(fw, m, d, fac)
+    s = fw.SCALINGS[scaling]
+    nb = fw.nblocks(m, d, s)
+    codes, scales = [], []
+    for r, w in enumerate(Ws):
+        whit = torch.empty(m, d, device=DEV) if r == 0 else None
+        am = torch.empty(nb, device=DEV) if r == 0 else None
+        c, sc = L.encode(torch.from_numpy(w).to(DEV), 0, s, whitened=whit, amax_out=am)
+        codes.append(c)
+        scales.append(sc)
+        if r == 0:
+            e = G.encode(w, T, "e4m3", scaling)
+            err = rel_fro(whit.cpu().numpy(), e["whitened"])
+            assert err <= 1e-5, f"whitened rel err {err:.3e}"
+            assert_codes(c.cpu().numpy(), e["codes"])
+            # scales and amax are those of the GPU's own whitened tensor
+            cq, sq, amq = G.quantize(whit.cpu().numpy(), "e4m3", scaling)
+            assert np.array_equal(sc.cpu().numpy(), sq.ravel())
+            assert np.array_equal(am.cpu().numpy(), amq.ravel().astype(np.float32))
+            assert np.array_equal(c.cpu().numpy(), cq)
+    out = L.decode_reduce(torch.stack(codes), torch.stack(scales), 0, s)
+    ref = G.decode_reduce([c.cpu().numpy() for c in codes], [x.cpu().numpy().reshape(G.nblocks(m, d, scaling))
+                                                             for x in scales], Tinv, "e4m3", scaling)
+    err = rel_fro(out.cpu().numpy(), ref)
+    assert err <= 1e-5, f"decode (same payloads) rel err {err:.3e}"
+    assert L.flags() == 0
+
+
+def test_fused_equals_multikernel_and_is_repeatable(fw):
+    m, d = 1536, 6144
+    print("[fused vs multi-kernel, repeated calls]", flush=True)
+    Ws, fac = _case(m, d, 2, seed=7)
+    W = torch.from_numpy(Ws[0]).to(DEV)
+    outs = {}
+    payload = None
+    for fused in (False, True):
+        fw.set_fused(fused)
+        L = _layer_with_factor(fw, m, d, fac)
+        whit = torch.empty(m, d, device=DEV)
+        c, s = L.encode(W, 0, 0, whitened=whit)
+        if payload is None:
+            payload = (c.clone(), s.clone())   # both paths decode the same payload
+        o = L.decode_reduce(payload[0].unsqueeze(0), payload[1].reshape(1, 1), 0, 0)
+        outs[fused] = (whit.clone(), c.clone(), s.clone(), o.clone())
+        c, s = payload
+        if fused:
+            c1, s1 = outs[True][1], outs[True][2]
+            for it in range(25):   # barrier epochs advance; results stay identical
+                c2, s2 = L.encode(W, 0, 0)
+                o2 = L.decode_reduce(c, s.reshape(1, 1), 0, 0)
+                assert torch.equal(c2, c1) and torch.equal(s2, s1) and torch.equal(o2, o), it
+            assert L.counters()[5] == 26 and L.counters()[6] == 26
+        assert L.flags() == 0
+    assert rel_fro(outs[True][0].cpu().numpy(), outs[False][0].cpu().numpy()) <= 2e-6
+    assert_codes(outs[True][1].cpu().numpy(), outs[False][1].cpu().numpy())
+    assert rel_fro(outs[True][3].cpu().numpy(), outs[False][3].cpu().numpy()) <= 1e-5
+
+
+@pytest.mark.parametrize("scaling", ["tensor", "block"])
+def test_fused_shared_amax(fw, scaling):
+    """amax_in (the AllReduceMax result) drives the scale; amax_out still
+    reports the local amax."""
+    m, d = 200, 1544
+    print(f"[fused shared amax {scaling}]", flush=True)
+    fw.set_fused(True)
+    Ws, fac = _case(m, d, 1, seed=11)
+    L = _layer_with_factor(fw, m, d, fac)
+    s = fw.SCALINGS[scaling]
+    nb = fw.nblocks(m, d, s)
+    W = torch.from_numpy(Ws[0]).to(DEV)
+    whit = torch.empty(m, d, device=DEV)
+    local = torch.empty(nb, device=DEV)
+    L.encode(W, 0, s, whitened=whit, amax_out=local)
+    shared = local * 1.75
+    c, sc = L.encode(W, 0, s, amax_in=shared)
+    cq, sq, _ = G.quantize(whit.cpu().numpy(), "e4m3", scaling,
+                           amax_in=shared.cpu().numpy().astype(np.float64).reshape(G.nblocks(m, d, scaling)))
+    assert np.array_equal(c.cpu().numpy(), cq) and np.array_equal(sc.cpu().numpy(), sq.ravel())
+    local2 = torch.empty(nb, device=DEV)
+    L.encode(W, 0, s, amax_in=shared, amax_out=local2)
+    assert torch.equal(local2, local)
