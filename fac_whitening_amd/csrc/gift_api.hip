@@ -134,8 +134,7 @@ StateLayout state_layout(const gift_layer_desc& g) {
     const size_t ngr = (size_t)fused_groups(g);
     s.esync = take(ngr * 64);
     s.dsync = take(ngr * 64);
-    s.hsync = take(512 * 4);
-    s.amax2 = take(2 * (size_t)nblk((int)m, (int)d, GIFT_SCALE_BLOCK128) * 4);
+    s.apub = take(((size_t)fused_groups(g) * fused_cg(g) * 17 + 16) * 8);   // [tiles][16] + group words
   }
   if (g.transform == GIFT_DIAG) s.coef = take(2 * d * 4);
   if (g.transform == GIFT_CHOL_INPUT || g.transform == GIFT_CHOL_TWOSIDED) {
@@ -427,7 +426,7 @@ gift_status gift_encode(gift_layer_t L, const float* d_W, int64_t ldw, int32_t f
     a.CG = fused_cg(g);
     a.fmt = fmt;
     a.scaling = scaling;
-    a.nslots = (int)nblk(m, d, GIFT_SCALE_BLOCK128);
+
     a.epoch = (unsigned)(++L->counters[5]);
     a.W = d_W;
     a.ldw = ldw;
@@ -436,8 +435,8 @@ gift_status gift_encode(gift_layer_t L, const float* d_W, int64_t ldw, int32_t f
     a.coef = reinterpret_cast<const float*>(L->state + L->sl.coef);
     a.xch = reinterpret_cast<float*>(work + L->wl.xch);
     a.gsync = reinterpret_cast<unsigned*>(L->state + L->sl.esync);
-    a.hsync = reinterpret_cast<unsigned*>(L->state + L->sl.hsync);
-    a.amax_slots = reinterpret_cast<uint32_t*>(L->state + L->sl.amax2);
+
+    a.apub = reinterpret_cast<unsigned long long*>(L->state + L->sl.apub);
     a.flags = flags;
     a.amax_in = d_amax_in;
     a.amax_out = d_amax_out;
@@ -531,7 +530,7 @@ gift_status gift_decode_reduce(gift_layer_t L, const uint8_t* d_codes, int64_t c
                                       s));
     return GIFT_OK;
   }
-  if (fused_ok(g)) {
+  if (fused_ok(g) && R <= 64) {   // the kernel stages up to 64 replicas' scales
     gift::FusedArgs a{};
     a.mode = 1;
     a.m = m;
@@ -546,7 +545,7 @@ gift_status gift_decode_reduce(gift_layer_t L, const uint8_t* d_codes, int64_t c
     a.coef = reinterpret_cast<const float*>(L->state + L->sl.coef);
     a.xch = reinterpret_cast<float*>(work + L->wl.xch);
     a.gsync = reinterpret_cast<unsigned*>(L->state + L->sl.dsync);
-    a.hsync = reinterpret_cast<unsigned*>(L->state + L->sl.hsync);
+
     a.flags = reinterpret_cast<uint32_t*>(L->state + L->sl.flags);
     a.qcodes = d_codes;
     a.code_stride = code_stride;

@@ -20,7 +20,7 @@ struct StateLayout {
   size_t S_A = 0, A = 0, S_G = 0, G = 0, U = 0, coef = 0, tinv_a = 0, t_a = 0, lg_inv = 0, lg = 0,
          flags = 0, total = 0;
   // fused rank-k path: packed U operands, barrier counters, amax slots
-  size_t ub = 0, ua = 0, esync = 0, dsync = 0, hsync = 0, amax2 = 0;
+  size_t ub = 0, ua = 0, esync = 0, dsync = 0, apub = 0;
 };
 
 // Fused rank-k kernel geometry (48 x 768 tiles, 8 waves).
@@ -28,17 +28,16 @@ constexpr int kFusedTR = 48, kFusedTC = 768;
 
 // Arguments of the fused encode (mode 0) / decode-reduce (mode 1) kernel.
 struct FusedArgs {
-  int mode, m, d, CG, fmt, scaling, R, nslots;
+  int mode, m, d, CG, fmt, scaling, R;
   unsigned epoch;
   const float* W;
   int64_t ldw;
   const uint4* ub;
   const uint4* ua;
   const float* coef;
-  float* xch;
-  unsigned* gsync;
-  unsigned* hsync;
-  uint32_t* amax_slots;
+  float* xch;                 // workspace: projection partials [tiles][48][32]
+  unsigned* gsync;            // state: one grow-only counter per row group (64 B apart)
+  unsigned long long* apub;   // state: [tiles][16] epoch-tagged amax words
   unsigned* flags;
   const float* amax_in;
   float* amax_out;

@@ -9,7 +9,8 @@
 //  * One workgroup (8 waves) owns a 48 x 768 tile of the gradient and keeps it
 //    in registers from the first load to the last store: the tensor is read
 //    from HBM once.  A tile is 3 x 24 sub-tiles of 16 rows x 32 columns; wave
-//    w owns the sub-tiles (rb, w + 8 q), rb, q in 0..2.
+//    w owns the 3 column blocks w, w + 8, w + 16 in all 3 row blocks, so each
+//    packed U operand a wave loads serves three sub-tiles.
 //  * In a sub-tile, lane l holds row l % 16 and columns 4 g .. 4 g + 3 and
 //    16 + 4 g .. 16 + 4 g + 3 (g = l / 16).  These eight values are the A
 //    operand of the projection MFMA (16x16x32 bf16, with U_k's rows permuted
@@ -22,13 +23,13 @@
 //  * P needs whole rows: the workgroups of one row group (same 48 rows)
 //    publish their partial P through device-scope atomics in the workspace,
 //    meet at a counter barrier, and sum the partials in a fixed order.
-//  * Encode: a per-tensor (or per-128x128) amax needs every tile: workgroups
-//    combine amax with device-scope atomicMax and meet at a two-level
-//    barrier (one counter per id % 8 group, then one top counter).
-//  * Counters live in the layer state and only grow: barrier number e waits
-//    for count >= members * e (wrap-safe), so nothing is reset between calls.
-//    Every wait is bounded; a timeout sets GIFT_FLAG_SPIN_TIMEOUT and the
-//    kernel still exits.
+//  * Encode: every workgroup publishes its tile's amax (per tensor, or per
+//    128 x 128 block it touches) as 64-bit words tagged with the call's
+//    epoch, and reads the words of the workgroups it depends on until all
+//    carry the current epoch (an all-gather: no serial chain of atomics).
+//  * Counters and tags live in the layer state and only grow, so nothing is
+//    reset between calls.  Every wait is bounded; a timeout sets
+//    GIFT_FLAG_SPIN_TIMEOUT and the kernel still exits.
 #include "fp8_codec.hpp"
 #include "gift_internal.hpp"
 
@@ -42,7 +43,7 @@ constexpr int kSpinLimit = 1 << 20;
 __device__ __forceinline__ unsigned ld_dev(const unsigned* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float ldf_dev(const float* p) {
+__device__ __forceinline__ unsigned long long ld_dev64(const unsigned long long* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -57,6 +58,21 @@ __device__ __forceinline__ void wait_reach(const unsigned* p, unsigned target, u
   }
 }
 
+// Wait until the 64-bit word carries `epoch` in its upper half; return it.
+__device__ __forceinline__ unsigned long long wait_tag(const unsigned long long* p, unsigned epoch,
+                                                       unsigned* flags) {
+  unsigned long long v = ld_dev64(p);
+  int spins = 0;
+  while ((unsigned)(v >> 32) != epoch) {
+    if (++spins > kSpinLimit) {
+      atomicOr(flags, (unsigned)GIFT_FLAG_SPIN_TIMEOUT);
+      break;
+    }
+    v = ld_dev64(p);
+  }
+  return v;
+}
+
 __device__ __forceinline__ uint32_t absbits_f(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
 
 __device__ __forceinline__ void split3(float x, __bf16& h, __bf16& m, __bf16& l) {
@@ -68,6 +84,18 @@ __device__ __forceinline__ void split3(float x, __bf16& h, __bf16& m, __bf16& l)
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Buffer resources: loads outside [0, bytes) return 0 and stores there are
+// dropped, so edge tiles need no branches around their memory operations
+// (branches would force a full wait on every outstanding load).
+typedef int int32x4 __attribute__((ext_vector_type(4)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kOff = (int)0x80000000u;   // an offset past any buffer used here
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)(uint32_t)bytes, kRsrcWord3);
+}
 
 // Column of sub-tile position (g, j) in the permuted operand order.
 __device__ __forceinline__ int perm_col(int g, int j) { return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4); }
@@ -115,13 +143,73 @@ hipError_t launch_pack_u(const float* U, int d, void* ub, void* ua, hipStream_t 
 // The fused kernel
 // ---------------------------------------------------------------------------
 
-constexpr int TR = 48, TC = 768, NSUB = 9;
+constexpr int TR = kFusedTR, TC = kFusedTC, NSUB = 9;
+constexpr int kApub = 16;   // published amax words per workgroup
 
+// Decode the 4 codes of one 32-bit word.
+template <int FMT>
+__device__ __forceinline__ void dec4(uint32_t w, float* v) {
+  float2v lo, hi;
+  if constexpr (FMT == 0) {
+    lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  } else {
+    lo = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
+    hi = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, true);
+  }
+  v[0] = lo[0];
+  v[1] = lo[1];
+  v[2] = hi[0];
+  v[3] = hi[1];
+}
+
+// Sub-tile i of wave w: column block cb = w + 8 (i / 3), row block rb = i % 3.
+#define SUB_RB(i) ((i) % 3)
+#define SUB_CB(i) (wave + 8 * ((i) / 3))
+
+// Flat streaming of a tile: 8-element chunks, chunk q of the tile is row
+// q / 96, columns 8 (q % 96) .. + 7; thread t owns chunks t + 512 j.
+constexpr int kTilePad = TC + 4;            // LDS row stride of the staged tile (floats)
+constexpr int kCPT = TR * TC / 8 / 512;     // chunks per thread (9)
+constexpr int kMaxRFused = 64;              // replicas whose scales are staged in LDS
+
+typedef int int32x2 __attribute__((ext_vector_type(2)));
+
+template <int FMT>
+__device__ __forceinline__ void load_chunks(const FusedArgs& a, int r, const int* off, int32x2* dst) {
+  const auto q = make_rsrc(a.qcodes + (int64_t)r * a.code_stride, (int64_t)a.m * a.d);
+#pragma unroll
+  for (int j = 0; j < kCPT; ++j) dst[j] = __builtin_amdgcn_raw_buffer_load_b64(q, off[j], 0, 0);
+}
+
+template <int FMT>
+__device__ __forceinline__ void accum_chunks(float (*acc)[8], const int32x2* c, const float* ssc_r, const int* sidx,
+                                             bool first) {
+#pragma unroll
+  for (int j = 0; j < kCPT; ++j) {
+    float v[8];
+    dec4<FMT>((uint32_t)c[j][0], v);
+    dec4<FMT>((uint32_t)c[j][1], v + 4);
+    const float s = ssc_r[sidx[j]];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[j][k] = first ? s * v[k] : acc[j][k] + s * v[k];
+  }
+}
+
+template <int FMT>
 __global__ void __launch_bounds__(512)
 k_fused(FusedArgs a) {
-  __shared__ float cp[8][3][16][33];   // per-wave projection partials
-  __shared__ float pf[TR][33];         // full projection of the tile rows, times c
-  __shared__ uint32_t wmax[8];
+  // The staged tile (fp32, padded rows); after it has been read into
+  // registers the same memory holds the per-wave projection partials and the
+  // projection of the tile rows, and finally the outgoing tile.
+  __shared__ float smem[TR * kTilePad];
+  __shared__ float ssc[kMaxRFused][12];   // decode scales of the tile's blocks
+  __shared__ uint32_t blk[2][8];          // combined amax of the blocks of this tile
+  __shared__ uint32_t wmax[16];
+  __shared__ float srs[12];               // reciprocal scales of those blocks
+  __shared__ uint32_t sam[12];            // the amax bits they come from
+  float (*cp)[3][16][33] = reinterpret_cast<float (*)[3][16][33]>(smem);
+  float (*pf)[33] = reinterpret_cast<float (*)[33]>(smem + 8 * 3 * 16 * 33);
   const int G = gridDim.x;
   const int g = blockIdx.x, rg = g / a.CG, cgi = g % a.CG;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -129,74 +217,82 @@ k_fused(FusedArgs a) {
   const int row0 = rg * TR, col0 = cgi * TC;
   const int m = a.m, d = a.d;
   const bool enc = a.mode == 0;
+  const int nbd = (int)cdiv(d, kBlock);
+  const int rb0 = row0 / kBlock, cb0 = col0 / kBlock;
 
   float x[NSUB][8];
-  bool live[NSUB];
+  bool live[3];
 #pragma unroll
-  for (int i = 0; i < NSUB; ++i) {
-    const int rb = i / 3, cb = wave + 8 * (i % 3);
-    live[i] = col0 + cb * 32 < d && row0 + rb * 16 < m;
-  }
+  for (int q = 0; q < 3; ++q) live[q] = col0 + (wave + 8 * q) * 32 < d;
 
-  // ---- load (encode) or dequantise-reduce (decode) the tile -----------------
+  // ---- stream the tile in (flat, coalesced) and stage it in LDS --------------
   if (enc) {
+    const auto wr = make_rsrc(a.W, ((int64_t)(m - 1) * a.ldw + d) * 4);
+    int32x4 v[2 * kCPT];
 #pragma unroll
-    for (int i = 0; i < NSUB; ++i) {
-      const int rb = i / 3, cb = wave + 8 * (i % 3);
-      const int row = row0 + rb * 16 + lr, c = col0 + cb * 32 + 4 * lg;
-      float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
-      if (row < m) {
-        const float* p = a.W + (int64_t)row * a.ldw;
-        if (c < d) v0 = *reinterpret_cast<const float4*>(p + c);
-        if (c + 16 < d) v1 = *reinterpret_cast<const float4*>(p + c + 16);
-      }
-      x[i][0] = v0.x; x[i][1] = v0.y; x[i][2] = v0.z; x[i][3] = v0.w;
-      x[i][4] = v1.x; x[i][5] = v1.y; x[i][6] = v1.z; x[i][7] = v1.w;
+    for (int j = 0; j < 2 * kCPT; ++j) {
+      const int q = tid + 512 * j, r = q / 192, c = (q % 192) * 4;
+      const bool ok = row0 + r < m && col0 + c < d;
+      v[j] = __builtin_amdgcn_raw_buffer_load_b128(wr, ok ? (int)(((int64_t)(row0 + r) * a.ldw + col0 + c) * 4) : kOff,
+                                                   0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 2 * kCPT; ++j) {
+      const int q = tid + 512 * j, r = q / 192, c = (q % 192) * 4;
+      *reinterpret_cast<int32x4*>(smem + r * kTilePad + c) = v[j];
     }
   } else {
-    const int nbd = (int)cdiv(d, kBlock);
-    for (int r = 0; r < a.R; ++r) {
-      const uint8_t* q = a.qcodes + (int64_t)r * a.code_stride;
-      const float* sr = a.qscales + (int64_t)r * a.scale_stride;
-      uint32_t w0[NSUB], w1[NSUB];
-      float sc[NSUB];
-#pragma unroll
-      for (int i = 0; i < NSUB; ++i) {
-        const int rb = i / 3, cb = wave + 8 * (i % 3);
-        const int row = row0 + rb * 16 + lr, c = col0 + cb * 32 + 4 * lg;
-        w0[i] = 0u;
-        w1[i] = 0u;
-        if (row < m) {
-          const uint8_t* p = q + (int64_t)row * d;
-          if (c < d) w0[i] = *reinterpret_cast<const uint32_t*>(p + c);
-          if (c + 16 < d) w1[i] = *reinterpret_cast<const uint32_t*>(p + c + 16);
-        }
-        const int slot = a.scaling == 0 ? 0 : ((row0 + rb * 16) / kBlock) * nbd + (col0 + cb * 32) / kBlock;
-        sc[i] = live[i] ? sr[slot] : 0.f;
-      }
-#pragma unroll
-      for (int i = 0; i < NSUB; ++i) {
-        float v[8];
-        if (a.fmt == 0) {
-          v[0] = __builtin_amdgcn_cvt_f32_fp8((int)w0[i], 0); v[1] = __builtin_amdgcn_cvt_f32_fp8((int)w0[i], 1);
-          v[2] = __builtin_amdgcn_cvt_f32_fp8((int)w0[i], 2); v[3] = __builtin_amdgcn_cvt_f32_fp8((int)w0[i], 3);
-          v[4] = __builtin_amdgcn_cvt_f32_fp8((int)w1[i], 0); v[5] = __builtin_amdgcn_cvt_f32_fp8((int)w1[i], 1);
-          v[6] = __builtin_amdgcn_cvt_f32_fp8((int)w1[i], 2); v[7] = __builtin_amdgcn_cvt_f32_fp8((int)w1[i], 3);
-        } else {
-          v[0] = __builtin_amdgcn_cvt_f32_bf8((int)w0[i], 0); v[1] = __builtin_amdgcn_cvt_f32_bf8((int)w0[i], 1);
-          v[2] = __builtin_amdgcn_cvt_f32_bf8((int)w0[i], 2); v[3] = __builtin_amdgcn_cvt_f32_bf8((int)w0[i], 3);
-          v[4] = __builtin_amdgcn_cvt_f32_bf8((int)w1[i], 0); v[5] = __builtin_amdgcn_cvt_f32_bf8((int)w1[i], 1);
-          v[6] = __builtin_amdgcn_cvt_f32_bf8((int)w1[i], 2); v[7] = __builtin_amdgcn_cvt_f32_bf8((int)w1[i], 3);
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[i][j] = (r == 0) ? sc[i] * v[j] : x[i][j] + sc[i] * v[j];
+    // scales of the tile's blocks, per replica, into LDS
+    const int R = a.R;
+    if (a.scaling == 0) {
+      for (int r = tid; r < R; r += 512) ssc[r][0] = a.qscales[(int64_t)r * a.scale_stride];
+    } else {
+      const int nbm = (int)cdiv(m, kBlock);
+      for (int t = tid; t < R * 12; t += 512) {
+        const int r = t / 12, e = t % 12, br = rb0 + e / 6, bc = cb0 + e % 6;
+        ssc[r][e] = (br < nbm && bc < nbd) ? a.qscales[(int64_t)r * a.scale_stride + br * nbd + bc] : 0.f;
       }
     }
+    int off[kCPT], sidx[kCPT];
 #pragma unroll
-    for (int i = 0; i < NSUB; ++i)
+    for (int j = 0; j < kCPT; ++j) {
+      const int q = tid + 512 * j, r = q / 96, c = (q % 96) * 8;
+      const bool ok = row0 + r < m && col0 + c < d;
+      off[j] = ok ? (row0 + r) * d + col0 + c : kOff;
+      sidx[j] = a.scaling == 0 ? 0 : ((row0 + r) / kBlock - rb0) * 6 + (col0 + c) / kBlock - cb0;
+    }
+    __syncthreads();
+    float acc[kCPT][8];
+    int32x2 ca[kCPT], cb[kCPT];
+    load_chunks<FMT>(a, 0, off, ca);
+    for (int r = 0; r < R; r += 2) {
+      if (r + 1 < R) load_chunks<FMT>(a, r + 1, off, cb);
+      accum_chunks<FMT>(acc, ca, ssc[r], sidx, r == 0);
+      if (r + 1 >= R) break;
+      if (r + 2 < R) load_chunks<FMT>(a, r + 2, off, ca);
+      accum_chunks<FMT>(acc, cb, ssc[r + 1], sidx, false);
+    }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[i][j] *= a.invR;
+    for (int j = 0; j < kCPT; ++j) {
+      const int q = tid + 512 * j, r = q / 96, c = (q % 96) * 8;
+      float* dst = smem + r * kTilePad + c;
+      *reinterpret_cast<float4*>(dst) =
+          make_float4(acc[j][0] * a.invR, acc[j][1] * a.invR, acc[j][2] * a.invR, acc[j][3] * a.invR);
+      *reinterpret_cast<float4*>(dst + 4) =
+          make_float4(acc[j][4] * a.invR, acc[j][5] * a.invR, acc[j][6] * a.invR, acc[j][7] * a.invR);
+    }
   }
+  __syncthreads();
+  // each lane takes its sub-tile layout out of the staged tile
+#pragma unroll
+  for (int i = 0; i < NSUB; ++i) {
+    const float* src = smem + (SUB_RB(i) * 16 + lr) * kTilePad + SUB_CB(i) * 32 + 4 * lg;
+    const float4 v0 = *reinterpret_cast<const float4*>(src);
+    const float4 v1 = *reinterpret_cast<const float4*>(src + 16);
+    x[i][0] = v0.x; x[i][1] = v0.y; x[i][2] = v0.z; x[i][3] = v0.w;
+    x[i][4] = v1.x; x[i][5] = v1.y; x[i][6] = v1.z; x[i][7] = v1.w;
+  }
+  __syncthreads();
 
   // ---- projection P = X U (partials of this tile) ---------------------------
   floatx4 acc[3][2];
@@ -205,31 +301,40 @@ k_fused(FusedArgs a) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) acc[rb][h] = (floatx4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < NSUB; ++i) {
-    if (!live[i]) continue;
-    const int rb = i / 3, cb = wave + 8 * (i % 3);
-    const int cbg = (col0 >> 5) + cb;
-    bf16x8 xh, xm, xl;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      __bf16 h, mm, l;
-      split3(x[i][j], h, mm, l);
-      xh[j] = h;
-      xm[j] = mm;
-      xl[j] = l;
-    }
+  for (int q = 0; q < 3; ++q) {
+    if (!live[q]) continue;
+    const int cbg = (col0 >> 5) + wave + 8 * q;
+    bf16x8 u[2][3];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint4* ub = a.ub + ((int64_t)(cbg * 2 + h) * 3) * 64 + lane;
-      const bf16x8 uh = as_bf16x8(ub[0]), um = as_bf16x8(ub[64]), ul = as_bf16x8(ub[128]);
-      floatx4 c = acc[rb][h];
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xm, um, c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, ul, c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, uh, c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, um, c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xm, uh, c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, uh, c, 0, 0, 0);
-      acc[rb][h] = c;
+      u[h][0] = as_bf16x8(ub[0]);
+      u[h][1] = as_bf16x8(ub[64]);
+      u[h][2] = as_bf16x8(ub[128]);
+    }
+#pragma unroll
+    for (int rb = 0; rb < 3; ++rb) {
+      const int i = q * 3 + rb;
+      bf16x8 xh, xm, xl;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        __bf16 h, mm, l;
+        split3(x[i][j], h, mm, l);
+        xh[j] = h;
+        xm[j] = mm;
+        xl[j] = l;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        floatx4 c = acc[rb][h];
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xm, u[h][1], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, u[h][2], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, u[h][0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, u[h][1], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xm, u[h][0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, u[h][0], c, 0, 0, 0);
+        acc[rb][h] = c;
+      }
     }
   }
 #pragma unroll
@@ -239,14 +344,22 @@ k_fused(FusedArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) cp[wave][rb][4 * lg + e][lr + 16 * h] = acc[rb][h][e];
   __syncthreads();
-  // sum the 8 waves (fixed order) and publish this tile's partial
-  float* xg = a.xch + (int64_t)g * TR * 32;
-  for (int e = tid; e < TR * 32; e += 512) {
-    const int r = e >> 5, k = e & 31;
-    float s = cp[0][r >> 4][r & 15][k];
+  // sum the 8 waves (fixed order) and publish this tile's partial: 768
+  // 64-bit words, each an exchange at device scope
+  {
+    unsigned long long* xg = reinterpret_cast<unsigned long long*>(a.xch + (int64_t)g * TR * 32);
+    for (int e = tid; e < TR * 16; e += 512) {
+      const int r = e >> 4, k = (e & 15) * 2;
+      float s0 = cp[0][r >> 4][r & 15][k], s1 = cp[0][r >> 4][r & 15][k + 1];
 #pragma unroll
-    for (int w = 1; w < 8; ++w) s += cp[w][r >> 4][r & 15][k];
-    atomicExch(xg + e, s);
+      for (int w = 1; w < 8; ++w) {
+        s0 += cp[w][r >> 4][r & 15][k];
+        s1 += cp[w][r >> 4][r & 15][k + 1];
+      }
+      const unsigned long long v = (unsigned long long)__float_as_uint(s0) |
+                                   ((unsigned long long)__float_as_uint(s1) << 32);
+      atomicExch(xg + e, v);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -257,13 +370,32 @@ k_fused(FusedArgs a) {
   }
   __syncthreads();
   // the row group's partials, summed in column-group order, times c
-  const float* cvec = a.coef + (enc ? 0 : 32);
-  for (int e = tid; e < TR * 32; e += 512) {
-    const int r = e >> 5, k = e & 31;
-    const float* src = a.xch + ((int64_t)rg * a.CG * TR) * 32 + e;
-    float s = ldf_dev(src);
-    for (int h = 1; h < a.CG; ++h) s += ldf_dev(src + (int64_t)h * TR * 32);
-    pf[r][k] = s * cvec[k];
+  {
+    const float* cvec = a.coef + (enc ? 0 : 32);
+    const unsigned long long* base =
+        reinterpret_cast<const unsigned long long*>(a.xch + (int64_t)rg * a.CG * TR * 32);
+    for (int e = tid; e < TR * 16; e += 512) {
+      unsigned long long v[16];
+      const int cg = a.CG;
+#pragma unroll
+      for (int h = 0; h < 16; ++h) v[h] = h < cg ? ld_dev64(base + (int64_t)h * TR * 16 + e) : 0ull;
+      float s0 = __uint_as_float((uint32_t)v[0]), s1 = __uint_as_float((uint32_t)(v[0] >> 32));
+#pragma unroll
+      for (int h = 1; h < 16; ++h) {
+        if (h < cg) {
+          s0 += __uint_as_float((uint32_t)v[h]);
+          s1 += __uint_as_float((uint32_t)(v[h] >> 32));
+        }
+      }
+      for (int h = 16; h < cg; ++h) {   // more than 16 column groups (d > 12288)
+        const unsigned long long w = ld_dev64(base + (int64_t)h * TR * 16 + e);
+        s0 += __uint_as_float((uint32_t)w);
+        s1 += __uint_as_float((uint32_t)(w >> 32));
+      }
+      const int r = e >> 4, k = (e & 15) * 2;
+      pf[r][k] = s0 * cvec[k];
+      pf[r][k + 1] = s1 * cvec[k + 1];
+    }
   }
   __syncthreads();
 
@@ -282,59 +414,69 @@ k_fused(FusedArgs a) {
     }
   }
 #pragma unroll
-  for (int i = 0; i < NSUB; ++i) {
-    if (!live[i]) continue;
-    const int rb = i / 3, cb = wave + 8 * (i % 3);
-    const int cbg = (col0 >> 5) + cb;
+  for (int q = 0; q < 3; ++q) {
+    if (!live[q]) continue;
+    const int cbg = (col0 >> 5) + wave + 8 * q;
 #pragma unroll
     for (int grp = 0; grp < 2; ++grp) {
       const uint4* ua = a.ua + ((int64_t)(cbg * 2 + grp) * 3) * 64 + lane;
       const bf16x8 uh = as_bf16x8(ua[0]), um = as_bf16x8(ua[64]), ul = as_bf16x8(ua[128]);
-      floatx4 c = (floatx4){alpha * x[i][4 * grp], alpha * x[i][4 * grp + 1], alpha * x[i][4 * grp + 2],
-                            alpha * x[i][4 * grp + 3]};
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(um, pm[rb], c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uh, pl[rb], c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ul, ph[rb], c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uh, pm[rb], c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(um, ph[rb], c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uh, ph[rb], c, 0, 0, 0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[i][4 * grp + e] = c[e];
+      for (int rb = 0; rb < 3; ++rb) {
+        const int i = q * 3 + rb;
+        floatx4 c = (floatx4){alpha * x[i][4 * grp], alpha * x[i][4 * grp + 1], alpha * x[i][4 * grp + 2],
+                              alpha * x[i][4 * grp + 3]};
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(um, pm[rb], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uh, pl[rb], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ul, ph[rb], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uh, pm[rb], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(um, ph[rb], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uh, ph[rb], c, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[i][4 * grp + e] = c[e];
+      }
     }
   }
 
   if (!enc) {
     // ---- decode: store W^ --------------------------------------------------
+    __syncthreads();   // everyone is done with pf (aliased by the tile)
 #pragma unroll
     for (int i = 0; i < NSUB; ++i) {
-      const int rb = i / 3, cb = wave + 8 * (i % 3);
-      const int row = row0 + rb * 16 + lr, c = col0 + cb * 32 + 4 * lg;
-      if (row >= m) continue;
-      float* p = a.out + (int64_t)row * a.ldo;
-      if (c < d) *reinterpret_cast<float4*>(p + c) = make_float4(x[i][0], x[i][1], x[i][2], x[i][3]);
-      if (c + 16 < d) *reinterpret_cast<float4*>(p + c + 16) = make_float4(x[i][4], x[i][5], x[i][6], x[i][7]);
+      float* dst = smem + (SUB_RB(i) * 16 + lr) * kTilePad + SUB_CB(i) * 32 + 4 * lg;
+      *reinterpret_cast<float4*>(dst) = make_float4(x[i][0], x[i][1], x[i][2], x[i][3]);
+      *reinterpret_cast<float4*>(dst + 16) = make_float4(x[i][4], x[i][5], x[i][6], x[i][7]);
+    }
+    __syncthreads();
+    const auto orr = make_rsrc(a.out, ((int64_t)(m - 1) * a.ldo + d) * 4);
+#pragma unroll
+    for (int j = 0; j < 2 * kCPT; ++j) {
+      const int q = tid + 512 * j, r = q / 192, c = (q % 192) * 4;
+      const bool ok = row0 + r < m && col0 + c < d;
+      const int32x4 v = *reinterpret_cast<const int32x4*>(smem + r * kTilePad + c);
+      __builtin_amdgcn_raw_buffer_store_b128(v, orr, ok ? (int)(((int64_t)(row0 + r) * a.ldo + col0 + c) * 4) : kOff,
+                                             0, 0);
     }
     return;
   }
 
   // ---- encode: inspection copy, amax, scale, quantise -----------------------
   if (a.whitened) {
+    const auto wh = make_rsrc(a.whitened, (int64_t)m * d * 4);
 #pragma unroll
     for (int i = 0; i < NSUB; ++i) {
-      const int rb = i / 3, cb = wave + 8 * (i % 3);
-      const int row = row0 + rb * 16 + lr, c = col0 + cb * 32 + 4 * lg;
-      if (row >= m) continue;
-      float* p = a.whitened + (int64_t)row * d;
-      if (c < d) *reinterpret_cast<float4*>(p + c) = make_float4(x[i][0], x[i][1], x[i][2], x[i][3]);
-      if (c + 16 < d) *reinterpret_cast<float4*>(p + c + 16) = make_float4(x[i][4], x[i][5], x[i][6], x[i][7]);
+      const int row = row0 + SUB_RB(i) * 16 + lr, c = col0 + SUB_CB(i) * 32 + 4 * lg;
+      const int o = (row * d + c) * 4;
+      const int32x4 v0 = {__float_as_int(x[i][0]), __float_as_int(x[i][1]), __float_as_int(x[i][2]), __float_as_int(x[i][3])};
+      const int32x4 v1 = {__float_as_int(x[i][4]), __float_as_int(x[i][5]), __float_as_int(x[i][6]), __float_as_int(x[i][7])};
+      __builtin_amdgcn_raw_buffer_store_b128(v0, wh, (row < m && c < d) ? o : kOff, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(v1, wh, (row < m && c + 16 < d) ? o + 64 : kOff, 0, 0);
     }
   }
-  const int nbd = (int)cdiv(d, kBlock);
-  const unsigned par = a.epoch & 1u;
-  uint32_t* slots = a.amax_slots + (size_t)par * a.nslots;
-  uint32_t* other = a.amax_slots + (size_t)(par ^ 1u) * a.nslots;
-  uint32_t tmax = 0;     // the wave's max over its sub-tiles (per-tensor)
-  uint32_t smax[NSUB];   // per sub-tile (per-block)
+  // Blocks this tile touches: rows row0 .. row0 + 47 lie in at most two
+  // 128-row blocks (rb0, rb0 + 1); columns col0 .. col0 + 767 in the six
+  // 128-column blocks cb0 .. cb0 + 5 (col0 is a multiple of 768).
+  uint32_t smax[NSUB];
 #pragma unroll
   for (int i = 0; i < NSUB; ++i) {
     uint32_t v = 0;
@@ -348,65 +490,117 @@ k_fused(FusedArgs a) {
       v = v > u ? v : u;
     }
     smax[i] = v;
-    tmax = tmax > v ? tmax : v;
   }
-  const bool need_sync = a.amax_in == nullptr || a.amax_out != nullptr;
-  if (need_sync) {
-    if (a.scaling == 0) {
-      if (lane == 0) wmax[wave] = tmax;
-      __syncthreads();
-      if (tid == 0) {
-        uint32_t v = wmax[0];
-        for (int w = 1; w < 8; ++w) v = v > wmax[w] ? v : wmax[w];
-        if (v) atomicMax(slots, v);
-        if (g == 0) atomicExch(other, 0u);
-      }
-    } else if (lane == 0) {
+  // local amax of this tile, per block entry (2 x 6) or per tensor (entry 0)
+  if (tid < 16) wmax[tid] = 0u;
+  __syncthreads();
+  if (lane == 0) {
 #pragma unroll
-      for (int i = 0; i < NSUB; ++i) {
-        if (!live[i]) continue;
-        const int rb = i / 3, cb = wave + 8 * (i % 3);
-        const int slot = ((row0 + rb * 16) / kBlock) * nbd + (col0 + cb * 32) / kBlock;
-        if (smax[i]) atomicMax(slots + slot, smax[i]);
-        atomicExch(other + slot, 0u);
-      }
+    for (int i = 0; i < NSUB; ++i) {
+      if (!live[i / 3] || smax[i] == 0u) continue;
+      const int e = a.scaling == 0 ? 0
+                                   : ((row0 + SUB_RB(i) * 16) / kBlock - rb0) * 6 + (col0 + SUB_CB(i) * 32) / kBlock - cb0;
+      atomicMax(&wmax[e], smax[i]);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) {
-      const int x8 = g & 7;
-      const unsigned nsub = G < 8 ? (unsigned)G : 8u;
-      const unsigned nx = (unsigned)((G - x8 + 7) / 8);
-      unsigned* hs = a.hsync;
-      const unsigned s1 = atomicAdd(hs + x8 * 16, 1u) + 1u;
-      if (s1 == nx * a.epoch) {
-        const unsigned s2 = atomicAdd(hs + 128, 1u) + 1u;
-        if (s2 == nsub * a.epoch)
-          for (unsigned y = 0; y < nsub; ++y) atomicExch(hs + 144 + y * 16, a.epoch);
+  }
+  __syncthreads();
+  const bool need_sync = a.amax_in == nullptr || a.amax_out != nullptr;
+  if (tid < 16) blk[tid >> 3][tid & 7] = 0u;
+  __syncthreads();
+  if (need_sync) {
+    unsigned long long* pub = a.apub;
+    const unsigned long long tag = (unsigned long long)a.epoch << 32;
+    // the tag makes each word self-validating: no ordering with other data
+    // is needed.  The words are published with atomic exchanges, which take
+    // effect at the device's coherence point at once (a plain device-scope
+    // store became visible to other dies only microseconds later).
+    if (a.scaling == 0) {
+      // per tensor: one word per workgroup in a compact array, so a single
+      // wave reads all of them with a few coalesced loads per round
+      unsigned long long* pt = pub + (int64_t)G * kApub;
+      if (tid == 0) atomicExch(pt + g, tag | wmax[0]);
+      if (wave == 0) {
+        uint32_t v = 0;
+        for (int base = 0; base < G; base += 256) {
+          unsigned long long w[4];
+          int spins = 0;
+          for (;;) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int h = base + lane + 64 * j;
+              w[j] = h < G ? ld_dev64(pt + h) : tag;
+            }
+            bool ok = true;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ok = ok && (unsigned)(w[j] >> 32) == a.epoch;
+            if (__all(ok)) break;
+            if (++spins > kSpinLimit) {
+              if (lane == 0) atomicOr(a.flags, (unsigned)GIFT_FLAG_SPIN_TIMEOUT);
+              break;
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v = v > (uint32_t)w[j] ? v : (uint32_t)w[j];
+        }
+        for (int o = 32; o > 0; o >>= 1) {
+          const uint32_t u = (uint32_t)__shfl_xor((int)v, o, 64);
+          v = v > u ? v : u;
+        }
+        if (lane == 0) blk[0][0] = v;
       }
-      wait_reach(hs + 144 + x8 * 16, a.epoch, a.flags);
+    } else {
+      if (tid < kApub) atomicExch(pub + (int64_t)g * kApub + tid, tag | wmax[tid]);
+      // the tiles of this column group whose rows meet blocks rb0, rb0 + 1
+      const int r_lo = (rb0 * kBlock) / TR;
+      const int r_hi = min((int)cdiv(m, TR) - 1, ((rb0 + 2) * kBlock - 1) / TR);
+      const int nr = r_hi - r_lo + 1;
+      for (int t = tid; t < nr * 12; t += 512) {
+        const int rr = r_lo + t / 12, e = t % 12;
+        const int h = rr * a.CG + cgi;
+        const unsigned long long w = wait_tag(pub + (int64_t)h * kApub + e, a.epoch, a.flags);
+        const int brow = (rr * TR) / kBlock + e / 6;   // global block row of that entry
+        const int slot_r = brow - rb0;
+        if (slot_r >= 0 && slot_r < 2 && (uint32_t)w) atomicMax(&blk[slot_r][e % 6], (uint32_t)w);
+      }
     }
     __syncthreads();
   }
-  const float fmax = fp8_fmax(a.fmt);
+  // scale pair of every block entry of this tile (entry 0 per tensor);
+  // the workgroup holding a block's top-left sub-tile writes its scale and
+  // local amax
+  const float fmax = fp8_fmax(FMT);
+  if (tid < 12 && (a.scaling != 0 || tid == 0)) {
+    const int br = rb0 + tid / 6, bc = cb0 + tid % 6;
+    // blocks rb0 and cb0 .. cb0 + 5 always meet the tile; rb0 + 1 may not
+    const bool inside = br * kBlock < m && bc * kBlock < d && br * kBlock < row0 + TR;
+    srs[tid] = 0.0f;
+    sam[tid] = 0u;
+    if (inside) {
+      const int slot = a.scaling == 0 ? 0 : br * nbd + bc;
+      const uint32_t local = blk[tid / 6][tid % 6];
+      const uint32_t am = a.amax_in ? absbits_f(a.amax_in[slot]) : local;
+      float r, sc;
+      scale_pair(am, fmax, r, sc);
+      srs[tid] = r;
+      sam[tid] = am;
+      const bool leader = a.scaling == 0 ? g == 0 : (br * kBlock >= row0 && bc * kBlock >= col0);
+      if (leader) {
+        if (a.scales) a.scales[slot] = sc;
+        if (a.amax_out) a.amax_out[slot] = __uint_as_float(local);
+        if (am >= 0x7F800000u) atomicOr(a.flags, (unsigned)GIFT_FLAG_NONFINITE);
+      }
+    }
+  }
+  __syncthreads();   // the tile memory now receives the codes
+  if (!a.codes) return;
 #pragma unroll
   for (int i = 0; i < NSUB; ++i) {
-    if (!live[i]) continue;
-    const int rb = i / 3, cb = wave + 8 * (i % 3);
-    const int row = row0 + rb * 16 + lr, c = col0 + cb * 32 + 4 * lg;
-    const int slot = a.scaling == 0 ? 0 : ((row0 + rb * 16) / kBlock) * nbd + (col0 + cb * 32) / kBlock;
-    const uint32_t local = need_sync ? ld_dev(slots + slot) : 0u;
-    const uint32_t am = a.amax_in ? absbits_f(a.amax_in[slot]) : local;
-    float r, s;
-    scale_pair(am, fmax, r, s);
-    const bool leader = (row0 + rb * 16) % kBlock == 0 && (col0 + cb * 32) % kBlock == 0 && lane == 0 &&
-                        (a.scaling != 0 || (g == 0 && i == 0 && wave == 0));
-    if (leader) {
-      a.scales[slot] = s;
-      if (a.amax_out) a.amax_out[slot] = __uint_as_float(local);
-      if (am >= 0x7F800000u) atomicOr(a.flags, (unsigned)GIFT_FLAG_NONFINITE);
-    }
-    if (!a.codes || row >= m) continue;
+    if (!live[i / 3]) continue;
+    const int rbl = SUB_RB(i), cbl = SUB_CB(i);
+    const int e = a.scaling == 0 ? 0
+                                 : ((row0 + rbl * 16) / kBlock - rb0) * 6 + (col0 + cbl * 32) / kBlock - cb0;
+    const float r = srs[e];
+    const uint32_t am = sam[e];
     uint32_t q0, q1;
     if (am >= 0x7F800000u) {
       q0 = q1 = 0x7F7F7F7Fu;
@@ -414,14 +608,14 @@ k_fused(FusedArgs a) {
       // a non-finite element under a finite shared amax: exact integer path
       uint32_t e[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) e[j] = a.fmt == 0 ? enc_e4m3(x[i][j] * r) : enc_e5m2(x[i][j] * r);
+      for (int j = 0; j < 8; ++j) e[j] = enc_fp8<FMT>(x[i][j] * r);
       q0 = e[0] | (e[1] << 8) | (e[2] << 16) | (e[3] << 24);
       q1 = e[4] | (e[5] << 8) | (e[6] << 16) | (e[7] << 24);
     } else {
       float y[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) y[j] = __builtin_amdgcn_fmed3f(x[i][j] * r, fmax, -fmax);
-      if (a.fmt == 0) {
+      if constexpr (FMT == 0) {
         q0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
         q0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)q0, true);
         q1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
@@ -433,14 +627,26 @@ k_fused(FusedArgs a) {
         q1 = __builtin_amdgcn_cvt_pk_bf8_f32(y[6], y[7], (int)q1, true);
       }
     }
-    uint8_t* p = a.codes + (int64_t)row * d;
-    if (c < d) *reinterpret_cast<uint32_t*>(p + c) = q0;
-    if (c + 16 < d) *reinterpret_cast<uint32_t*>(p + c + 16) = q1;
+    uint8_t* cs = reinterpret_cast<uint8_t*>(smem) + (rbl * 16 + lr) * (TC + 16) + cbl * 32 + 4 * lg;
+    *reinterpret_cast<uint32_t*>(cs) = q0;
+    *reinterpret_cast<uint32_t*>(cs + 16) = q1;
+  }
+  __syncthreads();
+  const auto cr = make_rsrc(a.codes, (int64_t)m * d);
+#pragma unroll
+  for (int j = 0; j < kCPT; ++j) {
+    const int q = tid + 512 * j, r = q / 96, c = (q % 96) * 8;
+    const bool ok = row0 + r < m && col0 + c < d;
+    const int32x2 v = *reinterpret_cast<const int32x2*>(reinterpret_cast<const uint8_t*>(smem) + r * (TC + 16) + c);
+    __builtin_amdgcn_raw_buffer_store_b64(v, cr, ok ? (row0 + r) * d + col0 + c : kOff, 0, 0);
   }
 }
 
 hipError_t launch_fused(const FusedArgs& args, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(k_fused, dim3((unsigned)grid), dim3(512), 0, s, args);
+  if (args.fmt == 0)
+    hipLaunchKernelGGL(k_fused<0>, dim3((unsigned)grid), dim3(512), 0, s, args);
+  else
+    hipLaunchKernelGGL(k_fused<1>, dim3((unsigned)grid), dim3(512), 0, s, args);
   return hipGetLastError();
 }
 
