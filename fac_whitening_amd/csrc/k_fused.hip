@@ -196,9 +196,8 @@ __device__ __forceinline__ void accum_chunks(float (*acc)[8], const int32x2* c, 
   }
 }
 
-template <int FMT>
-__global__ void __launch_bounds__(512)
-k_fused(FusedArgs a) {
+template <int FMT, bool ENC>
+__device__ __forceinline__ void fused_body(const FusedArgs& a) {
   // The staged tile (fp32, padded rows); after it has been read into
   // registers the same memory holds the per-wave projection partials and the
   // projection of the tile rows, and finally the outgoing tile.
@@ -216,7 +215,7 @@ k_fused(FusedArgs a) {
   const int lr = lane & 15, lg = lane >> 4;
   const int row0 = rg * TR, col0 = cgi * TC;
   const int m = a.m, d = a.d;
-  const bool enc = a.mode == 0;
+  constexpr bool enc = ENC;
   const int nbd = (int)cdiv(d, kBlock);
   const int rb0 = row0 / kBlock, cb0 = col0 / kBlock;
 
@@ -642,11 +641,29 @@ k_fused(FusedArgs a) {
   }
 }
 
+// One kernel per direction and format (distinct names in traces).
+template <int FMT>
+__global__ void __launch_bounds__(512) k_rank_encode(FusedArgs a) {
+  fused_body<FMT, true>(a);
+}
+template <int FMT>
+__global__ void __launch_bounds__(512) k_rank_decode(FusedArgs a) {
+  fused_body<FMT, false>(a);
+}
+
 hipError_t launch_fused(const FusedArgs& args, int grid, hipStream_t s) {
-  if (args.fmt == 0)
-    hipLaunchKernelGGL(k_fused<0>, dim3((unsigned)grid), dim3(512), 0, s, args);
-  else
-    hipLaunchKernelGGL(k_fused<1>, dim3((unsigned)grid), dim3(512), 0, s, args);
+  const dim3 gd((unsigned)grid), bd(512);
+  if (args.mode == 0) {
+    if (args.fmt == 0)
+      hipLaunchKernelGGL(k_rank_encode<0>, gd, bd, 0, s, args);
+    else
+      hipLaunchKernelGGL(k_rank_encode<1>, gd, bd, 0, s, args);
+  } else {
+    if (args.fmt == 0)
+      hipLaunchKernelGGL(k_rank_decode<0>, gd, bd, 0, s, args);
+    else
+      hipLaunchKernelGGL(k_rank_decode<1>, gd, bd, 0, s, args);
+  }
   return hipGetLastError();
 }
 
