@@ -106,8 +106,10 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    # timed region: events around every call on the stream the kernels use
-    enc_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # timed region: HIP events around every call of the dominant kernel
+    # (decode-reduce), on the stream the kernels use (torch's current
+    # stream).  Each event adds about 2.5 us to the step, so only the
+    # dominant call is bracketed.
     dec_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -115,9 +117,7 @@ def main():
     start.record()
     for i in range(args.steps):
         W, codes, scales, out = sets[i % len(sets)]
-        enc_ev[i][0].record()
         L.encode(W, fw.E4M3, scaling, codes=codes[0], scales=scales[0])
-        enc_ev[i][1].record()
         dec_ev[i][0].record()
         L.decode_reduce(codes, scales, fw.E4M3, scaling, out=out)
         dec_ev[i][1].record()
@@ -125,8 +125,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(stop)
-    t_enc = float(np.mean([a.elapsed_time(b) for a, b in enc_ev]))
     t_dec = float(np.mean([a.elapsed_time(b) for a, b in dec_ev]))
+    t_enc = total_ms / args.steps - t_dec     # the rest of the step: encode and the event gaps
     ms_per_step = total_ms / args.steps
     grad_bytes = 4.0 * m * d
     value = grad_bytes / (ms_per_step * 1e-3) / 1e9         # GB/s of fp32 gradient
@@ -136,16 +136,16 @@ def main():
     u_bytes = d * k * 4 + 68 * 4
     enc_bytes = 4.0 * m * d + u_bytes + m * d + 4 * nb
     dec_bytes = R * (m * d + 4 * nb) + u_bytes + 4.0 * m * d
-    dominant = "decode" if t_dec >= t_enc else "encode"
-    dom_bytes = dec_bytes if dominant == "decode" else enc_bytes
-    dom_ms = max(t_dec, t_enc)
+    dominant = "decode"
+    dom_bytes = dec_bytes
+    dom_ms = t_dec
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     kernel = f"k_rank_{dominant}<0>"
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(kernel, args.scaling),
                 "kernel": kernel,
                 "unit_frac": round((enc_bytes + dec_bytes) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                "encode_ms": round(t_enc, 5), "decode_ms": round(t_dec, 5),
+                "decode_ms": round(t_dec, 5), "rest_of_step_ms": round(t_enc, 5),
                 "alg_bytes_encode": int(enc_bytes), "alg_bytes_decode": int(dec_bytes)}
 
     result = {

@@ -175,28 +175,64 @@ constexpr int kMaxRFused = 64;              // replicas whose scales are staged 
 
 typedef int int32x2 __attribute__((ext_vector_type(2)));
 
-template <int FMT>
-__device__ __forceinline__ void load_chunks(const FusedArgs& a, int r, const int* off, int32x2* dst) {
-  const auto q = make_rsrc(a.qcodes + (int64_t)r * a.code_stride, (int64_t)a.m * a.d);
-#pragma unroll
-  for (int j = 0; j < kCPT; ++j) dst[j] = __builtin_amdgcn_raw_buffer_load_b64(q, off[j], 0, 0);
-}
+// Decode streaming.  A replica's tile (48 x 768 codes = 36 KiB) is read as
+// flat bytes f: thread t takes the 16-byte chunks f = 16 (t + 512 j), j < 4
+// (the first 32 KiB), and the 8-byte chunk f = 32768 + 8 t (the rest); a
+// 16-byte chunk never crosses a row (768 = 48 x 16).  Replicas past R are
+// read through an empty buffer resource (no memory traffic, zeros), so every
+// load is issued unconditionally and the loads of three replicas stay in
+// flight.
+constexpr int kDCPT = 4;                    // 16-byte chunks per thread
+constexpr int kDTail = 32768;               // first byte of the 8-byte chunks
+
+struct CodeBuf {
+  int32x4 v[kDCPT];
+  int32x2 t;
+};
 
 template <int FMT>
-__device__ __forceinline__ void accum_chunks(float (*acc)[8], const int32x2* c, const float* ssc_r, const int* sidx,
-                                             bool first) {
+__device__ __forceinline__ void load_codes(const FusedArgs& a, int R, int r, const int* off, int offt, CodeBuf& dst) {
+  const bool in = r < R;
+  const auto q = make_rsrc(a.qcodes + (in ? (int64_t)r * a.code_stride : 0), in ? (int64_t)a.m * a.d : 0);
 #pragma unroll
-  for (int j = 0; j < kCPT; ++j) {
-    float v[8];
-    dec4<FMT>((uint32_t)c[j][0], v);
-    dec4<FMT>((uint32_t)c[j][1], v + 4);
-    const float s = ssc_r[sidx[j]];
+  for (int j = 0; j < kDCPT; ++j) dst.v[j] = __builtin_amdgcn_raw_buffer_load_b128(q, off[j], 0, 0);
+  dst.t = __builtin_amdgcn_raw_buffer_load_b64(q, offt, 0, 0);
+}
+
+// hi[j] is false where a chunk's upper 8 codes lie past the row end (d is a
+// multiple of 8, not always of 16): they belong to the next row and are
+// replaced by zero codes.
+// PT: one scale for the whole replica (`sr`), else the chunk's block scale
+// from the LDS table `ssc_r`.
+template <int FMT, bool PT>
+__device__ __forceinline__ void accum_codes(float (*acc)[16], float* acct, const CodeBuf& c, const float* ssc_r,
+                                            float sr, const int* sidx, int sidxt, const bool* hi, bool first) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc[j][k] = first ? s * v[k] : acc[j][k] + s * v[k];
+  for (int j = 0; j < kDCPT; ++j) {
+    float v[16];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) dec4<FMT>((w < 2 || hi[j]) ? (uint32_t)c.v[j][w] : 0u, v + 4 * w);
+    const float s = PT ? sr : ssc_r[sidx[j]];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) acc[j][k] = first ? s * v[k] : acc[j][k] + s * v[k];
   }
+  float v[8];
+  dec4<FMT>((uint32_t)c.t[0], v);
+  dec4<FMT>((uint32_t)c.t[1], v + 4);
+  const float s = PT ? sr : ssc_r[sidxt];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acct[k] = first ? s * v[k] : acct[k] + s * v[k];
 }
 
-template <int FMT, bool ENC>
+// SC: the decode's scaling (0 per tensor, 1 per block) as a compile-time
+// constant (-1: read at run time).  Per tensor, each replica's scale is one
+// uniform word read in the replica loop; per block the scales of the tile's
+// blocks are staged in LDS first.
+// RC > 0: the decode's replica count is a compile-time constant and the
+// replica loop is unrolled, so every wait on a load names exactly the loads
+// it needs (a runtime trip count rotates the buffers through different
+// registers per iteration and the waits become full drains).
+template <int FMT, bool ENC, int RC, int SC>
 __device__ __forceinline__ void fused_body(const FusedArgs& a) {
   // The staged tile (fp32, padded rows); after it has been read into
   // registers the same memory holds the per-wave projection partials and the
@@ -241,44 +277,81 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
       *reinterpret_cast<int32x4*>(smem + r * kTilePad + c) = v[j];
     }
   } else {
-    // scales of the tile's blocks, per replica, into LDS
-    const int R = a.R;
-    if (a.scaling == 0) {
-      for (int r = tid; r < R; r += 512) ssc[r][0] = a.qscales[(int64_t)r * a.scale_stride];
-    } else {
-      const int nbm = (int)cdiv(m, kBlock);
-      for (int t = tid; t < R * 12; t += 512) {
-        const int r = t / 12, e = t % 12, br = rb0 + e / 6, bc = cb0 + e % 6;
-        ssc[r][e] = (br < nbm && bc < nbd) ? a.qscales[(int64_t)r * a.scale_stride + br * nbd + bc] : 0.f;
-      }
-    }
-    int off[kCPT], sidx[kCPT];
+    const int R = RC > 0 ? RC : a.R;
+    int off[kDCPT], sidx[kDCPT];
+    bool hi[kDCPT];
 #pragma unroll
-    for (int j = 0; j < kCPT; ++j) {
-      const int q = tid + 512 * j, r = q / 96, c = (q % 96) * 8;
+    for (int j = 0; j < kDCPT; ++j) {
+      const int f = 16 * (tid + 512 * j), r = f / TC, c = f % TC;
       const bool ok = row0 + r < m && col0 + c < d;
       off[j] = ok ? (row0 + r) * d + col0 + c : kOff;
-      sidx[j] = a.scaling == 0 ? 0 : ((row0 + r) / kBlock - rb0) * 6 + (col0 + c) / kBlock - cb0;
+      hi[j] = col0 + c + 8 < d;
+      sidx[j] = (a.scaling == 0 || !ok) ? 0 : ((row0 + r) / kBlock - rb0) * 6 + (col0 + c) / kBlock - cb0;
     }
-    __syncthreads();
-    float acc[kCPT][8];
-    int32x2 ca[kCPT], cb[kCPT];
-    load_chunks<FMT>(a, 0, off, ca);
-    for (int r = 0; r < R; r += 2) {
-      if (r + 1 < R) load_chunks<FMT>(a, r + 1, off, cb);
-      accum_chunks<FMT>(acc, ca, ssc[r], sidx, r == 0);
-      if (r + 1 >= R) break;
-      if (r + 2 < R) load_chunks<FMT>(a, r + 2, off, ca);
-      accum_chunks<FMT>(acc, cb, ssc[r + 1], sidx, false);
+    const int ft = kDTail + 8 * tid, rt = ft / TC, ct = ft % TC;
+    const bool okt = row0 + rt < m && col0 + ct < d;
+    const int offt = okt ? (row0 + rt) * d + col0 + ct : kOff;
+    const int sidxt = (a.scaling == 0 || !okt) ? 0 : ((row0 + rt) / kBlock - rb0) * 6 + (col0 + ct) / kBlock - cb0;
+    // The scale words are loaded first, then the first two replicas' codes;
+    // storing the scales into LDS then waits only for the older scale loads
+    // (loads retire in order), while the code stream stays in flight.
+    float acc[kDCPT][16], acct[8];
+    CodeBuf b0, b1, b2;
+    constexpr bool PT = SC == 0;
+    if constexpr (PT) {
+      load_codes<FMT>(a, R, 0, off, offt, b0);
+      load_codes<FMT>(a, R, 1, off, offt, b1);
+    } else {
+      // The last wave stages the block scales in LDS before it starts its
+      // code stream; the other waves start theirs at once.  (A scale load
+      // issued behind the code loads would wait for all of them: loads
+      // retire in order.)
+      if (wave == 7) {
+        const int nbm = (int)cdiv(m, kBlock);
+        for (int t = lane; t < R * 12; t += 64) {
+          const int r = t / 12, e = t % 12, br = rb0 + e / 6, bc = cb0 + e % 6;
+          ssc[r][e] = (br < nbm && bc < nbd) ? a.qscales[(int64_t)r * a.scale_stride + br * nbd + bc] : 0.f;
+        }
+      }
+      load_codes<FMT>(a, R, 0, off, offt, b0);
+      load_codes<FMT>(a, R, 1, off, offt, b1);
+      __syncthreads();
     }
+    // per-tensor scale of replica r: a uniform word (scalar load)
+    auto rscale = [&](int r) -> float { return PT ? a.qscales[(int64_t)r * a.scale_stride] : 0.f; };
+    auto three = [&](int r) -> bool {   // replicas r .. r + 2; false once past R
+      load_codes<FMT>(a, R, r + 2, off, offt, b2);
+      accum_codes<FMT, PT>(acc, acct, b0, ssc[r], rscale(r), sidx, sidxt, hi, r == 0);
+      if (r + 1 >= R) return false;
+      load_codes<FMT>(a, R, r + 3, off, offt, b0);
+      accum_codes<FMT, PT>(acc, acct, b1, ssc[r + 1], rscale(r + 1), sidx, sidxt, hi, false);
+      if (r + 2 >= R) return false;
+      load_codes<FMT>(a, R, r + 4, off, offt, b1);
+      accum_codes<FMT, PT>(acc, acct, b2, ssc[r + 2], rscale(r + 2), sidx, sidxt, hi, false);
+      return true;
+    };
+    if constexpr (RC > 0) {
 #pragma unroll
-    for (int j = 0; j < kCPT; ++j) {
-      const int q = tid + 512 * j, r = q / 96, c = (q % 96) * 8;
+      for (int r = 0; r < RC; r += 3)
+        if (!three(r)) break;
+    } else {
+      for (int r = 0; r < R; r += 3)
+        if (!three(r)) break;
+    }
+    const float ir = a.invR;
+#pragma unroll
+    for (int j = 0; j < kDCPT; ++j) {
+      const int f = 16 * (tid + 512 * j), r = f / TC, c = f % TC;
       float* dst = smem + r * kTilePad + c;
-      *reinterpret_cast<float4*>(dst) =
-          make_float4(acc[j][0] * a.invR, acc[j][1] * a.invR, acc[j][2] * a.invR, acc[j][3] * a.invR);
-      *reinterpret_cast<float4*>(dst + 4) =
-          make_float4(acc[j][4] * a.invR, acc[j][5] * a.invR, acc[j][6] * a.invR, acc[j][7] * a.invR);
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        *reinterpret_cast<float4*>(dst + 4 * w) = make_float4(acc[j][4 * w] * ir, acc[j][4 * w + 1] * ir,
+                                                              acc[j][4 * w + 2] * ir, acc[j][4 * w + 3] * ir);
+    }
+    {
+      float* dst = smem + rt * kTilePad + ct;
+      *reinterpret_cast<float4*>(dst) = make_float4(acct[0] * ir, acct[1] * ir, acct[2] * ir, acct[3] * ir);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(acct[4] * ir, acct[5] * ir, acct[6] * ir, acct[7] * ir);
     }
   }
   __syncthreads();
@@ -641,14 +714,33 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
   }
 }
 
-// One kernel per direction and format (distinct names in traces).
+// One kernel per direction and format (distinct names in traces); the
+// decode also per replica count 4, 8, 16 (0: any count up to 64).
 template <int FMT>
 __global__ void __launch_bounds__(512) k_rank_encode(FusedArgs a) {
-  fused_body<FMT, true>(a);
+  fused_body<FMT, true, 0, -1>(a);
 }
-template <int FMT>
+template <int FMT, int RC, int SC>
 __global__ void __launch_bounds__(512) k_rank_decode(FusedArgs a) {
-  fused_body<FMT, false>(a);
+  fused_body<FMT, false, RC, SC>(a);
+}
+
+template <int FMT, int SC>
+static void launch_decode(const FusedArgs& args, dim3 gd, dim3 bd, hipStream_t s) {
+  switch (args.R) {
+    case 4: hipLaunchKernelGGL((k_rank_decode<FMT, 4, SC>), gd, bd, 0, s, args); break;
+    case 8: hipLaunchKernelGGL((k_rank_decode<FMT, 8, SC>), gd, bd, 0, s, args); break;
+    case 16: hipLaunchKernelGGL((k_rank_decode<FMT, 16, SC>), gd, bd, 0, s, args); break;
+    default: hipLaunchKernelGGL((k_rank_decode<FMT, 0, SC>), gd, bd, 0, s, args); break;
+  }
+}
+
+template <int FMT>
+static void launch_decode(const FusedArgs& args, dim3 gd, dim3 bd, hipStream_t s) {
+  if (args.scaling == 0)
+    launch_decode<FMT, 0>(args, gd, bd, s);
+  else
+    launch_decode<FMT, 1>(args, gd, bd, s);
 }
 
 hipError_t launch_fused(const FusedArgs& args, int grid, hipStream_t s) {
@@ -660,9 +752,9 @@ hipError_t launch_fused(const FusedArgs& args, int grid, hipStream_t s) {
       hipLaunchKernelGGL(k_rank_encode<1>, gd, bd, 0, s, args);
   } else {
     if (args.fmt == 0)
-      hipLaunchKernelGGL(k_rank_decode<0>, gd, bd, 0, s, args);
+      launch_decode<0>(args, gd, bd, s);
     else
-      hipLaunchKernelGGL(k_rank_decode<1>, gd, bd, 0, s, args);
+      launch_decode<1>(args, gd, bd, s);
   }
   return hipGetLastError();
 }
