@@ -55,6 +55,21 @@ struct FusedArgs {
 hipError_t launch_fused(const FusedArgs& args, int grid, hipStream_t s);
 hipError_t launch_pack_u(const float* U, int d, void* ub, void* ua, hipStream_t s);
 
+// Refresh products Y = A X (A symmetric d x d): each workgroup takes 256
+// columns of A and a range of its rows; the partial sums of the ranges are
+// added in a fixed order.  At least ~2 workgroups per compute unit.
+constexpr int kAqCols = 256;
+__host__ __device__ inline int aq_rows_per_split(int d) {
+  const int cb = (int)cdiv(d, kAqCols);
+  int splits = (int)cdiv(512, cb);
+  const int max_splits = (int)cdiv(d, 64);
+  if (splits > max_splits) splits = max_splits;
+  if (splits < 1) splits = 1;
+  return (int)cdiv(cdiv(d, splits), 32) * 32;
+}
+__host__ __device__ inline int aq_splits(int d) { return (int)cdiv(d, aq_rows_per_split(d)); }
+constexpr int kGramRows = 64;   // rows per partial of the l x l Gram products
+
 // Offsets (bytes) inside the per-call workspace.  Regions overlap between
 // calls of different kinds (encode / decode / refresh never run at once on
 // one workspace).
@@ -69,6 +84,7 @@ struct WorkLayout {
   size_t Y = 0, Q = 0, Z = 0;   // fp64 [d][l]
   size_t small = 0;             // fp64 scratch for the l x l solvers
   size_t gpart = 0;             // fp64 [nchunk][l][l]
+  size_t apart = 0;             // fp64 [splits][d][l]: partials of A X
   size_t chol = 0;              // fp64 [n][n] (Cholesky variants)
   size_t chol2 = 0;             // fp64 [n][n]
   size_t total = 0;

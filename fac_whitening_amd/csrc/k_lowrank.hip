@@ -75,19 +75,6 @@ hipError_t launch_lr_project(const float* x, int64_t ldx, int m, int d, const fl
   return hipGetLastError();
 }
 
-// Refresh flavour: fp32 X (the statistics A), fp64 basis and accumulators;
-// each workgroup owns 16 rows and walks all of d (no partials).
-hipError_t launch_project_f64(const float* x, int64_t ldx, int m, int d, const double* Q, int lp,
-                              double* out, hipStream_t s) {
-  if (m == 0 || d == 0) return hipSuccess;
-  dim3 grid(1, (unsigned)cdiv(m, 16));
-  if (lp == 48)
-    hipLaunchKernelGGL((k_project<48, 16, 64, true, double, double>), grid, dim3(256), 0, s, x, ldx, m, d, Q, out);
-  else
-    hipLaunchKernelGGL((k_project<64, 16, 64, true, double, double>), grid, dim3(256), 0, s, x, ldx, m, d, Q, out);
-  return hipGetLastError();
-}
-
 // out[i][j] = alpha x[i][j] + sum_t (c_t sum_chunk part[chunk][i][t]) U[j][t]
 // Tile: 16 rows x 256 columns; wave w owns rows 4w..4w+3, lane l columns
 // 4l..4l+3.  Optionally the amax of |out| per 128 x 128 tile (or tensor).

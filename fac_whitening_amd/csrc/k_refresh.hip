@@ -7,17 +7,16 @@
 // Martinsson & Tropp 2011, specialised to symmetric A):
 //   Y = A Omega;  q times { Q = orth(Y); Y = A Q };  Q = orth(Y);
 //   B = Q^T (A Q) = V Theta V^T;  U = Q V[:, :k].
-// orth is CholeskyQR2 (Fukaya et al. 2014) with fp64 Gram and Cholesky; the
+// orth is CholeskyQR with fp64 Gram and Cholesky (Fukaya et al. 2014): one
+// pass between products, two (CholeskyQR2) for the Rayleigh-Ritz basis; the
 // l x l eigenproblem is solved by cyclic two-sided Jacobi (Golub & Van Loan,
-// §8.5) in fp64 inside one workgroup, with parallel (round-robin) ordering.
+// §8.5) in fp64 in one wave, with parallel (round-robin) ordering.  The
+// products A X run on the fp64 matrix cores.
 // A is read as fp32; every other quantity is fp64 until the basis U and the
 // coefficient vectors are written as fp32.
 #include "gift_internal.hpp"
 
 namespace gift {
-
-hipError_t launch_project_f64(const float* x, int64_t ldx, int m, int d, const double* Q, int lp,
-                              double* part, hipStream_t s);
 
 // Small-buffer layout (fp64 elements).
 constexpr int kSmTrace = 0;            // [0] tr(A)
@@ -45,6 +44,99 @@ __global__ void k_omega64(const float* __restrict__ om, int d, int l, int lp, do
   out[i] = c < l ? (double)om[(int64_t)r * l + c] : 0.0;
 }
 
+// Partial products of Y = A X for symmetric A (fp32, d x d) and X (fp64,
+// d x LP): part[s][i][c] = sum_{j in row range s} A[j][i] X[j][c], which is
+// (A X)[i][c] summed over the ranges.  fp64 matrix cores
+// (v_mfma_f64_16x16x4f64): lane l supplies the A operand Aop[l % 16][l / 16]
+// and the B operand Bop[l / 16][l % 16]; slot e of lane l holds
+// D[4 e + l / 16][l % 16].  Here Aop[m][k] = A[j + k][i + m] (A's symmetry:
+// rows of A are read, coalesced) and Bop[k][n] = X[j + k][n].  Wave w of
+// workgroup (b, s) owns columns 256 b + 64 w .. + 63 of A; A is read from
+// memory once, X (a few MB) from L2.  A's fp32 values are exact in fp64.
+typedef double double4v __attribute__((ext_vector_type(4)));
+
+template <int LP>
+__global__ void __launch_bounds__(256) k_aq(const float* __restrict__ A, int d, const double* __restrict__ X,
+                                            int jrows, double* __restrict__ part) {
+  constexpr int NT = LP / 16;    // output column tiles
+  constexpr int KB = 4;          // 4-row k-steps per block (16 rows)
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lm = lane & 15, lk = lane >> 4;
+  const int i0 = blockIdx.x * kAqCols + wave * 64;
+  const int j0 = blockIdx.y * jrows;
+  const int j1 = min(d, j0 + jrows);
+  int ic[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) ic[mt] = min(i0 + 16 * mt + lm, d - 1);   // clamped: loads stay in bounds
+  double4v acc[4][NT];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = (double4v){0.0, 0.0, 0.0, 0.0};
+  struct Blk {
+    float a[KB][4];
+    double b[KB][NT];
+  };
+  auto load = [&](int jb, Blk& t) {
+#pragma unroll
+    for (int ks = 0; ks < KB; ++ks) {
+      const int jr = min(jb + 4 * ks + lk, d - 1);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) t.a[ks][mt] = A[(int64_t)jr * d + ic[mt]];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) t.b[ks][nt] = X[(int64_t)jr * LP + 16 * nt + lm];
+    }
+  };
+  auto compute = [&](int jb, const Blk& t) {
+#pragma unroll
+    for (int ks = 0; ks < KB; ++ks) {
+      const bool in = jb + 4 * ks + lk < j1;   // rows past the range contribute zero
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const double av = in ? (double)t.a[ks][mt] : 0.0;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, t.b[ks][nt], acc[mt][nt], 0, 0, 0);
+      }
+    }
+  };
+  Blk cur, nxt;
+  load(j0, cur);
+  for (int jb = j0; jb < j1; jb += 4 * KB) {
+    if (jb + 4 * KB < j1) load(jb + 4 * KB, nxt);   // in flight while this block computes
+    compute(jb, cur);
+    cur = nxt;
+  }
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = i0 + 16 * mt + 4 * e + lk;
+        if (row < d) part[((int64_t)blockIdx.y * d + row) * LP + 16 * nt + lm] = acc[mt][nt][e];
+      }
+}
+
+// out[e] = sum_{p < nparts} part[p][e], in order p = 0, 1, ... (deterministic)
+__global__ void __launch_bounds__(256) k_sum_parts(const double* __restrict__ part, int nparts, int64_t n,
+                                                   double* __restrict__ out) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  double s = 0.0;
+  int p = 0;
+  for (; p + 4 <= nparts; p += 4) {   // four independent loads in flight, summed in order
+    const double v0 = part[(int64_t)p * n + e], v1 = part[(int64_t)(p + 1) * n + e];
+    const double v2 = part[(int64_t)(p + 2) * n + e], v3 = part[(int64_t)(p + 3) * n + e];
+    s += v0;
+    s += v1;
+    s += v2;
+    s += v3;
+  }
+  for (; p < nparts; ++p) s += part[(int64_t)p * n + e];
+  out[e] = s;
+}
+
 // part[ch][a][b] = sum_{i in rows of chunk ch} X[i][a] Y[i][b]  (fp64, LP <= 64)
 template <int LP>
 __global__ void __launch_bounds__(256) k_gram_parts(const double* __restrict__ X, const double* __restrict__ Y,
@@ -55,11 +147,11 @@ __global__ void __launch_bounds__(256) k_gram_parts(const double* __restrict__ X
   double acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.0;
-  const int r0 = blockIdx.x * 256;
-  for (int s0 = r0; s0 < min(d, r0 + 256); s0 += 32) {
+  const int r0 = blockIdx.x * kGramRows;
+  for (int s0 = r0; s0 < min(d, r0 + kGramRows); s0 += 32) {
     for (int e = threadIdx.x; e < 32 * LP; e += 256) {
       int rr = e / LP, c = e % LP;
-      bool ok = s0 + rr < d && s0 + rr < r0 + 256;
+      bool ok = s0 + rr < d && s0 + rr < r0 + kGramRows;
       Xs[rr][c] = ok ? X[(int64_t)(s0 + rr) * LP + c] : 0.0;
       Ys[rr][c] = ok ? Y[(int64_t)(s0 + rr) * LP + c] : 0.0;
     }
@@ -83,176 +175,271 @@ __global__ void __launch_bounds__(256) k_gram_parts(const double* __restrict__ X
   }
 }
 
-// One workgroup: G = sum of Gram partials (l x l), G = L L^T, writes
-// M = L^-T (upper triangular, zero outside l x l) into small[kSmM].
-template <int LP>
-__global__ void __launch_bounds__(256) k_chol_inv_small(const double* __restrict__ part, int nch, int l,
-                                                        double* __restrict__ small, uint32_t* __restrict__ flags) {
-  __shared__ double Gm[LP][LP + 1];
-  __shared__ double Li[LP][LP + 1];
-  __shared__ int bad;
-  const int tid = threadIdx.x;
-  if (tid == 0) bad = 0;
-  for (int o = tid; o < LP * LP; o += 256) {
-    double s = 0.0;
-    for (int ch = 0; ch < nch; ++ch) s += part[(int64_t)ch * LP * LP + o];
-    Gm[o / LP][o % LP] = s;
-    Li[o / LP][o % LP] = 0.0;
-  }
-  __syncthreads();
-  // right-looking Cholesky on the leading l x l block (lower triangle of Gm)
-  for (int j = 0; j < l; ++j) {
-    if (tid == 0) {
-      double p = Gm[j][j];
-      if (!(p > 0.0)) {
-        bad = 1;
-        p = __longlong_as_double(0x7FF8000000000000LL);
-      }
-      Gm[j][j] = sqrt(p);
-    }
-    __syncthreads();
-    for (int i = j + 1 + tid; i < l; i += 256) Gm[i][j] /= Gm[j][j];
-    __syncthreads();
-    for (int o = tid; o < l * l; o += 256) {
-      int i = o / l, c = o % l;
-      if (i > j && c > j && c <= i) Gm[i][c] -= Gm[i][j] * Gm[c][j];
-    }
-    __syncthreads();
-  }
-  // L^-1 column by column (forward substitution), one thread per column
-  if (tid < l) {
-    int c = tid;
-    for (int i = c; i < l; ++i) {
-      double s = (i == c) ? 1.0 : 0.0;
-      for (int q = c; q < i; ++q) s -= Gm[i][q] * Li[q][c];
-      Li[i][c] = s / Gm[i][i];
-    }
-  }
-  __syncthreads();
-  // M = (L^-1)^T: M[a][b] = Li[b][a]
-  for (int o = tid; o < LP * LP; o += 256) {
-    int a = o / LP, b = o % LP;
-    small[kSmM + o] = (a < l && b < l) ? Li[b][a] : 0.0;
-  }
-  if (tid == 0 && bad) atomicOr(flags, (uint32_t)GIFT_FLAG_NONFINITE);
+// 1 / x and 1 / sqrt(x) from the hardware estimates and two Newton steps
+// each (about one ulp: the rotations stay orthogonal to rounding).
+__device__ __forceinline__ double rcp_nr(double x) {
+  double r = __builtin_amdgcn_rcp(x);
+  r = r * (2.0 - x * r);
+  return r * (2.0 - x * r);
+}
+__device__ __forceinline__ double rsq_nr(double x) {
+  double y = __builtin_amdgcn_rsq(x);
+  y = y * (1.5 - 0.5 * x * y * y);
+  return y * (1.5 - 0.5 * x * y * y);
 }
 
-// out[i][:NC] = X[i][:LP] * M[:LP][:NC] with M in small[kSmM] ([LP][LPM]).
+// One wave: G (LP x LP, leading l x l used) = L L^T, writes M = L^-T (upper
+// triangular, zero outside l x l) into small[kSmM].  Lane i owns row i of L
+// (left-looking: column j from dot products with the finished columns) and
+// then column i of L^-1 (forward substitution); both live in LDS.  One wave
+// keeps its LDS accesses in program order, so no barrier is needed.  Rows
+// and columns past l are the identity.
+template <int LP>
+__global__ void __launch_bounds__(64) k_chol_inv_small(const double* __restrict__ G, int l,
+                                                       double* __restrict__ small, uint32_t* __restrict__ flags) {
+  __shared__ double Ls[LP][LP + 1];   // L, row-major
+  __shared__ double Xs[LP][LP + 1];   // L^-1, Xs[r][c]
+  __shared__ double Dinv[LP];         // 1 / L[j][j]
+  const int i = threadIdx.x;
+  const bool own = i < LP;
+  if (own) {
+    double g[LP];   // all loads in flight before the first store
+#pragma unroll
+    for (int q = 0; q < LP; ++q) g[q] = G[i * LP + q];
+#pragma unroll
+    for (int q = 0; q < LP; ++q) Ls[i][q] = (i < l && q < l) ? g[q] : (i == q ? 1.0 : 0.0);
+  }
+  bool bad = false;
+  // dot products with four partial sums (short dependency chains)
+  auto dot = [&](const double* x, const double* y, int lo, int hi) {
+    double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+    int q = lo;
+    for (; q + 4 <= hi; q += 4) {
+      s0 += x[q] * y[q];
+      s1 += x[q + 1] * y[q + 1];
+      s2 += x[q + 2] * y[q + 2];
+      s3 += x[q + 3] * y[q + 3];
+    }
+    for (; q < hi; ++q) s0 += x[q] * y[q];
+    return (s0 + s1) + (s2 + s3);
+  };
+  for (int j = 0; j < LP; ++j) {
+    const double r = own ? Ls[i][j] - dot(Ls[i], Ls[j], 0, j) : 0.0;
+    const double dj = __shfl(r, j, 64);   // the pivot, from lane j
+    double rs = rsq_nr(dj);               // 1 / L[j][j]
+    if (!(dj > 0.0)) {
+      bad = true;
+      rs = __longlong_as_double(0x7FF8000000000000LL);
+    }
+    if (own) Ls[i][j] = i > j ? r * rs : (i == j ? dj * rs : 0.0);
+    if (i == j) Dinv[j] = rs;
+  }
+  for (int rr = 0; rr < LP; ++rr) {
+    if (own) {
+      double v = rr == i ? 1.0 : 0.0;
+      // v -= sum_{q = i}^{rr - 1} L[rr][q] X[q][i]  (X column i read with stride)
+      double s0 = 0.0, s1 = 0.0;
+      int q = i;
+      for (; q + 2 <= rr; q += 2) {
+        s0 += Ls[rr][q] * Xs[q][i];
+        s1 += Ls[rr][q + 1] * Xs[q + 1][i];
+      }
+      for (; q < rr; ++q) s0 += Ls[rr][q] * Xs[q][i];
+      v -= s0 + s1;
+      Xs[rr][i] = rr >= i ? v * Dinv[rr] : 0.0;
+    }
+  }
+  if (own)
+    for (int c = 0; c < LP; ++c) small[kSmM + i * LP + c] = (i < l && c < l) ? Xs[c][i] : 0.0;
+  if (i == 0 && bad) atomicOr(flags, (uint32_t)GIFT_FLAG_NONFINITE);
+}
+
+// out[i][:NC] = X[i][:LP] * M[:LP][:NC] with M in small[kSmM] ([LP][ldm]).
+// Thread (i, g) computes the 8 outputs of row i in column group g; the rows
+// of X are read by the NC / 8 threads of a row together (one broadcast).
 template <int LP, int NC, typename TO>
 __global__ void __launch_bounds__(256) k_right_small(const double* __restrict__ X, int d,
                                                      const double* __restrict__ small, int ldm,
                                                      TO* __restrict__ out) {
+  constexpr int CPT = 8, NG = NC / CPT;
   __shared__ double Ms[LP][NC];
   for (int o = threadIdx.x; o < LP * NC; o += 256) Ms[o / NC][o % NC] = small[kSmM + (o / NC) * ldm + (o % NC)];
   __syncthreads();
-  int i = blockIdx.x * 256 + threadIdx.x;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int i = t / NG, g = t % NG;
   if (i >= d) return;
-  double xr[LP];
+  double acc[CPT];
 #pragma unroll
-  for (int a = 0; a < LP; ++a) xr[a] = X[(int64_t)i * LP + a];
-  for (int b = 0; b < NC; ++b) {
-    double s = 0.0;
+  for (int c = 0; c < CPT; ++c) acc[c] = 0.0;
+#pragma unroll 8
+  for (int a = 0; a < LP; ++a) {
+    const double x = X[(int64_t)i * LP + a];
 #pragma unroll
-    for (int a = 0; a < LP; ++a) s += xr[a] * Ms[a][b];
-    out[(int64_t)i * NC + b] = (TO)s;
+    for (int c = 0; c < CPT; ++c) acc[c] += x * Ms[a][g * CPT + c];
   }
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) out[(int64_t)i * NC + g * CPT + c] = (TO)acc[c];
 }
 
-// One workgroup: B = sum of partials (Q^T A Q), symmetrised; cyclic Jacobi;
-// Ritz values sorted descending (ties: lower index first); V_k (the first k
-// sorted eigenvectors) into small[kSmM] as [LP][32]; coefficients into coef.
+// Jacobi rotation annihilating B[p][q] (Golub & Van Loan, Alg. 8.5.1):
+// tau = (aqq - app) / (2 apq), t = sign(tau) / (|tau| + sqrt(1 + tau^2)),
+// c = 1 / sqrt(1 + t^2), s = t c.
+__device__ __forceinline__ void jacobi_rot(double app, double aqq, double apq, double& c, double& s) {
+  const double tau = (aqq - app) * rcp_nr(2.0 * apq);
+  const double at = fabs(tau);
+  double t;
+  if (at > 1e150) {
+    t = 0.5 * rcp_nr(tau);   // sqrt(1 + tau^2) = |tau| to double precision
+  } else {
+    const double u = 1.0 + tau * tau;
+    t = rcp_nr(at + u * rsq_nr(u));
+    if (tau < 0.0) t = -t;
+  }
+  c = rsq_nr(1.0 + t * t);
+  s = t * c;
+}
+
+// One workgroup: B (Q^T A Q, LP x LP, leading l x l used) symmetrised;
+// cyclic Jacobi; Ritz values sorted descending (ties: lower index first);
+// V_k (the first k sorted eigenvectors) into small[kSmM] as [LP][32];
+// coefficients into coef.  A round applies n / 2 disjoint rotations R_i
+// (round-robin ordering).  With J their product, B <- J^T B J acts on every
+// 2 x 2 block (pair i rows, pair j columns) independently,
+// B_ij <- R_i^T B_ij R_j, and V <- V J on pairs of columns; so a round is one
+// barrier-free pass over the blocks after the rotations are known.
 template <int LP>
-__global__ void __launch_bounds__(256) k_jacobi_coef(const double* __restrict__ part, int nch, int l, int k,
-                                                     int d, float damping_rel, double* __restrict__ small,
+__global__ void __launch_bounds__(256) k_jacobi_coef(const double* __restrict__ B0, int l, int k, int d,
+                                                     float damping_rel, double* __restrict__ small,
                                                      float* __restrict__ coef, uint32_t* __restrict__ flags) {
+  constexpr int NP = LP / 2;
   __shared__ double B[LP][LP + 1];
   __shared__ double V[LP][LP + 1];
-  __shared__ double cs[LP / 2][2];
+  __shared__ double cs[NP][2];
+  __shared__ int pq[NP][2];
   __shared__ int order[LP];
-  __shared__ double offn, alln;
+  __shared__ double red2[256][2];
   const int tid = threadIdx.x;
-  for (int o = tid; o < LP * LP; o += 256) {
-    double s = 0.0;
-    for (int ch = 0; ch < nch; ++ch) s += part[(int64_t)ch * LP * LP + o];
-    B[o / LP][o % LP] = s;
-  }
-  __syncthreads();
-  for (int o = tid; o < LP * LP; o += 256) V[o / LP][o % LP] = (o / LP == o % LP) ? 1.0 : 0.0;
-  // symmetrise in place (pairs a < b handled by one thread each)
-  for (int o = tid; o < LP * LP; o += 256) {
-    int a = o / LP, b = o % LP;
-    if (a < b) {
-      double v = (a < l && b < l) ? 0.5 * (B[a][b] + B[b][a]) : 0.0;
-      B[a][b] = v;
-      B[b][a] = v;
-    } else if (a == b && a >= l) {
-      B[a][a] = 0.0;
+  {
+    constexpr int NE = (LP * LP + 255) / 256;
+    double x[NE], y[NE];   // all loads in flight before the first store
+#pragma unroll
+    for (int u = 0; u < NE; ++u) {
+      const int o = min(tid + 256 * u, LP * LP - 1), a = o / LP, b = o % LP;
+      x[u] = B0[a * LP + b];
+      y[u] = B0[b * LP + a];
+    }
+#pragma unroll
+    for (int u = 0; u < NE; ++u) {
+      const int o = tid + 256 * u, a = o / LP, b = o % LP;
+      if (o < LP * LP) {
+        B[a][b] = (a < l && b < l) ? 0.5 * (x[u] + y[u]) : 0.0;
+        V[a][b] = a == b ? 1.0 : 0.0;
+      }
     }
   }
-  __syncthreads();
   const int n = (l + 1) & ~1;   // players in the round-robin (a dummy if l is odd)
   const int npair = n / 2;
+  __syncthreads();
   for (int sweep = 0; sweep < 30; ++sweep) {
     for (int round = 0; round < n - 1; ++round) {
       if (tid < npair) {
-        int i = tid;
-        int p = (i == 0) ? 0 : ((i - 1 + round) % (n - 1)) + 1;
-        int q = ((n - 2 - i + round) % (n - 1)) + 1;
-        if (p > q) { int t = p; p = q; q = t; }
-        double c = 1.0, s = 0.0;
-        if (q < l && B[p][q] != 0.0) {
-          double tau = (B[q][q] - B[p][p]) / (2.0 * B[p][q]);
-          double t = tau >= 0.0 ? 1.0 / (tau + sqrt(1.0 + tau * tau)) : -1.0 / (-tau + sqrt(1.0 + tau * tau));
-          c = 1.0 / sqrt(1.0 + t * t);
-          s = t * c;
+        // pair tid: players p < q (player 0 fixed, the rest rotate)
+        int v = tid - 1 + round;
+        if (v >= n - 1) v -= n - 1;
+        int w = n - 2 - tid + round;
+        if (w >= n - 1) w -= n - 1;
+        int p = tid == 0 ? 0 : v + 1, q = w + 1;
+        if (p > q) {
+          const int t = p;
+          p = q;
+          q = t;
         }
-        cs[i][0] = c;
-        cs[i][1] = s;
+        double c = 1.0, sn = 0.0;
+        if (q >= l) {
+          q = p;   // the dummy player: identity rotation on row / column p alone
+        } else if (B[p][q] != 0.0) {
+          jacobi_rot(B[p][p], B[q][q], B[p][q], c, sn);
+        }
+        cs[tid][0] = c;
+        cs[tid][1] = sn;
+        pq[tid][0] = p;
+        pq[tid][1] = q;
       }
       __syncthreads();
-      // rows: B <- J^T B
-      for (int o = tid; o < npair * l; o += 256) {
-        int i = o / l, jcol = o % l;
-        int p = (i == 0) ? 0 : ((i - 1 + round) % (n - 1)) + 1;
-        int q = ((n - 2 - i + round) % (n - 1)) + 1;
-        if (p > q) { int t = p; p = q; q = t; }
-        if (q >= l) continue;
-        double c = cs[i][0], s = cs[i][1];
-        double bp = B[p][jcol], bq = B[q][jcol];
-        B[p][jcol] = c * bp - s * bq;
-        B[q][jcol] = s * bp + c * bq;
+      // every operand is loaded before anything is stored (the blocks are
+      // disjoint), so the loads of all of a thread's blocks are in flight
+      // together
+      constexpr int NB = (NP * NP + 255) / 256, NV = (LP * NP + 255) / 256;
+      double bb[NB][4], rr[NB][4], vv[NV][2];
+      int bi[NB][4], vi[NV][2];
+      bool bok[NB], vok[NV];
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int o = tid + 256 * u, i = o / NP, j = o % NP;
+        bok[u] = o < NP * NP && i < npair && j < npair;
+        const int ii = bok[u] ? i : 0, jj = bok[u] ? j : 0;
+        const int pi = pq[ii][0], qi = pq[ii][1], pj = pq[jj][0], qj = pq[jj][1];
+        bi[u][0] = pi * (LP + 1) + pj;
+        bi[u][1] = pi * (LP + 1) + qj;
+        bi[u][2] = qi * (LP + 1) + pj;
+        bi[u][3] = qi * (LP + 1) + qj;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bb[u][e] = (&B[0][0])[bi[u][e]];
+        const double ci = cs[ii][0], si = cs[ii][1], cj = cs[jj][0], sj = cs[jj][1];
+        // rows (R_i^T), then columns (R_j)
+        const double rpp = ci * bb[u][0] - si * bb[u][2], rpq = ci * bb[u][1] - si * bb[u][3];
+        const double rqp = si * bb[u][0] + ci * bb[u][2], rqq = si * bb[u][1] + ci * bb[u][3];
+        rr[u][0] = cj * rpp - sj * rpq;
+        rr[u][1] = sj * rpp + cj * rpq;
+        rr[u][2] = cj * rqp - sj * rqq;
+        rr[u][3] = sj * rqp + cj * rqq;
       }
-      __syncthreads();
-      // columns: B <- B J, V <- V J
-      for (int o = tid; o < npair * l; o += 256) {
-        int i = o / l, r = o % l;
-        int p = (i == 0) ? 0 : ((i - 1 + round) % (n - 1)) + 1;
-        int q = ((n - 2 - i + round) % (n - 1)) + 1;
-        if (p > q) { int t = p; p = q; q = t; }
-        if (q >= l) continue;
-        double c = cs[i][0], s = cs[i][1];
-        double bp = B[r][p], bq = B[r][q];
-        B[r][p] = c * bp - s * bq;
-        B[r][q] = s * bp + c * bq;
-        double vp = V[r][p], vq = V[r][q];
-        V[r][p] = c * vp - s * vq;
-        V[r][q] = s * vp + c * vq;
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int o = tid + 256 * u, r = o / NP, j = o % NP;
+        vok[u] = o < LP * NP && r < l && j < npair;
+        const int jj = vok[u] ? j : 0, r0 = vok[u] ? r : 0;
+        const int pj = pq[jj][0], qj = pq[jj][1];
+        vi[u][0] = r0 * (LP + 1) + pj;
+        vi[u][1] = r0 * (LP + 1) + qj;
+        const double vp = (&V[0][0])[vi[u][0]], vq = (&V[0][0])[vi[u][1]];
+        const double cj = cs[jj][0], sj = cs[jj][1];
+        vv[u][0] = cj * vp - sj * vq;
+        vv[u][1] = sj * vp + cj * vq;
       }
+#pragma unroll
+      for (int u = 0; u < NB; ++u)
+        if (bok[u]) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) (&B[0][0])[bi[u][e]] = rr[u][e];
+        }
+#pragma unroll
+      for (int u = 0; u < NV; ++u)
+        if (vok[u]) {
+          (&V[0][0])[vi[u][0]] = vv[u][0];
+          (&V[0][0])[vi[u][1]] = vv[u][1];
+        }
       __syncthreads();
     }
-    if (tid == 0) {
-      double off = 0.0, all = 0.0;
-      for (int a = 0; a < l; ++a)
-        for (int b = 0; b < l; ++b) {
-          double v = B[a][b] * B[a][b];
-          all += v;
-          if (a != b) off += v;
-        }
-      offn = off;
-      alln = all;
+    // off-diagonal and total squared norms (fixed-order tree reduction)
+    double off = 0.0, all = 0.0;
+    for (int o = tid; o < l * l; o += 256) {
+      const int a = o / l, b = o % l;
+      const double v = B[a][b] * B[a][b];
+      all += v;
+      if (a != b) off += v;
     }
+    red2[tid][0] = off;
+    red2[tid][1] = all;
     __syncthreads();
-    const bool done = offn <= 1e-30 * alln;
+    for (int h = 128; h > 0; h >>= 1) {
+      if (tid < h) {
+        red2[tid][0] += red2[tid + h][0];
+        red2[tid][1] += red2[tid + h][1];
+      }
+      __syncthreads();
+    }
+    const bool done = red2[0][0] <= 1e-26 * red2[0][1];   // off-norm below 1e-13 of the norm
     __syncthreads();
     if (done) break;
   }
@@ -320,35 +507,49 @@ static hipError_t refresh_lowrank_lp(const float* A, int d, int k, int l, int q,
   double* Z = reinterpret_cast<double*>(work + w.Z);
   double* small = reinterpret_cast<double*>(work + w.small);
   double* gpart = reinterpret_cast<double*>(work + w.gpart);
-  const int nchG = (int)cdiv(d, 256);
+  const int nchG = (int)cdiv(d, kGramRows);
   const unsigned eb = (unsigned)cdiv((int64_t)d * LP, 256);
   hipLaunchKernelGGL(k_trace, dim3(1), dim3(1024), 0, s, A, d, small + kSmTrace);
   hipLaunchKernelGGL(k_omega64, dim3(eb), dim3(256), 0, s, omega, d, l, LP, Q);
+  double* apart = reinterpret_cast<double*>(work + w.apart);
+  double* gsum = gpart + (int64_t)nchG * LP * LP;      // the summed l x l matrix
+  const int jrows = aq_rows_per_split(d), nsplit = aq_splits(d);
+  const int64_t ny = (int64_t)d * LP;
   auto product = [&](const double* X, double* out) {   // out = A X
-    (void)launch_project_f64(A, d, d, d, X, LP, out, s);   // errors surface at the final hipGetLastError
+    hipLaunchKernelGGL((k_aq<LP>), dim3((unsigned)cdiv(d, kAqCols), (unsigned)nsplit), dim3(256), 0, s, A, d, X,
+                       jrows, apart);
+    hipLaunchKernelGGL(k_sum_parts, dim3((unsigned)cdiv(ny, 256)), dim3(256), 0, s, apart, nsplit, ny, out);
   };
-  auto orth = [&](const double* X, double* out) {       // CholeskyQR2
+  auto gram = [&](const double* X, const double* Y2) {  // gsum = X^T Y2
+    hipLaunchKernelGGL((k_gram_parts<LP>), dim3(nchG), dim3(256), 0, s, X, Y2, d, gpart);
+    hipLaunchKernelGGL(k_sum_parts, dim3((unsigned)cdiv(LP * LP, 256)), dim3(256), 0, s, gpart, nchG,
+                       (int64_t)LP * LP, gsum);
+  };
+  // CholeskyQR with `passes` passes.  Between products only the span of
+  // the basis matters (one pass; its orthogonality error, ~kappa^2 eps, is
+  // removed by the next pass over the next product); the basis of the
+  // Rayleigh-Ritz step takes two passes (CholeskyQR2).
+  auto orth = [&](const double* X, double* out, int passes) {
     const double* src = X;
-    for (int pass = 0; pass < 2; ++pass) {
-      hipLaunchKernelGGL((k_gram_parts<LP>), dim3(nchG), dim3(256), 0, s, src, src, d, gpart);
-      hipLaunchKernelGGL((k_chol_inv_small<LP>), dim3(1), dim3(256), 0, s, gpart, nchG, l, small, flags);
-      hipLaunchKernelGGL((k_right_small<LP, LP, double>), dim3((unsigned)cdiv(d, 256)), dim3(256), 0, s, src, d,
-                         small, LP, out);
+    for (int pass = 0; pass < passes; ++pass) {
+      gram(src, src);
+      hipLaunchKernelGGL((k_chol_inv_small<LP>), dim3(1), dim3(64), 0, s, gsum, l, small, flags);
+      hipLaunchKernelGGL((k_right_small<LP, LP, double>), dim3((unsigned)cdiv((int64_t)d * (LP / 8), 256)),
+                         dim3(256), 0, s, src, d, small, LP, out);
       src = out;
     }
   };
   product(Q, Y);                      // Y = A Omega
   for (int it = 0; it < q; ++it) {
-    orth(Y, Q);                       // Q = orth(Y)
+    orth(Y, Q, 1);                    // Q = orth(Y)
     product(Q, Y);                    // Y = A Q
   }
-  orth(Y, Q);                         // Q = orth(Y)
+  orth(Y, Q, 2);                      // Q = orth(Y)
   product(Q, Z);                      // Z = A Q
-  hipLaunchKernelGGL((k_gram_parts<LP>), dim3(nchG), dim3(256), 0, s, Q, Z, d, gpart);
-  hipLaunchKernelGGL((k_jacobi_coef<LP>), dim3(1), dim3(256), 0, s, gpart, nchG, l, k, d, damping_rel, small,
-                     coef, flags);
-  hipLaunchKernelGGL((k_right_small<LP, 32, float>), dim3((unsigned)cdiv(d, 256)), dim3(256), 0, s, Q, d, small,
-                     32, U);
+  gram(Q, Z);
+  hipLaunchKernelGGL((k_jacobi_coef<LP>), dim3(1), dim3(256), 0, s, gsum, l, k, d, damping_rel, small, coef, flags);
+  hipLaunchKernelGGL((k_right_small<LP, 32, float>), dim3((unsigned)cdiv((int64_t)d * 4, 256)), dim3(256), 0, s, Q,
+                     d, small, 32, U);
   return hipGetLastError();
 }
 
