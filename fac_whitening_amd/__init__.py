@@ -168,12 +168,12 @@ class Layer:
         return self._h
 
     def counters(self):
-        arr = (_i64 * 7)()
+        arr = (_i64 * 8)()
         _check(_lib.gift_layer_get_counters(self._h, arr), "gift_layer_get_counters")
         return list(arr)
 
     def set_counters(self, vals):
-        arr = (_i64 * 7)(*vals)
+        arr = (_i64 * 8)(*vals)
         _check(_lib.gift_layer_set_counters(self._h, arr), "gift_layer_set_counters")
 
     def flags(self, stream=None) -> int:

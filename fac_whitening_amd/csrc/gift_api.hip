@@ -23,7 +23,7 @@ struct gift_layer {
   char* state;
   // tokens A, tokens G, commits A, commits G, refreshes, fused encode and
   // decode barrier epochs (the device counters in the state only grow)
-  int64_t counters[7];
+  int64_t counters[8];
   bool ready;
 };
 
@@ -120,6 +120,7 @@ StateLayout state_layout(const gift_layer_desc& g) {
   if (stats_a) {
     s.S_A = take(d * d * 4);
     s.A = take(d * d * 4);
+    s.ssync = take(kStatsMaxGroups * 4);   // statistics: one grow-only flag per workgroup
   }
   if (stats_g) {
     s.S_G = take(m * m * 4);
@@ -248,15 +249,15 @@ gift_status gift_layer_destroy(gift_layer_t layer) {
   return GIFT_OK;
 }
 
-gift_status gift_layer_get_counters(gift_layer_t L, int64_t h[7]) {
+gift_status gift_layer_get_counters(gift_layer_t L, int64_t h[8]) {
   if (!L || !h) return GIFT_ERR_INVALID_ARG;
   std::memcpy(h, L->counters, sizeof(L->counters));
   return GIFT_OK;
 }
 
-gift_status gift_layer_set_counters(gift_layer_t L, const int64_t h[7]) {
+gift_status gift_layer_set_counters(gift_layer_t L, const int64_t h[8]) {
   if (!L || !h) return GIFT_ERR_INVALID_ARG;
-  for (int i = 0; i < 7; ++i)
+  for (int i = 0; i < 8; ++i)
     if (h[i] < 0) return GIFT_ERR_INVALID_ARG;
   std::memcpy(L->counters, h, sizeof(L->counters));
   L->ready = L->desc.transform == GIFT_EUCLID || h[4] > 0;
@@ -336,7 +337,13 @@ gift_status gift_accumulate_stats(gift_layer_t L, int32_t side, const void* d_x,
   }
   if (commit && L->counters[side] + T <= 0) return GIFT_ERR_NOT_READY;
   float* S = reinterpret_cast<float*>(L->state + (side == GIFT_SIDE_A ? L->sl.S_A : L->sl.S_G));
-  if (T > 0) GIFT_HIP(gift::launch_stats(d_x, dtype, T, ld, n, S, static_cast<hipStream_t>(stream)));
+  if (T > 0) {
+    unsigned* ssync = reinterpret_cast<unsigned*>(L->state + L->sl.ssync);
+    uint32_t* flags = reinterpret_cast<uint32_t*>(L->state + L->sl.flags);
+    const unsigned epoch = (unsigned)(++L->counters[7]);
+    GIFT_HIP(gift::launch_stats(d_x, dtype, T, ld, n, S, ssync, epoch, flags, device_cus(),
+                                static_cast<hipStream_t>(stream)));
+  }
   L->counters[side] += T;
   if (commit) return gift_commit_stats(L, side, stream);
   return GIFT_OK;

@@ -21,6 +21,8 @@ struct StateLayout {
          flags = 0, total = 0;
   // fused rank-k path: packed U operands, barrier counters, amax slots
   size_t ub = 0, ua = 0, esync = 0, dsync = 0, apub = 0;
+  // statistics: grow-only flags of the workgroups that share an output tile
+  size_t ssync = 0;
 };
 
 // Fused rank-k kernel geometry (48 x 768 tiles, 8 waves).
@@ -124,8 +126,13 @@ hipError_t launch_diag_apply(const float* x, int64_t ldx, int m, int d, const fl
                              int64_t ldo, int scaling, uint32_t* amax_slots, hipStream_t s);
 
 // Statistics.
-hipError_t launch_stats(const void* x, int dtype, int64_t T, int64_t ld, int n, float* S,
-                        hipStream_t s);
+// S += x^T x over T tokens (lower-triangle tiles).  The bf16 matrix-core
+// path splits the (tile, stage) work evenly over `cus` resident workgroups;
+// the workgroups sharing a tile add into S in a fixed order, handing over
+// through `sync` (grow-only, one word per workgroup) at `epoch`.
+constexpr int kStatsMaxGroups = 1024;
+hipError_t launch_stats(const void* x, int dtype, int64_t T, int64_t ld, int n, float* S, unsigned* sync,
+                        unsigned epoch, uint32_t* flags, int cus, hipStream_t s);
 hipError_t launch_commit(float* S, float* A, int n, double inv_count, float beta, int first,
                          hipStream_t s);
 

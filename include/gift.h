@@ -99,10 +99,11 @@ gift_status gift_layer_create(const gift_layer_desc* desc, void* d_state, size_t
 gift_status gift_layer_destroy(gift_layer_t layer);
 /* Host-side counters: [0] tokens pending in the A window, [1] tokens pending
  * in the G window, [2] commits of A, [3] commits of G, [4] refreshes,
- * [5] / [6] barrier epochs of the fused rank-k encode / decode (they must
- * travel with a copy of the state: the state's barrier counters only grow). */
-gift_status gift_layer_get_counters(gift_layer_t layer, int64_t h_counters[7]);
-gift_status gift_layer_set_counters(gift_layer_t layer, const int64_t h_counters[7]);
+ * [5] / [6] barrier epochs of the fused rank-k encode / decode, [7] barrier
+ * epoch of the statistics accumulation ([5]..[7] must travel with a copy of
+ * the state: the state's barrier words only grow). */
+gift_status gift_layer_get_counters(gift_layer_t layer, int64_t h_counters[8]);
+gift_status gift_layer_set_counters(gift_layer_t layer, const int64_t h_counters[8]);
 /* Reads the sticky device flags (GIFT_FLAG_*).  Synchronises `stream`. */
 gift_status gift_layer_flags(gift_layer_t layer, gift_stream_t stream, uint32_t* h_flags);
 /* Device addresses inside the state buffer, for inspection and for

@@ -185,6 +185,28 @@ def test_stats_exact_integer_bf16(fw):
     assert np.array_equal(A_gpu, A_gpu.T)
 
 
+def test_stats_ragged_tiles_bit_exact(fw):
+    """Matrix-core statistics on ragged shapes: n = 520 (two full 256-column
+    tiles and a partial one), T = 1000 (a partial 64-token stage), row
+    stride 528.  Integer activations in [-8, 8] keep every sum exact, so A
+    matches the oracle bit for bit; a second, Gaussian case is held to 1e-6."""
+    print("[stats ragged tiles]", flush=True)
+    rng = np.random.default_rng(43)
+    a = rng.integers(-8, 9, size=(1000, 528)).astype(np.float32)
+    x = torch.from_numpy(a).to(DEV).to(torch.bfloat16)[:, :520]
+    assert x.stride(0) == 528
+    L = fw.Layer(16, 520, "diag", device=DEV)
+    L.accumulate_stats(x, commit=True)
+    A_gpu = L.buffers()["A"].cpu().numpy()
+    assert np.array_equal(A_gpu, G.second_moment(a[:, :520]).astype(np.float32))
+    g = (rng.standard_normal((3000, 520)) * np.linspace(0.1, 3.0, 520)).astype(np.float32)
+    xg = torch.from_numpy(g).to(DEV).to(torch.bfloat16)
+    L2 = fw.Layer(16, 520, "diag", device=DEV)
+    L2.accumulate_stats(xg, commit=True)
+    ref = G.second_moment(xg.float().cpu().numpy())
+    assert rel_fro(L2.buffers()["A"].cpu().numpy(), ref) <= 1e-6
+
+
 def test_stats_split_windows_and_ema(fw):
     """Two accumulate calls in one window equal one call; EMA over 3 commits."""
     print("[stats windows / EMA]", flush=True)
