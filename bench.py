@@ -66,17 +66,42 @@ def main():
     case = synth.make_layer(4, device=dev, R=R)
     print(f"[bench] inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     L = fw.Layer(m, d, "lowrank", rank=k, oversample=16, power_iters=4, ema_decay=0.0, device=dev)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-    torch.cuda.synchronize()
-    ev[0].record()
     L.accumulate_stats(case.a_steps[0], fw.SIDE_A, commit=True)
-    ev[1].record()
     L.refresh(case.omega)
-    ev[2].record()
     torch.cuda.synchronize()
-    t_stats_ms = ev[0].elapsed_time(ev[1])
-    t_refresh_ms = ev[1].elapsed_time(ev[2])
     assert L.flags() == 0, "non-finite factor"
+
+    # ---- the statistics and refresh steps, timed warm (outside the unit)
+    def timed(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    scratch = fw.Layer(16, d, "diag", device=dev)    # its window absorbs the repeated batches
+    t_stats_ms = timed(lambda: scratch.accumulate_stats(case.a_steps[0], fw.SIDE_A))
+    del scratch
+    t_refresh_ms = timed(lambda: L.refresh(case.omega))
+    assert L.flags() == 0, "non-finite factor"
+    stats_flop = float(T) * d * (d + 1)                     # the symmetric triangle
+    refresh_flop = 12.0 * d * d * min(k + 16, d)            # six A X products of width l = 48
+    refresh_bytes = 6.0 * d * d * 4                          # A read by each product
+    stage_rooflines = {
+        "stats": {"ms": round(t_stats_ms, 4), "bound": "mfma", "achieved": round(stats_flop / t_stats_ms / 1e9, 1),
+                  "peak": BF16_PEAK_TFS, "unit": "TFLOP/s",
+                  "frac": round(stats_flop / t_stats_ms / 1e9 / BF16_PEAK_TFS, 4),
+                  "work": "A += a^T a, 16384 bf16 tokens x 6144 (triangle flops)"},
+        "refresh": {"ms": round(t_refresh_ms, 4), "bound": "fp64",
+                    "achieved": round(refresh_flop / t_refresh_ms / 1e9, 2), "peak": FP64_PEAK_TFS,
+                    "unit": "TFLOP/s", "frac": round(refresh_flop / t_refresh_ms / 1e9 / FP64_PEAK_TFS, 4),
+                    "hbm_frac": round(refresh_bytes / (t_refresh_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "work": "rank-32 subspace iteration (q = 4, l = 48) on the 6144 x 6144 A"},
+    }
 
     # ---- payloads: replica 0 is encoded inside each step; 1..R-1 in setup
     sets = []
@@ -140,7 +165,7 @@ def main():
     dom_bytes = dec_bytes
     dom_ms = t_dec
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    kernel = f"k_rank_{dominant}<0>"
+    kernel = f"k_rank_{dominant}<0, {R}, 0>"   # FP8 format, replica count, per-tensor scale
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(kernel, args.scaling),
                 "kernel": kernel,
@@ -159,8 +184,7 @@ def main():
                    "replicas": R, "tokens": T, "format": "e4m3", "scaling": args.scaling,
                    "cache": f"cold ({args.sets} rotating buffer sets)"},
         "roofline": roofline,
-        "setup": {"stats_ms": round(t_stats_ms, 3), "refresh_ms": round(t_refresh_ms, 3),
-                  "stats_tflops_triangle": round(T * d * (d + 1) / (t_stats_ms * 1e-3) / 1e12, 2)},
+        "stage_rooflines": stage_rooflines,
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu:
