@@ -132,10 +132,13 @@ StateLayout state_layout(const gift_layer_desc& g) {
     const size_t ncb = (size_t)cdiv((int64_t)d, 32);
     s.ub = take(ncb * 6 * 1024);
     s.ua = take(ncb * 6 * 1024);
-    const size_t ngr = (size_t)fused_groups(g);
-    s.esync = take(ngr * 64);
-    s.dsync = take(ngr * 64);
-    s.apub = take(((size_t)fused_groups(g) * fused_cg(g) * 17 + 16) * 8);   // [tiles][16] + group words
+    // tagged projection partials [tiles][48 x 32], then the row-group sums
+    // [row groups][48 x 32]
+    s.xpub = take((size_t)fused_groups(g) * (fused_cg(g) + 1) * kFusedTR * 32 * 8);
+    {
+      const size_t tiles = (size_t)fused_groups(g) * fused_cg(g);   // [tiles][16] + the per-tensor copies
+      s.apub = take((tiles * 16 + (size_t)kAmaxCopies * amax_copy_stride((int)tiles)) * 8);
+    }
   }
   if (g.transform == GIFT_DIAG) s.coef = take(2 * d * 4);
   if (g.transform == GIFT_CHOL_INPUT || g.transform == GIFT_CHOL_TWOSIDED) {
@@ -164,7 +167,6 @@ WorkLayout work_layout(const gift_layer_desc& g) {
   if (g.transform == GIFT_CHOL_TWOSIDED) w.tmp = take(m * d * 4);
   if (g.transform == GIFT_LOWRANK) {
     w.ppart = take((size_t)cdiv((int64_t)d, kProjChunk) * m * 32 * 4);
-    w.xch = take((size_t)fused_groups(g) * fused_cg(g) * kFusedTR * 32 * 4);
     const size_t lp = (size_t)lp_of(l_of(g));
     w.Y = take(d * lp * 8);
     w.Q = take(d * lp * 8);
@@ -441,8 +443,7 @@ gift_status gift_encode(gift_layer_t L, const float* d_W, int64_t ldw, int32_t f
     a.ub = reinterpret_cast<const uint4*>(L->state + L->sl.ub);
     a.ua = reinterpret_cast<const uint4*>(L->state + L->sl.ua);
     a.coef = reinterpret_cast<const float*>(L->state + L->sl.coef);
-    a.xch = reinterpret_cast<float*>(work + L->wl.xch);
-    a.gsync = reinterpret_cast<unsigned*>(L->state + L->sl.esync);
+    a.xpub = reinterpret_cast<unsigned long long*>(L->state + L->sl.xpub);
 
     a.apub = reinterpret_cast<unsigned long long*>(L->state + L->sl.apub);
     a.flags = flags;
@@ -551,8 +552,7 @@ gift_status gift_decode_reduce(gift_layer_t L, const uint8_t* d_codes, int64_t c
     a.ub = reinterpret_cast<const uint4*>(L->state + L->sl.ub);
     a.ua = reinterpret_cast<const uint4*>(L->state + L->sl.ua);
     a.coef = reinterpret_cast<const float*>(L->state + L->sl.coef);
-    a.xch = reinterpret_cast<float*>(work + L->wl.xch);
-    a.gsync = reinterpret_cast<unsigned*>(L->state + L->sl.dsync);
+    a.xpub = reinterpret_cast<unsigned long long*>(L->state + L->sl.xpub);
 
     a.flags = reinterpret_cast<uint32_t*>(L->state + L->sl.flags);
     a.qcodes = d_codes;

@@ -19,14 +19,20 @@ __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 
 struct StateLayout {
   size_t S_A = 0, A = 0, S_G = 0, G = 0, U = 0, coef = 0, tinv_a = 0, t_a = 0, lg_inv = 0, lg = 0,
          flags = 0, total = 0;
-  // fused rank-k path: packed U operands, barrier counters, amax slots
-  size_t ub = 0, ua = 0, esync = 0, dsync = 0, apub = 0;
+  // fused rank-k path: packed U operands, tagged projection partials and
+  // amax words
+  size_t ub = 0, ua = 0, xpub = 0, apub = 0;
   // statistics: grow-only flags of the workgroups that share an output tile
   size_t ssync = 0;
 };
 
 // Fused rank-k kernel geometry (48 x 768 tiles, 8 waves).
 constexpr int kFusedTR = 48, kFusedTC = 768;
+// Per-tensor amax words of the fused encode: kAmaxCopies copies of the
+// [tiles] array, each on its own 4 KiB page(s), so that no single memory
+// channel serves every workgroup's reads.
+constexpr int kAmaxCopies = 16;
+__host__ __device__ inline int amax_copy_stride(int tiles) { return (tiles + 511) / 512 * 512; }
 
 // Arguments of the fused encode (mode 0) / decode-reduce (mode 1) kernel.
 struct FusedArgs {
@@ -37,9 +43,8 @@ struct FusedArgs {
   const uint4* ub;
   const uint4* ua;
   const float* coef;
-  float* xch;                 // workspace: projection partials [tiles][48][32]
-  unsigned* gsync;            // state: one grow-only counter per row group (64 B apart)
-  unsigned long long* apub;   // state: [tiles][16] epoch-tagged amax words
+  unsigned long long* xpub;   // state: tagged projection partials [tiles][48][32], then sums [row groups][48][32]
+  unsigned long long* apub;   // state: [tiles][16] epoch-tagged amax words, then kAmaxCopies x [tiles]
   unsigned* flags;
   const float* amax_in;
   float* amax_out;
@@ -81,7 +86,6 @@ struct WorkLayout {
   size_t tmp = 0;       // fp32 [m][d]: second buffer (two-sided)
   size_t ppart = 0;     // fp32 [nchunk][m][k]: projection partials
   size_t amax = 0;      // uint32 [nblk]
-  size_t xch = 0;       // fp32 [tiles][48][32]: fused-path projection partials
   // refresh
   size_t Y = 0, Q = 0, Z = 0;   // fp64 [d][l]
   size_t small = 0;             // fp64 scratch for the l x l solvers

@@ -224,6 +224,38 @@ __device__ __forceinline__ void accum_codes(float (*acc)[16], float* acct, const
   for (int k = 0; k < 8; ++k) acct[k] = first ? s * v[k] : acct[k] + s * v[k];
 }
 
+// Projection / reconstruction operands of one wave's three column blocks,
+// [column block q][half or group][piece], read through a buffer resource
+// so that blocks past the last column read zeros instead of memory.
+struct UOps {
+  bf16x8 u[3][2][3];
+};
+
+__device__ __forceinline__ void load_uops(const uint4* packed, int d, int cbg0, UOps& o) {
+  const auto rs = make_rsrc(packed, cdiv(d, 32) * 6 * 1024);
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int q = 0; q < 3; ++q)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        const int off = ((((cbg0 + 8 * q) * 2 + h) * 3 + p) * 64 + lane) * 16;
+        o.u[q][h][p] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+      }
+}
+
+// Published projection words: (tag << 32) | float bits.  The tag makes each
+// word self-validating, so a producer never waits for its own stores (on
+// this architecture that wait would also wait for every load in flight) and
+// readers need no separate barrier: they read until every word carries it.
+__device__ __forceinline__ unsigned long long tagged(unsigned tag, float v) {
+  return ((unsigned long long)tag << 32) | __float_as_uint(v);
+}
+
+constexpr int kXW = TR * 32;        // projection words per tile (1536)
+constexpr int kXPT = kXW / 512;     // of them per thread (3)
+
 // SC: the decode's scaling (0 per tensor, 1 per block) as a compile-time
 // constant (-1: read at run time).  Per tensor, each replica's scale is one
 // uniform word read in the replica loop; per block the scales of the tile's
@@ -232,6 +264,12 @@ __device__ __forceinline__ void accum_codes(float (*acc)[16], float* acct, const
 // replica loop is unrolled, so every wait on a load names exactly the loads
 // it needs (a runtime trip count rotates the buffers through different
 // registers per iteration and the waits become full drains).
+//
+// Order of the memory operations (loads retire in order, so whatever is
+// needed first is issued first): tile data, then the projection operands;
+// the projection partials go out with atomic exchanges nobody waits for;
+// the reconstruction operands are requested before the partner partials are
+// read, so they arrive while the row group finishes its own partials.
 template <int FMT, bool ENC, int RC, int SC>
 __device__ __forceinline__ void fused_body(const FusedArgs& a) {
   // The staged tile (fp32, padded rows); after it has been read into
@@ -247,18 +285,23 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
   float (*pf)[33] = reinterpret_cast<float (*)[33]>(smem + 8 * 3 * 16 * 33);
   const int G = gridDim.x;
   const int g = blockIdx.x, rg = g / a.CG, cgi = g % a.CG;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
   const int lr = lane & 15, lg = lane >> 4;
   const int row0 = rg * TR, col0 = cgi * TC;
   const int m = a.m, d = a.d;
   constexpr bool enc = ENC;
   const int nbd = (int)cdiv(d, kBlock);
   const int rb0 = row0 / kBlock, cb0 = col0 / kBlock;
+  const int cbg0 = (col0 >> 5) + wave;   // this wave's first 32-column block
+  const unsigned tag = (a.epoch << 1) | (enc ? 0u : 1u);
+  if (tid < 16) wmax[tid] = 0u;
 
   float x[NSUB][8];
   bool live[3];
 #pragma unroll
   for (int q = 0; q < 3; ++q) live[q] = col0 + (wave + 8 * q) * 32 < d;
+  UOps uo;
 
   // ---- stream the tile in (flat, coalesced) and stage it in LDS --------------
   if (enc) {
@@ -271,6 +314,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
       v[j] = __builtin_amdgcn_raw_buffer_load_b128(wr, ok ? (int)(((int64_t)(row0 + r) * a.ldw + col0 + c) * 4) : kOff,
                                                    0, 0);
     }
+    load_uops(a.ub, d, cbg0, uo);
 #pragma unroll
     for (int j = 0; j < 2 * kCPT; ++j) {
       const int q = tid + 512 * j, r = q / 192, c = (q % 192) * 4;
@@ -292,15 +336,17 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
     const bool okt = row0 + rt < m && col0 + ct < d;
     const int offt = okt ? (row0 + rt) * d + col0 + ct : kOff;
     const int sidxt = (a.scaling == 0 || !okt) ? 0 : ((row0 + rt) / kBlock - rb0) * 6 + (col0 + ct) / kBlock - cb0;
-    // The scale words are loaded first, then the first two replicas' codes;
-    // storing the scales into LDS then waits only for the older scale loads
-    // (loads retire in order), while the code stream stays in flight.
     float acc[kDCPT][16], acct[8];
     CodeBuf b0, b1, b2;
     constexpr bool PT = SC == 0;
+    // the projection operands go out right behind the last replica's codes
+    auto load = [&](int r, CodeBuf& b) {
+      load_codes<FMT>(a, R, r, off, offt, b);
+      if (RC > 0 && r == R - 1) load_uops(a.ub, d, cbg0, uo);
+    };
     if constexpr (PT) {
-      load_codes<FMT>(a, R, 0, off, offt, b0);
-      load_codes<FMT>(a, R, 1, off, offt, b1);
+      load(0, b0);
+      load(1, b1);
     } else {
       // The last wave stages the block scales in LDS before it starts its
       // code stream; the other waves start theirs at once.  (A scale load
@@ -313,20 +359,20 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
           ssc[r][e] = (br < nbm && bc < nbd) ? a.qscales[(int64_t)r * a.scale_stride + br * nbd + bc] : 0.f;
         }
       }
-      load_codes<FMT>(a, R, 0, off, offt, b0);
-      load_codes<FMT>(a, R, 1, off, offt, b1);
+      load(0, b0);
+      load(1, b1);
       __syncthreads();
     }
     // per-tensor scale of replica r: a uniform word (scalar load)
     auto rscale = [&](int r) -> float { return PT ? a.qscales[(int64_t)r * a.scale_stride] : 0.f; };
     auto three = [&](int r) -> bool {   // replicas r .. r + 2; false once past R
-      load_codes<FMT>(a, R, r + 2, off, offt, b2);
+      load(r + 2, b2);
       accum_codes<FMT, PT>(acc, acct, b0, ssc[r], rscale(r), sidx, sidxt, hi, r == 0);
       if (r + 1 >= R) return false;
-      load_codes<FMT>(a, R, r + 3, off, offt, b0);
+      load(r + 3, b0);
       accum_codes<FMT, PT>(acc, acct, b1, ssc[r + 1], rscale(r + 1), sidx, sidxt, hi, false);
       if (r + 2 >= R) return false;
-      load_codes<FMT>(a, R, r + 4, off, offt, b1);
+      load(r + 4, b1);
       accum_codes<FMT, PT>(acc, acct, b2, ssc[r + 2], rscale(r + 2), sidx, sidxt, hi, false);
       return true;
     };
@@ -337,6 +383,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
     } else {
       for (int r = 0; r < R; r += 3)
         if (!three(r)) break;
+      load_uops(a.ub, d, cbg0, uo);
     }
     const float ir = a.invR;
 #pragma unroll
@@ -367,145 +414,167 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
   __syncthreads();
 
   // ---- projection P = X U (partials of this tile) ---------------------------
-  floatx4 acc[3][2];
-#pragma unroll
-  for (int rb = 0; rb < 3; ++rb)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) acc[rb][h] = (floatx4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int q = 0; q < 3; ++q) {
-    if (!live[q]) continue;
-    const int cbg = (col0 >> 5) + wave + 8 * q;
-    bf16x8 u[2][3];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint4* ub = a.ub + ((int64_t)(cbg * 2 + h) * 3) * 64 + lane;
-      u[h][0] = as_bf16x8(ub[0]);
-      u[h][1] = as_bf16x8(ub[64]);
-      u[h][2] = as_bf16x8(ub[128]);
-    }
-#pragma unroll
-    for (int rb = 0; rb < 3; ++rb) {
-      const int i = q * 3 + rb;
-      bf16x8 xh, xm, xl;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        __bf16 h, mm, l;
-        split3(x[i][j], h, mm, l);
-        xh[j] = h;
-        xm[j] = mm;
-        xl[j] = l;
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        floatx4 c = acc[rb][h];
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xm, u[h][1], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, u[h][2], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, u[h][0], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, u[h][1], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xm, u[h][0], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, u[h][0], c, 0, 0, 0);
-        acc[rb][h] = c;
-      }
-    }
-  }
-#pragma unroll
-  for (int rb = 0; rb < 3; ++rb)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) cp[wave][rb][4 * lg + e][lr + 16 * h] = acc[rb][h][e];
-  __syncthreads();
-  // sum the 8 waves (fixed order) and publish this tile's partial: 768
-  // 64-bit words, each an exchange at device scope
   {
-    unsigned long long* xg = reinterpret_cast<unsigned long long*>(a.xch + (int64_t)g * TR * 32);
-    for (int e = tid; e < TR * 16; e += 512) {
-      const int r = e >> 4, k = (e & 15) * 2;
-      float s0 = cp[0][r >> 4][r & 15][k], s1 = cp[0][r >> 4][r & 15][k + 1];
+    floatx4 acc[3][2];
 #pragma unroll
-      for (int w = 1; w < 8; ++w) {
-        s0 += cp[w][r >> 4][r & 15][k];
-        s1 += cp[w][r >> 4][r & 15][k + 1];
-      }
-      const unsigned long long v = (unsigned long long)__float_as_uint(s0) |
-                                   ((unsigned long long)__float_as_uint(s1) << 32);
-      atomicExch(xg + e, v);
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) {
-    unsigned* gc = a.gsync + rg * 16;
-    atomicAdd(gc, 1u);
-    wait_reach(gc, (unsigned)a.CG * a.epoch, a.flags);
-  }
-  __syncthreads();
-  // the row group's partials, summed in column-group order, times c
-  {
-    const float* cvec = a.coef + (enc ? 0 : 32);
-    const unsigned long long* base =
-        reinterpret_cast<const unsigned long long*>(a.xch + (int64_t)rg * a.CG * TR * 32);
-    for (int e = tid; e < TR * 16; e += 512) {
-      unsigned long long v[16];
-      const int cg = a.CG;
+    for (int rb = 0; rb < 3; ++rb)
 #pragma unroll
-      for (int h = 0; h < 16; ++h) v[h] = h < cg ? ld_dev64(base + (int64_t)h * TR * 16 + e) : 0ull;
-      float s0 = __uint_as_float((uint32_t)v[0]), s1 = __uint_as_float((uint32_t)(v[0] >> 32));
+      for (int h = 0; h < 2; ++h) acc[rb][h] = (floatx4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int h = 1; h < 16; ++h) {
-        if (h < cg) {
-          s0 += __uint_as_float((uint32_t)v[h]);
-          s1 += __uint_as_float((uint32_t)(v[h] >> 32));
+    for (int q = 0; q < 3; ++q) {
+      if (!live[q]) continue;
+#pragma unroll
+      for (int rb = 0; rb < 3; ++rb) {
+        const int i = q * 3 + rb;
+        bf16x8 xh, xm, xl;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          __bf16 h, mm, l;
+          split3(x[i][j], h, mm, l);
+          xh[j] = h;
+          xm[j] = mm;
+          xl[j] = l;
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const bf16x8* u = uo.u[q][h];
+          floatx4 c = acc[rb][h];
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xm, u[1], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, u[2], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, u[0], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, u[1], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xm, u[0], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, u[0], c, 0, 0, 0);
+          acc[rb][h] = c;
         }
       }
-      for (int h = 16; h < cg; ++h) {   // more than 16 column groups (d > 12288)
-        const unsigned long long w = ld_dev64(base + (int64_t)h * TR * 16 + e);
-        s0 += __uint_as_float((uint32_t)w);
-        s1 += __uint_as_float((uint32_t)(w >> 32));
+    }
+#pragma unroll
+    for (int rb = 0; rb < 3; ++rb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cp[wave][rb][4 * lg + e][lr + 16 * h] = acc[rb][h][e];
+  }
+  __syncthreads();
+  // sum the 8 waves (fixed order) and publish this tile's partial: word
+  // e = 32 row + k of the tile, one atomic exchange each (it takes effect at
+  // the device's coherence point; nobody waits for it)
+  unsigned long long* xg = a.xpub + (int64_t)g * kXW;
+#pragma unroll
+  for (int j = 0; j < kXPT; ++j) {
+    const int e = tid + 512 * j, r = e >> 5, k = e & 31;
+    float s = cp[0][r >> 4][r & 15][k];
+#pragma unroll
+    for (int w = 1; w < 8; ++w) s += cp[w][r >> 4][r & 15][k];
+    __hip_atomic_exchange(xg + e, tagged(tag, s), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // the reconstruction operands, before the partner words
+  load_uops(a.ua, d, cbg0, uo);
+  // Reduce-scatter, then all-gather, inside the row group: workgroup cgi
+  // sums the slice [cgi S, cgi S + S) of the 48 x 32 words over the CG
+  // partials (in column-group order) and publishes the sums; every workgroup
+  // then reads the row group's sums.  Each word is read until it carries this
+  // call's tag.  (Each workgroup reading every partial would move CG times
+  // the data through the device-scope path on every polling round.)
+  {
+    const int cg = a.CG;
+    const unsigned long long* rowpub = a.xpub + (int64_t)rg * cg * kXW;
+    unsigned long long* sums = a.xpub + (int64_t)G * kXW + (int64_t)rg * kXW;
+    const int S = (kXW + cg - 1) / cg;
+    for (int t = tid; t < S; t += 512) {   // one pass unless CG < 3
+      const int e = cgi * S + t;
+      if (e >= kXW) break;
+      float s = 0.f;
+      for (int h0 = 0; h0 < cg; h0 += 16) {
+        unsigned long long w[16];
+        int spins = 0;
+        for (;;) {
+          // all loads first, then the tests (a test inside the load's
+          // branch would wait for each load in turn); partners past the
+          // row group are not read
+#pragma unroll
+          for (int h = 0; h < 16; ++h)
+            if (h0 + h < cg) w[h] = ld_dev64(rowpub + (int64_t)(h0 + h) * kXW + e);
+          bool ok = true;
+#pragma unroll
+          for (int h = 0; h < 16; ++h) ok = ok && (h0 + h >= cg || (unsigned)(w[h] >> 32) == tag);
+          if (ok) break;
+          if (++spins > kSpinLimit) {
+            atomicOr(a.flags, (unsigned)GIFT_FLAG_SPIN_TIMEOUT);
+            break;
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < 16; ++h) {
+          const float v = __uint_as_float((uint32_t)w[h]);
+          if (h0 + h == 0)
+            s = v;
+          else if (h0 + h < cg)
+            s += v;
+        }
       }
-      const int r = e >> 4, k = (e & 15) * 2;
-      pf[r][k] = s0 * cvec[k];
-      pf[r][k + 1] = s1 * cvec[k + 1];
+      __hip_atomic_exchange(sums + e, tagged(tag, s), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const float* cvec = a.coef + (enc ? 0 : 32);
+    unsigned long long w[kXPT];
+    int spins = 0;
+    for (;;) {
+      bool ok = true;
+#pragma unroll
+      for (int j = 0; j < kXPT; ++j) {
+        w[j] = ld_dev64(sums + tid + 512 * j);
+        ok = ok && (unsigned)(w[j] >> 32) == tag;
+      }
+      if (ok) break;
+      if (++spins > kSpinLimit) {
+        atomicOr(a.flags, (unsigned)GIFT_FLAG_SPIN_TIMEOUT);
+        break;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kXPT; ++j) {
+      const int e = tid + 512 * j;
+      pf[e >> 5][e & 31] = __uint_as_float((uint32_t)w[j]) * cvec[e & 31];
     }
   }
   __syncthreads();
 
   // ---- reconstruction X~ = alpha X + (P c) U^T ------------------------------
-  const float alpha = a.coef[64 + (enc ? 0 : 1)];
-  bf16x8 ph[3], pm[3], pl[3];
+  {
+    const float alpha = a.coef[64 + (enc ? 0 : 1)];
+    bf16x8 ph[3], pm[3], pl[3];
 #pragma unroll
-  for (int rb = 0; rb < 3; ++rb) {
+    for (int rb = 0; rb < 3; ++rb) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      __bf16 h, mm, l;
-      split3(pf[rb * 16 + lr][8 * lg + j], h, mm, l);
-      ph[rb][j] = h;
-      pm[rb][j] = mm;
-      pl[rb][j] = l;
+      for (int j = 0; j < 8; ++j) {
+        __bf16 h, mm, l;
+        split3(pf[rb * 16 + lr][8 * lg + j], h, mm, l);
+        ph[rb][j] = h;
+        pm[rb][j] = mm;
+        pl[rb][j] = l;
+      }
     }
-  }
 #pragma unroll
-  for (int q = 0; q < 3; ++q) {
-    if (!live[q]) continue;
-    const int cbg = (col0 >> 5) + wave + 8 * q;
+    for (int q = 0; q < 3; ++q) {
+      if (!live[q]) continue;
 #pragma unroll
-    for (int grp = 0; grp < 2; ++grp) {
-      const uint4* ua = a.ua + ((int64_t)(cbg * 2 + grp) * 3) * 64 + lane;
-      const bf16x8 uh = as_bf16x8(ua[0]), um = as_bf16x8(ua[64]), ul = as_bf16x8(ua[128]);
+      for (int grp = 0; grp < 2; ++grp) {
+        const bf16x8 uh = uo.u[q][grp][0], um = uo.u[q][grp][1], ul = uo.u[q][grp][2];
 #pragma unroll
-      for (int rb = 0; rb < 3; ++rb) {
-        const int i = q * 3 + rb;
-        floatx4 c = (floatx4){alpha * x[i][4 * grp], alpha * x[i][4 * grp + 1], alpha * x[i][4 * grp + 2],
-                              alpha * x[i][4 * grp + 3]};
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(um, pm[rb], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uh, pl[rb], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ul, ph[rb], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uh, pm[rb], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(um, ph[rb], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uh, ph[rb], c, 0, 0, 0);
+        for (int rb = 0; rb < 3; ++rb) {
+          const int i = q * 3 + rb;
+          floatx4 c = (floatx4){alpha * x[i][4 * grp], alpha * x[i][4 * grp + 1], alpha * x[i][4 * grp + 2],
+                                alpha * x[i][4 * grp + 3]};
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(um, pm[rb], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uh, pl[rb], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ul, ph[rb], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uh, pm[rb], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(um, ph[rb], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uh, ph[rb], c, 0, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[i][4 * grp + e] = c[e];
+          for (int e = 0; e < 4; ++e) x[i][4 * grp + e] = c[e];
+        }
       }
     }
   }
@@ -545,10 +614,9 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
       __builtin_amdgcn_raw_buffer_store_b128(v1, wh, (row < m && c + 16 < d) ? o + 64 : kOff, 0, 0);
     }
   }
-  // Blocks this tile touches: rows row0 .. row0 + 47 lie in at most two
-  // 128-row blocks (rb0, rb0 + 1); columns col0 .. col0 + 767 in the six
-  // 128-column blocks cb0 .. cb0 + 5 (col0 is a multiple of 768).
-  uint32_t smax[NSUB];
+  // |x| bit patterns order like |x| (NaN above +Inf): the lane maximum of
+  // each sub-tile.  Dead column blocks hold zeros.
+  uint32_t lmax[NSUB];
 #pragma unroll
   for (int i = 0; i < NSUB; ++i) {
     uint32_t v = 0;
@@ -557,41 +625,60 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
       const uint32_t b = absbits_f(x[i][j]);
       v = v > b ? v : b;
     }
+    lmax[i] = v;
+  }
+  // Blocks this tile touches: rows row0 .. row0 + 47 lie in at most two
+  // 128-row blocks (rb0, rb0 + 1); columns col0 .. col0 + 767 in the six
+  // 128-column blocks cb0 .. cb0 + 5 (col0 is a multiple of 768).  Local
+  // amax of this tile per block entry (2 x 6), or per tensor (entry 0).
+  if (a.scaling == 0) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int i = 0; i < NSUB; ++i) v = v > lmax[i] ? v : lmax[i];
     for (int o = 32; o > 0; o >>= 1) {
       const uint32_t u = (uint32_t)__shfl_xor((int)v, o, 64);
       v = v > u ? v : u;
     }
-    smax[i] = v;
-  }
-  // local amax of this tile, per block entry (2 x 6) or per tensor (entry 0)
-  if (tid < 16) wmax[tid] = 0u;
-  __syncthreads();
-  if (lane == 0) {
+    if (lane == 0) wmax[8 + wave] = v;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t t = wmax[8];
+#pragma unroll
+      for (int w = 1; w < 8; ++w) t = t > wmax[8 + w] ? t : wmax[8 + w];
+      wmax[0] = t;
+    }
+  } else {
 #pragma unroll
     for (int i = 0; i < NSUB; ++i) {
-      if (!live[i / 3] || smax[i] == 0u) continue;
-      const int e = a.scaling == 0 ? 0
-                                   : ((row0 + SUB_RB(i) * 16) / kBlock - rb0) * 6 + (col0 + SUB_CB(i) * 32) / kBlock - cb0;
-      atomicMax(&wmax[e], smax[i]);
+      uint32_t v = lmax[i];
+      for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t u = (uint32_t)__shfl_xor((int)v, o, 64);
+        v = v > u ? v : u;
+      }
+      if (lane == 0 && live[i / 3] && v != 0u) {
+        const int e = ((row0 + SUB_RB(i) * 16) / kBlock - rb0) * 6 + (col0 + SUB_CB(i) * 32) / kBlock - cb0;
+        atomicMax(&wmax[e], v);
+      }
     }
   }
-  __syncthreads();
-  const bool need_sync = a.amax_in == nullptr || a.amax_out != nullptr;
   if (tid < 16) blk[tid >> 3][tid & 7] = 0u;
   __syncthreads();
+  const bool need_sync = a.amax_in == nullptr || a.amax_out != nullptr;
   if (need_sync) {
     unsigned long long* pub = a.apub;
-    const unsigned long long tag = (unsigned long long)a.epoch << 32;
+    const unsigned long long etag = (unsigned long long)a.epoch << 32;
     // the tag makes each word self-validating: no ordering with other data
     // is needed.  The words are published with atomic exchanges, which take
-    // effect at the device's coherence point at once (a plain device-scope
-    // store became visible to other dies only microseconds later).
+    // effect at the device's coherence point at once.
     if (a.scaling == 0) {
-      // per tensor: one word per workgroup in a compact array, so a single
-      // wave reads all of them with a few coalesced loads per round
-      unsigned long long* pt = pub + (int64_t)G * kApub;
-      if (tid == 0) atomicExch(pt + g, tag | wmax[0]);
+      // per tensor: one word per workgroup, written into kAmaxCopies copies
+      // of a compact array (lane c of wave 0 writes copy c); workgroup g
+      // reads copy g % kAmaxCopies with one wave, a few coalesced loads per
+      // round
+      const int cstride = amax_copy_stride(G);
+      unsigned long long* pt = pub + (int64_t)G * kApub + (int64_t)(g % kAmaxCopies) * cstride;
       if (wave == 0) {
+        if (lane < kAmaxCopies) atomicExch(pub + (int64_t)G * kApub + (int64_t)lane * cstride + g, etag | wmax[0]);
         uint32_t v = 0;
         for (int base = 0; base < G; base += 256) {
           unsigned long long w[4];
@@ -600,7 +687,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int h = base + lane + 64 * j;
-              w[j] = h < G ? ld_dev64(pt + h) : tag;
+              w[j] = h < G ? ld_dev64(pt + h) : etag;
             }
             bool ok = true;
 #pragma unroll
@@ -621,7 +708,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
         if (lane == 0) blk[0][0] = v;
       }
     } else {
-      if (tid < kApub) atomicExch(pub + (int64_t)g * kApub + tid, tag | wmax[tid]);
+      if (tid < kApub) atomicExch(pub + (int64_t)g * kApub + tid, etag | wmax[tid]);
       // the tiles of this column group whose rows meet blocks rb0, rb0 + 1
       const int r_lo = (rb0 * kBlock) / TR;
       const int r_hi = min((int)cdiv(m, TR) - 1, ((rb0 + 2) * kBlock - 1) / TR);
@@ -676,7 +763,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
     uint32_t q0, q1;
     if (am >= 0x7F800000u) {
       q0 = q1 = 0x7F7F7F7Fu;
-    } else if (smax[i] >= 0x7F800000u) {
+    } else if (lmax[i] >= 0x7F800000u) {
       // a non-finite element under a finite shared amax: exact integer path
       uint32_t e[8];
 #pragma unroll
