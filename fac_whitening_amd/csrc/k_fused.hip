@@ -21,14 +21,17 @@
 //    the six products h*h, h*m, m*h, h*l, l*h, m*m are accumulated in fp32;
 //    what is dropped is below 2^-26 of each product.
 //  * P needs whole rows: the workgroups of one row group (same 48 rows)
-//    publish their partial P through device-scope atomics in the workspace,
-//    meet at a counter barrier, and sum the partials in a fixed order.
+//    publish their partial P as epoch-tagged words in the layer state; each
+//    sums one slice of the partials in column-group order and publishes the
+//    sums (a reduce-scatter), then every workgroup reads the row group's
+//    sums.  A reader re-reads a word until it carries the call's tag, so
+//    there is no barrier and no writer ever waits for its own stores.
 //  * Encode: every workgroup publishes its tile's amax (per tensor, or per
 //    128 x 128 block it touches) as 64-bit words tagged with the call's
 //    epoch, and reads the words of the workgroups it depends on until all
 //    carry the current epoch (an all-gather: no serial chain of atomics).
-//  * Counters and tags live in the layer state and only grow, so nothing is
-//    reset between calls.  Every wait is bounded; a timeout sets
+//  * Tags derive from per-direction call counters that only grow, so
+//    nothing is reset between calls.  Every wait is bounded; a timeout sets
 //    GIFT_FLAG_SPIN_TIMEOUT and the kernel still exits.
 #include "fp8_codec.hpp"
 #include "gift_internal.hpp"

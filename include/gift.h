@@ -99,9 +99,10 @@ gift_status gift_layer_create(const gift_layer_desc* desc, void* d_state, size_t
 gift_status gift_layer_destroy(gift_layer_t layer);
 /* Host-side counters: [0] tokens pending in the A window, [1] tokens pending
  * in the G window, [2] commits of A, [3] commits of G, [4] refreshes,
- * [5] / [6] barrier epochs of the fused rank-k encode / decode, [7] barrier
- * epoch of the statistics accumulation ([5]..[7] must travel with a copy of
- * the state: the state's barrier words only grow). */
+ * [5] / [6] call epochs of the fused rank-k encode / decode (the tags of
+ * their exchange words), [7] barrier epoch of the statistics accumulation
+ * ([5]..[7] must travel with a copy of the state: the words they tag in the
+ * state only grow). */
 gift_status gift_layer_get_counters(gift_layer_t layer, int64_t h_counters[8]);
 gift_status gift_layer_set_counters(gift_layer_t layer, const int64_t h_counters[8]);
 /* Reads the sticky device flags (GIFT_FLAG_*).  Synchronises `stream`. */
@@ -242,7 +243,7 @@ int32_t gift_last_hip_error(void);
  * within the same tolerances; the persistent kernels keep the tile in
  * registers and read the gradient once.  Returns the previous setting.
  * Calls on one layer must be ordered on one stream (the persistent kernels
- * synchronise their workgroups through counters in the layer state). */
+ * exchange epoch-tagged words through the layer state). */
 int32_t gift_set_fused(int32_t enable);
 
 #ifdef __cplusplus
