@@ -39,7 +39,10 @@ def parse():
     p.add_argument("--scaling", default="tensor", choices=["tensor", "block"])
     p.add_argument("--sets", type=int, default=4)
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
-    p.add_argument("--extra", action="store_true", help="also time statistics / refresh / Euclidean")
+    p.add_argument("--config", default="unit", choices=["unit", "selective", "stress"],
+                   help="unit: the headline encode + decode unit (default); selective: the whole "
+                        "600M-class gradient buffer (168 tensors, 13 rank-32); stress: one step of "
+                        "the 4096 x 16384 stress layer (statistics, refresh, encode, decode R = 16)")
     return p.parse_args()
 
 
@@ -57,6 +60,10 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.config == "selective":
+        return bench_selective(args, torch, fw, synth, dev)
+    if args.config == "stress":
+        return bench_stress(args, torch, fw, synth, dev)
     m, d, T, R, k = 1536, 6144, 16384, 8, 32
     scaling = fw.SCALINGS[args.scaling]
     nb = fw.nblocks(m, d, scaling)
@@ -189,6 +196,141 @@ def main():
     }
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(case, L, R, m, d, args.scaling)
+    print(json.dumps(result), flush=True)
+
+
+def _event_ms(torch, fn, reps):
+    """Mean event-timed milliseconds of fn() over reps calls (one untimed call first)."""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def bench_selective(args, torch, fw, synth, dev):
+    """Whole-buffer encode + decode-reduce of the 600M-class deployment: 168
+    weight gradients (906M fp32 values, 3.62 GB), the fc2 gradients of 13
+    layers rank-32 whitened, the other 155 Euclidean; E4M3 per tensor,
+    R = 8 (replicas 1..7 encoded in setup).  One step = every tensor's
+    encode of replica 0 and decode-reduce, in order on one stream.  The
+    rank-32 layers' statistics (T = 8192 bf16 tokens) and refresh run in
+    setup.  Gradients: the direct Gaussian draw (synth.direct_gradient)."""
+    R, Ttok = 8, 8192
+    f, s = fw.E4M3, fw.SCALE_TENSOR
+    items = []
+    t0 = time.time()
+    state_gift = 0
+    for (l, name, mo, di, alpha, gift) in synth.selective_tensors():
+        seed = lambda r: synth.seed_for(3, synth.ROLE_A, l * 8 + list(synth.SELECTIVE_SHAPES).index(name), r)
+        if gift:
+            L = fw.Layer(mo, di, "lowrank", device=dev)
+            a = synth.gaussian_rows(Ttok, di, alpha, None, synth.seed_for(3, synth.ROLE_A, l, 0, 1), dev,
+                                    torch.bfloat16)
+            L.accumulate_stats(a, fw.SIDE_A, commit=True)
+            del a
+            L.refresh(synth.omega(di, 48, synth.seed_for(3, synth.ROLE_OMEGA, l), dev))
+            state_gift += L.state.numel()
+        else:
+            L = fw.Layer(mo, di, "euclid", device=dev)
+        codes = torch.empty(R, mo, di, dtype=torch.uint8, device=dev)
+        scales = torch.empty(R, 1, dtype=torch.float32, device=dev)
+        for r in range(1, R):
+            Wr = synth.direct_gradient(mo, di, alpha, Ttok, seed(r), dev)
+            L.encode(Wr, f, s, codes=codes[r], scales=scales[r])
+            del Wr
+        W0 = synth.direct_gradient(mo, di, alpha, Ttok, seed(0), dev)
+        items.append((L, W0, codes, scales, torch.empty(mo, di, dtype=torch.float32, device=dev), gift))
+    torch.cuda.synchronize()
+    assert all(L.flags() == 0 for L, *_ in items)
+    print(f"[bench selective] {len(items)} tensors ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    def step():
+        for L, W0, codes, scales, out, _ in items:
+            L.encode(W0, f, s, codes=codes[0], scales=scales[0])
+            L.decode_reduce(codes, scales, f, s, out=out)
+
+    steps = max(1, min(args.steps, 20))
+    ms = _event_ms(torch, step, steps)
+    n = sum(W0.numel() for _, W0, *_ in items)
+    alg = sum((4.0 + 1 + 4) * W0.numel() + R * W0.numel() + 4 * (R + 1) for _, W0, *_ in items)
+    n_gift = sum(1 for it in items if it[5])
+    grad_bytes = 4.0 * n
+    result = {
+        "metric": "whole-buffer encode+decode GB/s of fp32 grad (600M-class selective deployment)",
+        "value": round(grad_bytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": "f32",
+        "data": "synthetic (direct Gaussian gradients, bf16 power-law activations for the rank-32 layers)",
+        "config": {"workload": "600M-class selective: 24 layers x {q,k,v,o 1536x1536, fc1/fc3 6144x1536, "
+                               "fc2 1536x6144}; fc2 of layers 0-12 rank-32, the rest Euclidean; E4M3 per "
+                               "tensor; R=8", "tensors": len(items), "rank32_tensors": n_gift, "params": n},
+        "roofline": {"bound": "hbm", "achieved": round(alg / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "alg_bytes": int(alg)},
+        "memory": {"grad_bytes": int(grad_bytes), "rank32_state_bytes": int(state_gift),
+                   "state_over_grad": round(state_gift / grad_bytes, 4)},
+    }
+    print(json.dumps(result), flush=True)
+
+
+def bench_stress(args, torch, fw, synth, dev):
+    """One step of the stress layer (W 4096 x 16384, heavy-tailed): statistics
+    of T = 8192 bf16 tokens and commit, rank-32 refresh (every step), encode
+    of replica 0 and decode-reduce of R = 16 payloads, E5M2 per 128 x 128
+    block (replicas 1..15 encoded in setup).  Each stage event-timed."""
+    m, d, Ttok, R = 4096, 16384, 8192, 16
+    f, s = fw.E5M2, fw.SCALE_BLOCK128
+    nb = fw.nblocks(m, d, s)
+    a = synth.stress_activations(Ttok, d, 0, dev)
+    om = synth.omega(d, 48, synth.seed_for(5, synth.ROLE_OMEGA), dev)
+    L = fw.Layer(m, d, "lowrank", device=dev)
+    L.accumulate_stats(a, fw.SIDE_A, commit=True)
+    L.refresh(om)
+    codes = torch.empty(R, m, d, dtype=torch.uint8, device=dev)
+    scales = torch.empty(R, nb, dtype=torch.float32, device=dev)
+    for r in range(1, R):
+        Wr = synth.stress_gradient(m, d, 0, r, dev)
+        L.encode(Wr, f, s, codes=codes[r], scales=scales[r])
+        del Wr
+    W0 = synth.stress_gradient(m, d, 0, 0, dev)
+    out = torch.empty(m, d, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    assert L.flags() == 0
+    reps = 5
+    t_stats = _event_ms(torch, lambda: L.accumulate_stats(a, fw.SIDE_A, commit=True), reps)
+    t_refresh = _event_ms(torch, lambda: L.refresh(om), reps)
+
+    def unit():
+        L.encode(W0, f, s, codes=codes[0], scales=scales[0])
+        L.decode_reduce(codes, scales, f, s, out=out)
+    t_unit = _event_ms(torch, unit, reps)
+    assert L.flags() == 0
+    n = m * d
+    alg = (4.0 + 1) * n + R * n + 4.0 * n + 4 * nb * (R + 1) + d * 32 * 4 * 2
+    stats_flop = float(Ttok) * d * (d + 1)
+    refresh_flop = 12.0 * d * d * 48
+    result = {
+        "metric": "stress layer step: encode+decode GB/s of fp32 grad (4096x16384, R=16, E5M2 per block)",
+        "value": round(4.0 * n / (t_unit * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": reps,
+        "ms_per_step": round(t_stats + t_refresh + t_unit, 4), "higher_is_better": True, "dtype": "f32",
+        "data": "synthetic (Student-t(3) x i^-1.5 column scales, 0.1% outlier columns x100)",
+        "config": {"workload": "stress 4096x16384, rank-32 refreshed every step (q=4, p=16), E5M2 per "
+                               "128x128 block, R=16", "tokens": Ttok},
+        "stages_ms": {"stats_commit": round(t_stats, 4), "refresh": round(t_refresh, 4),
+                      "encode_decode": round(t_unit, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(alg / (t_unit * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(alg / (t_unit * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "alg_bytes": int(alg)},
+        "stage_rooflines": {
+            "stats": {"achieved": round(stats_flop / t_stats / 1e9, 1), "peak": BF16_PEAK_TFS, "unit": "TFLOP/s",
+                      "frac": round(stats_flop / t_stats / 1e9 / BF16_PEAK_TFS, 4)},
+            "refresh": {"achieved": round(refresh_flop / t_refresh / 1e9, 2), "peak": FP64_PEAK_TFS,
+                        "unit": "TFLOP/s", "frac": round(refresh_flop / t_refresh / 1e9 / FP64_PEAK_TFS, 4)}},
+    }
     print(json.dumps(result), flush=True)
 
 

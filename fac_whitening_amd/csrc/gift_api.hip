@@ -94,8 +94,9 @@ int device_cus() {
 
 // The fused path keeps every tile resident (one 512-thread workgroup per
 // compute unit at most), so it is taken when the tiles fit on the device.
+// The Euclidean codec takes the same kernels without the transform.
 bool fused_ok(const gift_layer_desc& g) {
-  if (!g_fused_enabled || g.transform != GIFT_LOWRANK) return false;
+  if (!g_fused_enabled || (g.transform != GIFT_LOWRANK && g.transform != GIFT_EUCLID)) return false;
   const int64_t tiles = (int64_t)fused_groups(g) * fused_cg(g);
   const int cus = device_cus();
   return cus > 0 && tiles <= cus;
@@ -135,10 +136,10 @@ StateLayout state_layout(const gift_layer_desc& g) {
     // tagged projection partials [tiles][48 x 32], then the row-group sums
     // [row groups][48 x 32]
     s.xpub = take((size_t)fused_groups(g) * (fused_cg(g) + 1) * kFusedTR * 32 * 8);
-    {
-      const size_t tiles = (size_t)fused_groups(g) * fused_cg(g);   // [tiles][16] + the per-tensor copies
-      s.apub = take((tiles * 16 + (size_t)kAmaxCopies * amax_copy_stride((int)tiles)) * 8);
-    }
+  }
+  if (g.transform == GIFT_LOWRANK || g.transform == GIFT_EUCLID) {
+    const size_t tiles = (size_t)fused_groups(g) * fused_cg(g);   // [tiles][16] + the per-tensor copies
+    s.apub = take((tiles * 16 + (size_t)kAmaxCopies * amax_copy_stride((int)tiles)) * 8);
   }
   if (g.transform == GIFT_DIAG) s.coef = take(2 * d * 4);
   if (g.transform == GIFT_CHOL_INPUT || g.transform == GIFT_CHOL_TWOSIDED) {
@@ -166,7 +167,7 @@ WorkLayout work_layout(const gift_layer_desc& g) {
   if (g.transform != GIFT_EUCLID) w.tile = take(m * d * 4);
   if (g.transform == GIFT_CHOL_TWOSIDED) w.tmp = take(m * d * 4);
   if (g.transform == GIFT_LOWRANK) {
-    w.ppart = take((size_t)cdiv((int64_t)d, kProjChunk) * m * 32 * 4);
+    w.ppart = take((size_t)cdiv((int64_t)d, kProjChunk) * m * 32 * 8);
     const size_t lp = (size_t)lp_of(l_of(g));
     w.Y = take(d * lp * 8);
     w.Q = take(d * lp * 8);
@@ -440,10 +441,13 @@ gift_status gift_encode(gift_layer_t L, const float* d_W, int64_t ldw, int32_t f
     a.epoch = (unsigned)(++L->counters[5]);
     a.W = d_W;
     a.ldw = ldw;
-    a.ub = reinterpret_cast<const uint4*>(L->state + L->sl.ub);
-    a.ua = reinterpret_cast<const uint4*>(L->state + L->sl.ua);
-    a.coef = reinterpret_cast<const float*>(L->state + L->sl.coef);
-    a.xpub = reinterpret_cast<unsigned long long*>(L->state + L->sl.xpub);
+    a.lr = g.transform == GIFT_LOWRANK;
+    if (a.lr) {
+      a.ub = reinterpret_cast<const uint4*>(L->state + L->sl.ub);
+      a.ua = reinterpret_cast<const uint4*>(L->state + L->sl.ua);
+      a.coef = reinterpret_cast<const float*>(L->state + L->sl.coef);
+      a.xpub = reinterpret_cast<unsigned long long*>(L->state + L->sl.xpub);
+    }
 
     a.apub = reinterpret_cast<unsigned long long*>(L->state + L->sl.apub);
     a.flags = flags;
@@ -477,7 +481,7 @@ gift_status gift_encode(gift_layer_t L, const float* d_W, int64_t ldw, int32_t f
       ldx = d;
       break;
     case GIFT_LOWRANK: {
-      float* ppart = reinterpret_cast<float*>(work + L->wl.ppart);
+      double* ppart = reinterpret_cast<double*>(work + L->wl.ppart);
       const float* U = reinterpret_cast<const float*>(L->state + L->sl.U);
       const float* coef = reinterpret_cast<const float*>(L->state + L->sl.coef);
       GIFT_HIP(gift::launch_lr_project(d_W, ldw, m, d, U, g.rank, ppart, s));
@@ -534,7 +538,7 @@ gift_status gift_decode_reduce(gift_layer_t L, const uint8_t* d_codes, int64_t c
   if (!L->ready) return GIFT_ERR_NOT_READY;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* work = static_cast<char*>(d_work);
-  if (g.transform == GIFT_EUCLID) {
+  if (g.transform == GIFT_EUCLID && !(fused_ok(g) && R <= 64)) {
     GIFT_HIP(gift::launch_dequant_sum(d_codes, code_stride, d_scales, scale_stride, R, m, d, fmt, scaling, d_out, ldo,
                                       s));
     return GIFT_OK;
@@ -549,10 +553,13 @@ gift_status gift_decode_reduce(gift_layer_t L, const uint8_t* d_codes, int64_t c
     a.scaling = scaling;
     a.R = R;
     a.epoch = (unsigned)(++L->counters[6]);
-    a.ub = reinterpret_cast<const uint4*>(L->state + L->sl.ub);
-    a.ua = reinterpret_cast<const uint4*>(L->state + L->sl.ua);
-    a.coef = reinterpret_cast<const float*>(L->state + L->sl.coef);
-    a.xpub = reinterpret_cast<unsigned long long*>(L->state + L->sl.xpub);
+    a.lr = g.transform == GIFT_LOWRANK;
+    if (a.lr) {
+      a.ub = reinterpret_cast<const uint4*>(L->state + L->sl.ub);
+      a.ua = reinterpret_cast<const uint4*>(L->state + L->sl.ua);
+      a.coef = reinterpret_cast<const float*>(L->state + L->sl.coef);
+      a.xpub = reinterpret_cast<unsigned long long*>(L->state + L->sl.xpub);
+    }
 
     a.flags = reinterpret_cast<uint32_t*>(L->state + L->sl.flags);
     a.qcodes = d_codes;
@@ -578,7 +585,7 @@ gift_status gift_decode_reduce(gift_layer_t L, const uint8_t* d_codes, int64_t c
                                        ldo, scaling, nullptr, s));
       break;
     case GIFT_LOWRANK: {
-      float* ppart = reinterpret_cast<float*>(work + L->wl.ppart);
+      double* ppart = reinterpret_cast<double*>(work + L->wl.ppart);
       const float* U = reinterpret_cast<const float*>(L->state + L->sl.U);
       const float* coef = reinterpret_cast<const float*>(L->state + L->sl.coef);
       GIFT_HIP(gift::launch_lr_project(Ub, d, m, d, U, g.rank, ppart, s));

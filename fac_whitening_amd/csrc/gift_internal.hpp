@@ -37,6 +37,7 @@ __host__ __device__ inline int amax_copy_stride(int tiles) { return (tiles + 511
 // Arguments of the fused encode (mode 0) / decode-reduce (mode 1) kernel.
 struct FusedArgs {
   int mode, m, d, CG, fmt, scaling, R;
+  int lr;                     // 1: rank-k transform; 0: Euclidean (T_A = I)
   unsigned epoch;
   const float* W;
   int64_t ldw;
@@ -84,7 +85,7 @@ struct WorkLayout {
   // encode / decode
   size_t tile = 0;      // fp32 [m][d]: whitened tensor (encode) or reduced U (decode)
   size_t tmp = 0;       // fp32 [m][d]: second buffer (two-sided)
-  size_t ppart = 0;     // fp32 [nchunk][m][k]: projection partials
+  size_t ppart = 0;     // fp64 [nchunk][m][k]: projection partials
   size_t amax = 0;      // uint32 [nblk]
   // refresh
   size_t Y = 0, Q = 0, Z = 0;   // fp64 [d][l]
@@ -121,9 +122,9 @@ hipError_t launch_dequant_sum(const uint8_t* codes, int64_t code_stride, const f
 
 // Low-rank transform pieces: partials of X U, then out = alpha X + (P c) U^T.
 hipError_t launch_lr_project(const float* x, int64_t ldx, int m, int d, const float* U, int k,
-                             float* ppart, hipStream_t s);
+                             double* ppart, hipStream_t s);
 hipError_t launch_lr_apply(const float* x, int64_t ldx, int m, int d, const float* U, int k,
-                           const float* ppart, const float* coef, int which, float* out,
+                           const double* ppart, const float* coef, int which, float* out,
                            int64_t ldo, int scaling, uint32_t* amax_slots, hipStream_t s);
 // Column scaling out = x * v[j] (diagonal transform), with optional amax.
 hipError_t launch_diag_apply(const float* x, int64_t ldx, int m, int d, const float* v, float* out,

@@ -273,7 +273,10 @@ constexpr int kXPT = kXW / 512;     // of them per thread (3)
 // the projection partials go out with atomic exchanges nobody waits for;
 // the reconstruction operands are requested before the partner partials are
 // read, so they arrive while the row group finishes its own partials.
-template <int FMT, bool ENC, int RC, int SC>
+// LR: the rank-k transform (false: the Euclidean codec, T_A = I: the same
+// tile schedule, amax all-gather and quantiser without the projection,
+// exchange and reconstruction).
+template <int FMT, bool ENC, int RC, int SC, bool LR>
 __device__ __forceinline__ void fused_body(const FusedArgs& a) {
   // The staged tile (fp32, padded rows); after it has been read into
   // registers the same memory holds the per-wave projection partials and the
@@ -317,7 +320,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
       v[j] = __builtin_amdgcn_raw_buffer_load_b128(wr, ok ? (int)(((int64_t)(row0 + r) * a.ldw + col0 + c) * 4) : kOff,
                                                    0, 0);
     }
-    load_uops(a.ub, d, cbg0, uo);
+    if constexpr (LR) load_uops(a.ub, d, cbg0, uo);
 #pragma unroll
     for (int j = 0; j < 2 * kCPT; ++j) {
       const int q = tid + 512 * j, r = q / 192, c = (q % 192) * 4;
@@ -345,7 +348,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
     // the projection operands go out right behind the last replica's codes
     auto load = [&](int r, CodeBuf& b) {
       load_codes<FMT>(a, R, r, off, offt, b);
-      if (RC > 0 && r == R - 1) load_uops(a.ub, d, cbg0, uo);
+      if (LR && RC > 0 && r == R - 1) load_uops(a.ub, d, cbg0, uo);
     };
     if constexpr (PT) {
       load(0, b0);
@@ -386,7 +389,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
     } else {
       for (int r = 0; r < R; r += 3)
         if (!three(r)) break;
-      load_uops(a.ub, d, cbg0, uo);
+      if constexpr (LR) load_uops(a.ub, d, cbg0, uo);
     }
     const float ir = a.invR;
 #pragma unroll
@@ -405,6 +408,19 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
     }
   }
   __syncthreads();
+  if constexpr (!LR && !ENC) {
+    // Euclidean decode: the staged tile is the output
+    const auto orr = make_rsrc(a.out, ((int64_t)(m - 1) * a.ldo + d) * 4);
+#pragma unroll
+    for (int j = 0; j < 2 * kCPT; ++j) {
+      const int q = tid + 512 * j, r = q / 192, c = (q % 192) * 4;
+      const bool ok = row0 + r < m && col0 + c < d;
+      const int32x4 v = *reinterpret_cast<const int32x4*>(smem + r * kTilePad + c);
+      __builtin_amdgcn_raw_buffer_store_b128(v, orr, ok ? (int)(((int64_t)(row0 + r) * a.ldo + col0 + c) * 4) : kOff,
+                                             0, 0);
+    }
+    return;
+  }
   // each lane takes its sub-tile layout out of the staged tile
 #pragma unroll
   for (int i = 0; i < NSUB; ++i) {
@@ -416,6 +432,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
   }
   __syncthreads();
 
+  if constexpr (LR) {
   // ---- projection P = X U (partials of this tile) ---------------------------
   {
     floatx4 acc[3][2];
@@ -581,6 +598,8 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
       }
     }
   }
+
+  }   // LR
 
   if (!enc) {
     // ---- decode: store W^ --------------------------------------------------
@@ -804,47 +823,74 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
   }
 }
 
-// One kernel per direction and format (distinct names in traces); the
-// decode also per replica count 4, 8, 16 (0: any count up to 64).
+// One kernel per direction, transform and format (distinct names in
+// traces); the decode also per replica count 4, 8, 16 (0: any count up
+// to 64) and scaling.
 template <int FMT>
 __global__ void __launch_bounds__(512) k_rank_encode(FusedArgs a) {
-  fused_body<FMT, true, 0, -1>(a);
+  fused_body<FMT, true, 0, -1, true>(a);
 }
 template <int FMT, int RC, int SC>
 __global__ void __launch_bounds__(512) k_rank_decode(FusedArgs a) {
-  fused_body<FMT, false, RC, SC>(a);
+  fused_body<FMT, false, RC, SC, true>(a);
+}
+template <int FMT>
+__global__ void __launch_bounds__(512) k_euclid_encode(FusedArgs a) {
+  fused_body<FMT, true, 0, -1, false>(a);
+}
+template <int FMT, int RC, int SC>
+__global__ void __launch_bounds__(512) k_euclid_decode(FusedArgs a) {
+  fused_body<FMT, false, RC, SC, false>(a);
 }
 
-template <int FMT, int SC>
+template <int FMT, int SC, bool LR>
 static void launch_decode(const FusedArgs& args, dim3 gd, dim3 bd, hipStream_t s) {
-  switch (args.R) {
-    case 4: hipLaunchKernelGGL((k_rank_decode<FMT, 4, SC>), gd, bd, 0, s, args); break;
-    case 8: hipLaunchKernelGGL((k_rank_decode<FMT, 8, SC>), gd, bd, 0, s, args); break;
-    case 16: hipLaunchKernelGGL((k_rank_decode<FMT, 16, SC>), gd, bd, 0, s, args); break;
-    default: hipLaunchKernelGGL((k_rank_decode<FMT, 0, SC>), gd, bd, 0, s, args); break;
+  if constexpr (LR) {
+    switch (args.R) {
+      case 4: hipLaunchKernelGGL((k_rank_decode<FMT, 4, SC>), gd, bd, 0, s, args); break;
+      case 8: hipLaunchKernelGGL((k_rank_decode<FMT, 8, SC>), gd, bd, 0, s, args); break;
+      case 16: hipLaunchKernelGGL((k_rank_decode<FMT, 16, SC>), gd, bd, 0, s, args); break;
+      default: hipLaunchKernelGGL((k_rank_decode<FMT, 0, SC>), gd, bd, 0, s, args); break;
+    }
+  } else {
+    switch (args.R) {
+      case 4: hipLaunchKernelGGL((k_euclid_decode<FMT, 4, SC>), gd, bd, 0, s, args); break;
+      case 8: hipLaunchKernelGGL((k_euclid_decode<FMT, 8, SC>), gd, bd, 0, s, args); break;
+      case 16: hipLaunchKernelGGL((k_euclid_decode<FMT, 16, SC>), gd, bd, 0, s, args); break;
+      default: hipLaunchKernelGGL((k_euclid_decode<FMT, 0, SC>), gd, bd, 0, s, args); break;
+    }
   }
 }
 
-template <int FMT>
+template <int FMT, bool LR>
 static void launch_decode(const FusedArgs& args, dim3 gd, dim3 bd, hipStream_t s) {
   if (args.scaling == 0)
-    launch_decode<FMT, 0>(args, gd, bd, s);
+    launch_decode<FMT, 0, LR>(args, gd, bd, s);
   else
-    launch_decode<FMT, 1>(args, gd, bd, s);
+    launch_decode<FMT, 1, LR>(args, gd, bd, s);
 }
 
 hipError_t launch_fused(const FusedArgs& args, int grid, hipStream_t s) {
   const dim3 gd((unsigned)grid), bd(512);
   if (args.mode == 0) {
-    if (args.fmt == 0)
+    if (args.lr && args.fmt == 0)
       hipLaunchKernelGGL(k_rank_encode<0>, gd, bd, 0, s, args);
-    else
+    else if (args.lr)
       hipLaunchKernelGGL(k_rank_encode<1>, gd, bd, 0, s, args);
+    else if (args.fmt == 0)
+      hipLaunchKernelGGL(k_euclid_encode<0>, gd, bd, 0, s, args);
+    else
+      hipLaunchKernelGGL(k_euclid_encode<1>, gd, bd, 0, s, args);
+  } else if (args.lr) {
+    if (args.fmt == 0)
+      launch_decode<0, true>(args, gd, bd, s);
+    else
+      launch_decode<1, true>(args, gd, bd, s);
   } else {
     if (args.fmt == 0)
-      launch_decode<0>(args, gd, bd, s);
+      launch_decode<0, false>(args, gd, bd, s);
     else
-      launch_decode<1>(args, gd, bd, s);
+      launch_decode<1, false>(args, gd, bd, s);
   }
   return hipGetLastError();
 }

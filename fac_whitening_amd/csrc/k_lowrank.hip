@@ -9,6 +9,10 @@
 // Encode uses (alpha, c) = (rho^-1/2, c_enc), decode (rho^1/2, c_dec).
 // The projection is split over column chunks of 256 and the partial
 // products are summed in a fixed order by the consumer (deterministic).
+// Partials and their sum are float64: with d in the tens of thousands and
+// heavy-tailed rows, P is a long sum whose float32 rounding, amplified by
+// the cancellation between alpha X and the low-rank term, would reach the
+// 1e-5 relative budget of the whitened tensor.
 #include "gift_internal.hpp"
 
 namespace gift {
@@ -66,11 +70,11 @@ __global__ void __launch_bounds__(256) k_project(const float* __restrict__ x, in
 }
 
 hipError_t launch_lr_project(const float* x, int64_t ldx, int m, int d, const float* U, int k,
-                             float* ppart, hipStream_t s) {
+                             double* ppart, hipStream_t s) {
   (void)k;
   if (m == 0 || d == 0) return hipSuccess;
   dim3 grid((unsigned)cdiv(d, kProjChunk), (unsigned)cdiv(m, 32));
-  hipLaunchKernelGGL((k_project<32, 8, kProjChunk, false, float, float>), grid, dim3(256), 0, s, x, ldx, m, d, U,
+  hipLaunchKernelGGL((k_project<32, 8, kProjChunk, false, float, double>), grid, dim3(256), 0, s, x, ldx, m, d, U,
                      ppart);
   return hipGetLastError();
 }
@@ -79,7 +83,7 @@ hipError_t launch_lr_project(const float* x, int64_t ldx, int m, int d, const fl
 // Tile: 16 rows x 256 columns; wave w owns rows 4w..4w+3, lane l columns
 // 4l..4l+3.  Optionally the amax of |out| per 128 x 128 tile (or tensor).
 __global__ void __launch_bounds__(256) k_lr_apply(const float* __restrict__ x, int64_t ldx, int m, int d,
-                                                  const float* __restrict__ U, const float* __restrict__ part,
+                                                  const float* __restrict__ U, const double* __restrict__ part,
                                                   int nchunk, const float* __restrict__ coef, int which,
                                                   float* __restrict__ out, int64_t ldo, int scaling,
                                                   uint32_t* __restrict__ slots) {
@@ -105,10 +109,10 @@ __global__ void __launch_bounds__(256) k_lr_apply(const float* __restrict__ x, i
   // Reduce the projection partials of these 16 rows (fixed chunk order).
   for (int i = tid; i < 16 * KP; i += 256) {
     int r = i / KP, t = i % KP;
-    float acc = 0.f;
+    double acc = 0.0;
     if (row0 + r < m)
       for (int ch = 0; ch < nchunk; ++ch) acc += part[((int64_t)ch * m + row0 + r) * KP + t];
-    Pc[r][t] = acc * c[t];
+    Pc[r][t] = (float)(acc * (double)c[t]);
   }
   __syncthreads();
   const int col = col0 + lane * 4;
@@ -168,7 +172,7 @@ __global__ void __launch_bounds__(256) k_lr_apply(const float* __restrict__ x, i
 }
 
 hipError_t launch_lr_apply(const float* x, int64_t ldx, int m, int d, const float* U, int k,
-                           const float* ppart, const float* coef, int which, float* out,
+                           const double* ppart, const float* coef, int which, float* out,
                            int64_t ldo, int scaling, uint32_t* amax_slots, hipStream_t s) {
   (void)k;
   if (m == 0 || d == 0) return hipSuccess;

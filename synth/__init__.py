@@ -151,6 +151,44 @@ def make_layer(cfg_id: int, device="cpu", R=None, steps=None, T=None, m=None, d=
     return LayerCase(W=W, a_steps=a_steps, delta_steps=delta_steps, omega=om, cfg=c)
 
 
+# Llama-600M-class selective deployment: 24 decoder layers, each with
+# q, k, v, o (1536 x 1536), fc1, fc3 (6144 x 1536: d_out x d_in) and fc2
+# (1536 x 6144); 13 fc2 layers take the rank-32 path, the other tensors the
+# Euclidean one.  Per-layer anisotropy exponents alpha_l ~ U[0.8, 1.8].
+SELECTIVE_SHAPES = {"q": (1536, 1536), "k": (1536, 1536), "v": (1536, 1536), "o": (1536, 1536),
+                    "fc1": (6144, 1536), "fc3": (6144, 1536), "fc2": (1536, 6144)}
+SELECTIVE_LAYERS, SELECTIVE_GIFT = 24, 13
+
+
+def selective_alphas(n_layers: int = SELECTIVE_LAYERS) -> np.ndarray:
+    """alpha_l ~ U[0.8, 1.8], one per decoder layer."""
+    rng = np.random.default_rng(seed_for(3, ROLE_EXP))
+    return rng.uniform(0.8, 1.8, n_layers)
+
+
+def selective_tensors(n_layers: int = SELECTIVE_LAYERS, n_gift: int = SELECTIVE_GIFT):
+    """(layer, name, d_out, d_in, alpha, gift) for every weight gradient of the
+    selective deployment; the fc2 tensors of layers 0 .. n_gift - 1 are the
+    rank-32 ones."""
+    al = selective_alphas(n_layers)
+    out = []
+    for l in range(n_layers):
+        for name, (mo, di) in SELECTIVE_SHAPES.items():
+            out.append((l, name, mo, di, float(al[l]), name == "fc2" and l < n_gift))
+    return out
+
+
+def direct_gradient(m: int, d: int, alpha: float, T: int, seed: int, device) -> torch.Tensor:
+    """The Gaussian limit of delta^T a / T without drawing the T tokens:
+    W = diag(sigma) Z diag(i^-alpha/2) / sqrt(T), sigma_j = j^-1/2, Z iid
+    N(0, 1) [d_out][d_in] (no input-side rotation: it changes neither the
+    sizes nor the value distribution the codec sees)."""
+    z = torch.randn(m, d, generator=generator(seed, device), device=device, dtype=torch.float32)
+    rs = power_spectrum(m, 1.0).sqrt().to(device=device, dtype=torch.float32)
+    cs = power_spectrum(d, alpha).sqrt().to(device=device, dtype=torch.float32)
+    return (z * rs.unsqueeze(1) * cs.unsqueeze(0) / float(T) ** 0.5).contiguous()
+
+
 def stress_gradient(m: int, d: int, seed_layer: int, replica: int, device,
                     outlier_frac: float = 1e-3, outlier_mult: float = 100.0) -> torch.Tensor:
     """Heavy-tailed gradient: W_ji = t_ji c_i, t ~ Student-t(3), c_i = i^-1.5,
