@@ -148,6 +148,7 @@ hipError_t launch_pack_u(const float* U, int d, void* ub, void* ua, hipStream_t 
 
 constexpr int TR = kFusedTR, TC = kFusedTC, NSUB = 9;
 constexpr int kApub = 16;   // published amax words per workgroup
+constexpr int kPipeDepth = 6;   // block-pipelined decode: units in flight per thread
 
 // Decode the 4 codes of one 32-bit word.
 template <int FMT>
@@ -187,6 +188,12 @@ typedef int int32x2 __attribute__((ext_vector_type(2)));
 // flight.
 constexpr int kDCPT = 4;                    // 16-byte chunks per thread
 constexpr int kDTail = 32768;               // first byte of the 8-byte chunks
+
+// One replica of one 16-row block (block-pipelined decode).
+struct Unit {
+  int32x4 v;    // 16 codes
+  int32x2 t;    // 8 codes
+};
 
 struct CodeBuf {
   int32x4 v[kDCPT];
@@ -287,7 +294,9 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
   __shared__ uint32_t wmax[16];
   __shared__ float srs[12];               // reciprocal scales of those blocks
   __shared__ uint32_t sam[12];            // the amax bits they come from
-  float (*cp)[3][16][33] = reinterpret_cast<float (*)[3][16][33]>(smem);
+  // cp[rb][wave]: the row block's partials lie in the first 5.5 tile rows
+  // (rb 0), the next 5.5 (rb 1), ...
+  float (*cp)[8][16][33] = reinterpret_cast<float (*)[8][16][33]>(smem);
   float (*pf)[33] = reinterpret_cast<float (*)[33]>(smem + 8 * 3 * 16 * 33);
   const int G = gridDim.x;
   const int g = blockIdx.x, rg = g / a.CG, cgi = g % a.CG;
@@ -302,17 +311,59 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
   const int cbg0 = (col0 >> 5) + wave;   // this wave's first 32-column block
   const unsigned tag = (a.epoch << 1) | (enc ? 0u : 1u);
   if (tid < 16) wmax[tid] = 0u;
+  // PIPE: the projection of each 16-row block runs as soon as the block is
+  // in (the rank-k encode; the rank-k decode with a compile-time replica
+  // count of at most 8 streams the replicas block by block: at 16 the
+  // unrolled stream no longer fits the registers)
+  constexpr bool PIPE = LR && (ENC || (RC > 0 && RC <= 8));
 
   float x[NSUB][8];
   bool live[3];
 #pragma unroll
   for (int q = 0; q < 3; ++q) live[q] = col0 + (wave + 8 * q) * 32 < d;
   UOps uo;
+  // projection P = X U of row block rb (this wave's partial, 16 rows x 32)
+  floatx4 pacc[3][2];
+#pragma unroll
+  for (int rb = 0; rb < 3; ++rb)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) pacc[rb][h] = (floatx4){0.f, 0.f, 0.f, 0.f};
+  auto project_rb = [&](int rb) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      if (!live[q]) continue;
+      const int i = q * 3 + rb;
+      bf16x8 xh, xm, xl;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        __bf16 h, mm, l;
+        split3(x[i][j], h, mm, l);
+        xh[j] = h;
+        xm[j] = mm;
+        xl[j] = l;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bf16x8* u = uo.u[q][h];
+        floatx4 c = pacc[rb][h];
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xm, u[1], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, u[2], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, u[0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, u[1], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xm, u[0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, u[0], c, 0, 0, 0);
+        pacc[rb][h] = c;
+      }
+    }
+  };
 
   // ---- stream the tile in (flat, coalesced) and stage it in LDS --------------
-  if (enc) {
+  if constexpr (ENC) {
     const auto wr = make_rsrc(a.W, ((int64_t)(m - 1) * a.ldw + d) * 4);
-    int32x4 v[2 * kCPT];
+    // the projection operands first: loads complete in order, so the
+    // projection of a row block then waits for that block's data only
+    if constexpr (LR) load_uops(a.ub, d, cbg0, uo);
+    int32x4 v[2 * kCPT];   // chunks 6 rb .. 6 rb + 5 hold row block rb
 #pragma unroll
     for (int j = 0; j < 2 * kCPT; ++j) {
       const int q = tid + 512 * j, r = q / 192, c = (q % 192) * 4;
@@ -320,11 +371,131 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
       v[j] = __builtin_amdgcn_raw_buffer_load_b128(wr, ok ? (int)(((int64_t)(row0 + r) * a.ldw + col0 + c) * 4) : kOff,
                                                    0, 0);
     }
-    if constexpr (LR) load_uops(a.ub, d, cbg0, uo);
+    if constexpr (LR) {
+      // each 16-row block is staged, read back in the sub-tile layout and
+      // projected as soon as it lands, while the later blocks stream in
 #pragma unroll
-    for (int j = 0; j < 2 * kCPT; ++j) {
-      const int q = tid + 512 * j, r = q / 192, c = (q % 192) * 4;
-      *reinterpret_cast<int32x4*>(smem + r * kTilePad + c) = v[j];
+      for (int rb = 0; rb < 3; ++rb) {
+#pragma unroll
+        for (int j = 6 * rb; j < 6 * rb + 6; ++j) {
+          const int q = tid + 512 * j, r = q / 192, c = (q % 192) * 4;
+          *reinterpret_cast<int32x4*>(smem + r * kTilePad + c) = v[j];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+          const float* src = smem + (rb * 16 + lr) * kTilePad + (wave + 8 * q) * 32 + 4 * lg;
+          const float4 v0 = *reinterpret_cast<const float4*>(src);
+          const float4 v1 = *reinterpret_cast<const float4*>(src + 16);
+          float* xi = x[q * 3 + rb];
+          xi[0] = v0.x; xi[1] = v0.y; xi[2] = v0.z; xi[3] = v0.w;
+          xi[4] = v1.x; xi[5] = v1.y; xi[6] = v1.z; xi[7] = v1.w;
+        }
+        project_rb(rb);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2 * kCPT; ++j) {
+        const int q = tid + 512 * j, r = q / 192, c = (q % 192) * 4;
+        *reinterpret_cast<int32x4*>(smem + r * kTilePad + c) = v[j];
+      }
+    }
+  } else if constexpr (PIPE) {
+    // Units (row block rb, replica r), rb-major; a unit is the block's
+    // 16 x 768 codes of one replica: the 16-byte chunk at byte 16 t and the
+    // 8-byte chunk at 8192 + 8 t of thread t (768 = 48 x 16: a 16-byte
+    // chunk never crosses a row).  kPipeDepth units in flight.
+    constexpr int NU = 3 * RC;
+    constexpr bool PT = SC == 0;
+    const int fA = 16 * tid, rA = fA / TC, cA = fA % TC;
+    const int fB = 8192 + 8 * tid, rB = fB / TC, cB = fB % TC;
+    const bool hiA = col0 + cA + 8 < d;   // the upper 8 codes of chunk A lie inside the row
+    int offA[3], offB[3], sA[3], sB[3];
+#pragma unroll
+    for (int rb = 0; rb < 3; ++rb) {
+      const int ra = row0 + 16 * rb + rA, rbw = row0 + 16 * rb + rB;
+      const bool okA = ra < m && col0 + cA < d, okB = rbw < m && col0 + cB < d;
+      offA[rb] = okA ? ra * d + col0 + cA : kOff;
+      offB[rb] = okB ? rbw * d + col0 + cB : kOff;
+      sA[rb] = (PT || !okA) ? 0 : (ra / kBlock - rb0) * 6 + (col0 + cA) / kBlock - cb0;
+      sB[rb] = (PT || !okB) ? 0 : (rbw / kBlock - rb0) * 6 + (col0 + cB) / kBlock - cb0;
+    }
+    if constexpr (!PT) {
+      // the last wave stages the block scales before its code stream starts
+      if (wave == 7) {
+        const int nbm = (int)cdiv(m, kBlock);
+        for (int t = lane; t < RC * 12; t += 64) {
+          const int r = t / 12, e = t % 12, br = rb0 + e / 6, bc = cb0 + e % 6;
+          ssc[r][e] = (br < nbm && bc < nbd) ? a.qscales[(int64_t)r * a.scale_stride + br * nbd + bc] : 0.f;
+        }
+      }
+    }
+    // the projection operands first (loads complete in order)
+    load_uops(a.ub, d, cbg0, uo);
+    Unit buf[kPipeDepth];
+    auto issue = [&](int u, Unit& U) {
+      const int rb = u / RC, r = u % RC;
+      const bool in = u < NU;
+      const auto q = make_rsrc(a.qcodes + (in ? (int64_t)r * a.code_stride : 0), in ? (int64_t)m * d : 0);
+      U.v = __builtin_amdgcn_raw_buffer_load_b128(q, in ? offA[rb < 3 ? rb : 2] : kOff, 0, 0);
+      U.t = __builtin_amdgcn_raw_buffer_load_b64(q, in ? offB[rb < 3 ? rb : 2] : kOff, 0, 0);
+    };
+#pragma unroll
+    for (int u = 0; u < kPipeDepth; ++u) issue(u, buf[u]);
+    if constexpr (!PT) __syncthreads();   // the staged scales are visible
+    float accA[16], accB[8];
+    const float ir = a.invR;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int rb = u / RC, r = u % RC;
+      Unit& U = buf[u % kPipeDepth];
+      {
+        const float sa = PT ? a.qscales[(int64_t)r * a.scale_stride] : ssc[r][sA[rb]];
+        const float sb = PT ? sa : ssc[r][sB[rb]];
+        float va[16], vb[8];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) dec4<FMT>((w < 2 || hiA) ? (uint32_t)U.v[w] : 0u, va + 4 * w);
+        dec4<FMT>((uint32_t)U.t[0], vb);
+        dec4<FMT>((uint32_t)U.t[1], vb + 4);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) accA[k] = r == 0 ? sa * va[k] : accA[k] + sa * va[k];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) accB[k] = r == 0 ? sb * vb[k] : accB[k] + sb * vb[k];
+      }
+      issue(u + kPipeDepth, U);   // past the last unit: an empty buffer resource, no memory traffic
+      if (r == RC - 1) {
+        // the block's mean into its rows of the tile, then its projection
+        float* da = smem + (16 * rb + rA) * kTilePad + cA;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          *reinterpret_cast<float4*>(da + 4 * w) =
+              make_float4(accA[4 * w] * ir, accA[4 * w + 1] * ir, accA[4 * w + 2] * ir, accA[4 * w + 3] * ir);
+        float* db = smem + (16 * rb + rB) * kTilePad + cB;
+        *reinterpret_cast<float4*>(db) = make_float4(accB[0] * ir, accB[1] * ir, accB[2] * ir, accB[3] * ir);
+        *reinterpret_cast<float4*>(db + 4) = make_float4(accB[4] * ir, accB[5] * ir, accB[6] * ir, accB[7] * ir);
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+          const float* src = smem + (rb * 16 + lr) * kTilePad + (wave + 8 * q) * 32 + 4 * lg;
+          const float4 v0 = *reinterpret_cast<const float4*>(src);
+          const float4 v1 = *reinterpret_cast<const float4*>(src + 16);
+          float* xi = x[q * 3 + rb];
+          xi[0] = v0.x; xi[1] = v0.y; xi[2] = v0.z; xi[3] = v0.w;
+          xi[4] = v1.x; xi[5] = v1.y; xi[6] = v1.z; xi[7] = v1.w;
+        }
+        project_rb(rb);
+        // partials into LDS: block b's lie in tile rows 5.5 b .. 5.5 b + 5.5,
+        // which are free once every block before the one being read is read:
+        // blocks 0 and 1 after block 1's barrier, block 2 after the last
+        if (rb == 1) {
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) cp[b][wave][4 * lg + e][lr + 16 * h] = pacc[b][h][e];
+        }
+      }
     }
   } else {
     const int R = RC > 0 ? RC : a.R;
@@ -407,6 +578,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
       *reinterpret_cast<float4*>(dst + 4) = make_float4(acct[4] * ir, acct[5] * ir, acct[6] * ir, acct[7] * ir);
     }
   }
+  if constexpr (!PIPE) {
   __syncthreads();
   if constexpr (!LR && !ENC) {
     // Euclidean decode: the staged tile is the output
@@ -430,52 +602,21 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
     x[i][0] = v0.x; x[i][1] = v0.y; x[i][2] = v0.z; x[i][3] = v0.w;
     x[i][4] = v1.x; x[i][5] = v1.y; x[i][6] = v1.z; x[i][7] = v1.w;
   }
-  __syncthreads();
+  }   // staging of everything but the rank-k encode
+  __syncthreads();   // every sub-tile read is done: the tile memory is free
 
   if constexpr (LR) {
-  // ---- projection P = X U (partials of this tile) ---------------------------
-  {
-    floatx4 acc[3][2];
+  if constexpr (!PIPE) {
 #pragma unroll
-    for (int rb = 0; rb < 3; ++rb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) acc[rb][h] = (floatx4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      if (!live[q]) continue;
-#pragma unroll
-      for (int rb = 0; rb < 3; ++rb) {
-        const int i = q * 3 + rb;
-        bf16x8 xh, xm, xl;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          __bf16 h, mm, l;
-          split3(x[i][j], h, mm, l);
-          xh[j] = h;
-          xm[j] = mm;
-          xl[j] = l;
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const bf16x8* u = uo.u[q][h];
-          floatx4 c = acc[rb][h];
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xm, u[1], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, u[2], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, u[0], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, u[1], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xm, u[0], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, u[0], c, 0, 0, 0);
-          acc[rb][h] = c;
-        }
-      }
-    }
-#pragma unroll
-    for (int rb = 0; rb < 3; ++rb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) cp[wave][rb][4 * lg + e][lr + 16 * h] = acc[rb][h][e];
+    for (int rb = 0; rb < 3; ++rb) project_rb(rb);
   }
+  // (the block-pipelined decode has written blocks 0 and 1 already)
+#pragma unroll
+  for (int rb = (PIPE && !ENC) ? 2 : 0; rb < 3; ++rb)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cp[rb][wave][4 * lg + e][lr + 16 * h] = pacc[rb][h][e];
   __syncthreads();
   // sum the 8 waves (fixed order) and publish this tile's partial: word
   // e = 32 row + k of the tile, one atomic exchange each (it takes effect at
@@ -484,9 +625,9 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
 #pragma unroll
   for (int j = 0; j < kXPT; ++j) {
     const int e = tid + 512 * j, r = e >> 5, k = e & 31;
-    float s = cp[0][r >> 4][r & 15][k];
+    float s = cp[r >> 4][0][r & 15][k];
 #pragma unroll
-    for (int w = 1; w < 8; ++w) s += cp[w][r >> 4][r & 15][k];
+    for (int w = 1; w < 8; ++w) s += cp[r >> 4][w][r & 15][k];
     __hip_atomic_exchange(xg + e, tagged(tag, s), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   // the reconstruction operands, before the partner words

@@ -150,3 +150,32 @@ def test_fused_shared_amax(fw, scaling):
     local2 = torch.empty(nb, device=DEV)
     L.encode(W, 0, s, amax_in=shared, amax_out=local2)
     assert torch.equal(local2, local)
+
+
+@pytest.mark.parametrize("R", [4, 8])
+@pytest.mark.parametrize("scaling", ["tensor", "block"])
+@pytest.mark.parametrize("shape", [(200, 1544), (1536, 6144)])
+def test_fused_decode_compiled_replica_counts(fw, R, scaling, shape):
+    """The decode compiled for a fixed replica count (4, 8: the replicas
+    stream block by block and each 16-row block is projected as it lands)
+    against the oracle's decode-reduce of the same payloads, on a ragged
+    multi-tile shape (d % 16 == 8) and the full layer."""
+    m, d = shape
+    print(f"[fused decode R={R} {scaling} {shape}]", flush=True)
+    fw.set_fused(True)
+    Ws, fac = _case(m, d, R, seed=3 * R + m)
+    _, Tinv = G.transform_lowrank(fac)
+    L = _layer_with_factor(fw, m, d, fac)
+    s = fw.SCALINGS[scaling]
+    nb = fw.nblocks(m, d, s)
+    codes = torch.empty(R, m, d, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(R, nb, dtype=torch.float32, device=DEV)
+    for r, w in enumerate(Ws):
+        L.encode(torch.from_numpy(w).to(DEV), 0, s, codes=codes[r], scales=scales[r])
+    out = L.decode_reduce(codes, scales, 0, s)
+    bm, bd = G.nblocks(m, d, scaling)
+    ref = G.decode_reduce([codes[r].cpu().numpy() for r in range(R)],
+                          [scales[r].cpu().numpy().reshape(bm, bd) for r in range(R)], Tinv, "e4m3", scaling)
+    err = rel_fro(out.cpu().numpy(), ref)
+    assert err <= 1e-5, f"decode rel err {err:.3e}"
+    assert L.flags() == 0
