@@ -47,6 +47,12 @@ R9  Knee (Note §简化三, "the layers before the sharp drop"): cut after the
     ratio; 0/0 counts as 1; ties go to the smallest i).
 R10 EMA of A (not on the pages): the first commit sets A to the batch
     statistics, later commits A <- beta A + (1 - beta) A_batch.
+R11 Error feedback (Note 算法 1, lines 11-15): the residual is added to the
+    whitened tensor in float32 (U~ = fp32(W~ + R)), U~ is scaled and
+    quantised, and the new residual is the float32 rounding of
+    U~ - s dec(q) (one rounding of the exact difference).  The whitened
+    tensor itself (W~) is what the inspection output shows; the amax and
+    the codes are those of U~.
 """
 from __future__ import annotations
 
@@ -334,6 +340,20 @@ def encode(W, T, fmt: str, scaling: str, L_G=None, amax_in=None):
     Wt = whiten(W, T, L_G)
     codes, scales, am = quantize(Wt, fmt, scaling, amax_in)
     return dict(whitened=Wt, codes=codes, scales=scales, amax=am)
+
+
+def encode_ef(W, T, R, fmt: str, scaling: str, L_G=None, amax_in=None):
+    """[Note] Algorithm 1 with error feedback (lines 10-15, R11): whiten,
+    add the residual, scale, quantise, and carry the quantisation error of
+    U~ to the next step.  R is the float32 residual [m][d] of the previous
+    step (zeros at the first).  Returns dict(whitened, u_tilde, codes,
+    scales, amax, residual)."""
+    Wt = whiten(W, T, L_G)
+    Ut = (Wt + np.asarray(R, dtype=np.float32)).astype(np.float32)
+    codes, scales, am = quantize(Ut, fmt, scaling, amax_in)
+    deq = dequantize(codes, scales, fmt, scaling)
+    Rn = (Ut.astype(np.float64) - deq).astype(np.float32)
+    return dict(whitened=Wt, u_tilde=Ut, codes=codes, scales=scales, amax=am, residual=Rn)
 
 
 def decode_reduce(codes_list, scales_list, Tinv, fmt: str, scaling: str, L_G=None):

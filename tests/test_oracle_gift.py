@@ -453,3 +453,71 @@ def test_layer_scores_mean_over_steps():
     counts = np.array([[10, 30], [0, 4]])
     sc = G.layer_scores(counts, [100, 50], n_steps=2)
     np.testing.assert_allclose(sc, [40 / 200, 4 / 100])
+
+
+# ---------------------------------------------------------------------------
+# Error feedback ([Note] 算法 1, lines 11-15; reading R11)
+# ---------------------------------------------------------------------------
+
+def _spacing(y, fmt):
+    """Distance between consecutive finite FP8 values in the binade of |y|,
+    from the format's layout (E4M3: bias 7, 3 mantissa bits, normals from
+    2^-6; E5M2: bias 15, 2 mantissa bits, normals from 2^-14)."""
+    mant, emin = (3, -6) if fmt == "e4m3" else (2, -14)
+    a = np.abs(np.asarray(y, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** emin)))
+    return 2.0 ** (e - mant)
+
+
+def _ef_steps(tiny, kind, fmt, scaling, steps=4):
+    T = G.build_transform(kind, A=tiny["A"], lam=tiny["lam"], omega=tiny["omega"])[0]
+    rng = np.random.default_rng(11)
+    m, d = tiny["W"][0].shape
+    R = np.zeros((m, d), np.float32)
+    outs = []
+    for t in range(steps):
+        W = (tiny["W"][t % len(tiny["W"])] * (1.0 + 0.3 * rng.standard_normal((m, d)))).astype(np.float32)
+        e = G.encode_ef(W, T, R, fmt, scaling)
+        outs.append((e, R))
+        R = e["residual"]
+    return outs
+
+
+@pytest.mark.parametrize("kind", ["lowrank", "diag"])
+@pytest.mark.parametrize("fmt,scaling", [("e4m3", "tensor"), ("e5m2", "block")])
+def test_error_feedback_telescopes(tiny, kind, fmt, scaling):
+    """R_t = U~_t - deq_t and U~_t = W~_t + R_{t-1} give, with R_0 = 0,
+    sum_t deq_t + R_T = sum_t W~_t (up to the float32 roundings of U~ and R):
+    nothing the quantiser rounds away is lost, it is carried."""
+    outs = _ef_steps(tiny, kind, fmt, scaling)
+    sum_deq = sum(G.dequantize(e["codes"], e["scales"], fmt, scaling) for e, _ in outs)
+    sum_w = sum(e["whitened"].astype(np.float64) for e, _ in outs)
+    lhs = sum_deq + outs[-1][0]["residual"].astype(np.float64)
+    err = np.linalg.norm(lhs - sum_w) / np.linalg.norm(sum_w)
+    assert err < 1e-6, err
+    # dropping the residual breaks it at the quantiser's error level
+    no_ef = sum(G.dequantize(*G.quantize(e["whitened"], fmt, scaling)[:2], fmt, scaling) for e, _ in outs)
+    assert np.linalg.norm(no_ef - sum_w) / np.linalg.norm(sum_w) > 100 * err
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_error_feedback_residual_is_half_a_step(tiny, fmt):
+    """Each new residual is the rounding error of U~'s code: at most half the
+    FP8 spacing at U~ r, times the scale (plus the float32 rounding of y)."""
+    for e, _ in _ef_steps(tiny, "lowrank", fmt, "tensor"):
+        s = float(e["scales"][0, 0])
+        y = e["u_tilde"].astype(np.float64) / s
+        bound = 0.5 * s * _spacing(y, fmt) + 4e-7 * np.abs(e["u_tilde"]) + 1e-30
+        assert np.all(np.abs(e["residual"].astype(np.float64)) <= bound)
+
+
+def test_error_feedback_first_step_is_plain_encode(tiny):
+    """With a zero residual the codes and scales are those of Algorithm 1
+    without error feedback, and the residual is U~ - s dec(q)."""
+    T = G.build_transform("lowrank", A=tiny["A"], lam=tiny["lam"], omega=tiny["omega"])[0]
+    W = tiny["W"][0]
+    e = G.encode_ef(W, T, np.zeros_like(W), "e4m3", "block")
+    p = G.encode(W, T, "e4m3", "block")
+    assert np.array_equal(e["codes"], p["codes"]) and np.array_equal(e["scales"], p["scales"])
+    deq = G.dequantize(p["codes"], p["scales"], "e4m3", "block")
+    assert np.array_equal(e["residual"], (p["whitened"].astype(np.float64) - deq).astype(np.float32))
