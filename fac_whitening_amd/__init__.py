@@ -40,7 +40,7 @@ STATUS = {0: "GIFT_OK", 1: "GIFT_ERR_INVALID_ARG", 2: "GIFT_ERR_WORKSPACE", 3: "
 EXPORTS = [
     "gift_layer_state_bytes", "gift_layer_create", "gift_layer_destroy", "gift_layer_get_counters",
     "gift_layer_set_counters", "gift_layer_flags", "gift_layer_buffers", "gift_layer_mark_ready",
-    "gift_accumulate_stats", "gift_commit_stats", "gift_refresh_factors", "gift_encode",
+    "gift_accumulate_stats", "gift_commit_stats", "gift_refresh_factors", "gift_encode", "gift_encode_ef",
     "gift_decode_reduce", "gift_payload_bytes", "gift_profiler_create", "gift_profiler_destroy",
     "gift_profiler_workspace_bytes", "gift_profile_step", "gift_select_layers", "gift_status_string",
     "gift_last_hip_error", "gift_set_fused",
@@ -76,6 +76,7 @@ _sig("gift_accumulate_stats", _i32, _vp, _i32, _vp, _i32, _i64, _i64, _i32, _vp)
 _sig("gift_commit_stats", _i32, _vp, _i32, _vp)
 _sig("gift_refresh_factors", _i32, _vp, _vp, _vp, _sz, _vp)
 _sig("gift_encode", _i32, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp)
+_sig("gift_encode_ef", _i32, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp)
 _sig("gift_decode_reduce", _i32, _vp, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _vp, _i64, _vp, _sz, _vp)
 _sig("gift_payload_bytes", _sz, _i32, _i32, _i32)
 _sig("gift_profiler_create", _i32, _i32, _i32, _i32, _vp, _vp, _P(_vp))
@@ -221,7 +222,7 @@ class Layer:
 
     # -- encode / decode --------------------------------------------------
     def encode(self, W: torch.Tensor, fmt=E4M3, scaling=SCALE_TENSOR, amax_in=None, codes=None, scales=None,
-               amax_out=None, whitened=None, want_codes=True, stream=None):
+               amax_out=None, whitened=None, want_codes=True, resid=None, stream=None):
         fmt = FORMATS.get(fmt, fmt)
         scaling = SCALINGS.get(scaling, scaling)
         m, d = self.m, self.d
@@ -233,9 +234,17 @@ class Layer:
                 codes = torch.empty(m, d, dtype=torch.uint8, device=W.device)
             if scales is None:
                 scales = torch.empty(nb, dtype=torch.float32, device=W.device)
-        _check(_lib.gift_encode(self._h, _ptr(W), W.stride(0), fmt, scaling, _ptr(amax_in), _ptr(amax_out),
-                                _ptr(codes) if want_codes else None, _ptr(scales) if want_codes else None,
-                                _ptr(whitened), _ptr(self.work), self.work_bytes, _stream(stream)), "gift_encode")
+        if resid is None:
+            _check(_lib.gift_encode(self._h, _ptr(W), W.stride(0), fmt, scaling, _ptr(amax_in), _ptr(amax_out),
+                                    _ptr(codes) if want_codes else None, _ptr(scales) if want_codes else None,
+                                    _ptr(whitened), _ptr(self.work), self.work_bytes, _stream(stream)), "gift_encode")
+        else:
+            if resid.dtype != torch.float32 or resid.shape != (m, d) or not resid.is_contiguous():
+                raise ValueError("resid must be a contiguous fp32 [d_out][d_in] tensor")
+            _check(_lib.gift_encode_ef(self._h, _ptr(W), W.stride(0), fmt, scaling, _ptr(amax_in), _ptr(amax_out),
+                                       _ptr(codes) if want_codes else None, _ptr(scales) if want_codes else None,
+                                       _ptr(whitened), _ptr(resid), _ptr(self.work), self.work_bytes,
+                                       _stream(stream)), "gift_encode_ef")
         return codes, scales
 
     def decode_reduce(self, codes: torch.Tensor, scales: torch.Tensor, fmt=E4M3, scaling=SCALE_TENSOR, out=None,

@@ -409,9 +409,12 @@ gift_status gift_refresh_factors(gift_layer_t L, const float* d_omega, void* d_w
 // Encode / decode
 // ---------------------------------------------------------------------------
 
-gift_status gift_encode(gift_layer_t L, const float* d_W, int64_t ldw, int32_t fmt, int32_t scaling,
-                        const float* d_amax_in, float* d_amax_out, uint8_t* d_codes, float* d_scales,
-                        float* d_whitened, void* d_work, size_t work_bytes, gift_stream_t stream) {
+// Encode with an optional error-feedback residual (d_resid: NULL or fp32
+// [m][d], read, and rewritten when codes are produced).
+static gift_status encode_impl(gift_layer_t L, const float* d_W, int64_t ldw, int32_t fmt, int32_t scaling,
+                               const float* d_amax_in, float* d_amax_out, uint8_t* d_codes, float* d_scales,
+                               float* d_whitened, float* d_resid, void* d_work, size_t work_bytes,
+                               gift_stream_t stream) {
   if (!L) return GIFT_ERR_INVALID_ARG;
   const gift_layer_desc& g = L->desc;
   const int m = g.d_out, d = g.d_in;
@@ -421,6 +424,7 @@ gift_status gift_encode(gift_layer_t L, const float* d_W, int64_t ldw, int32_t f
   if (d_codes && (!aligned16(d_codes) || !d_scales)) return GIFT_ERR_INVALID_ARG;
   if (!d_codes && !d_amax_out) return GIFT_ERR_INVALID_ARG;
   if (d_whitened && !aligned16(d_whitened)) return GIFT_ERR_INVALID_ARG;
+  if (d_resid && !aligned16(d_resid)) return GIFT_ERR_INVALID_ARG;
   if (!d_work || (reinterpret_cast<uintptr_t>(d_work) & 255u)) return GIFT_ERR_INVALID_ARG;
   if (work_bytes < L->wl.total) return GIFT_ERR_WORKSPACE;
   if (!L->ready) return GIFT_ERR_NOT_READY;
@@ -456,6 +460,7 @@ gift_status gift_encode(gift_layer_t L, const float* d_W, int64_t ldw, int32_t f
     a.codes = d_codes;
     a.scales = d_scales;
     a.whitened = d_whitened;
+    a.resid = d_resid;
     const int grid = fused_groups(g) * a.CG;
     hipError_t e = gift::launch_fused(a, grid, s);
     if (e != hipSuccess) {
@@ -468,26 +473,31 @@ gift_status gift_encode(gift_layer_t L, const float* d_W, int64_t ldw, int32_t f
   const float* X = d_W;
   int64_t ldx = ldw;
   float* out = d_whitened ? d_whitened : reinterpret_cast<float*>(work + L->wl.tile);
+  // with error feedback the amax is that of W~ + R: the whitening epilogues
+  // then skip theirs and one amax pass over both follows
+  uint32_t* wslots = d_resid ? nullptr : slots;
   switch (g.transform) {
     case GIFT_EUCLID:
-      GIFT_HIP(gift::launch_amax(d_W, ldw, m, d, scaling, slots, s));
+      GIFT_HIP(gift::launch_amax(d_W, ldw, m, d, scaling, d_resid, slots, s));
       if (d_whitened) GIFT_HIP(hipMemcpy2DAsync(d_whitened, (size_t)d * 4, d_W, (size_t)ldw * 4, (size_t)d * 4, m,
                                                 hipMemcpyDeviceToDevice, s));
       break;
     case GIFT_DIAG:
       GIFT_HIP(gift::launch_diag_apply(d_W, ldw, m, d, reinterpret_cast<const float*>(L->state + L->sl.coef), out, d,
-                                       scaling, slots, s));
+                                       scaling, wslots, s));
       X = out;
       ldx = d;
+      if (d_resid) GIFT_HIP(gift::launch_amax(X, ldx, m, d, scaling, d_resid, slots, s));
       break;
     case GIFT_LOWRANK: {
       double* ppart = reinterpret_cast<double*>(work + L->wl.ppart);
       const float* U = reinterpret_cast<const float*>(L->state + L->sl.U);
       const float* coef = reinterpret_cast<const float*>(L->state + L->sl.coef);
       GIFT_HIP(gift::launch_lr_project(d_W, ldw, m, d, U, g.rank, ppart, s));
-      GIFT_HIP(gift::launch_lr_apply(d_W, ldw, m, d, U, g.rank, ppart, coef, 0, out, d, scaling, slots, s));
+      GIFT_HIP(gift::launch_lr_apply(d_W, ldw, m, d, U, g.rank, ppart, coef, 0, out, d, scaling, wslots, s));
       X = out;
       ldx = d;
+      if (d_resid) GIFT_HIP(gift::launch_amax(X, ldx, m, d, scaling, d_resid, slots, s));
       break;
     }
     case GIFT_CHOL_INPUT:
@@ -503,7 +513,7 @@ gift_status gift_encode(gift_layer_t L, const float* d_W, int64_t ldw, int32_t f
       }
       GIFT_HIP(gift::launch_trmm(src, lds, m, d, reinterpret_cast<const float*>(L->state + L->sl.tinv_a), 0, out, d,
                                  s));
-      GIFT_HIP(gift::launch_amax(out, d, m, d, scaling, slots, s));
+      GIFT_HIP(gift::launch_amax(out, d, m, d, scaling, d_resid, slots, s));
       X = out;
       ldx = d;
       break;
@@ -512,12 +522,28 @@ gift_status gift_encode(gift_layer_t L, const float* d_W, int64_t ldw, int32_t f
       return GIFT_ERR_INVALID_ARG;
   }
   if (d_codes) {
-    GIFT_HIP(gift::launch_quantize(X, ldx, m, d, fmt, scaling, slots, d_amax_in, d_amax_out, d_codes, d_scales, flags,
-                                   s));
+    GIFT_HIP(gift::launch_quantize(X, ldx, m, d, fmt, scaling, slots, d_amax_in, d_amax_out, d_codes, d_scales,
+                                   d_resid, flags, s));
   } else {
     GIFT_HIP(gift::launch_amax_out(slots, d_amax_out, nb, s));   // amax only
   }
   return GIFT_OK;
+}
+
+gift_status gift_encode(gift_layer_t L, const float* d_W, int64_t ldw, int32_t fmt, int32_t scaling,
+                        const float* d_amax_in, float* d_amax_out, uint8_t* d_codes, float* d_scales,
+                        float* d_whitened, void* d_work, size_t work_bytes, gift_stream_t stream) {
+  return encode_impl(L, d_W, ldw, fmt, scaling, d_amax_in, d_amax_out, d_codes, d_scales, d_whitened, nullptr,
+                     d_work, work_bytes, stream);
+}
+
+gift_status gift_encode_ef(gift_layer_t L, const float* d_W, int64_t ldw, int32_t fmt, int32_t scaling,
+                           const float* d_amax_in, float* d_amax_out, uint8_t* d_codes, float* d_scales,
+                           float* d_whitened, float* d_resid, void* d_work, size_t work_bytes,
+                           gift_stream_t stream) {
+  if (!d_resid) return GIFT_ERR_INVALID_ARG;
+  return encode_impl(L, d_W, ldw, fmt, scaling, d_amax_in, d_amax_out, d_codes, d_scales, d_whitened, d_resid,
+                     d_work, work_bytes, stream);
 }
 
 gift_status gift_decode_reduce(gift_layer_t L, const uint8_t* d_codes, int64_t code_stride, const float* d_scales,

@@ -52,6 +52,7 @@ struct FusedArgs {
   uint8_t* codes;
   float* scales;
   float* whitened;
+  float* resid;               // error feedback: fp32 [m][d] residual, read and rewritten (NULL: none)
   const uint8_t* qcodes;
   int64_t code_stride;
   const float* qscales;
@@ -108,13 +109,15 @@ WorkLayout work_layout(const gift_layer_desc& desc);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s);
 hipError_t launch_fill_f32(float* p, float v, size_t n, hipStream_t s);
 
-// amax of |x| over a [m][ld] fp32 tensor into uint32 slots (bit patterns).
-hipError_t launch_amax(const float* x, int64_t ld, int m, int d, int scaling, uint32_t* slots,
-                       hipStream_t s);
-// quantise x [m][ld] with amax slots (or amax_in) -> codes, scales, amax_out.
+// amax of |x + resid| over a [m][ld] fp32 tensor into uint32 slots (bit
+// patterns); resid: NULL or fp32 [m][d] (error feedback).
+hipError_t launch_amax(const float* x, int64_t ld, int m, int d, int scaling, const float* resid,
+                       uint32_t* slots, hipStream_t s);
+// quantise u = x [m][ld] (+ resid) with amax slots (or amax_in) -> codes,
+// scales, amax_out; with resid also resid <- u - s dec(code).
 hipError_t launch_quantize(const float* x, int64_t ld, int m, int d, int fmt, int scaling,
                            const uint32_t* slots, const float* amax_in, float* amax_out,
-                           uint8_t* codes, float* scales, uint32_t* flags, hipStream_t s);
+                           uint8_t* codes, float* scales, float* resid, uint32_t* flags, hipStream_t s);
 // U = (1/R) sum_r s_r dec(q_r) -> fp32 [m][ldo]
 hipError_t launch_dequant_sum(const uint8_t* codes, int64_t code_stride, const float* scales,
                               int64_t scale_stride, int R, int m, int d, int fmt, int scaling,

@@ -41,10 +41,24 @@ __device__ __forceinline__ uint32_t halfwave_max(uint32_t v) {
   return v;
 }
 
-// amax of |x| (as uint32 bit patterns: exact and order-independent) per
-// 128 x 128 tile or for the whole tensor.
+// fp32(x + resid) elementwise (the error-feedback sum U~ = W~ + R of
+// GIFT 阅读笔记 Algorithm 1); resid is [m][d], NULL adds nothing.
+__device__ __forceinline__ float4 add_resid(float4 v, const float* __restrict__ resid, int64_t i) {
+  if (resid) {
+    const float4 e = *reinterpret_cast<const float4*>(resid + i);
+    v.x += e.x;
+    v.y += e.y;
+    v.z += e.z;
+    v.w += e.w;
+  }
+  return v;
+}
+
+// amax of |x (+ resid)| (as uint32 bit patterns: exact and
+// order-independent) per 128 x 128 tile or for the whole tensor.
 __global__ void __launch_bounds__(256) k_amax(const float* __restrict__ x, int64_t ld, int m, int d,
-                                              int scaling, uint32_t* __restrict__ slots) {
+                                              int scaling, const float* __restrict__ resid,
+                                              uint32_t* __restrict__ slots) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = blockIdx.x * 256 + lane * 4;
   const int r0 = blockIdx.y * kBlock;
@@ -53,6 +67,7 @@ __global__ void __launch_bounds__(256) k_amax(const float* __restrict__ x, int64
   if (col < d) {
     for (int r = r0 + wave; r < r1; r += 4) {
       float4 v = *reinterpret_cast<const float4*>(x + (int64_t)r * ld + col);
+      v = add_resid(v, resid, (int64_t)r * d + col);
       mx = umax(mx, umax(umax(absbits(v.x), absbits(v.y)), umax(absbits(v.z), absbits(v.w))));
     }
   }
@@ -71,20 +86,25 @@ __global__ void __launch_bounds__(256) k_amax(const float* __restrict__ x, int64
   }
 }
 
-hipError_t launch_amax(const float* x, int64_t ld, int m, int d, int scaling, uint32_t* slots,
-                       hipStream_t s) {
+hipError_t launch_amax(const float* x, int64_t ld, int m, int d, int scaling, const float* resid,
+                       uint32_t* slots, hipStream_t s) {
   if (m == 0 || d == 0) return hipSuccess;
   dim3 grid((unsigned)cdiv(d, 256), (unsigned)cdiv(m, kBlock));
-  hipLaunchKernelGGL(k_amax, grid, dim3(256), 0, s, x, ld, m, d, scaling, slots);
+  hipLaunchKernelGGL(k_amax, grid, dim3(256), 0, s, x, ld, m, d, scaling, resid, slots);
   return hipGetLastError();
 }
 
+// With resid (error feedback, GIFT 阅读笔记 Algorithm 1): the quantised
+// tensor is u = fp32(x + resid), and resid is overwritten with
+// fp32(u - s dec(code)), the difference rounded once (each element is read
+// and rewritten by the same lane).
 template <int FMT>
 __global__ void __launch_bounds__(256) k_quantize(const float* __restrict__ x, int64_t ld, int m, int d,
                                                   int scaling, const uint32_t* __restrict__ slots,
                                                   const float* __restrict__ amax_in,
                                                   float* __restrict__ amax_out, uint8_t* __restrict__ codes,
-                                                  float* __restrict__ scales, uint32_t* __restrict__ flags) {
+                                                  float* __restrict__ scales, float* __restrict__ resid,
+                                                  uint32_t* __restrict__ flags) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = blockIdx.x * 256 + lane * 4;
   const int r0 = blockIdx.y * kBlock;
@@ -106,6 +126,7 @@ __global__ void __launch_bounds__(256) k_quantize(const float* __restrict__ x, i
   const bool bad = am >= 0x7F800000u;
   for (int rr = r0 + wave; rr < r1; rr += 4) {
     float4 v = *reinterpret_cast<const float4*>(x + (int64_t)rr * ld + col);
+    v = add_resid(v, resid, (int64_t)rr * d + col);
     uint32_t c0, c1, c2, c3;
     if (bad) {
       c0 = c1 = c2 = c3 = 0x7Fu;
@@ -116,20 +137,25 @@ __global__ void __launch_bounds__(256) k_quantize(const float* __restrict__ x, i
       c3 = enc_fp8<FMT>(v.w * r);
     }
     *reinterpret_cast<uint32_t*>(codes + (int64_t)rr * d + col) = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    if (resid) {
+      const float4 e = make_float4(__builtin_fmaf(-sc, dec_fp8<FMT>(c0), v.x), __builtin_fmaf(-sc, dec_fp8<FMT>(c1), v.y),
+                                   __builtin_fmaf(-sc, dec_fp8<FMT>(c2), v.z), __builtin_fmaf(-sc, dec_fp8<FMT>(c3), v.w));
+      *reinterpret_cast<float4*>(resid + (int64_t)rr * d + col) = e;
+    }
   }
 }
 
 hipError_t launch_quantize(const float* x, int64_t ld, int m, int d, int fmt, int scaling,
                            const uint32_t* slots, const float* amax_in, float* amax_out,
-                           uint8_t* codes, float* scales, uint32_t* flags, hipStream_t s) {
+                           uint8_t* codes, float* scales, float* resid, uint32_t* flags, hipStream_t s) {
   if (m == 0 || d == 0) return hipSuccess;
   dim3 grid((unsigned)cdiv(d, 256), (unsigned)cdiv(m, kBlock));
   if (fmt == 0)
     hipLaunchKernelGGL(k_quantize<0>, grid, dim3(256), 0, s, x, ld, m, d, scaling, slots, amax_in,
-                       amax_out, codes, scales, flags);
+                       amax_out, codes, scales, resid, flags);
   else
     hipLaunchKernelGGL(k_quantize<1>, grid, dim3(256), 0, s, x, ld, m, d, scaling, slots, amax_in,
-                       amax_out, codes, scales, flags);
+                       amax_out, codes, scales, resid, flags);
   return hipGetLastError();
 }
 

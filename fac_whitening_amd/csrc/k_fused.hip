@@ -293,6 +293,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
   __shared__ uint32_t blk[2][8];          // combined amax of the blocks of this tile
   __shared__ uint32_t wmax[16];
   __shared__ float srs[12];               // reciprocal scales of those blocks
+  __shared__ float sss[12];               // and their scales (error feedback)
   __shared__ uint32_t sam[12];            // the amax bits they come from
   // cp[rb][wave]: the row block's partials lie in the first 5.5 tile rows
   // (rb 0), the next 5.5 (rb 1), ...
@@ -764,7 +765,22 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
     return;
   }
 
-  // ---- encode: inspection copy, amax, scale, quantise -----------------------
+  // ---- encode: inspection copy, error feedback, amax, scale, quantise -------
+  // The residual R (error feedback, Algorithm 1) is read in the sub-tile
+  // layout of x: sub-tile i of this lane holds row row0 + 16 SUB_RB(i) + lr,
+  // columns c .. c + 3 and c + 16 .. c + 19, c = col0 + 32 SUB_CB(i) + 4 lg.
+  const bool ef = a.resid != nullptr;
+  const auto rr = make_rsrc(a.resid, ef ? (int64_t)m * d * 4 : 0);
+  int32x4 rv[NSUB][2];
+  if (ef) {
+#pragma unroll
+    for (int i = 0; i < NSUB; ++i) {
+      const int row = row0 + SUB_RB(i) * 16 + lr, c = col0 + SUB_CB(i) * 32 + 4 * lg;
+      const int o = (row * d + c) * 4;
+      rv[i][0] = __builtin_amdgcn_raw_buffer_load_b128(rr, (row < m && c < d) ? o : kOff, 0, 0);
+      rv[i][1] = __builtin_amdgcn_raw_buffer_load_b128(rr, (row < m && c + 16 < d) ? o + 64 : kOff, 0, 0);
+    }
+  }
   if (a.whitened) {
     const auto wh = make_rsrc(a.whitened, (int64_t)m * d * 4);
 #pragma unroll
@@ -776,6 +792,13 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
       __builtin_amdgcn_raw_buffer_store_b128(v0, wh, (row < m && c < d) ? o : kOff, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b128(v1, wh, (row < m && c + 16 < d) ? o + 64 : kOff, 0, 0);
     }
+  }
+  if (ef) {
+    // U~ = fp32(W~ + R); entries outside the tensor read zeros
+#pragma unroll
+    for (int i = 0; i < NSUB; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[i][j] += __int_as_float(rv[i][j >> 2][j & 3]);
   }
   // |x| bit patterns order like |x| (NaN above +Inf): the lane maximum of
   // each sub-tile.  Dead column blocks hold zeros.
@@ -896,6 +919,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
     // blocks rb0 and cb0 .. cb0 + 5 always meet the tile; rb0 + 1 may not
     const bool inside = br * kBlock < m && bc * kBlock < d && br * kBlock < row0 + TR;
     srs[tid] = 0.0f;
+    sss[tid] = 0.0f;
     sam[tid] = 0u;
     if (inside) {
       const int slot = a.scaling == 0 ? 0 : br * nbd + bc;
@@ -904,6 +928,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
       float r, sc;
       scale_pair(am, fmax, r, sc);
       srs[tid] = r;
+      sss[tid] = sc;
       sam[tid] = am;
       const bool leader = a.scaling == 0 ? g == 0 : (br * kBlock >= row0 && bc * kBlock >= col0);
       if (leader) {
@@ -952,6 +977,23 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
     uint8_t* cs = reinterpret_cast<uint8_t*>(smem) + (rbl * 16 + lr) * (TC + 16) + cbl * 32 + 4 * lg;
     *reinterpret_cast<uint32_t*>(cs) = q0;
     *reinterpret_cast<uint32_t*>(cs + 16) = q1;
+    if (ef) {
+      // new residual fp32(U~ - s dec(q)), the difference rounded once
+      const float sc = sss[e];
+      float dv[8];
+      dec4<FMT>(q0, dv);
+      dec4<FMT>(q1, dv + 4);
+      int32x4 o0, o1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        o0[j] = __float_as_int(__builtin_fmaf(-sc, dv[j], x[i][j]));
+        o1[j] = __float_as_int(__builtin_fmaf(-sc, dv[4 + j], x[i][4 + j]));
+      }
+      const int row = row0 + rbl * 16 + lr, c = col0 + cbl * 32 + 4 * lg;
+      const int o = (row * d + c) * 4;
+      __builtin_amdgcn_raw_buffer_store_b128(o0, rr, (row < m && c < d) ? o : kOff, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(o1, rr, (row < m && c + 16 < d) ? o + 64 : kOff, 0, 0);
+    }
   }
   __syncthreads();
   const auto cr = make_rsrc(a.codes, (int64_t)m * d);

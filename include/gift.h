@@ -162,7 +162,7 @@ gift_status gift_refresh_factors(gift_layer_t layer, const float* d_omega, void*
 
 /* ---------------------------------------------------------------------------
  * Encode one replica's gradient ([Note] Algorithm 1, lines 10-13 without
- * error feedback; Euclidean lines 4-6):
+ * error feedback (see gift_encode_ef); Euclidean lines 4-6):
  *   W~ = W T_A (two-sided: L_G^-1 W T_A), amax per tensor or per 128x128
  *   tile (edge tiles: their valid region), r = fp32(FMAX / amax),
  *   code = FP8(fp32(w~ * r)) with round-to-nearest-even (ties to the even
@@ -182,6 +182,27 @@ gift_status gift_encode(gift_layer_t layer, const float* d_W, int64_t ldw, int32
                         int32_t scaling, const float* d_amax_in, float* d_amax_out,
                         uint8_t* d_codes, float* d_scales, float* d_whitened, void* d_work,
                         size_t work_bytes, gift_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Encode with error feedback ([Note] Algorithm 1, lines 10-15: the
+ * residual of the previous step is added in the whitened coordinates):
+ *   U~ = fp32(W~ + R), amax, scale and codes of U~ exactly as gift_encode
+ *   computes them for W~, then R <- fp32(U~ - s dec(code)) (the difference
+ *   rounded once).
+ * d_resid:      fp32 [d_out][d_in] (leading dimension d_in), caller-owned,
+ *               one per worker (replica); zero it before the first step.
+ *               Read, and rewritten when d_codes is given; an amax-only call
+ *               (d_codes NULL: d_amax_out receives the amax of U~, e.g. for
+ *               the AllReduceMax of a shared scale) leaves it unchanged.
+ *               Must not overlap d_W, d_whitened, d_codes or d_scales.
+ * d_whitened:   receives W~ (without the residual).
+ * Other arguments, errors and the NULL-resid case as gift_encode
+ * (d_resid NULL: GIFT_ERR_INVALID_ARG).
+ * ------------------------------------------------------------------------- */
+gift_status gift_encode_ef(gift_layer_t layer, const float* d_W, int64_t ldw, int32_t fmt,
+                           int32_t scaling, const float* d_amax_in, float* d_amax_out,
+                           uint8_t* d_codes, float* d_scales, float* d_whitened, float* d_resid,
+                           void* d_work, size_t work_bytes, gift_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Decode-reduce R replica payloads ([Note] Eq. (1) and Algorithm 1, lines

@@ -349,11 +349,21 @@ def encode_ef(W, T, R, fmt: str, scaling: str, L_G=None, amax_in=None):
     step (zeros at the first).  Returns dict(whitened, u_tilde, codes,
     scales, amax, residual)."""
     Wt = whiten(W, T, L_G)
-    Ut = (Wt + np.asarray(R, dtype=np.float32)).astype(np.float32)
+    out = error_feedback(Wt, R, fmt, scaling, amax_in)
+    out["whitened"] = Wt
+    return out
+
+
+def error_feedback(Wt, R, fmt: str, scaling: str, amax_in=None):
+    """The error-feedback step of [Note] Algorithm 1 (lines 11-15, R11) on
+    an already whitened float32 tensor Wt: U~ = fp32(Wt + R), scale and
+    quantise U~, new residual fp32(U~ - s dec(q)).  Returns dict(u_tilde,
+    codes, scales, amax, residual)."""
+    Ut = (np.asarray(Wt, dtype=np.float32) + np.asarray(R, dtype=np.float32)).astype(np.float32)
     codes, scales, am = quantize(Ut, fmt, scaling, amax_in)
     deq = dequantize(codes, scales, fmt, scaling)
     Rn = (Ut.astype(np.float64) - deq).astype(np.float32)
-    return dict(whitened=Wt, u_tilde=Ut, codes=codes, scales=scales, amax=am, residual=Rn)
+    return dict(u_tilde=Ut, codes=codes, scales=scales, amax=am, residual=Rn)
 
 
 def decode_reduce(codes_list, scales_list, Tinv, fmt: str, scaling: str, L_G=None):

@@ -31,3 +31,21 @@ def assert_codes(got, want, min_same=0.999, max_step=1):
     assert same >= min_same, f"identical codes {same:.6f} < {min_same}"
     assert step <= max_step, f"code step distance {step} > {max_step}"
     return same, step
+
+
+def layer_with_factor(fw, m, d, fac, device):
+    """A rank-32 layer whose state holds the oracle's factor (basis U and the
+    coefficients c_enc, c_dec, rho^-1/2, rho^1/2), marked ready: stage
+    isolation of the encode / decode kernels from the refresh."""
+    import torch
+
+    L = fw.Layer(m, d, "lowrank", device=device)
+    b = L.buffers()
+    b["U"].copy_(torch.from_numpy(fac["U"].astype(np.float32)))
+    coef = np.zeros(68, np.float32)
+    coef[:32] = fac["c_enc"]
+    coef[32:64] = fac["c_dec"]
+    coef[64], coef[65] = fac["rho"] ** -0.5, fac["rho"] ** 0.5
+    b["coef"].copy_(torch.from_numpy(coef))
+    L.mark_ready()
+    return L

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 from oracle import gift as G
-from tests.helpers import assert_codes, rel_fro
+from tests.helpers import assert_codes, layer_with_factor, rel_fro
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -44,16 +44,7 @@ def _case(m, d, R, seed):
 
 
 def _layer_with_factor(fw, m, d, fac):
-    L = fw.Layer(m, d, "lowrank", device=DEV)
-    b = L.buffers()
-    b["U"].copy_(torch.from_numpy(fac["U"].astype(np.float32)))
-    coef = np.zeros(68, np.float32)
-    coef[:32] = fac["c_enc"]
-    coef[32:64] = fac["c_dec"]
-    coef[64], coef[65] = fac["rho"] ** -0.5, fac["rho"] ** 0.5
-    b["coef"].copy_(torch.from_numpy(coef))
-    L.mark_ready()
-    return L
+    return layer_with_factor(fw, m, d, fac, DEV)
 
 
 SHAPES = [(100, 1000), (200, 1544), (48, 768), (1536, 6144)]
