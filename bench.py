@@ -5,7 +5,8 @@ gradient (rank-32 input-side whitening, E4M3, per-tensor scale) and
 gift_decode_reduce of R = 8 replica payloads into one fp32 gradient, on one
 stream.  The other 7 payloads are encoded during setup.  Statistics
 (T = 16384 bf16 tokens) and the rank-32 refresh run in setup and are timed
-separately.
+separately, as is the encode alone, without and with error feedback
+(stage_rooflines).
 
 Timed region: W untimed warmup steps, then K steps bracketed by
 torch.cuda.synchronize(); the input buffers rotate over 4 independent sets
@@ -179,6 +180,28 @@ def main():
                 "unit_frac": round((enc_bytes + dec_bytes) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "decode_ms": round(t_dec, 5), "rest_of_step_ms": round(t_enc, 5),
                 "alg_bytes_encode": int(enc_bytes), "alg_bytes_decode": int(dec_bytes)}
+
+    # the encode alone, without and with error feedback (Algorithm 1: the
+    # residual is read and rewritten beside the codes), outside the unit
+    resids = [torch.zeros(m, d, dtype=torch.float32, device=dev) for _ in sets]
+    turn = [0]
+
+    def enc(ef):
+        j = turn[0] % len(sets)
+        turn[0] += 1
+        W, codes, scales, _ = sets[j]
+        L.encode(W, fw.E4M3, scaling, codes=codes[0], scales=scales[0], resid=resids[j] if ef else None)
+
+    for name, ef in (("encode", False), ("encode_ef", True)):
+        t = _event_ms(torch, lambda: enc(ef), 40)
+        b = enc_bytes + (8.0 * m * d if ef else 0.0)
+        stage_rooflines[name] = {
+            "ms": round(t, 5), "bound": "hbm", "achieved": round(b / (t * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(b / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "alg_bytes": int(b),
+            "work": "rank-32 whitening, amax, E4M3 codes of one replica"
+                    + (" + fp32 residual read and rewritten" if ef else "")}
+    torch.cuda.synchronize()
+    assert L.flags() == 0
 
     result = {
         "metric": "GIFT encode+decode GB/s of fp32 grad (1536\u00d76144, r=32); % of HBM peak",

@@ -30,6 +30,9 @@
 //    128 x 128 block it touches) as 64-bit words tagged with the call's
 //    epoch, and reads the words of the workgroups it depends on until all
 //    carry the current epoch (an all-gather: no serial chain of atomics).
+//  * Error feedback (Algorithm 1): the _ef encode reads the residual R in
+//    the sub-tile layout of the registers, quantises W~ + R and rewrites R
+//    with what the codes did not carry, in the same pass.
 //  * Tags derive from per-direction call counters that only grow, so
 //    nothing is reset between calls.  Every wait is bounded; a timeout sets
 //    GIFT_FLAG_SPIN_TIMEOUT and the kernel still exits.
@@ -283,7 +286,7 @@ constexpr int kXPT = kXW / 512;     // of them per thread (3)
 // LR: the rank-k transform (false: the Euclidean codec, T_A = I: the same
 // tile schedule, amax all-gather and quantiser without the projection,
 // exchange and reconstruction).
-template <int FMT, bool ENC, int RC, int SC, bool LR>
+template <int FMT, bool ENC, int RC, int SC, bool LR, bool EF = false>
 __device__ __forceinline__ void fused_body(const FusedArgs& a) {
   // The staged tile (fp32, padded rows); after it has been read into
   // registers the same memory holds the per-wave projection partials and the
@@ -769,10 +772,9 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
   // The residual R (error feedback, Algorithm 1) is read in the sub-tile
   // layout of x: sub-tile i of this lane holds row row0 + 16 SUB_RB(i) + lr,
   // columns c .. c + 3 and c + 16 .. c + 19, c = col0 + 32 SUB_CB(i) + 4 lg.
-  const bool ef = a.resid != nullptr;
-  const auto rr = make_rsrc(a.resid, ef ? (int64_t)m * d * 4 : 0);
+  const auto rr = make_rsrc(a.resid, EF ? (int64_t)m * d * 4 : 0);
   int32x4 rv[NSUB][2];
-  if (ef) {
+  if constexpr (EF) {
 #pragma unroll
     for (int i = 0; i < NSUB; ++i) {
       const int row = row0 + SUB_RB(i) * 16 + lr, c = col0 + SUB_CB(i) * 32 + 4 * lg;
@@ -793,7 +795,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
       __builtin_amdgcn_raw_buffer_store_b128(v1, wh, (row < m && c + 16 < d) ? o + 64 : kOff, 0, 0);
     }
   }
-  if (ef) {
+  if constexpr (EF) {
     // U~ = fp32(W~ + R); entries outside the tensor read zeros
 #pragma unroll
     for (int i = 0; i < NSUB; ++i)
@@ -977,7 +979,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
     uint8_t* cs = reinterpret_cast<uint8_t*>(smem) + (rbl * 16 + lr) * (TC + 16) + cbl * 32 + 4 * lg;
     *reinterpret_cast<uint32_t*>(cs) = q0;
     *reinterpret_cast<uint32_t*>(cs + 16) = q1;
-    if (ef) {
+    if constexpr (EF) {
       // new residual fp32(U~ - s dec(q)), the difference rounded once
       const float sc = sss[e];
       float dv[8];
@@ -1007,11 +1009,15 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
 }
 
 // One kernel per direction, transform and format (distinct names in
-// traces); the decode also per replica count 4, 8, 16 (0: any count up
-// to 64) and scaling.
+// traces); the encode also with error feedback (_ef), the decode per
+// replica count 4, 8, 16 (0: any count up to 64) and scaling.
 template <int FMT>
 __global__ void __launch_bounds__(512) k_rank_encode(FusedArgs a) {
   fused_body<FMT, true, 0, -1, true>(a);
+}
+template <int FMT>
+__global__ void __launch_bounds__(512) k_rank_encode_ef(FusedArgs a) {
+  fused_body<FMT, true, 0, -1, true, true>(a);
 }
 template <int FMT, int RC, int SC>
 __global__ void __launch_bounds__(512) k_rank_decode(FusedArgs a) {
@@ -1020,6 +1026,10 @@ __global__ void __launch_bounds__(512) k_rank_decode(FusedArgs a) {
 template <int FMT>
 __global__ void __launch_bounds__(512) k_euclid_encode(FusedArgs a) {
   fused_body<FMT, true, 0, -1, false>(a);
+}
+template <int FMT>
+__global__ void __launch_bounds__(512) k_euclid_encode_ef(FusedArgs a) {
+  fused_body<FMT, true, 0, -1, false, true>(a);
 }
 template <int FMT, int RC, int SC>
 __global__ void __launch_bounds__(512) k_euclid_decode(FusedArgs a) {
@@ -1056,14 +1066,18 @@ static void launch_decode(const FusedArgs& args, dim3 gd, dim3 bd, hipStream_t s
 hipError_t launch_fused(const FusedArgs& args, int grid, hipStream_t s) {
   const dim3 gd((unsigned)grid), bd(512);
   if (args.mode == 0) {
-    if (args.lr && args.fmt == 0)
-      hipLaunchKernelGGL(k_rank_encode<0>, gd, bd, 0, s, args);
-    else if (args.lr)
-      hipLaunchKernelGGL(k_rank_encode<1>, gd, bd, 0, s, args);
-    else if (args.fmt == 0)
-      hipLaunchKernelGGL(k_euclid_encode<0>, gd, bd, 0, s, args);
-    else
-      hipLaunchKernelGGL(k_euclid_encode<1>, gd, bd, 0, s, args);
+    // kernel by transform, error feedback and format
+    const int which = (args.lr ? 4 : 0) + (args.resid ? 2 : 0) + (args.fmt == 0 ? 0 : 1);
+    switch (which) {
+      case 0: hipLaunchKernelGGL(k_euclid_encode<0>, gd, bd, 0, s, args); break;
+      case 1: hipLaunchKernelGGL(k_euclid_encode<1>, gd, bd, 0, s, args); break;
+      case 2: hipLaunchKernelGGL(k_euclid_encode_ef<0>, gd, bd, 0, s, args); break;
+      case 3: hipLaunchKernelGGL(k_euclid_encode_ef<1>, gd, bd, 0, s, args); break;
+      case 4: hipLaunchKernelGGL(k_rank_encode<0>, gd, bd, 0, s, args); break;
+      case 5: hipLaunchKernelGGL(k_rank_encode<1>, gd, bd, 0, s, args); break;
+      case 6: hipLaunchKernelGGL(k_rank_encode_ef<0>, gd, bd, 0, s, args); break;
+      default: hipLaunchKernelGGL(k_rank_encode_ef<1>, gd, bd, 0, s, args); break;
+    }
   } else if (args.lr) {
     if (args.fmt == 0)
       launch_decode<0, true>(args, gd, bd, s);
