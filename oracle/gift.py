@@ -53,11 +53,24 @@ R11 Error feedback (Note 算法 1, lines 11-15): the residual is added to the
     U~ - s dec(q) (one rounding of the exact difference).  The whitened
     tensor itself (W~) is what the inspection output shows; the amax and
     the codes are those of U~.
+R12 FP4 payload (the pages name NVFP4 without defining it): E2M1 elements
+    (``oracle.fp4``) in blocks of 16 consecutive elements of a row, each
+    block with an E4M3 scale, under one fp32 scale per tensor:
+      g     = fp32(amax_T / (6 * 448))       (amax_T local or shared; 0 -> 0)
+      sig_b = fp32(amax_b / (6 g))           (the block scale before coding)
+      sc_b  = E4M3(sig_b)                    (RNE, saturating at 448)
+      S_b   = fp32(dec(sc_b) * g)            (the block's effective scale)
+      r_b   = fp32(1 / S_b) (0 if S_b = 0),  y = fp32(x * r_b),  q = E2M1(y)
+    dequantised value S_b * dec(q).  A non-finite amax_T gives g = NaN,
+    every block scale 0x7F and codes 0; a block whose amax is NaN gets scale
+    0x7F and codes 0.  Every quotient and product is of float32 values
+    computed exactly in float64 and rounded once to float32.
 """
 from __future__ import annotations
 
 import numpy as np
 
+from . import fp4 as _fp4
 from . import fp8 as _fp8
 
 TRANSFORMS = ("euclid", "diag", "lowrank", "chol", "twosided")
@@ -302,8 +315,87 @@ def dequant_reduce(codes_list, scales_list, fmt: str, scaling: str) -> np.ndarra
     return acc / R
 
 
+# ---------------------------------------------------------------------------
+# FP4 payload (R12)
+# ---------------------------------------------------------------------------
+
+FP4_BLOCK = 16
+FP4_TSCALE_DIV = _fp4.FMAX * _fp8.FMAX["e4m3"]   # 6 * 448: the largest block scale times the largest element
+
+
+def quantize_fp4(X32, amax_in=None) -> dict:
+    """Two-level FP4 quantiser of a float32 [m][d] tensor (d a multiple of
+    16), reading R12.  Returns dict(codes uint8 [m][d] (values 0..15),
+    bscales uint8 [m][d/16] (E4M3 codes), tscale float32, amax float64 (the
+    amax_T used)).  amax_in: the shared per-tensor amax (AllReduceMax), or
+    None for the local one."""
+    X32 = np.asarray(X32, dtype=np.float32)
+    m, d = X32.shape
+    assert d % FP4_BLOCK == 0
+    x = _f64(X32).reshape(m, d // FP4_BLOCK, FP4_BLOCK)
+    am_t = float(np.abs(x).max()) if amax_in is None else float(np.asarray(amax_in, dtype=np.float64).ravel()[0])
+    if x.size == 0 and amax_in is None:
+        am_t = 0.0
+    if not np.isfinite(am_t):
+        g = np.float32(np.nan)
+    else:
+        g = np.float32(am_t / FP4_TSCALE_DIV)
+    amax_b = np.abs(x).max(axis=2) if x.size else np.zeros((m, 0))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        if np.isnan(g):
+            sig = np.full(amax_b.shape, np.nan, dtype=np.float32)
+        elif g == 0:
+            sig = np.zeros(amax_b.shape, dtype=np.float32)
+        else:
+            sig = (amax_b / (6.0 * float(g))).astype(np.float32)
+        sc = _fp8.encode(sig, "e4m3")
+        S = (_fp8.decode(sc, "e4m3") * float(g)).astype(np.float32)
+        r = np.where(S > 0, (1.0 / S.astype(np.float64)).astype(np.float32), np.float32(0.0))
+        r = np.where(np.isnan(S), np.float32(np.nan), r).astype(np.float32)
+        y = (x * r.astype(np.float64)[:, :, None]).astype(np.float32)
+    codes = _fp4.encode(y)
+    codes = np.where(np.isnan(S)[:, :, None], 0, codes).astype(np.uint8)
+    return dict(codes=codes.reshape(m, d), bscales=sc.astype(np.uint8), tscale=g, amax=am_t)
+
+
+def fp4_block_scales(bscales, tscale) -> np.ndarray:
+    """S_b = fp32(dec(sc_b) * g) per block (R12), float32 [m][d/16]."""
+    return (_fp8.decode(bscales, "e4m3") * float(np.float32(tscale))).astype(np.float32)
+
+
+def dequantize_fp4(codes, bscales, tscale) -> np.ndarray:
+    """S_b * dec(q) per element, float64 [m][d]."""
+    S = fp4_block_scales(bscales, tscale).astype(np.float64)
+    return _fp4.decode(codes) * np.repeat(S, FP4_BLOCK, axis=1)
+
+
+def dequant_reduce_fp4(codes_list, bscales_list, tscales) -> np.ndarray:
+    """U = (1/R) sum_r S_{b,r} dec(q_r) (R5 with the FP4 payload)."""
+    R = len(codes_list)
+    acc = None
+    for c, b, t in zip(codes_list, bscales_list, tscales):
+        v = dequantize_fp4(c, b, t)
+        acc = v if acc is None else acc + v
+    return acc / R
+
+
+def error_feedback_fp4(Wt, R, amax_in=None) -> dict:
+    """R11 with the FP4 payload: U~ = fp32(Wt + R), quantise U~ (R12), new
+    residual fp32(U~ - S_b dec(q))."""
+    Ut = (np.asarray(Wt, dtype=np.float32) + np.asarray(R, dtype=np.float32)).astype(np.float32)
+    out = quantize_fp4(Ut, amax_in)
+    deq = dequantize_fp4(out["codes"], out["bscales"], out["tscale"])
+    out["u_tilde"] = Ut
+    out["residual"] = (Ut.astype(np.float64) - deq).astype(np.float32)
+    return out
+
+
 def payload_bytes(m: int, d: int, scaling: str) -> int:
-    """Codes (1 B/element) plus one float32 scale per tile."""
+    """FP8: codes (1 B/element) plus one float32 scale per tile.  FP4
+    ("block16", R12): half a byte per element, one E4M3 byte per 16
+    elements, one float32 tensor scale."""
+    if scaling == "block16":
+        return m * d // 2 + m * d // FP4_BLOCK + 4
     bm, bd = nblocks(m, d, scaling)
     return m * d + 4 * bm * bd
 
