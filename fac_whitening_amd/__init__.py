@@ -26,8 +26,8 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 # enums (include/gift.h)
 EUCLID, DIAG, LOWRANK, CHOL_INPUT, CHOL_TWOSIDED = range(5)
-E4M3, E5M2 = 0, 1
-SCALE_TENSOR, SCALE_BLOCK128 = 0, 1
+E4M3, E5M2, E2M1 = 0, 1, 2
+SCALE_TENSOR, SCALE_BLOCK128, SCALE_BLOCK16 = 0, 1, 2
 BF16, FP32 = 0, 1
 SIDE_A, SIDE_G = 0, 1
 FLAG_NONFINITE, FLAG_SPIN_TIMEOUT = 1, 2
@@ -41,7 +41,7 @@ EXPORTS = [
     "gift_layer_state_bytes", "gift_layer_create", "gift_layer_destroy", "gift_layer_get_counters",
     "gift_layer_set_counters", "gift_layer_flags", "gift_layer_buffers", "gift_layer_mark_ready",
     "gift_accumulate_stats", "gift_commit_stats", "gift_refresh_factors", "gift_encode", "gift_encode_ef",
-    "gift_decode_reduce", "gift_payload_bytes", "gift_profiler_create", "gift_profiler_destroy",
+    "gift_decode_reduce", "gift_encode_fp4", "gift_decode_reduce_fp4", "gift_payload_bytes", "gift_profiler_create", "gift_profiler_destroy",
     "gift_profiler_workspace_bytes", "gift_profile_step", "gift_select_layers", "gift_status_string",
     "gift_last_hip_error", "gift_set_fused",
 ]
@@ -77,6 +77,8 @@ _sig("gift_commit_stats", _i32, _vp, _i32, _vp)
 _sig("gift_refresh_factors", _i32, _vp, _vp, _vp, _sz, _vp)
 _sig("gift_encode", _i32, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp)
 _sig("gift_encode_ef", _i32, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp)
+_sig("gift_encode_fp4", _i32, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp)
+_sig("gift_decode_reduce_fp4", _i32, _vp, _vp, _i64, _vp, _i64, _vp, _i32, _vp, _i64, _vp, _sz, _vp)
 _sig("gift_decode_reduce", _i32, _vp, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _vp, _i64, _vp, _sz, _vp)
 _sig("gift_payload_bytes", _sz, _i32, _i32, _i32)
 _sig("gift_profiler_create", _i32, _i32, _i32, _i32, _vp, _vp, _P(_vp))
@@ -264,6 +266,47 @@ class Layer:
         _check(_lib.gift_decode_reduce(self._h, _ptr(codes), cs, _ptr(scales), ss, R, fmt, scaling, _ptr(out),
                                        out.stride(0), _ptr(self.work), self.work_bytes, _stream(stream)),
                "gift_decode_reduce")
+        return out
+
+    def encode_fp4(self, W: torch.Tensor, amax_in=None, codes=None, bscales=None, tscale=None, amax_out=None,
+                   whitened=None, want_codes=True, resid=None, stream=None):
+        """FP4 payload: codes [m][d/2] uint8 (two per byte, even column low),
+        bscales [m][d/16] uint8 (E4M3), tscale [1] fp32."""
+        m, d = self.m, self.d
+        if W.dtype != torch.float32 or W.shape != (m, d) or W.stride(1) != 1:
+            raise ValueError("W must be fp32 [d_out][d_in] with unit column stride")
+        if resid is not None and (resid.dtype != torch.float32 or resid.shape != (m, d) or not resid.is_contiguous()):
+            raise ValueError("resid must be a contiguous fp32 [d_out][d_in] tensor")
+        if want_codes:
+            if codes is None:
+                codes = torch.empty(m, d // 2, dtype=torch.uint8, device=W.device)
+            if bscales is None:
+                bscales = torch.empty(m, d // 16, dtype=torch.uint8, device=W.device)
+            if tscale is None:
+                tscale = torch.empty(1, dtype=torch.float32, device=W.device)
+        _check(_lib.gift_encode_fp4(self._h, _ptr(W), W.stride(0), _ptr(amax_in), _ptr(amax_out),
+                                    _ptr(codes) if want_codes else None, _ptr(bscales) if want_codes else None,
+                                    _ptr(tscale) if want_codes else None, _ptr(whitened), _ptr(resid),
+                                    _ptr(self.work), self.work_bytes, _stream(stream)), "gift_encode_fp4")
+        return codes, bscales, tscale
+
+    def decode_reduce_fp4(self, codes: torch.Tensor, bscales: torch.Tensor, tscales: torch.Tensor, out=None,
+                          stream=None):
+        """codes [R][m][d/2], bscales [R][m][d/16] uint8, tscales [R] fp32."""
+        m, d = self.m, self.d
+        if codes.dim() == 2:
+            codes, bscales = codes.unsqueeze(0), bscales.unsqueeze(0)
+        R = codes.shape[0]
+        tscales = tscales.reshape(-1)
+        if tscales.numel() < R or tscales.dtype != torch.float32 or not tscales.is_contiguous():
+            raise ValueError("tscales must be a contiguous fp32 tensor of R entries")
+        if out is None:
+            out = torch.empty(m, d, dtype=torch.float32, device=codes.device)
+        cs = codes.stride(0) if R > 1 else m * d // 2
+        bs = bscales.stride(0) if R > 1 else m * d // 16
+        _check(_lib.gift_decode_reduce_fp4(self._h, _ptr(codes), cs, _ptr(bscales), bs, _ptr(tscales), R, _ptr(out),
+                                           out.stride(0), _ptr(self.work), self.work_bytes, _stream(stream)),
+               "gift_decode_reduce_fp4")
         return out
 
 

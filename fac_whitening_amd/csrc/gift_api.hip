@@ -214,6 +214,8 @@ int32_t gift_set_fused(int32_t enable) {
 
 size_t gift_payload_bytes(int32_t d_out, int32_t d_in, int32_t scaling) {
   if (d_out < 0 || d_in < 0) return 0;
+  if (scaling == GIFT_SCALE_BLOCK16)   // FP4: half a byte per code, one E4M3 byte per 16, the tensor scale
+    return (size_t)d_out * (size_t)d_in / 2 + (size_t)d_out * (size_t)d_in / 16 + 4;
   return (size_t)d_out * (size_t)d_in + 4 * (size_t)nblk(d_out, d_in, scaling);
 }
 
@@ -409,19 +411,60 @@ gift_status gift_refresh_factors(gift_layer_t L, const float* d_omega, void* d_w
 // Encode / decode
 // ---------------------------------------------------------------------------
 
+// Multi-kernel map back of the reduced whitened tensor Ub (fp32 [m][d] in
+// the workspace) to d_out: W^ = Ub T_A^-1 (two-sided: L_G Ub L_A^T).
+static gift_status unwhiten_multi(gift_layer_t L, const float* Ub, float* d_out, int64_t ldo, char* work,
+                                  hipStream_t s) {
+  const gift_layer_desc& g = L->desc;
+  const int m = g.d_out, d = g.d_in;
+  switch (g.transform) {
+    case GIFT_DIAG:
+      GIFT_HIP(gift::launch_diag_apply(Ub, d, m, d, reinterpret_cast<const float*>(L->state + L->sl.coef) + d, d_out,
+                                       ldo, GIFT_SCALE_TENSOR, nullptr, s));
+      break;
+    case GIFT_LOWRANK: {
+      double* ppart = reinterpret_cast<double*>(work + L->wl.ppart);
+      const float* U = reinterpret_cast<const float*>(L->state + L->sl.U);
+      const float* coef = reinterpret_cast<const float*>(L->state + L->sl.coef);
+      GIFT_HIP(gift::launch_lr_project(Ub, d, m, d, U, g.rank, ppart, s));
+      GIFT_HIP(gift::launch_lr_apply(Ub, d, m, d, U, g.rank, ppart, coef, 1, d_out, ldo, GIFT_SCALE_TENSOR, nullptr,
+                                     s));
+      break;
+    }
+    case GIFT_CHOL_INPUT:
+      GIFT_HIP(gift::launch_trmm(Ub, d, m, d, reinterpret_cast<const float*>(L->state + L->sl.t_a), 0, d_out, ldo, s));
+      break;
+    case GIFT_CHOL_TWOSIDED: {
+      float* tmp = reinterpret_cast<float*>(work + L->wl.tmp);
+      GIFT_HIP(gift::launch_trmm(Ub, d, m, d, reinterpret_cast<const float*>(L->state + L->sl.t_a), 0, tmp, d, s));
+      GIFT_HIP(gift::launch_trmm(tmp, d, m, d, reinterpret_cast<const float*>(L->state + L->sl.lg), 1, d_out, ldo, s));
+      break;
+    }
+    default:
+      return GIFT_ERR_INVALID_ARG;
+  }
+  return GIFT_OK;
+}
+
 // Encode with an optional error-feedback residual (d_resid: NULL or fp32
 // [m][d], read, and rewritten when codes are produced).
 static gift_status encode_impl(gift_layer_t L, const float* d_W, int64_t ldw, int32_t fmt, int32_t scaling,
                                const float* d_amax_in, float* d_amax_out, uint8_t* d_codes, float* d_scales,
-                               float* d_whitened, float* d_resid, void* d_work, size_t work_bytes,
-                               gift_stream_t stream) {
+                               uint8_t* d_bscales, float* d_tscale, float* d_whitened, float* d_resid, void* d_work,
+                               size_t work_bytes, gift_stream_t stream) {
   if (!L) return GIFT_ERR_INVALID_ARG;
   const gift_layer_desc& g = L->desc;
   const int m = g.d_out, d = g.d_in;
-  if (fmt != GIFT_E4M3 && fmt != GIFT_E5M2) return GIFT_ERR_INVALID_ARG;
-  if (scaling != GIFT_SCALE_TENSOR && scaling != GIFT_SCALE_BLOCK128) return GIFT_ERR_INVALID_ARG;
+  const bool fp4 = fmt == GIFT_E2M1;
+  if (fp4) {
+    if (scaling != GIFT_SCALE_BLOCK16 || d % 16 != 0) return GIFT_ERR_INVALID_ARG;
+    if (d_codes && (!aligned16(d_codes) || !d_bscales || !d_tscale)) return GIFT_ERR_INVALID_ARG;
+  } else {
+    if (fmt != GIFT_E4M3 && fmt != GIFT_E5M2) return GIFT_ERR_INVALID_ARG;
+    if (scaling != GIFT_SCALE_TENSOR && scaling != GIFT_SCALE_BLOCK128) return GIFT_ERR_INVALID_ARG;
+    if (d_codes && (!aligned16(d_codes) || !d_scales)) return GIFT_ERR_INVALID_ARG;
+  }
   if (!d_W || !aligned16(d_W) || ldw < d || ldw % 4 != 0) return GIFT_ERR_INVALID_ARG;
-  if (d_codes && (!aligned16(d_codes) || !d_scales)) return GIFT_ERR_INVALID_ARG;
   if (!d_codes && !d_amax_out) return GIFT_ERR_INVALID_ARG;
   if (d_whitened && !aligned16(d_whitened)) return GIFT_ERR_INVALID_ARG;
   if (d_resid && !aligned16(d_resid)) return GIFT_ERR_INVALID_ARG;
@@ -432,8 +475,10 @@ static gift_status encode_impl(gift_layer_t L, const float* d_W, int64_t ldw, in
   char* work = static_cast<char*>(d_work);
   uint32_t* slots = reinterpret_cast<uint32_t*>(work + L->wl.amax);
   uint32_t* flags = reinterpret_cast<uint32_t*>(L->state + L->sl.flags);
-  const int64_t nb = nblk(m, d, scaling);
-  if (fused_ok(g)) {
+  // FP4 takes the amax per tensor; its block amax is taken by the quantiser
+  const int amax_scaling = fp4 ? GIFT_SCALE_TENSOR : scaling;
+  const int64_t nb = nblk(m, d, amax_scaling);
+  if (fused_ok(g) && !fp4) {
     gift::FusedArgs a{};
     a.mode = 0;
     a.m = m;
@@ -478,26 +523,26 @@ static gift_status encode_impl(gift_layer_t L, const float* d_W, int64_t ldw, in
   uint32_t* wslots = d_resid ? nullptr : slots;
   switch (g.transform) {
     case GIFT_EUCLID:
-      GIFT_HIP(gift::launch_amax(d_W, ldw, m, d, scaling, d_resid, slots, s));
+      GIFT_HIP(gift::launch_amax(d_W, ldw, m, d, amax_scaling, d_resid, slots, s));
       if (d_whitened) GIFT_HIP(hipMemcpy2DAsync(d_whitened, (size_t)d * 4, d_W, (size_t)ldw * 4, (size_t)d * 4, m,
                                                 hipMemcpyDeviceToDevice, s));
       break;
     case GIFT_DIAG:
       GIFT_HIP(gift::launch_diag_apply(d_W, ldw, m, d, reinterpret_cast<const float*>(L->state + L->sl.coef), out, d,
-                                       scaling, wslots, s));
+                                       amax_scaling, wslots, s));
       X = out;
       ldx = d;
-      if (d_resid) GIFT_HIP(gift::launch_amax(X, ldx, m, d, scaling, d_resid, slots, s));
+      if (d_resid) GIFT_HIP(gift::launch_amax(X, ldx, m, d, amax_scaling, d_resid, slots, s));
       break;
     case GIFT_LOWRANK: {
       double* ppart = reinterpret_cast<double*>(work + L->wl.ppart);
       const float* U = reinterpret_cast<const float*>(L->state + L->sl.U);
       const float* coef = reinterpret_cast<const float*>(L->state + L->sl.coef);
       GIFT_HIP(gift::launch_lr_project(d_W, ldw, m, d, U, g.rank, ppart, s));
-      GIFT_HIP(gift::launch_lr_apply(d_W, ldw, m, d, U, g.rank, ppart, coef, 0, out, d, scaling, wslots, s));
+      GIFT_HIP(gift::launch_lr_apply(d_W, ldw, m, d, U, g.rank, ppart, coef, 0, out, d, amax_scaling, wslots, s));
       X = out;
       ldx = d;
-      if (d_resid) GIFT_HIP(gift::launch_amax(X, ldx, m, d, scaling, d_resid, slots, s));
+      if (d_resid) GIFT_HIP(gift::launch_amax(X, ldx, m, d, amax_scaling, d_resid, slots, s));
       break;
     }
     case GIFT_CHOL_INPUT:
@@ -513,7 +558,7 @@ static gift_status encode_impl(gift_layer_t L, const float* d_W, int64_t ldw, in
       }
       GIFT_HIP(gift::launch_trmm(src, lds, m, d, reinterpret_cast<const float*>(L->state + L->sl.tinv_a), 0, out, d,
                                  s));
-      GIFT_HIP(gift::launch_amax(out, d, m, d, scaling, d_resid, slots, s));
+      GIFT_HIP(gift::launch_amax(out, d, m, d, amax_scaling, d_resid, slots, s));
       X = out;
       ldx = d;
       break;
@@ -521,7 +566,10 @@ static gift_status encode_impl(gift_layer_t L, const float* d_W, int64_t ldw, in
     default:
       return GIFT_ERR_INVALID_ARG;
   }
-  if (d_codes) {
+  if (d_codes && fp4) {
+    GIFT_HIP(gift::launch_quantize_fp4(X, ldx, m, d, slots, d_amax_in, d_amax_out, d_codes, d_bscales, d_tscale,
+                                       d_resid, flags, s));
+  } else if (d_codes) {
     GIFT_HIP(gift::launch_quantize(X, ldx, m, d, fmt, scaling, slots, d_amax_in, d_amax_out, d_codes, d_scales,
                                    d_resid, flags, s));
   } else {
@@ -533,17 +581,26 @@ static gift_status encode_impl(gift_layer_t L, const float* d_W, int64_t ldw, in
 gift_status gift_encode(gift_layer_t L, const float* d_W, int64_t ldw, int32_t fmt, int32_t scaling,
                         const float* d_amax_in, float* d_amax_out, uint8_t* d_codes, float* d_scales,
                         float* d_whitened, void* d_work, size_t work_bytes, gift_stream_t stream) {
-  return encode_impl(L, d_W, ldw, fmt, scaling, d_amax_in, d_amax_out, d_codes, d_scales, d_whitened, nullptr,
-                     d_work, work_bytes, stream);
+  if (fmt == GIFT_E2M1) return GIFT_ERR_INVALID_ARG;   // gift_encode_fp4
+  return encode_impl(L, d_W, ldw, fmt, scaling, d_amax_in, d_amax_out, d_codes, d_scales, nullptr, nullptr,
+                     d_whitened, nullptr, d_work, work_bytes, stream);
 }
 
 gift_status gift_encode_ef(gift_layer_t L, const float* d_W, int64_t ldw, int32_t fmt, int32_t scaling,
                            const float* d_amax_in, float* d_amax_out, uint8_t* d_codes, float* d_scales,
                            float* d_whitened, float* d_resid, void* d_work, size_t work_bytes,
                            gift_stream_t stream) {
-  if (!d_resid) return GIFT_ERR_INVALID_ARG;
-  return encode_impl(L, d_W, ldw, fmt, scaling, d_amax_in, d_amax_out, d_codes, d_scales, d_whitened, d_resid,
-                     d_work, work_bytes, stream);
+  if (!d_resid || fmt == GIFT_E2M1) return GIFT_ERR_INVALID_ARG;
+  return encode_impl(L, d_W, ldw, fmt, scaling, d_amax_in, d_amax_out, d_codes, d_scales, nullptr, nullptr,
+                     d_whitened, d_resid, d_work, work_bytes, stream);
+}
+
+gift_status gift_encode_fp4(gift_layer_t L, const float* d_W, int64_t ldw, const float* d_amax_in,
+                            float* d_amax_out, uint8_t* d_codes, uint8_t* d_bscales, float* d_tscale,
+                            float* d_whitened, float* d_resid, void* d_work, size_t work_bytes,
+                            gift_stream_t stream) {
+  return encode_impl(L, d_W, ldw, GIFT_E2M1, GIFT_SCALE_BLOCK16, d_amax_in, d_amax_out, d_codes, nullptr, d_bscales,
+                     d_tscale, d_whitened, d_resid, d_work, work_bytes, stream);
 }
 
 gift_status gift_decode_reduce(gift_layer_t L, const uint8_t* d_codes, int64_t code_stride, const float* d_scales,
@@ -605,32 +662,34 @@ gift_status gift_decode_reduce(gift_layer_t L, const uint8_t* d_codes, int64_t c
   }
   float* Ub = reinterpret_cast<float*>(work + L->wl.tile);
   GIFT_HIP(gift::launch_dequant_sum(d_codes, code_stride, d_scales, scale_stride, R, m, d, fmt, scaling, Ub, d, s));
-  switch (g.transform) {
-    case GIFT_DIAG:
-      GIFT_HIP(gift::launch_diag_apply(Ub, d, m, d, reinterpret_cast<const float*>(L->state + L->sl.coef) + d, d_out,
-                                       ldo, scaling, nullptr, s));
-      break;
-    case GIFT_LOWRANK: {
-      double* ppart = reinterpret_cast<double*>(work + L->wl.ppart);
-      const float* U = reinterpret_cast<const float*>(L->state + L->sl.U);
-      const float* coef = reinterpret_cast<const float*>(L->state + L->sl.coef);
-      GIFT_HIP(gift::launch_lr_project(Ub, d, m, d, U, g.rank, ppart, s));
-      GIFT_HIP(gift::launch_lr_apply(Ub, d, m, d, U, g.rank, ppart, coef, 1, d_out, ldo, scaling, nullptr, s));
-      break;
-    }
-    case GIFT_CHOL_INPUT:
-      GIFT_HIP(gift::launch_trmm(Ub, d, m, d, reinterpret_cast<const float*>(L->state + L->sl.t_a), 0, d_out, ldo, s));
-      break;
-    case GIFT_CHOL_TWOSIDED: {
-      float* tmp = reinterpret_cast<float*>(work + L->wl.tmp);
-      GIFT_HIP(gift::launch_trmm(Ub, d, m, d, reinterpret_cast<const float*>(L->state + L->sl.t_a), 0, tmp, d, s));
-      GIFT_HIP(gift::launch_trmm(tmp, d, m, d, reinterpret_cast<const float*>(L->state + L->sl.lg), 1, d_out, ldo, s));
-      break;
-    }
-    default:
-      return GIFT_ERR_INVALID_ARG;
+  return unwhiten_multi(L, Ub, d_out, ldo, work, s);
+}
+
+gift_status gift_decode_reduce_fp4(gift_layer_t L, const uint8_t* d_codes, int64_t code_stride,
+                                   const uint8_t* d_bscales, int64_t bscale_stride, const float* d_tscales, int32_t R,
+                                   float* d_out, int64_t ldo, void* d_work, size_t work_bytes, gift_stream_t stream) {
+  if (!L) return GIFT_ERR_INVALID_ARG;
+  const gift_layer_desc& g = L->desc;
+  const int m = g.d_out, d = g.d_in;
+  if (d % 16 != 0) return GIFT_ERR_INVALID_ARG;
+  if (R < 1 || !d_codes || !d_bscales || !d_tscales || !d_out) return GIFT_ERR_INVALID_ARG;
+  if (!aligned16(d_codes) || !aligned16(d_out) || ldo < d || ldo % 4 != 0) return GIFT_ERR_INVALID_ARG;
+  if (R > 1 && (code_stride < (int64_t)m * d / 2 || code_stride % 16 != 0)) return GIFT_ERR_INVALID_ARG;
+  if (R > 1 && bscale_stride < (int64_t)m * d / 16) return GIFT_ERR_INVALID_ARG;
+  if (!d_work || (reinterpret_cast<uintptr_t>(d_work) & 255u)) return GIFT_ERR_INVALID_ARG;
+  if (work_bytes < L->wl.total) return GIFT_ERR_WORKSPACE;
+  if (!L->ready) return GIFT_ERR_NOT_READY;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* work = static_cast<char*>(d_work);
+  if (g.transform == GIFT_EUCLID) {
+    GIFT_HIP(gift::launch_dequant_sum_fp4(d_codes, code_stride, d_bscales, bscale_stride, d_tscales, R, m, d, d_out,
+                                          ldo, s));
+    return GIFT_OK;
   }
-  return GIFT_OK;
+  float* Ub = reinterpret_cast<float*>(work + L->wl.tile);
+  GIFT_HIP(gift::launch_dequant_sum_fp4(d_codes, code_stride, d_bscales, bscale_stride, d_tscales, R, m, d, Ub, d,
+                                        s));
+  return unwhiten_multi(L, Ub, d_out, ldo, work, s);
 }
 
 // ---------------------------------------------------------------------------

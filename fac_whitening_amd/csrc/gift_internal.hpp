@@ -118,6 +118,17 @@ hipError_t launch_amax(const float* x, int64_t ld, int m, int d, int scaling, co
 hipError_t launch_quantize(const float* x, int64_t ld, int m, int d, int fmt, int scaling,
                            const uint32_t* slots, const float* amax_in, float* amax_out,
                            uint8_t* codes, float* scales, float* resid, uint32_t* flags, hipStream_t s);
+// FP4 (E2M1, 16-element row blocks with E4M3 scales, fp32 tensor scale):
+// quantise u = x (+ resid) with the tensor amax in slot[0] (or amax_in) ->
+// codes [m][d/2], bscales [m][d/16], tscale[0], amax_out[0]; with resid
+// also resid <- u - S_b dec(code).  d a multiple of 16.
+hipError_t launch_quantize_fp4(const float* x, int64_t ld, int m, int d, const uint32_t* slot, const float* amax_in,
+                               float* amax_out, uint8_t* codes, uint8_t* bscales, float* tscale, float* resid,
+                               uint32_t* flags, hipStream_t s);
+// U = (1/R) sum_r S_{b,r} dec(q_r) of R FP4 payloads -> fp32 [m][ldo]
+hipError_t launch_dequant_sum_fp4(const uint8_t* codes, int64_t code_stride, const uint8_t* bscales,
+                                  int64_t bscale_stride, const float* tscales, int R, int m, int d, float* out,
+                                  int64_t ldo, hipStream_t s);
 // U = (1/R) sum_r s_r dec(q_r) -> fp32 [m][ldo]
 hipError_t launch_dequant_sum(const uint8_t* codes, int64_t code_stride, const float* scales,
                               int64_t scale_stride, int R, int m, int d, int fmt, int scaling,

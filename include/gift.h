@@ -63,8 +63,10 @@ enum gift_transform {
   GIFT_CHOL_TWOSIDED = 4    /* W~ = L_G^-1 W L_A^-T ([Note] Eq. (11)); map back Eq. (14) */
 };
 
-enum gift_format { GIFT_E4M3 = 0, GIFT_E5M2 = 1 };          /* [Note] §前置知识, FP8 */
-enum gift_scaling { GIFT_SCALE_TENSOR = 0, GIFT_SCALE_BLOCK128 = 1 };
+/* FP8 ([Note] §前置知识); E2M1 = FP4 ([Abs] NVFP4), only through the _fp4 calls */
+enum gift_format { GIFT_E4M3 = 0, GIFT_E5M2 = 1, GIFT_E2M1 = 2 };
+/* BLOCK16: the FP4 payload's 16-element row blocks (gift_payload_bytes only) */
+enum gift_scaling { GIFT_SCALE_TENSOR = 0, GIFT_SCALE_BLOCK128 = 1, GIFT_SCALE_BLOCK16 = 2 };
 enum gift_dtype { GIFT_BF16 = 0, GIFT_FP32 = 1 };
 enum gift_side { GIFT_SIDE_A = 0, GIFT_SIDE_G = 1 };      /* input / output statistics */
 enum { GIFT_FLAG_NONFINITE = 1u, GIFT_FLAG_SPIN_TIMEOUT = 2u };
@@ -218,8 +220,49 @@ gift_status gift_decode_reduce(gift_layer_t layer, const uint8_t* d_codes, int64
                                int32_t fmt, int32_t scaling, float* d_out, int64_t ldo,
                                void* d_work, size_t work_bytes, gift_stream_t stream);
 
-/* Payload size of one replica: d_out * d_in code bytes + 4 * nblk scale bytes. */
+/* Payload size of one replica: d_out * d_in code bytes + 4 * nblk scale
+ * bytes (FP8); d_out * d_in / 2 + d_out * d_in / 16 + 4 (GIFT_SCALE_BLOCK16,
+ * the FP4 payload). */
 size_t gift_payload_bytes(int32_t d_out, int32_t d_in, int32_t scaling);
+
+/* ---------------------------------------------------------------------------
+ * FP4 payload ([Abs]: NVFP4 named as a low-precision communication format;
+ * [Note] summary: the coordinate change carries over to FP4.  The pages
+ * leave the layout open; this library's reading):
+ *   elements E2M1 (OCP 4-bit float: values +-{0, 0.5, 1, 1.5, 2, 3, 4, 6},
+ *   round to nearest, ties to the even code, saturating, NaN -> +0),
+ *   blocks of 16 consecutive elements of a row, each with an E4M3 scale,
+ *   one fp32 scale per tensor:
+ *     g     = fp32(amax_T / (6 * 448)),  sig_b = fp32(amax_b / (6 g)),
+ *     sc_b  = E4M3(sig_b),  S_b = fp32(dec(sc_b) * g),
+ *     code  = E2M1(fp32(x * fp32(1 / S_b)))  (x * 0 when S_b = 0),
+ *   value S_b * dec(code).  A non-finite amax_T sets g = NaN, every block
+ *   scale 0x7F (NaN), codes 0 and GIFT_FLAG_NONFINITE.
+ * Requires d_in % 16 == 0.  Both calls take the multi-kernel route.
+ *
+ * gift_encode_fp4: W~ as gift_encode (with d_resid: U~ = W~ + R and
+ * R <- fp32(U~ - S_b dec(code)), as gift_encode_ef).
+ * d_amax_in:    NULL or fp32 [1]: shared amax_T (the AllReduceMax)
+ * d_amax_out:   NULL or fp32 [1]: local amax_T (of U~ with d_resid)
+ * d_codes:      uint8 [d_out][d_in / 2], column 2j in the low nibble;
+ *               NULL = only compute d_amax_out (d_resid unchanged)
+ * d_bscales:    uint8 [d_out][d_in / 16] E4M3 block scale codes
+ * d_tscale:     fp32 [1]: g
+ * d_whitened, d_resid, d_work: as gift_encode / gift_encode_ef (d_resid may
+ *               be NULL).
+ * gift_decode_reduce_fp4: U = (1/R) sum_r S_{b,r} dec(q_r) (fp32, r in
+ * increasing order), then W^ as gift_decode_reduce.  Replica r at
+ * d_codes + r * code_stride (bytes), d_bscales + r * bscale_stride (bytes),
+ * d_tscales[r].
+ * ------------------------------------------------------------------------- */
+gift_status gift_encode_fp4(gift_layer_t layer, const float* d_W, int64_t ldw, const float* d_amax_in,
+                            float* d_amax_out, uint8_t* d_codes, uint8_t* d_bscales, float* d_tscale,
+                            float* d_whitened, float* d_resid, void* d_work, size_t work_bytes,
+                            gift_stream_t stream);
+gift_status gift_decode_reduce_fp4(gift_layer_t layer, const uint8_t* d_codes, int64_t code_stride,
+                                   const uint8_t* d_bscales, int64_t bscale_stride,
+                                   const float* d_tscales, int32_t R, float* d_out, int64_t ldo,
+                                   void* d_work, size_t work_bytes, gift_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * FP8 boundary-hit profiler ([Note] §简化三, Fig. 3): over the first steps of

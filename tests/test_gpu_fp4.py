@@ -1,0 +1,178 @@
+"""The FP4 payload (E2M1 elements, 16-element row blocks with E4M3 scales,
+one fp32 tensor scale) through gift_encode_fp4 / gift_decode_reduce_fp4,
+against the oracle.
+
+Pages: the GIFT abstract names NVFP4 as a communication format and the
+GIFT 阅读笔记 summary calls the coordinate change forward compatible with
+FP4; the layout is the oracle's reading R12.  Algorithm 1 gives the steps
+(whiten, scale, quantise, reduce, map back; error feedback on request).
+
+Stage isolation: the oracle quantises the GPU's own whitened tensor (plus
+the GPU's previous residual), so codes, block scales, tensor scale, amax and
+residual must agree bit for bit; the decoded mean is compared with the
+oracle's reduction of the GPU's payloads mapped back with the oracle's
+transform.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import fp4
+from oracle import gift as G
+from tests.helpers import layer_with_factor, rel_fro
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def fw():
+    import fac_whitening_amd as fw
+    yield fw
+    fw.set_fused(True)
+
+
+def _layer(fw, kind, m, d, seed):
+    rng = np.random.default_rng(seed + 1)
+    L = fw.Layer(m, d, kind, device=DEV)
+    if kind == "euclid":
+        return L
+    a = (rng.standard_normal((512, d)) * np.arange(1, d + 1) ** -0.75).astype(np.float32)
+    L.accumulate_stats(torch.from_numpy(a).to(DEV), fw.SIDE_A, commit=True)
+    if kind == "twosided":
+        dl = (rng.standard_normal((512, m)) * np.arange(1, m + 1) ** -0.5).astype(np.float32)
+        L.accumulate_stats(torch.from_numpy(dl).to(DEV), fw.SIDE_G, commit=True)
+    om = torch.from_numpy(rng.standard_normal((d, 48)).astype(np.float32)).to(DEV) if kind == "lowrank" else None
+    L.refresh(om)
+    return L
+
+
+def _grad(m, d, rng, heavy=False):
+    base = rng.standard_t(3, (m, d)) if heavy else rng.standard_normal((m, d))
+    return (base * np.arange(1, d + 1) ** -0.5 * np.arange(1, m + 1)[:, None] ** -0.25).astype(np.float32)
+
+
+def _same(a, b):
+    a, b = np.asarray(a), np.asarray(b)
+    return a.shape == b.shape and bool(np.all((a == b) | (np.isnan(a) & np.isnan(b))))
+
+
+CASES = [
+    ("euclid", (100, 1008)),
+    ("euclid", (1536, 6144)),
+    ("lowrank", (200, 1536)),
+    ("lowrank", (1536, 6144)),
+    ("diag", (96, 272)),
+    ("chol", (96, 272)),
+    ("twosided", (96, 272)),
+]
+
+
+@pytest.mark.parametrize("ef", [False, True])
+@pytest.mark.parametrize("kind,shape", CASES)
+def test_fp4_encode_stage_isolated(fw, kind, shape, ef):
+    """Three steps (the second with a zero gradient when error feedback
+    carries a residual, the third with a shared amax 1.5x the local one):
+    every output bit for bit against the oracle on the GPU's W~ (+ R)."""
+    m, d = shape
+    print(f"[fp4 encode {kind} {shape} ef={ef}]", flush=True)
+    rng = np.random.default_rng(m + d)
+    L = _layer(fw, kind, m, d, seed=m * 3 + d)
+    resid = torch.zeros(m, d, device=DEV) if ef else None
+    for t in range(3):
+        w = np.zeros((m, d), np.float32) if (t == 1 and ef) else _grad(m, d, rng, heavy=t == 2)
+        Wg = torch.from_numpy(w).to(DEV)
+        R_prev = resid.cpu().numpy() if ef else np.zeros((m, d), np.float32)
+        am1 = torch.empty(1, device=DEV)
+        L.encode_fp4(Wg, amax_out=am1, want_codes=False, resid=resid)
+        amax_in = am1 * 1.5 if t == 2 else None
+        wh = torch.empty(m, d, device=DEV)
+        am2 = torch.empty(1, device=DEV)
+        codes, bsc, tsc = L.encode_fp4(Wg, amax_in=amax_in, whitened=wh, amax_out=am2, resid=resid)
+        torch.cuda.synchronize()
+        assert L.flags() == 0
+        wh_np = wh.cpu().numpy()
+        ref = G.error_feedback_fp4(wh_np, R_prev, amax_in=None if amax_in is None else amax_in.cpu().numpy())
+        assert np.array_equal(codes.cpu().numpy(), fp4.pack(ref["codes"])), f"codes differ at step {t}"
+        assert np.array_equal(bsc.cpu().numpy(), ref["bscales"]), f"block scales differ at step {t}"
+        assert tsc.item() == ref["tscale"] or (np.isnan(tsc.item()) and np.isnan(ref["tscale"]))
+        am_ref = np.float32(np.abs(ref["u_tilde"]).max())
+        assert am1.item() == am_ref and am2.item() == am_ref
+        if ef:
+            assert _same(resid.cpu().numpy(), ref["residual"]), f"residual differs at step {t}"
+    L.close()
+
+
+@pytest.mark.parametrize("R", [1, 4, 16])
+@pytest.mark.parametrize("kind", ["euclid", "lowrank"])
+def test_fp4_decode_reduce(fw, kind, R):
+    """The mean of R FP4 payloads mapped back: Euclidean within the fp32
+    rounding of the sum; rank-32 with the oracle's factor in the layer state
+    and the oracle's inverse transform."""
+    m, d = 200, 1536
+    print(f"[fp4 decode {kind} R={R}]", flush=True)
+    rng = np.random.default_rng(17 + R)
+    if kind == "lowrank":
+        T = 1024
+        sd = np.arange(1, d + 1) ** -0.75
+        a0 = (rng.standard_normal((T, d)) * sd).astype(np.float32)
+        A = G.second_moment(a0)
+        fac = G.lowrank_factor(A, rng.standard_normal((d, 48)).astype(np.float32), 32, 4, G.damping(A))
+        L = layer_with_factor(fw, m, d, fac, DEV)
+        _, Tinv = G.transform_lowrank(fac)
+    else:
+        L = fw.Layer(m, d, "euclid", device=DEV)
+        Tinv = None
+    codes = torch.empty(R, m, d // 2, dtype=torch.uint8, device=DEV)
+    bsc = torch.empty(R, m, d // 16, dtype=torch.uint8, device=DEV)
+    tsc = torch.empty(R, device=DEV)
+    for r in range(R):
+        L.encode_fp4(torch.from_numpy(_grad(m, d, rng, heavy=r % 2 == 1)).to(DEV), codes=codes[r], bscales=bsc[r],
+                     tscale=tsc[r:r + 1])
+    out = L.decode_reduce_fp4(codes, bsc, tsc)
+    torch.cuda.synchronize()
+    assert L.flags() == 0
+    cl = [fp4.unpack(codes[r].cpu().numpy()) for r in range(R)]
+    U = G.dequant_reduce_fp4(cl, [bsc[r].cpu().numpy() for r in range(R)], tsc.cpu().numpy())
+    ref = U if Tinv is None else G.unwhiten(U, Tinv)
+    err = rel_fro(out.cpu().numpy(), ref)
+    print(f"  decoded rel err {err:.3e}", flush=True)
+    assert err <= (1e-6 if Tinv is None else 1e-5), err
+    L.close()
+
+
+def test_fp4_nonfinite(fw):
+    """An Inf in the gradient: NaN tensor scale, every block scale 0x7F,
+    codes 0, the flag set; the decoded tensor is NaN."""
+    m, d = 64, 256
+    L = fw.Layer(m, d, "euclid", device=DEV)
+    w = _grad(m, d, np.random.default_rng(3))
+    w[5, 9] = np.inf
+    codes, bsc, tsc = L.encode_fp4(torch.from_numpy(w).to(DEV))
+    out = L.decode_reduce_fp4(codes, bsc, tsc)
+    torch.cuda.synchronize()
+    assert L.flags() & fw.FLAG_NONFINITE
+    assert np.isnan(tsc.item()) and bool((bsc == 0x7F).all()) and not bool(codes.any())
+    assert bool(torch.isnan(out).all())
+    L.close()
+
+
+def test_fp4_argument_checks(fw):
+    """d_in not a multiple of 16 and E2M1 through the FP8 call are refused
+    before anything is enqueued."""
+    L = fw.Layer(64, 264, "euclid", device=DEV)
+    W = torch.zeros(64, 264, device=DEV)
+    with pytest.raises(fw.GiftError):
+        L.encode_fp4(W)
+    L.close()
+    L = fw.Layer(64, 256, "euclid", device=DEV)
+    W = torch.zeros(64, 256, device=DEV)
+    c = torch.empty(64, 256, dtype=torch.uint8, device=DEV)
+    sc = torch.empty(1, device=DEV)
+    st = fw._lib.gift_encode(L.handle, W.data_ptr(), 256, fw.E2M1, fw.SCALE_BLOCK16, None, None, c.data_ptr(),
+                             sc.data_ptr(), None, L.work.data_ptr(), ctypes.c_size_t(L.work_bytes), None)
+    assert st == 1
+    assert fw.payload_bytes(4096, 16384, fw.SCALE_BLOCK16) == G.payload_bytes(4096, 16384, "block16")
+    L.close()
