@@ -304,7 +304,9 @@ def bench_stress(args, torch, fw, synth, dev):
     """One step of the stress layer (W 4096 x 16384, heavy-tailed): statistics
     of T = 8192 bf16 tokens and commit, rank-32 refresh (every step), encode
     of replica 0 and decode-reduce of R = 16 payloads, E5M2 per 128 x 128
-    block (replicas 1..15 encoded in setup).  Each stage event-timed."""
+    block (replicas 1..15 encoded in setup).  Each stage event-timed; the
+    encode + decode also with the FP4 payload (E2M1 with 16-element E4M3
+    block scales) as a stage of its own."""
     m, d, Ttok, R = 4096, 16384, 8192, 16
     f, s = fw.E5M2, fw.SCALE_BLOCK128
     nb = fw.nblocks(m, d, s)
@@ -334,6 +336,24 @@ def bench_stress(args, torch, fw, synth, dev):
     assert L.flags() == 0
     n = m * d
     alg = (4.0 + 1) * n + R * n + 4.0 * n + 4 * nb * (R + 1) + d * 32 * 4 * 2
+    # the FP4 payload (E2M1, 16-element row blocks with E4M3 scales): the
+    # same unit with R = 16 FP4 payloads
+    del codes
+    c4 = torch.empty(R, m, d // 2, dtype=torch.uint8, device=dev)
+    b4 = torch.empty(R, m, d // 16, dtype=torch.uint8, device=dev)
+    t4 = torch.empty(R, dtype=torch.float32, device=dev)
+    for r in range(1, R):
+        Wr = synth.stress_gradient(m, d, 0, r, dev)
+        L.encode_fp4(Wr, codes=c4[r], bscales=b4[r], tscale=t4[r:r + 1])
+        del Wr
+
+    def unit_fp4():
+        L.encode_fp4(W0, codes=c4[0], bscales=b4[0], tscale=t4[0:1])
+        L.decode_reduce_fp4(c4, b4, t4, out=out)
+    t_fp4 = _event_ms(torch, unit_fp4, reps)
+    assert L.flags() == 0
+    pay4 = n / 2 + n / 16
+    alg4 = 4.0 * n + pay4 + R * pay4 + 4.0 * n + 4 * (R + 1) + d * 32 * 4 * 2
     stats_flop = float(Ttok) * d * (d + 1)
     refresh_flop = 12.0 * d * d * 48
     result = {
@@ -344,7 +364,7 @@ def bench_stress(args, torch, fw, synth, dev):
         "config": {"workload": "stress 4096x16384, rank-32 refreshed every step (q=4, p=16), E5M2 per "
                                "128x128 block, R=16", "tokens": Ttok},
         "stages_ms": {"stats_commit": round(t_stats, 4), "refresh": round(t_refresh, 4),
-                      "encode_decode": round(t_unit, 4)},
+                      "encode_decode": round(t_unit, 4), "encode_decode_fp4": round(t_fp4, 4)},
         "roofline": {"bound": "hbm", "achieved": round(alg / (t_unit * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(alg / (t_unit * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "alg_bytes": int(alg)},
@@ -352,7 +372,11 @@ def bench_stress(args, torch, fw, synth, dev):
             "stats": {"achieved": round(stats_flop / t_stats / 1e9, 1), "peak": BF16_PEAK_TFS, "unit": "TFLOP/s",
                       "frac": round(stats_flop / t_stats / 1e9 / BF16_PEAK_TFS, 4)},
             "refresh": {"achieved": round(refresh_flop / t_refresh / 1e9, 2), "peak": FP64_PEAK_TFS,
-                        "unit": "TFLOP/s", "frac": round(refresh_flop / t_refresh / 1e9 / FP64_PEAK_TFS, 4)}},
+                        "unit": "TFLOP/s", "frac": round(refresh_flop / t_refresh / 1e9 / FP64_PEAK_TFS, 4)},
+            "encode_decode_fp4": {"achieved": round(alg4 / (t_fp4 * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": round(alg4 / (t_fp4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                  "alg_bytes": int(alg4),
+                                  "work": "encode of replica 0 and decode-reduce of 16 FP4 payloads"}},
     }
     print(json.dumps(result), flush=True)
 

@@ -137,3 +137,38 @@ def test_stress_encode_decode_block_rows(fw, stress, fmt):
         err = rel_fro(got, ref)
         print(f"  decoded block row {b}: rel err {err:.3e}", flush=True)
         assert err <= 1e-5
+
+
+def test_stress_fp4_rows(fw, stress):
+    """The FP4 payload (E2M1, 16-element row blocks with E4M3 scales, fp32
+    tensor scale) of the 16 stress replicas: the tensor amax against the
+    whole GPU whitened tensor; codes, block scales and tensor scale of whole
+    rows bit for bit against the oracle on the GPU's whitened rows with the
+    GPU's tensor amax; the decoded mean of those rows mapped back with the
+    oracle's transform."""
+    from oracle import fp4
+    L, Ws, Tinv = stress["L"], stress["Ws"], stress["Tinv"]
+    print(f"[stress fp4, R={R}]", flush=True)
+    codes = torch.empty(R, M, D // 2, dtype=torch.uint8, device=DEV)
+    bsc = torch.empty(R, M, D // 16, dtype=torch.uint8, device=DEV)
+    tsc = torch.empty(R, device=DEV)
+    whit = torch.empty(M, D, device=DEV)
+    am = torch.empty(1, device=DEV)
+    for r in range(R):
+        L.encode_fp4(Ws[r], codes=codes[r], bscales=bsc[r], tscale=tsc[r:r + 1],
+                     whitened=whit if r == 0 else None, amax_out=am if r == 0 else None)
+    out = L.decode_reduce_fp4(codes, bsc, tsc)
+    torch.cuda.synchronize()
+    assert L.flags() == 0
+    assert am.item() == whit.abs().max().item()
+    rows = torch.from_numpy(_rows()).to(DEV)
+    g_whit = whit[rows].cpu().numpy()
+    ref = G.quantize_fp4(g_whit, amax_in=am.cpu().numpy())
+    assert np.array_equal(codes[0][rows].cpu().numpy(), fp4.pack(ref["codes"]))
+    assert np.array_equal(bsc[0][rows].cpu().numpy(), ref["bscales"])
+    assert tsc[0].item() == ref["tscale"]
+    cl = [fp4.unpack(codes[r][rows].cpu().numpy()) for r in range(R)]
+    U = G.dequant_reduce_fp4(cl, [bsc[r][rows].cpu().numpy() for r in range(R)], tsc.cpu().numpy())
+    err = rel_fro(out[rows].cpu().numpy(), G.unwhiten(U, Tinv))
+    print(f"  decoded rows rel err {err:.3e}", flush=True)
+    assert err <= 1e-5
