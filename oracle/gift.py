@@ -53,6 +53,13 @@ R11 Error feedback (Note 算法 1, lines 11-15): the residual is added to the
     U~ - s dec(q) (one rounding of the exact difference).  The whitened
     tensor itself (W~) is what the inspection output shows; the amax and
     the codes are those of U~.
+R13 Per-block Euclidean baseline (Note, experiment setup: block size 512,
+    nothing more): blocks of 512 consecutive elements of each tensor's
+    row-major order, restarting at every tensor; a tensor's last block may
+    be shorter; each block scaled and quantised as R4 with its own amax.
+    A model's Euclidean gradients form one flat bucket: the tensors one
+    after another, their codes in the same order, their scales tensor by
+    tensor.
 R12 FP4 payload (the pages name NVFP4 without defining it): E2M1 elements
     (``oracle.fp4``) in blocks of 16 consecutive elements of a row, each
     block with an E4M3 scale, under one fp32 scale per tensor:
@@ -313,6 +320,80 @@ def dequant_reduce(codes_list, scales_list, fmt: str, scaling: str) -> np.ndarra
         v = dequantize(c, s, fmt, scaling)
         acc = v if acc is None else acc + v
     return acc / R
+
+
+# ---------------------------------------------------------------------------
+# Flat buckets of Euclidean tensors (Algorithm 1, lines 3-8; R13)
+# ---------------------------------------------------------------------------
+
+FLAT_BLOCK = 512
+
+
+def quantize_flat(x, fmt: str, block=None, amax_in=None):
+    """Euclidean FP8 of one tensor in its row-major order: one scale for the
+    tensor (block None) or one per ``block`` consecutive elements (the last
+    block may be shorter).  Each block is quantised as a 1 x n tensor with
+    R4.  Returns (codes uint8 [n], scales float32 [nb], amax float64 [nb])."""
+    v = np.asarray(x, dtype=np.float32).ravel()
+    n = v.size
+    bl = n if block is None else block
+    nb = 1 if block is None else -(-n // block)
+    codes = np.empty(n, dtype=np.uint8)
+    scales = np.empty(nb, dtype=np.float32)
+    am = np.empty(nb)
+    for b in range(nb):
+        seg = v[b * bl:(b + 1) * bl].reshape(1, -1)
+        a_in = None if amax_in is None else np.array([[np.asarray(amax_in, dtype=np.float64).ravel()[b]]])
+        c, sc, a = quantize(seg, fmt, "tensor", a_in)
+        codes[b * bl:(b + 1) * bl] = c.ravel()
+        scales[b] = sc[0, 0]
+        am[b] = a[0, 0]
+    return codes, scales, am
+
+
+def dequantize_flat(codes, scales, fmt: str, block=None) -> np.ndarray:
+    """s_b dec(q) per element, float64 [n]."""
+    c = np.asarray(codes, dtype=np.uint8).ravel()
+    n = c.size
+    bl = n if block is None else block
+    idx = np.arange(n) // max(bl, 1)
+    return _fp8.decode(c, fmt) * _f64(scales).ravel()[idx]
+
+
+def bucket_quantize(tensors, fmt: str, block=None, amax_in=None):
+    """A flat bucket: each tensor quantised by ``quantize_flat``; codes and
+    scales concatenated in tensor order (amax_in: the concatenated shared
+    amax of every scale block, or None)."""
+    cs, ss, ams = [], [], []
+    off = 0
+    for t in tensors:
+        n = np.asarray(t).size
+        nb = 1 if block is None else -(-n // block)
+        a_in = None if amax_in is None else np.asarray(amax_in).ravel()[off:off + nb]
+        c, sc, a = quantize_flat(t, fmt, block, a_in)
+        cs.append(c)
+        ss.append(sc)
+        ams.append(a)
+        off += nb
+    return np.concatenate(cs), np.concatenate(ss), np.concatenate(ams)
+
+
+def bucket_dequant_reduce(codes_list, scales_list, sizes, fmt: str, block=None) -> np.ndarray:
+    """(1/R) sum_r s_r dec(q_r) over a bucket of tensors with the given
+    element counts (R5), float64 [sum sizes]."""
+    R = len(codes_list)
+    out = []
+    co = so = 0
+    for n in sizes:
+        nb = 1 if block is None else -(-n // block)
+        acc = None
+        for c, sc in zip(codes_list, scales_list):
+            v = dequantize_flat(np.asarray(c).ravel()[co:co + n], np.asarray(sc).ravel()[so:so + nb], fmt, block)
+            acc = v if acc is None else acc + v
+        out.append(acc / R)
+        co += n
+        so += nb
+    return np.concatenate(out) if out else np.zeros(0)
 
 
 # ---------------------------------------------------------------------------
