@@ -27,7 +27,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 # enums (include/gift.h)
 EUCLID, DIAG, LOWRANK, CHOL_INPUT, CHOL_TWOSIDED = range(5)
 E4M3, E5M2, E2M1 = 0, 1, 2
-SCALE_TENSOR, SCALE_BLOCK128, SCALE_BLOCK16 = 0, 1, 2
+SCALE_TENSOR, SCALE_BLOCK128, SCALE_BLOCK16, SCALE_BLOCK512 = 0, 1, 2, 3
 BF16, FP32 = 0, 1
 SIDE_A, SIDE_G = 0, 1
 FLAG_NONFINITE, FLAG_SPIN_TIMEOUT = 1, 2
@@ -43,7 +43,9 @@ EXPORTS = [
     "gift_accumulate_stats", "gift_commit_stats", "gift_refresh_factors", "gift_encode", "gift_encode_ef",
     "gift_decode_reduce", "gift_encode_fp4", "gift_decode_reduce_fp4", "gift_payload_bytes", "gift_profiler_create", "gift_profiler_destroy",
     "gift_profiler_workspace_bytes", "gift_profile_step", "gift_select_layers", "gift_status_string",
-    "gift_last_hip_error", "gift_set_fused",
+    "gift_last_hip_error", "gift_set_fused", "gift_bucket_table_bytes", "gift_bucket_create",
+    "gift_bucket_destroy", "gift_bucket_sizes", "gift_bucket_flags", "gift_bucket_amax", "gift_bucket_encode",
+    "gift_bucket_decode_reduce", "gift_scale_sync_due",
 ]
 
 
@@ -89,6 +91,15 @@ _sig("gift_select_layers", _i32, _vp, _i32, _P(ctypes.c_double), _P(_i32), _P(_i
 _sig("gift_status_string", ctypes.c_char_p, _i32)
 _sig("gift_last_hip_error", _i32)
 _sig("gift_set_fused", _i32, _i32)
+_sig("gift_bucket_table_bytes", _sz, _i32)
+_sig("gift_bucket_create", _i32, _i32, _P(_i64), _i32, _vp, _sz, _vp, _P(_vp))
+_sig("gift_bucket_destroy", _i32, _vp)
+_sig("gift_bucket_sizes", _i32, _vp, _P(_i64), _P(_i64), _P(_sz))
+_sig("gift_bucket_flags", _i32, _vp, _vp, _P(ctypes.c_uint32))
+_sig("gift_bucket_amax", _i32, _vp, _vp, _vp, _vp)
+_sig("gift_bucket_encode", _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp)
+_sig("gift_bucket_decode_reduce", _i32, _vp, _vp, _i64, _vp, _i64, _i32, _i32, _vp, _vp)
+_sig("gift_scale_sync_due", _i32, _i64, _i32)
 
 
 def set_fused(enable: bool) -> bool:
@@ -344,6 +355,84 @@ class Profiler:
     def close(self):
         if getattr(self, "_h", None):
             _lib.gift_profiler_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def scale_sync_due(step: int, period: int) -> bool:
+    """Whether `step` is a scale-sync step of a schedule syncing every
+    `period` steps (gift_scale_sync_due)."""
+    return bool(_lib.gift_scale_sync_due(step, period))
+
+
+class Bucket:
+    """Flat gradient bucket of Euclidean tensors (gift_bucket_*): the tensors
+    of `sizes` elements lie one after another in one flat fp32 buffer."""
+
+    def __init__(self, sizes, scaling=SCALE_TENSOR, device="cuda", stream=None):
+        self.sizes = [int(n) for n in sizes]
+        self.scaling = SCALINGS.get(scaling, scaling)
+        n = len(self.sizes)
+        tb = int(_lib.gift_bucket_table_bytes(n))
+        self.table = _alloc(tb, device)
+        arr = (_i64 * n)(*self.sizes)
+        h = _vp()
+        _check(_lib.gift_bucket_create(n, arr, self.scaling, _ptr(self.table), tb, _stream(stream), ctypes.byref(h)),
+               "gift_bucket_create")
+        self._h = h
+        ne, ns, wb = _i64(), _i64(), _sz()
+        _check(_lib.gift_bucket_sizes(h, ctypes.byref(ne), ctypes.byref(ns), ctypes.byref(wb)), "gift_bucket_sizes")
+        self.numel, self.nscales, self.work_bytes = ne.value, ns.value, wb.value
+        self.work = _alloc(max(self.work_bytes, 256), device)
+
+    def _grad(self, g):
+        if g.dtype != torch.float32 or not g.is_contiguous() or g.numel() < self.numel:
+            raise ValueError("the bucket needs a contiguous fp32 buffer of all its elements")
+
+    def amax(self, grad, amax_out=None, stream=None):
+        self._grad(grad)
+        if amax_out is None:
+            amax_out = torch.empty(self.nscales, dtype=torch.float32, device=grad.device)
+        _check(_lib.gift_bucket_amax(self._h, _ptr(grad), _ptr(amax_out), _stream(stream)), "gift_bucket_amax")
+        return amax_out
+
+    def encode(self, grad, fmt=E4M3, amax_in=None, amax_out=None, codes=None, scales=None, stream=None):
+        self._grad(grad)
+        if codes is None:
+            codes = torch.empty(self.numel, dtype=torch.uint8, device=grad.device)
+        if scales is None:
+            scales = torch.empty(self.nscales, dtype=torch.float32, device=grad.device)
+        _check(_lib.gift_bucket_encode(self._h, _ptr(grad), FORMATS.get(fmt, fmt), _ptr(amax_in), _ptr(amax_out),
+                                       _ptr(codes), _ptr(scales), _ptr(self.work), self.work_bytes, _stream(stream)),
+               "gift_bucket_encode")
+        return codes, scales
+
+    def decode_reduce(self, codes, scales, fmt=E4M3, out=None, stream=None):
+        """codes [R][numel] uint8, scales [R][nscales] fp32."""
+        if codes.dim() == 1:
+            codes, scales = codes.unsqueeze(0), scales.unsqueeze(0)
+        R = codes.shape[0]
+        if out is None:
+            out = torch.empty(self.numel, dtype=torch.float32, device=codes.device)
+        cs = codes.stride(0) if R > 1 else self.numel
+        ss = scales.stride(0) if R > 1 else self.nscales
+        _check(_lib.gift_bucket_decode_reduce(self._h, _ptr(codes), cs, _ptr(scales), ss, R, FORMATS.get(fmt, fmt),
+                                              _ptr(out), _stream(stream)), "gift_bucket_decode_reduce")
+        return out
+
+    def flags(self, stream=None) -> int:
+        f = ctypes.c_uint32()
+        _check(_lib.gift_bucket_flags(self._h, _stream(stream), ctypes.byref(f)), "gift_bucket_flags")
+        return f.value
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.gift_bucket_destroy(self._h)
             self._h = None
 
     def __del__(self):

@@ -27,6 +27,13 @@ struct gift_layer {
   bool ready;
 };
 
+struct gift_bucket {
+  int32_t n = 0, scaling = 0;
+  int64_t numel = 0, nscales = 0;
+  std::vector<int64_t> host;   // chunk_start, elem_off, scale_off (n + 1 each), the source of the table copy
+  gift::BucketTable t{};
+};
+
 struct gift_profiler {
   int32_t n_layers, fmt, scaling;
   uint64_t* counts;
@@ -784,6 +791,126 @@ gift_status gift_select_layers(gift_profiler_t P, int32_t max_select, double* h_
   for (int i = 0; i < nsel; ++i) h_selected[i] = order[(size_t)i];
   *h_n_selected = nsel;
   return GIFT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Flat gradient buckets
+// ---------------------------------------------------------------------------
+
+size_t gift_bucket_table_bytes(int32_t n) {
+  if (n < 1) return 0;
+  return gift::align256((size_t)(n + 1) * 3 * 8) + 256;
+}
+
+gift_status gift_bucket_create(int32_t n, const int64_t* h_numel, int32_t scaling, void* d_table, size_t table_bytes,
+                               gift_stream_t stream, gift_bucket_t* out) {
+  if (n < 1 || !h_numel || !d_table || !out || (reinterpret_cast<uintptr_t>(d_table) & 255u)) return GIFT_ERR_INVALID_ARG;
+  if (scaling != GIFT_SCALE_TENSOR && scaling != GIFT_SCALE_BLOCK512) return GIFT_ERR_INVALID_ARG;
+  if (table_bytes < gift_bucket_table_bytes(n)) return GIFT_ERR_WORKSPACE;
+  for (int32_t i = 0; i < n; ++i)
+    if (h_numel[i] < 4 || h_numel[i] % 4 != 0) return GIFT_ERR_INVALID_ARG;
+  gift_bucket* B = new (std::nothrow) gift_bucket;
+  if (!B) return GIFT_ERR_INVALID_ARG;
+  const size_t n1 = (size_t)n + 1;
+  B->n = n;
+  B->scaling = scaling;
+  B->host.assign(3 * n1, 0);
+  int64_t* cs = B->host.data();
+  int64_t* eo = cs + n1;
+  int64_t* so = eo + n1;
+  for (int32_t i = 0; i < n; ++i) {
+    cs[i + 1] = cs[i] + gift::cdiv(h_numel[i], 2048);
+    eo[i + 1] = eo[i] + h_numel[i];
+    so[i + 1] = so[i] + (scaling == GIFT_SCALE_TENSOR ? 1 : gift::cdiv(h_numel[i], 512));
+  }
+  B->numel = eo[n];
+  B->nscales = so[n];
+  char* tb = static_cast<char*>(d_table);
+  B->t.chunk_start = reinterpret_cast<const int64_t*>(tb);
+  B->t.elem_off = reinterpret_cast<const int64_t*>(tb) + n1;
+  B->t.scale_off = reinterpret_cast<const int64_t*>(tb) + 2 * n1;
+  B->t.n = n;
+  B->t.chunks = cs[n];
+  B->t.flags = reinterpret_cast<uint32_t*>(tb + gift::align256(n1 * 3 * 8));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(tb, B->host.data(), n1 * 3 * 8, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = gift::launch_fill_u32(B->t.flags, 0u, 1, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);   // the host copy source must outlive the transfer
+  if (e != hipSuccess) {
+    delete B;
+    return hip_fail(e);
+  }
+  *out = B;
+  return GIFT_OK;
+}
+
+gift_status gift_bucket_destroy(gift_bucket_t B) {
+  delete B;
+  return GIFT_OK;
+}
+
+gift_status gift_bucket_sizes(gift_bucket_t B, int64_t* h_numel, int64_t* h_nscales, size_t* h_workspace_bytes) {
+  if (!B) return GIFT_ERR_INVALID_ARG;
+  if (h_numel) *h_numel = B->numel;
+  if (h_nscales) *h_nscales = B->nscales;
+  if (h_workspace_bytes) *h_workspace_bytes = gift::align256((size_t)B->nscales * 4);
+  return GIFT_OK;
+}
+
+gift_status gift_bucket_flags(gift_bucket_t B, gift_stream_t stream, uint32_t* h_flags) {
+  if (!B || !h_flags) return GIFT_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  GIFT_HIP(hipMemcpyAsync(h_flags, B->t.flags, 4, hipMemcpyDeviceToHost, s));
+  GIFT_HIP(hipStreamSynchronize(s));
+  return GIFT_OK;
+}
+
+gift_status gift_bucket_amax(gift_bucket_t B, const float* d_grad, float* d_amax_out, gift_stream_t stream) {
+  if (!B || !d_grad || !d_amax_out || !aligned16(d_grad)) return GIFT_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t* slots = reinterpret_cast<uint32_t*>(d_amax_out);   // |x| bit patterns order like the floats
+  GIFT_HIP(gift::launch_fill_u32(slots, 0u, (size_t)B->nscales, s));
+  GIFT_HIP(gift::launch_bucket_amax(B->t, d_grad, B->scaling == GIFT_SCALE_BLOCK512, slots, device_cus(), s));
+  return GIFT_OK;
+}
+
+gift_status gift_bucket_encode(gift_bucket_t B, const float* d_grad, int32_t fmt, const float* d_amax_in,
+                               float* d_amax_out, uint8_t* d_codes, float* d_scales, void* d_work, size_t work_bytes,
+                               gift_stream_t stream) {
+  if (!B || !d_grad || !d_codes || !d_scales || !aligned16(d_grad) || !aligned16(d_codes)) return GIFT_ERR_INVALID_ARG;
+  if (fmt != GIFT_E4M3 && fmt != GIFT_E5M2) return GIFT_ERR_INVALID_ARG;
+  const bool local = !d_amax_in || d_amax_out;
+  if (local && (!d_work || (reinterpret_cast<uintptr_t>(d_work) & 255u))) return GIFT_ERR_INVALID_ARG;
+  if (local && work_bytes < (size_t)B->nscales * 4) return GIFT_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int blk = B->scaling == GIFT_SCALE_BLOCK512;
+  const int cus = device_cus();
+  uint32_t* slots = static_cast<uint32_t*>(d_work);
+  if (local) {
+    GIFT_HIP(gift::launch_fill_u32(slots, 0u, (size_t)B->nscales, s));
+    GIFT_HIP(gift::launch_bucket_amax(B->t, d_grad, blk, slots, cus, s));
+  }
+  GIFT_HIP(gift::launch_bucket_quantize(B->t, d_grad, fmt, blk, slots, d_amax_in, d_amax_out, d_codes, d_scales, cus,
+                                        s));
+  return GIFT_OK;
+}
+
+gift_status gift_bucket_decode_reduce(gift_bucket_t B, const uint8_t* d_codes, int64_t code_stride,
+                                      const float* d_scales, int64_t scale_stride, int32_t R, int32_t fmt,
+                                      float* d_out, gift_stream_t stream) {
+  if (!B || !d_codes || !d_scales || !d_out || R < 1 || !aligned16(d_codes) || !aligned16(d_out))
+    return GIFT_ERR_INVALID_ARG;
+  if (fmt != GIFT_E4M3 && fmt != GIFT_E5M2) return GIFT_ERR_INVALID_ARG;
+  if (R > 1 && (code_stride < B->numel || code_stride % 16 != 0 || scale_stride < B->nscales))
+    return GIFT_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  GIFT_HIP(gift::launch_bucket_dequant_sum(B->t, d_codes, code_stride, d_scales, scale_stride, R, fmt,
+                                           B->scaling == GIFT_SCALE_BLOCK512, d_out, device_cus(), s));
+  return GIFT_OK;
+}
+
+int32_t gift_scale_sync_due(int64_t step, int32_t period) {
+  return (period > 0 && step >= 0 && step % period == 0) ? 1 : 0;
 }
 
 }  // extern "C"

@@ -129,6 +129,25 @@ hipError_t launch_quantize_fp4(const float* x, int64_t ld, int m, int d, const u
 hipError_t launch_dequant_sum_fp4(const uint8_t* codes, int64_t code_stride, const uint8_t* bscales,
                                   int64_t bscale_stride, const float* tscales, int R, int m, int d, float* out,
                                   int64_t ldo, hipStream_t s);
+// Flat gradient buckets (Euclidean codec over many tensors, one launch per
+// phase).  Prefix tables in device memory, n + 1 entries each.
+struct BucketTable {
+  const int64_t* chunk_start;   // first 2048-element chunk of each tensor
+  const int64_t* elem_off;      // first element of each tensor in the flat buffer
+  const int64_t* scale_off;     // first scale of each tensor
+  int n;
+  int64_t chunks;
+  uint32_t* flags;
+};
+hipError_t launch_bucket_amax(const BucketTable& t, const float* g, int block512, uint32_t* slots, int cus,
+                              hipStream_t s);
+hipError_t launch_bucket_quantize(const BucketTable& t, const float* g, int fmt, int block512, const uint32_t* slots,
+                                  const float* amax_in, float* amax_out, uint8_t* codes, float* scales, int cus,
+                                  hipStream_t s);
+hipError_t launch_bucket_dequant_sum(const BucketTable& t, const uint8_t* codes, int64_t code_stride,
+                                     const float* scales, int64_t scale_stride, int R, int fmt, int block512,
+                                     float* out, int cus, hipStream_t s);
+
 // U = (1/R) sum_r s_r dec(q_r) -> fp32 [m][ldo]
 hipError_t launch_dequant_sum(const uint8_t* codes, int64_t code_stride, const float* scales,
                               int64_t scale_stride, int R, int m, int d, int fmt, int scaling,

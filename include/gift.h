@@ -41,6 +41,7 @@ typedef int32_t gift_status;
 typedef void* gift_stream_t;                 /* a hipStream_t */
 typedef struct gift_layer* gift_layer_t;       /* opaque host handle */
 typedef struct gift_profiler* gift_profiler_t; /* opaque host handle */
+typedef struct gift_bucket* gift_bucket_t;     /* opaque host handle */
 
 enum {
   GIFT_OK = 0,
@@ -65,8 +66,14 @@ enum gift_transform {
 
 /* FP8 ([Note] §前置知识); E2M1 = FP4 ([Abs] NVFP4), only through the _fp4 calls */
 enum gift_format { GIFT_E4M3 = 0, GIFT_E5M2 = 1, GIFT_E2M1 = 2 };
-/* BLOCK16: the FP4 payload's 16-element row blocks (gift_payload_bytes only) */
-enum gift_scaling { GIFT_SCALE_TENSOR = 0, GIFT_SCALE_BLOCK128 = 1, GIFT_SCALE_BLOCK16 = 2 };
+/* BLOCK16: the FP4 payload's 16-element row blocks (gift_payload_bytes only);
+ * BLOCK512: 512 consecutive elements of a tensor (gift_bucket_* only) */
+enum gift_scaling {
+  GIFT_SCALE_TENSOR = 0,
+  GIFT_SCALE_BLOCK128 = 1,
+  GIFT_SCALE_BLOCK16 = 2,
+  GIFT_SCALE_BLOCK512 = 3
+};
 enum gift_dtype { GIFT_BF16 = 0, GIFT_FP32 = 1 };
 enum gift_side { GIFT_SIDE_A = 0, GIFT_SIDE_G = 1 };      /* input / output statistics */
 enum { GIFT_FLAG_NONFINITE = 1u, GIFT_FLAG_SPIN_TIMEOUT = 2u };
@@ -263,6 +270,63 @@ gift_status gift_decode_reduce_fp4(gift_layer_t layer, const uint8_t* d_codes, i
                                    const uint8_t* d_bscales, int64_t bscale_stride,
                                    const float* d_tscales, int32_t R, float* d_out, int64_t ldo,
                                    void* d_work, size_t work_bytes, gift_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Flat gradient buckets: the Euclidean FP8 path of every layer outside the
+ * selected set ([Note] Algorithm 1, lines 3-8) over a whole buffer of
+ * tensors, one launch per phase.
+ *
+ * A bucket describes n tensors of h_numel[i] fp32 elements (each a multiple
+ * of 4, >= 4) lying one after another in one flat buffer (tensor i starts at
+ * element sum_{j<i} numel_j; 16-byte aligned buffers).  Codes use the same
+ * offsets (1 byte per element).  Scales are numbered tensor by tensor:
+ *   GIFT_SCALE_TENSOR:   one per tensor;
+ *   GIFT_SCALE_BLOCK512: one per 512 consecutive elements of a tensor
+ *                        (blocks restart at every tensor; the last block of
+ *                        a tensor may be shorter): the per-block Euclidean
+ *                        baseline of [Note] (experiment setup, block 512).
+ * The quantiser is gift_encode's (R4 of the scale, RNE saturating codes,
+ * NaN scale and 0x7F codes for a non-finite amax, GIFT_FLAG_NONFINITE in the
+ * bucket's flag word).
+ *
+ * gift_bucket_create: d_table = caller-owned device memory of
+ *   gift_bucket_table_bytes(n) bytes, 256-byte aligned (the offset tables
+ *   and the flag word); the call copies the tables and synchronises stream.
+ * gift_bucket_sizes: total elements, number of scales, and the workspace
+ *   bytes gift_bucket_encode needs for a local amax.
+ * gift_bucket_amax: d_amax_out fp32 [nscales] = the amax of every scale
+ *   block (for the AllReduceMax of Algorithm 1, line 5).
+ * gift_bucket_encode: codes uint8 [numel] and scales fp32 [nscales] with the
+ *   shared amax d_amax_in (NULL: the local one, computed first into d_work);
+ *   d_amax_out NULL or fp32 [nscales] receives the local amax.
+ * gift_bucket_decode_reduce: U = (1/R) sum_r s_r dec(q_r) (fp32, r in
+ *   increasing order) into d_out fp32 [numel]; replica r at
+ *   d_codes + r * code_stride (bytes) and d_scales + r * scale_stride.
+ * ------------------------------------------------------------------------- */
+size_t gift_bucket_table_bytes(int32_t n);
+gift_status gift_bucket_create(int32_t n, const int64_t* h_numel, int32_t scaling, void* d_table,
+                               size_t table_bytes, gift_stream_t stream, gift_bucket_t* out);
+gift_status gift_bucket_destroy(gift_bucket_t bucket);
+gift_status gift_bucket_sizes(gift_bucket_t bucket, int64_t* h_numel, int64_t* h_nscales,
+                              size_t* h_workspace_bytes);
+gift_status gift_bucket_flags(gift_bucket_t bucket, gift_stream_t stream, uint32_t* h_flags);
+gift_status gift_bucket_amax(gift_bucket_t bucket, const float* d_grad, float* d_amax_out,
+                             gift_stream_t stream);
+gift_status gift_bucket_encode(gift_bucket_t bucket, const float* d_grad, int32_t fmt,
+                               const float* d_amax_in, float* d_amax_out, uint8_t* d_codes,
+                               float* d_scales, void* d_work, size_t work_bytes, gift_stream_t stream);
+gift_status gift_bucket_decode_reduce(gift_bucket_t bucket, const uint8_t* d_codes, int64_t code_stride,
+                                      const float* d_scales, int64_t scale_stride, int32_t R,
+                                      int32_t fmt, float* d_out, gift_stream_t stream);
+
+/* Scale-sync schedule ([Note] Algorithm 1, lines 16-19): the geometry-aware
+ * layers quantise with their local scale and, on a scale-sync step, with the
+ * scale shared across workers (the AllReduceMax of the local amaxes: an
+ * amax-only gift_encode / gift_encode_ef per replica, then the call with
+ * d_amax_in).  Returns 1 when `step` (0-based) is a sync step of a schedule
+ * that syncs every `period` steps starting at step 0, else 0; period <= 0
+ * never syncs (the local-scale default the pages prefer). */
+int32_t gift_scale_sync_due(int64_t step, int32_t period);
 
 /* ---------------------------------------------------------------------------
  * FP8 boundary-hit profiler ([Note] §简化三, Fig. 3): over the first steps of

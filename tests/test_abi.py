@@ -54,6 +54,25 @@ def test_host_side_checks_without_gpu():
     # calls with a NULL handle fail before touching the device
     assert lib.gift_encode(None, None, 0, 0, 0, None, None, None, None, None, None, 0, None) == 1
     assert lib.gift_profiler_create(0, 0, 0, None, None, None) == 1
+    # FP4 payload: half a byte per code, one E4M3 byte per 16 elements, the tensor scale
+    assert fw.payload_bytes(4096, 16384, fw.SCALE_BLOCK16) == 4096 * 16384 // 2 + 4096 * 1024 + 4
+    assert lib.gift_encode_fp4(None, None, 0, None, None, None, None, None, None, None, None, 0, None) == 1
+    # buckets: table size, argument checks before any device work
+    assert lib.gift_bucket_table_bytes(0) == 0 and lib.gift_bucket_table_bytes(168) % 256 == 0
+    h = ctypes.c_void_p()
+    sizes = (ctypes.c_int64 * 2)(1024, 6)                          # 6 is not a multiple of 4
+    assert lib.gift_bucket_create(2, sizes, fw.SCALE_TENSOR, None, 0, None, ctypes.byref(h)) == 1
+    assert lib.gift_bucket_create(2, sizes, fw.SCALE_BLOCK128, None, 0, None, ctypes.byref(h)) == 1
+
+
+def test_scale_sync_schedule():
+    """Algorithm 1, lines 16-19: local scales by default, a shared scale on
+    every period-th step from step 0; period <= 0 never syncs."""
+    import fac_whitening_amd as fw
+    assert [fw.scale_sync_due(t, 4) for t in range(9)] == [True, False, False, False, True, False, False, False, True]
+    assert not any(fw.scale_sync_due(t, 0) for t in range(5))
+    assert not any(fw.scale_sync_due(t, -3) for t in range(5))
+    assert all(fw.scale_sync_due(t, 1) for t in range(5))
 
 
 def test_product_path_has_no_oracle_or_cpu_fallback():
