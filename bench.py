@@ -239,27 +239,32 @@ def bench_selective(args, torch, fw, synth, dev):
     """Whole-buffer encode + decode-reduce of the 600M-class deployment: 168
     weight gradients (906M fp32 values, 3.62 GB), the fc2 gradients of 13
     layers rank-32 whitened, the other 155 Euclidean; E4M3 per tensor,
-    R = 8 (replicas 1..7 encoded in setup).  One step = every tensor's
-    encode of replica 0 and decode-reduce, in order on one stream.  The
-    rank-32 layers' statistics (T = 8192 bf16 tokens) and refresh run in
-    setup.  Gradients: the direct Gaussian draw (synth.direct_gradient)."""
+    R = 8 (replicas 1..7 encoded in setup).  One step = worker 0's share:
+    the 155 Euclidean tensors as one flat bucket (local amax and quantise
+    with the shared amax of the 8 replicas, then the decode-reduce: three
+    launches) and, for each rank-32 layer, its encode and decode-reduce (one
+    launch each).  The Euclidean tensors are also timed with one launch per
+    tensor and per phase (the same buffers), and with 512-element block
+    scales (the per-block Euclidean baseline).  The rank-32 layers'
+    statistics (T = 8192 bf16 tokens) and refresh run in setup.  Gradients:
+    the direct Gaussian draw (synth.direct_gradient)."""
     R, Ttok = 8, 8192
     f, s = fw.E4M3, fw.SCALE_TENSOR
-    items = []
     t0 = time.time()
     state_gift = 0
-    for (l, name, mo, di, alpha, gift) in synth.selective_tensors():
-        seed = lambda r: synth.seed_for(3, synth.ROLE_A, l * 8 + list(synth.SELECTIVE_SHAPES).index(name), r)
-        if gift:
-            L = fw.Layer(mo, di, "lowrank", device=dev)
-            a = synth.gaussian_rows(Ttok, di, alpha, None, synth.seed_for(3, synth.ROLE_A, l, 0, 1), dev,
-                                    torch.bfloat16)
-            L.accumulate_stats(a, fw.SIDE_A, commit=True)
-            del a
-            L.refresh(synth.omega(di, 48, synth.seed_for(3, synth.ROLE_OMEGA, l), dev))
-            state_gift += L.state.numel()
-        else:
-            L = fw.Layer(mo, di, "euclid", device=dev)
+    gift_items, eu = [], []
+    for k, (l, name, mo, di, alpha, gift) in enumerate(synth.selective_tensors()):
+        seed = lambda r, l=l, name=name: synth.seed_for(3, synth.ROLE_A, l * 8 + list(synth.SELECTIVE_SHAPES).index(name),
+                                                        r)
+        if not gift:
+            eu.append((mo, di, alpha, seed))
+            continue
+        L = fw.Layer(mo, di, "lowrank", device=dev)
+        a = synth.gaussian_rows(Ttok, di, alpha, None, synth.seed_for(3, synth.ROLE_A, l, 0, 1), dev, torch.bfloat16)
+        L.accumulate_stats(a, fw.SIDE_A, commit=True)
+        del a
+        L.refresh(synth.omega(di, 48, synth.seed_for(3, synth.ROLE_OMEGA, l), dev))
+        state_gift += L.state.numel()
         codes = torch.empty(R, mo, di, dtype=torch.uint8, device=dev)
         scales = torch.empty(R, 1, dtype=torch.float32, device=dev)
         for r in range(1, R):
@@ -267,22 +272,101 @@ def bench_selective(args, torch, fw, synth, dev):
             L.encode(Wr, f, s, codes=codes[r], scales=scales[r])
             del Wr
         W0 = synth.direct_gradient(mo, di, alpha, Ttok, seed(0), dev)
-        items.append((L, W0, codes, scales, torch.empty(mo, di, dtype=torch.float32, device=dev), gift))
-    torch.cuda.synchronize()
-    assert all(L.flags() == 0 for L, *_ in items)
-    print(f"[bench selective] {len(items)} tensors ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+        gift_items.append((L, W0, codes, scales, torch.empty(mo, di, dtype=torch.float32, device=dev)))
+    # the Euclidean tensors: one flat bucket per replica
+    sizes = [mo * di for (mo, di, _, _) in eu]
+    B = fw.Bucket(sizes, fw.SCALE_TENSOR, device=dev)
+    B512 = fw.Bucket(sizes, fw.SCALE_BLOCK512, device=dev)
+    n_eu = B.numel
+    stride = -(-n_eu // 16) * 16
+    codes_eu = torch.empty(R, stride, dtype=torch.uint8, device=dev)[:, :n_eu]
+    codes_512 = torch.empty(R, stride, dtype=torch.uint8, device=dev)[:, :n_eu]
+    scales_eu = torch.empty(R, B.nscales, dtype=torch.float32, device=dev)
+    scales_512 = torch.empty(R, B512.nscales, dtype=torch.float32, device=dev)
 
-    def step():
-        for L, W0, codes, scales, out, _ in items:
+    def replica(r):
+        g = torch.empty(n_eu, dtype=torch.float32, device=dev)
+        off = 0
+        for (mo, di, alpha, seed) in eu:
+            g[off:off + mo * di] = synth.direct_gradient(mo, di, alpha, Ttok, seed(r), dev).reshape(-1)
+            off += mo * di
+        return g
+    # AllReduceMax of the local amaxes over the replicas, then replicas 1..7
+    amax, amax512 = None, None
+    for r in range(R):
+        g = replica(r)
+        a, a5 = B.amax(g), B512.amax(g)
+        amax = a if amax is None else torch.maximum(amax, a)
+        amax512 = a5 if amax512 is None else torch.maximum(amax512, a5)
+        del g
+    for r in range(1, R):
+        g = replica(r)
+        B.encode(g, f, amax_in=amax, codes=codes_eu[r], scales=scales_eu[r])
+        B512.encode(g, f, amax_in=amax512, codes=codes_512[r], scales=scales_512[r])
+        del g
+    g0 = replica(0)
+    am0 = torch.empty(B.nscales, dtype=torch.float32, device=dev)
+    am0_512 = torch.empty(B512.nscales, dtype=torch.float32, device=dev)
+    out_eu = torch.empty(n_eu, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    assert all(L.flags() == 0 for L, *_ in gift_items) and B.flags() == 0
+    print(f"[bench selective] {len(eu)} Euclidean + {len(gift_items)} rank-32 tensors ready in "
+          f"{time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    def gift_layers():
+        for L, W0, codes, scales, out in gift_items:
             L.encode(W0, f, s, codes=codes[0], scales=scales[0])
             L.decode_reduce(codes, scales, f, s, out=out)
 
+    def euclid_bucket():
+        B.encode(g0, f, amax_in=amax, amax_out=am0, codes=codes_eu[0], scales=scales_eu[0])
+        B.decode_reduce(codes_eu, scales_eu, f, out=out_eu)
+
+    def euclid_bucket_512():
+        B512.encode(g0, f, amax_in=amax512, amax_out=am0_512, codes=codes_512[0], scales=scales_512[0])
+        B512.decode_reduce(codes_512, scales_512, f, out=out_eu)
+
+    # the same Euclidean work with one launch per tensor and per phase
+    views, off = [], 0
+    for k, (mo, di, _, _) in enumerate(eu):
+        L = fw.Layer(mo, di, "euclid", device=dev)
+        views.append((L, g0[off:off + mo * di].view(mo, di),
+                      codes_eu[:, off:off + mo * di].unflatten(1, (mo, di)), scales_eu[:, k:k + 1],
+                      amax[k:k + 1], am0[k:k + 1], out_eu[off:off + mo * di].view(mo, di)))
+        off += mo * di
+
+    def euclid_per_tensor():
+        for L, W, c, sc, a_in, a_out, o in views:
+            L.encode(W, f, s, amax_in=a_in, amax_out=a_out, codes=c[0], scales=sc[0])
+            L.decode_reduce(c, sc, f, s, out=o)
+
+    def step():
+        euclid_bucket()
+        gift_layers()
+
     steps = max(1, min(args.steps, 20))
     ms = _event_ms(torch, step, steps)
-    n = sum(W0.numel() for _, W0, *_ in items)
-    alg = sum((4.0 + 1 + 4) * W0.numel() + R * W0.numel() + 4 * (R + 1) for _, W0, *_ in items)
-    n_gift = sum(1 for it in items if it[5])
+    ms_gift = _event_ms(torch, gift_layers, steps)
+    ms_bucket = _event_ms(torch, euclid_bucket, steps)
+    ms_per_tensor = _event_ms(torch, euclid_per_tensor, steps)
+    ms_512 = _event_ms(torch, euclid_bucket_512, steps)
+    torch.cuda.synchronize()
+    assert all(L.flags() == 0 for L, *_ in gift_items) and B.flags() == 0 and B512.flags() == 0
+    n_gift = sum(W0.numel() for _, W0, *_ in gift_items)
+    n = n_eu + n_gift
+    # algorithmic bytes: encode reads 4 B and writes 1 B per element, decode
+    # reads R payloads and writes 4 B (scales and U_k included)
+    alg_eu = (4.0 + 1 + 4) * n_eu + R * n_eu + 4 * (R + 1) * B.nscales
+    alg_512 = (4.0 + 1 + 4) * n_eu + R * n_eu + 4 * (R + 1) * B512.nscales
+    alg_gift = sum((4.0 + 1 + 4) * W0.numel() + R * W0.numel() + 4 * (R + 1) + 2 * W0.shape[1] * 32 * 4
+                   for _, W0, *_ in gift_items)
+    alg = alg_eu + alg_gift
     grad_bytes = 4.0 * n
+
+    def stage(t, b, work):
+        return {"ms": round(t, 4), "bound": "hbm", "achieved": round(b / (t * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(b / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "alg_bytes": int(b),
+                "work": work}
     result = {
         "metric": "whole-buffer encode+decode GB/s of fp32 grad (600M-class selective deployment)",
         "value": round(grad_bytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
@@ -290,10 +374,17 @@ def bench_selective(args, torch, fw, synth, dev):
         "data": "synthetic (direct Gaussian gradients, bf16 power-law activations for the rank-32 layers)",
         "config": {"workload": "600M-class selective: 24 layers x {q,k,v,o 1536x1536, fc1/fc3 6144x1536, "
                                "fc2 1536x6144}; fc2 of layers 0-12 rank-32, the rest Euclidean; E4M3 per "
-                               "tensor; R=8", "tensors": len(items), "rank32_tensors": n_gift, "params": n},
+                               "tensor; R=8", "tensors": len(eu) + len(gift_items), "rank32_tensors": len(gift_items),
+                   "params": n},
         "roofline": {"bound": "hbm", "achieved": round(alg / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "alg_bytes": int(alg)},
+        "stages": {
+            "euclid_bucket": stage(ms_bucket, alg_eu, "155 Euclidean tensors, one bucket: 3 launches"),
+            "euclid_per_tensor": stage(ms_per_tensor, alg_eu, "the same with one launch per tensor and phase"),
+            "euclid_bucket_block512": stage(ms_512, alg_512, "per-block Euclidean baseline, 512-element blocks"),
+            "rank32_layers": stage(ms_gift, alg_gift, "13 rank-32 fc2 layers, fused encode + decode each"),
+        },
         "memory": {"grad_bytes": int(grad_bytes), "rank32_state_bytes": int(state_gift),
                    "state_over_grad": round(state_gift / grad_bytes, 4)},
     }

@@ -819,7 +819,7 @@ gift_status gift_bucket_create(int32_t n, const int64_t* h_numel, int32_t scalin
   int64_t* eo = cs + n1;
   int64_t* so = eo + n1;
   for (int32_t i = 0; i < n; ++i) {
-    cs[i + 1] = cs[i] + gift::cdiv(h_numel[i], 2048);
+    cs[i + 1] = cs[i] + gift::cdiv(h_numel[i], 4096);   // 4096-element chunks
     eo[i + 1] = eo[i] + h_numel[i];
     so[i + 1] = so[i] + (scaling == GIFT_SCALE_TENSOR ? 1 : gift::cdiv(h_numel[i], 512));
   }

@@ -8,18 +8,21 @@
 //
 // The tensors lie one after another in one flat fp32 buffer (element
 // counts multiples of 4); codes use the same offsets, scales are numbered
-// tensor by tensor.  Work is cut into chunks of 2048 elements of one tensor
+// tensor by tensor.  Work is cut into chunks of 4096 elements of one tensor
 // (a tensor's last chunk may be partial); wave w of a 256-thread workgroup
-// takes elements 512 w .. 512 w + 511 of the chunk, lane l the float4s at
-// 4 l and 256 + 4 l, so one wave covers exactly one 512-element block and a
-// wave's loads are contiguous.  Workgroups loop over the chunks (grid
-// stride) and find a chunk's tensor by binary search in the prefix table.
+// takes elements 1024 w .. 1024 w + 1023 of the chunk (512-element blocks
+// 2w and 2w + 1), lane l the float4s at 256 h + 4 l, h = 0..3, so a wave's
+// loads are contiguous and h = 0, 1 (2, 3) cover one block.  Each
+// workgroup takes one contiguous range of chunks and follows the tensor
+// boundaries through the prefix table, so the chunk-to-tensor search runs
+// once per workgroup.
 #include "fp8_codec.hpp"
 #include "gift_internal.hpp"
 
 namespace gift {
 
-constexpr int kBChunk = 2048;
+constexpr int kBChunk = 4096;
+constexpr int kBH = 4;   // float4 loads per lane per chunk
 
 __device__ __forceinline__ int bucket_tensor(const int64_t* __restrict__ cs, int n, int64_t c) {
   int lo = 0, hi = n;   // the largest i with cs[i] <= c (cs[0] = 0, cs[n] = chunks)
@@ -31,29 +34,44 @@ __device__ __forceinline__ int bucket_tensor(const int64_t* __restrict__ cs, int
   return lo;
 }
 
-struct BChunk {
-  int tensor;
-  int64_t e;         // this lane's first element within the tensor
-  int64_t numel;     // the tensor's element count
-  int64_t base;      // the tensor's first element in the flat buffer
-  int64_t slot;      // scale index of this wave's block (or of the tensor)
-  bool blk_live;     // this wave's block exists
+// A workgroup's contiguous range of chunks and the tensor of the current one.
+struct BRange {
+  int64_t c, end;    // current chunk, one past the last
+  int i;             // tensor of chunk c
+  int64_t next;      // first chunk of tensor i + 1
+  __device__ BRange(const BucketTable& t) {
+    const int64_t per = (t.chunks + gridDim.x - 1) / gridDim.x;
+    c = (int64_t)blockIdx.x * per;
+    end = min(c + per, t.chunks);
+    i = c < end ? bucket_tensor(t.chunk_start, t.n, c) : 0;
+    next = c < end ? t.chunk_start[i + 1] : 0;
+  }
+  // move to chunk c + 1; returns true when it starts a new tensor
+  __device__ bool advance(const BucketTable& t) {
+    ++c;
+    if (c < end && c >= next) {
+      do {
+        ++i;
+        next = t.chunk_start[i + 1];
+      } while (c >= next);
+      return true;
+    }
+    return false;
+  }
 };
 
-__device__ __forceinline__ BChunk bucket_chunk(const BucketTable& t, int64_t c, int block512) {
-  BChunk b;
-  const int i = bucket_tensor(t.chunk_start, t.n, c);
-  const int64_t k = c - t.chunk_start[i];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  b.tensor = i;
-  b.base = t.elem_off[i];
-  b.numel = t.elem_off[i + 1] - b.base;
-  const int64_t e0 = k * kBChunk + 512 * wave;
-  b.e = e0 + 4 * lane;
-  b.blk_live = e0 < b.numel;
-  b.slot = t.scale_off[i] + (block512 ? 4 * k + wave : 0);
-  return b;
-}
+// This lane's part of chunk c of tensor i: element e0 + 256 h (h < 4) of
+// the tensor; the wave's blocks 2 w, 2 w + 1 of the chunk.
+struct BLane {
+  int64_t base, numel, e0, k;
+  __device__ BLane(const BucketTable& t, const BRange& r) {
+    base = t.elem_off[r.i];
+    numel = t.elem_off[r.i + 1] - base;
+    k = r.c - t.chunk_start[r.i];
+    e0 = k * kBChunk + 1024 * (threadIdx.x >> 6) + 4 * (threadIdx.x & 63);
+  }
+  __device__ bool live(int h) const { return e0 + 256 * h < numel; }
+};
 
 __device__ __forceinline__ uint32_t absb(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
 __device__ __forceinline__ uint32_t umax4(float4 v) {
@@ -64,27 +82,49 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
   return v;
 }
 
+// Workgroup max of v (every thread calls it), then one atomicMax.
+__device__ __forceinline__ void flush_tensor_max(uint32_t v, uint32_t* slot, uint32_t* red) {
+  v = wave_umax(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t m = max(max(red[0], red[1]), max(red[2], red[3]));
+    if (m) atomicMax(slot, m);
+  }
+  __syncthreads();
+}
+
 // amax (as |x| bit patterns) of every scale block into slots (zeroed before).
 __global__ void __launch_bounds__(256) k_bucket_amax(BucketTable t, const float* __restrict__ g, int block512,
                                                      uint32_t* __restrict__ slots) {
   __shared__ uint32_t red[4];
-  for (int64_t c = blockIdx.x; c < t.chunks; c += gridDim.x) {
-    const BChunk b = bucket_chunk(t, c, block512);
-    const float* x = g + b.base;
-    uint32_t v = 0;
-    if (b.e < b.numel) v = umax4(*reinterpret_cast<const float4*>(x + b.e));
-    if (b.e + 256 < b.numel) v = max(v, umax4(*reinterpret_cast<const float4*>(x + b.e + 256)));
-    v = wave_umax(v);
+  BRange r(t);
+  uint32_t run = 0;   // per tensor: this lane's max over the tensor's chunks so far
+  for (; r.c < r.end;) {
+    const BLane L(t, r);
+    const float* x = g + L.base;
+    float4 v[kBH];
+#pragma unroll
+    for (int h = 0; h < kBH; ++h)
+      v[h] = L.live(h) ? *reinterpret_cast<const float4*>(x + L.e0 + 256 * h) : make_float4(0.f, 0.f, 0.f, 0.f);
     if (block512) {
-      if ((threadIdx.x & 63) == 0 && b.blk_live) slots[b.slot] = v;   // one wave per block
-    } else {
-      if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        const uint32_t m = max(max(red[0], red[1]), max(red[2], red[3]));
-        if (m) atomicMax(slots + b.slot, m);
+      const uint32_t b0 = wave_umax(max(umax4(v[0]), umax4(v[1])));
+      const uint32_t b1 = wave_umax(max(umax4(v[2]), umax4(v[3])));
+      const int64_t blk = t.scale_off[r.i] + 8 * L.k + 2 * (threadIdx.x >> 6);
+      if ((threadIdx.x & 63) == 0) {
+        if (L.live(0)) slots[blk] = b0;   // one wave per block: no other writer
+        if (L.live(2)) slots[blk + 1] = b1;
       }
-      __syncthreads();   // red is rewritten by the next chunk
+      r.advance(t);
+    } else {
+#pragma unroll
+      for (int h = 0; h < kBH; ++h) run = max(run, umax4(v[h]));
+      const int i = r.i;
+      const bool last = r.advance(t) || r.c >= r.end;
+      if (last) {   // workgroup-uniform
+        flush_tensor_max(run, slots + t.scale_off[i], red);
+        run = 0;
+      }
     }
   }
 }
@@ -117,61 +157,79 @@ __global__ void __launch_bounds__(256) k_bucket_quantize(BucketTable t, const fl
                                                          float* __restrict__ amax_out, uint8_t* __restrict__ codes,
                                                          float* __restrict__ scales) {
   const float fmax = fp8_fmax(FMT);
-  for (int64_t c = blockIdx.x; c < t.chunks; c += gridDim.x) {
-    const BChunk b = bucket_chunk(t, c, block512);
-    if (!b.blk_live) continue;   // wave-uniform
-    const uint32_t am = amax_in ? absb(amax_in[b.slot]) : slots[b.slot];
-    float r, sc;
-    scale_pair(am, fmax, r, sc);
-    const bool bad = am >= 0x7F800000u;
-    const bool writer = (threadIdx.x & 63) == 0 && (block512 || (c == t.chunk_start[b.tensor] && threadIdx.x == 0));
-    if (writer) {
-      scales[b.slot] = sc;
-      if (amax_out) amax_out[b.slot] = __uint_as_float(slots[b.slot]);
-      if (bad) atomicOr(t.flags, (uint32_t)GIFT_FLAG_NONFINITE);
-    }
-    const float* x = g + b.base;
-    uint8_t* q = codes + b.base;
+  BRange r(t);
+  for (; r.c < r.end; r.advance(t)) {
+    const BLane L(t, r);
+    const float* x = g + L.base;
+    uint8_t* q = codes + L.base;
+    float4 v[kBH];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t e = b.e + 256 * h;
-      if (e >= b.numel) continue;
-      const float4 v = *reinterpret_cast<const float4*>(x + e);
-      *reinterpret_cast<uint32_t*>(q + e) = bad ? 0x7F7F7F7Fu : codes4<FMT>(v, r, fmax);
+    for (int h = 0; h < kBH; ++h)
+      v[h] = L.live(h) ? *reinterpret_cast<const float4*>(x + L.e0 + 256 * h) : make_float4(0.f, 0.f, 0.f, 0.f);
+    // the scale of each half of the wave's range (one block each; per
+    // tensor both are the tensor's)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (!L.live(2 * half)) continue;   // this lane has no element in the block (lane 0: the block is absent)
+      const int64_t slot = t.scale_off[r.i] + (block512 ? 8 * L.k + 2 * (threadIdx.x >> 6) + half : 0);
+      const uint32_t am = amax_in ? absb(amax_in[slot]) : slots[slot];
+      float rr, sc;
+      scale_pair(am, fmax, rr, sc);
+      const bool bad = am >= 0x7F800000u;
+      const bool writer = (threadIdx.x & 63) == 0 &&
+                          (block512 || (L.k == 0 && threadIdx.x == 0 && half == 0));
+      if (writer) {
+        scales[slot] = sc;
+        if (amax_out) amax_out[slot] = __uint_as_float(slots[slot]);
+        if (bad) atomicOr(t.flags, (uint32_t)GIFT_FLAG_NONFINITE);
+      }
+#pragma unroll
+      for (int h = 2 * half; h < 2 * half + 2; ++h)
+        if (L.live(h))
+          *reinterpret_cast<uint32_t*>(q + L.e0 + 256 * h) = bad ? 0x7F7F7F7Fu : codes4<FMT>(v[h], rr, fmax);
     }
   }
 }
 
 // U = (1/R) sum_r s_r dec(q_r), replicas in increasing r (from replica 0's
-// term, so a lone -0 stays -0).
-template <int FMT>
+// term, so a lone -0 stays -0).  RC: the replica count when known at
+// compile time (0: R at run time).
+template <int FMT, int RC>
 __global__ void __launch_bounds__(256) k_bucket_dequant_sum(BucketTable t, const uint8_t* __restrict__ codes,
                                                             int64_t code_stride, const float* __restrict__ scales,
-                                                            int64_t scale_stride, int R, int block512,
+                                                            int64_t scale_stride, int Rrt, int block512,
                                                             float* __restrict__ out, float invR) {
-  for (int64_t c = blockIdx.x; c < t.chunks; c += gridDim.x) {
-    const BChunk b = bucket_chunk(t, c, block512);
-    if (!b.blk_live) continue;
-    float acc[8];
-    const bool live1 = b.e + 256 < b.numel;
+  const int R = RC > 0 ? RC : Rrt;
+  BRange rg(t);
+  for (; rg.c < rg.end; rg.advance(t)) {
+    const BLane L(t, rg);
+    const int64_t s0 = t.scale_off[rg.i] + (block512 ? 8 * L.k + 2 * (threadIdx.x >> 6) : 0);
+    const int64_t s1 = s0 + (block512 ? 1 : 0);
+    float acc[kBH][4];
+#pragma unroll (RC > 0 ? RC : 1)
     for (int r = 0; r < R; ++r) {
-      const uint8_t* q = codes + (int64_t)r * code_stride + b.base;
-      const float s = scales[(int64_t)r * scale_stride + b.slot];
-      const uint32_t w0 = b.e < b.numel ? *reinterpret_cast<const uint32_t*>(q + b.e) : 0u;
-      const uint32_t w1 = live1 ? *reinterpret_cast<const uint32_t*>(q + b.e + 256) : 0u;
+      const uint8_t* q = codes + (int64_t)r * code_stride + L.base;
+      const float sa = scales[(int64_t)r * scale_stride + s0];
+      const float sb = L.live(2) ? scales[(int64_t)r * scale_stride + s1] : 0.0f;
+      uint32_t w[kBH];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float v0 = dec_fp8<FMT>((w0 >> (8 * j)) & 0xFFu), v1 = dec_fp8<FMT>((w1 >> (8 * j)) & 0xFFu);
-        acc[j] = r == 0 ? s * v0 : __builtin_fmaf(s, v0, acc[j]);
-        acc[4 + j] = r == 0 ? s * v1 : __builtin_fmaf(s, v1, acc[4 + j]);
+      for (int h = 0; h < kBH; ++h) w[h] = L.live(h) ? *reinterpret_cast<const uint32_t*>(q + L.e0 + 256 * h) : 0u;
+#pragma unroll
+      for (int h = 0; h < kBH; ++h) {
+        const float s = h < 2 ? sa : sb;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float v = dec_fp8<FMT>((w[h] >> (8 * j)) & 0xFFu);
+          acc[h][j] = r == 0 ? s * v : __builtin_fmaf(s, v, acc[h][j]);
+        }
       }
     }
-    float* o = out + b.base;
-    if (b.e < b.numel)
-      *reinterpret_cast<float4*>(o + b.e) = make_float4(acc[0] * invR, acc[1] * invR, acc[2] * invR, acc[3] * invR);
-    if (live1)
-      *reinterpret_cast<float4*>(o + b.e + 256) =
-          make_float4(acc[4] * invR, acc[5] * invR, acc[6] * invR, acc[7] * invR);
+    float* o = out + L.base;
+#pragma unroll
+    for (int h = 0; h < kBH; ++h)
+      if (L.live(h))
+        *reinterpret_cast<float4*>(o + L.e0 + 256 * h) =
+            make_float4(acc[h][0] * invR, acc[h][1] * invR, acc[h][2] * invR, acc[h][3] * invR);
   }
 }
 
@@ -200,17 +258,38 @@ hipError_t launch_bucket_quantize(const BucketTable& t, const float* g, int fmt,
   return hipGetLastError();
 }
 
+template <int FMT>
+static void launch_bds(const BucketTable& t, const uint8_t* codes, int64_t cst, const float* scales, int64_t sst,
+                       int R, int block512, float* out, dim3 gd, hipStream_t s) {
+  const float invR = 1.0f / (float)R;
+  switch (R) {
+    case 4:
+      hipLaunchKernelGGL((k_bucket_dequant_sum<FMT, 4>), gd, dim3(256), 0, s, t, codes, cst, scales, sst, R, block512,
+                         out, invR);
+      break;
+    case 8:
+      hipLaunchKernelGGL((k_bucket_dequant_sum<FMT, 8>), gd, dim3(256), 0, s, t, codes, cst, scales, sst, R, block512,
+                         out, invR);
+      break;
+    case 16:
+      hipLaunchKernelGGL((k_bucket_dequant_sum<FMT, 16>), gd, dim3(256), 0, s, t, codes, cst, scales, sst, R,
+                         block512, out, invR);
+      break;
+    default:
+      hipLaunchKernelGGL((k_bucket_dequant_sum<FMT, 0>), gd, dim3(256), 0, s, t, codes, cst, scales, sst, R, block512,
+                         out, invR);
+  }
+}
+
 hipError_t launch_bucket_dequant_sum(const BucketTable& t, const uint8_t* codes, int64_t code_stride,
                                      const float* scales, int64_t scale_stride, int R, int fmt, int block512,
                                      float* out, int cus, hipStream_t s) {
   if (t.chunks == 0) return hipSuccess;
-  const float invR = 1.0f / (float)R;
+  const dim3 gd(bucket_grid(t, cus));
   if (fmt == 0)
-    hipLaunchKernelGGL(k_bucket_dequant_sum<0>, dim3(bucket_grid(t, cus)), dim3(256), 0, s, t, codes, code_stride,
-                       scales, scale_stride, R, block512, out, invR);
+    launch_bds<0>(t, codes, code_stride, scales, scale_stride, R, block512, out, gd, s);
   else
-    hipLaunchKernelGGL(k_bucket_dequant_sum<1>, dim3(bucket_grid(t, cus)), dim3(256), 0, s, t, codes, code_stride,
-                       scales, scale_stride, R, block512, out, invR);
+    launch_bds<1>(t, codes, code_stride, scales, scale_stride, R, block512, out, gd, s);
   return hipGetLastError();
 }
 
