@@ -84,38 +84,62 @@ __global__ void __launch_bounds__(256) k_stats_valu(const TX* __restrict__ x, in
 // ---------------------------------------------------------------------------
 // bf16 matrix-core statistics: S += X^T X for 256 x 256 output tiles on or
 // below the diagonal, one workgroup (4 waves, 2 x 2) per tile.
-//  * X is token-major; the MFMA (16x16x32 bf16) wants 8 consecutive tokens
-//    per lane, so every thread loads 4 tokens x 8 columns (four 16-byte
-//    row segments), transposes them in registers (v_perm) and writes 8-byte
-//    column runs into LDS ([column][token], 64 tokens per stage, padded).
-//  * Two LDS stages: while a stage is multiplied, the next one's global
-//    loads are in flight in registers.
+//  * X is token-major and stays so in LDS: each side of a stage is 32 token
+//    rows x 256 columns (512 bytes a row), filled by direct global-to-LDS
+//    loads (16 bytes a lane; no registers), four stages deep: three stages
+//    of loads are in flight while one is multiplied.
+//  * The 32x32x16 bf16 MFMA wants 8 consecutive tokens of one column per
+//    lane.  The transposing LDS read (ds_read_b64_tr_b16) gives them: in a
+//    16-lane group, lane j points at 4 columns of token k0 + j / 4, and
+//    lane i receives column C + i at tokens k0 .. k0 + 3.  Two such reads
+//    make one operand.
+//  * Row t of a stage holds global 16-byte chunk g at slot g ^ 4 (t % 4):
+//    the loads write whole rows (the swizzle is in the global addresses)
+//    and the transposing reads of 32 lanes touch all 64 banks once.
 //  * Wave (wm, wn) owns rows 128 wm .. +127 and columns 128 wn .. +127 of
-//    the tile: 8 x 8 MFMA tiles, 256 fp32 accumulators per lane.
+//    the tile: 4 x 4 MFMA tiles of 32 x 32, 256 fp32 accumulators per
+//    lane.  With one wave per SIMD the 32 x 32 shape keeps the matrix pipe
+//    fuller than 16 x 16 (measured: about 0.84 against 0.55 of the bf16
+//    peak for back-to-back independent products).
 //  * bf16 x bf16 products are exact in fp32; sums are fp32 (exact for the
 //    integer-valued inputs of the exactness test).
-//  * Tokens past T read as zero (buffer bounds); columns past n are zeroed
-//    after the load and never written back; diagonal tiles write only i >= j.
+//  * Tokens past T and columns past n read as zero (buffer bounds); columns
+//    past n are never written back; diagonal tiles write only i >= j.
 // ---------------------------------------------------------------------------
 typedef __bf16 sbf16x8 __attribute__((ext_vector_type(8)));
-typedef float sfloatx4 __attribute__((ext_vector_type(4)));
-typedef int sint32x4 __attribute__((ext_vector_type(4)));
-typedef int sint32x2 __attribute__((ext_vector_type(2)));
+typedef float sfloatx16 __attribute__((ext_vector_type(16)));
+typedef short sshort4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSB = 256;            // output tile
-constexpr int kSK = 64;             // tokens per stage
-constexpr int kSPad = kSK;          // LDS row pitch (bf16): 128 bytes, one pass over the 32 banks
-// The 16-byte token chunks of LDS row c are stored XOR-swizzled by
-// f(c) = (c ^ c >> 3) & 7: the fragment reads (8 consecutive rows, one chunk)
-// and the transposed writes (rows 8 apart, one chunk) both touch 8 distinct
-// chunk positions, i.e. all 32 banks once.
-__device__ __forceinline__ int swz(int c) { return (c ^ (c >> 3)) & 7; }
+constexpr int kSK = 32;             // tokens per stage
+constexpr int kSStages = 4;         // LDS stages (three in flight)
+constexpr int kSRow = kSB * 2;      // bytes per token row of a side tile
+constexpr int kSSide = kSK * kSRow; // bytes per side and stage (16 KiB)
+constexpr int kOffOOB = (int)0x80000000u;   // an offset past any buffer: the load returns zeros
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t stats_rsrc(const void* p, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)(uint32_t)bytes, 0x00020000);
 }
 
 constexpr int kStatsSpinLimit = 1 << 22;
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef int sint32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte global-to-LDS load of every lane: lane l's 16 bytes from rsrc at
+// voff land at LDS byte lds + 16 l (lds wave-uniform, through M0).  Issued
+// as inline assembly so that the compiler does not track these LDS writes
+// (it would wait for every load in flight before each LDS read); the kernel
+// orders them itself with s_waitcnt vmcnt and barriers.
+__device__ __forceinline__ void lds_load16(sint32x4 rsrc, uint32_t lds, int voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds), "v"(voff), "s"(rsrc)
+      : "memory", "m0");
+}
 
 // Stages [s_a, s_b) of output tile (bi, bj), added into S.  A tile whose
 // stages are split over consecutive workgroups is added in a fixed order:
@@ -125,125 +149,118 @@ constexpr int kStatsSpinLimit = 1 << 22;
 template <bool DIAG>
 __device__ __forceinline__ void stats_segment(const uint16_t* __restrict__ x, int64_t T, int64_t ld, int n,
                                               float* __restrict__ S, int bi, int bj, int s_a, int s_b, int nst,
-                                              uint16_t (*As)[kSB][kSPad], uint16_t (*Bs)[kSB][kSPad],
-                                              unsigned* __restrict__ sync, unsigned epoch,
+                                              char* As, char* Bs, unsigned* __restrict__ sync, unsigned epoch,
                                               uint32_t* __restrict__ flags) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int row0 = bi * kSB, col0 = bj * kSB;   // i (A side) and j (B side) origins
-  // staging: block u (0, 1) of this thread: tokens 4 tg .. 4 tg + 3, columns
-  // 8 ig .. 8 ig + 7.  Eight consecutive lanes read 128 contiguous bytes of
-  // one token row; a 16-lane LDS write cycle covers 8 column groups x 2 token
-  // groups.
-  int tg[2], ig[2];
+  // loads: instruction q of wave w fills slots 64 (4 w + q) .. + 63 of a
+  // side tile: token row t = 2 (4 w + q) + lane / 32, slot lane % 32, which
+  // holds global chunk (lane % 32) ^ 4 (t % 4) of that row
+  int voff_a[4], voff_b[4];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int b = tid + 256 * u;
-    ig[u] = (b & 7) + 8 * ((b >> 7) & 3);
-    tg[u] = (b >> 3) & 15;
+  for (int q = 0; q < 4; ++q) {
+    const int t = 2 * (4 * wave + q) + (lane >> 5);
+    const int gch = (lane & 31) ^ (4 * (t & 3));
+    const int ca = row0 + 8 * gch, cb = col0 + 8 * gch;
+    voff_a[q] = ca < n ? (int)((t * ld + ca) * 2) : kOffOOB;
+    voff_b[q] = cb < n ? (int)((t * ld + cb) * 2) : kOffOOB;
   }
-  struct Regs {
-    sint32x4 a[2][4], b[2][4];
-  };
-  // Stages past T read through an empty buffer resource (zeros, no traffic).
-  auto gload = [&](int64_t t0, Regs& R) {
+  // Stage st into LDS buffer buf (stages past T read zeros, no traffic).
+  const uint32_t lds_a = (uint32_t)(uintptr_t)(lds_void*)As, lds_b = (uint32_t)(uintptr_t)(lds_void*)Bs;
+  auto issue = [&](int st, int buf) {
+    const int64_t t0 = (int64_t)st * kSK;
     const int64_t rows = T - t0 < kSK ? T - t0 : kSK;
-    const auto rs = stats_rsrc(x + (rows > 0 ? t0 * ld : 0), rows > 0 ? rows * ld * 2 : 0);
+    const uint64_t base = (uint64_t)(uintptr_t)(x + (rows > 0 ? t0 * ld : 0));
+    // buffer descriptor: base, stride 0, bytes, raw-buffer flags
+    const sint32x4 rs = {__builtin_amdgcn_readfirstlane((int)(uint32_t)base),
+                         __builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32) & 0xFFFF),
+                         __builtin_amdgcn_readfirstlane((int)(uint32_t)(rows > 0 ? rows * ld * 2 : 0)),
+                         0x00020000};
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t slot = (uint32_t)(buf * kSSide + 64 * (4 * wave + q) * 16);
+      lds_load16(rs, __builtin_amdgcn_readfirstlane(lds_a + slot), voff_a[q]);
+      if constexpr (!DIAG) lds_load16(rs, __builtin_amdgcn_readfirstlane(lds_b + slot), voff_b[q]);
+    }
+  };
+  constexpr int kLoads = DIAG ? 4 : 8;   // loads per thread per stage
+  sfloatx16 acc[4][4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 4 * tg[u] + r;
-        R.a[u][r] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)((t * ld + row0 + 8 * ig[u]) * 2), 0, 0);
-        if constexpr (!DIAG)
-          R.b[u][r] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)((t * ld + col0 + 8 * ig[u]) * 2), 0, 0);
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+  // Operand reads.  Lane l (group g = l / 16, i = l % 16) points at token
+  // 16 ks + 8 (g / 2) + 4 r + i / 4 and column 128 w + 32 mt + 16 (g % 2) +
+  // 4 (i % 4) of a side tile; with the swizzle its byte address is
+  //   8192 ks + 2048 r + [4096 (g / 2) + 512 (i / 4) + 16 (2 (g % 2) +
+  //   (i % 4) / 2 + 16 w) + 8 (i % 2)] + 64 (mt ^ (i / 4)):
+  // per lane, four offsets per side (one per mt), the rest immediate.
+  const int g = lane >> 4, li = lane & 15;
+  int offa[4], offb[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int common = 4096 * (g >> 1) + 512 * (li >> 2) + 16 * (2 * (g & 1) + ((li & 3) >> 1)) + 8 * (li & 1) +
+                       64 * (mt ^ (li >> 2));
+    offa[mt] = common + 256 * wm;
+    offb[mt] = common + 256 * wn;
+  }
+  auto frag = [&](const char* base, int off, int ks) {
+    const sshort4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) sshort4*)(base + off + 8192 * ks));
+    const sshort4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) sshort4*)(base + off + 8192 * ks + 2048));
+    const sshort4 v[2] = {lo, hi};
+    return __builtin_bit_cast(sbf16x8, v);
+  };
+  auto mfma_stage = [&](int buf) {
+    const char* LA = As + buf * kSSide;
+    const char* LB = (DIAG ? As : Bs) + buf * kSSide;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      sbf16x8 fa[4], fb[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        fb[t] = frag(LB, offb[t], ks);
+        fa[t] = frag(LA, offa[t], ks);
       }
-  };
-  // Columns past n are zeroed here, where the loaded registers are used (a
-  // select right after the load would wait for it).
-  auto lstore = [&](uint16_t (*L)[kSPad], const sint32x4 (*v)[4], int cbase) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const bool ok = cbase + 8 * ig[u] < n;
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // column 8 ig + 2w: low halves; column 8 ig + 2w + 1: high halves
-        const uint32_t a0 = ok ? (uint32_t)v[u][0][w] : 0u, a1 = ok ? (uint32_t)v[u][1][w] : 0u;
-        const uint32_t a2 = ok ? (uint32_t)v[u][2][w] : 0u, a3 = ok ? (uint32_t)v[u][3][w] : 0u;
-        const uint32_t l0 = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
-        const uint32_t l1 = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
-        const uint32_t h0 = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
-        const uint32_t h1 = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
-        const int c0 = 8 * ig[u] + 2 * w, c1 = c0 + 1;
-        const int ch = tg[u] >> 1, half = (tg[u] & 1) * 4;
-        *reinterpret_cast<sint32x2*>(&L[c0][8 * (ch ^ swz(c0)) + half]) = (sint32x2){(int)l0, (int)l1};
-        *reinterpret_cast<sint32x2*>(&L[c1][8 * (ch ^ swz(c1)) + half]) = (sint32x2){(int)h0, (int)h1};
-      }
+        for (int nt = 0; nt < 4; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mt], fb[nt], acc[mt][nt], 0, 0, 0);
     }
   };
-  sfloatx4 acc[8][8];
-#pragma unroll
-  for (int a = 0; a < 8; ++a)
-#pragma unroll
-    for (int b = 0; b < 8; ++b) acc[a][b] = (sfloatx4){0.f, 0.f, 0.f, 0.f};
-  const int lr = lane & 15, lq = lane >> 4;
-  // One 32-token half of a stage: the 8 B fragments are loaded first, the A
-  // fragments stream two row tiles ahead of their MFMAs.
-  auto half_mfma = [&](uint16_t (*LA)[kSPad], uint16_t (*LB)[kSPad], int kk) {
-    sbf16x8 fb[8];
-    const int ch = kk / 8 + lq;   // this lane's 8-token chunk
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const int c = 128 * wn + 16 * nt + lr;
-      fb[nt] = __builtin_bit_cast(sbf16x8, *reinterpret_cast<const sint32x4*>(&LB[c][8 * (ch ^ swz(c))]));
-    }
-    auto fa_of = [&](int mt) {
-      const int c = 128 * wm + 16 * mt + lr;
-      return __builtin_bit_cast(sbf16x8, *reinterpret_cast<const sint32x4*>(&LA[c][8 * (ch ^ swz(c))]));
-    };
-    sbf16x8 f0 = fa_of(0), f1 = fa_of(1);
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      const sbf16x8 f2 = fa_of(mt + 2 < 8 ? mt + 2 : 7);
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt)
-        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f0, fb[nt], acc[mt][nt], 0, 0, 0);
-      f0 = f1;
-      f1 = f2;
-    }
-  };
-  // Stage pipeline: LDS holds stages st (being multiplied) and st + 1; the
-  // registers hold the global loads of stage st + 2.  The transposed stores
-  // of stage st + 1 are issued after the first half's MFMAs, so they run
-  // while the matrix pipe works; the next global loads follow them.  The
-  // loop body has no branch: a store of a stage past the end lands in a
-  // buffer nobody reads.
-  Regs R0;
+  // Pipeline: stages s_a .. s_a + 2 are requested up front; each iteration
+  // waits for its own stage (the two later ones may stay in flight), syncs,
+  // requests stage st + 3 into the buffer of stage st - 1 and multiplies.
   __syncthreads();   // the previous segment's waves are done with the LDS stages
-  gload((int64_t)s_a * kSK, R0);
-  lstore(As[0], R0.a, row0);
-  if constexpr (!DIAG) lstore(Bs[0], R0.b, col0);
-  gload((int64_t)(s_a + 1) * kSK, R0);
-  auto iter = [&](int st, int buf) {
-    __syncthreads();   // stage st is in LDS; nobody reads buf ^ 1 any more
-    uint16_t (*LA)[kSPad] = As[buf];
-    uint16_t (*LB)[kSPad] = DIAG ? As[buf] : Bs[buf];
-    half_mfma(LA, LB, 0);
-    lstore(As[buf ^ 1], R0.a, row0);
-    if constexpr (!DIAG) lstore(Bs[buf ^ 1], R0.b, col0);
-    __builtin_amdgcn_sched_barrier(0);   // the prefetch registers are free before they are reloaded
-    gload((int64_t)(st + 2) * kSK, R0);
-    half_mfma(LA, LB, 32);
-  };
-  for (int st = s_a; st < s_b; ++st) iter(st, (st - s_a) & 1);
-  const int g = blockIdx.x, tid2 = threadIdx.x;
+#pragma unroll
+  for (int p = 0; p < kSStages - 1; ++p) issue(s_a + p, p);
+  for (int st = s_a; st < s_b; ++st) {
+    const int buf = (st - s_a) & (kSStages - 1);
+    if constexpr (DIAG) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kLoads & 0xF) | ((2 * kLoads >> 4) << 14));
+    else __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kLoads & 0xF) | ((2 * kLoads >> 4) << 14));
+    __syncthreads();
+    issue(st + kSStages - 1, (buf + kSStages - 1) & (kSStages - 1));
+    mfma_stage(buf);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // drain the loads past the range before the LDS is reused
+  const int gw = blockIdx.x, tid2 = threadIdx.x;
+  // A tile shared with another workgroup is read and written with
+  // device-coherent (agent-scope relaxed atomic) accesses, and the hand-off
+  // is ordered by waiting for those accesses to complete before the flag is
+  // raised, and by reading only after the flag is seen: no cache-wide
+  // release / acquire (on this multi-die device those write back and
+  // invalidate a whole L2 and stall every other workgroup on it).
+  const bool shared = s_a > 0 || s_b < nst;
   if (s_b < nst) {
     // the next workgroup holds the later stages of this tile: it adds first
     if (tid2 == 0) {
       int spins = 0;
-      // relaxed polls (an acquire per poll would invalidate the caches each
-      // time); one acquire fence once the flag is seen
-      while (__hip_atomic_load(sync + g + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
+      while (__hip_atomic_load(sync + gw + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
         if (++spins > kStatsSpinLimit) {
           atomicOr(flags, (uint32_t)GIFT_FLAG_SPIN_TIMEOUT);
           break;
@@ -252,45 +269,85 @@ __device__ __forceinline__ void stats_segment(const uint16_t* __restrict__ x, in
       }
     }
     __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
-  // S += acc: element (i, j) = (4 (lane / 16) + e, lane % 16) of MFMA tile (mt, nt)
+  // S += acc: register v of MFMA tile (mt, nt) is element
+  // (8 (v / 4) + 4 (lane / 32) + v % 4, lane % 32) of the 32 x 32 tile
+  const int lr = lane & 31, lh = lane >> 5;
+  if (shared) {
+    // device-coherent loads and stores (sc0 sc1), 64 loads in flight per
+    // row block; elements outside the output go to an offset past the end
+    const uint32_t nbytes = (uint32_t)((int64_t)n * n * 4);
+    const auto rs = stats_rsrc(S, nbytes);
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
+    for (int mt = 0; mt < 4; ++mt) {
+      int off[4][16];
+      float v[4][16];
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
+      for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = row0 + 128 * wm + 16 * mt + 4 * (lane >> 4) + e;
-        const int j = col0 + 128 * wn + 16 * nt + lr;
-        if (i < n && j < n && (!DIAG || i >= j)) {
-          float* p = S + (int64_t)i * n + j;
-          *p += acc[mt][nt][e];
+        for (int e = 0; e < 16; ++e) {
+          const int i = row0 + 128 * wm + 32 * mt + 8 * (e / 4) + 4 * lh + e % 4;
+          const int j = col0 + 128 * wn + 32 * nt + lr;
+          const bool ok = i < n && j < n && (!DIAG || i >= j);
+          off[nt][e] = ok ? (int)(uint32_t)(((int64_t)i * n + j) * 4) : (int)nbytes;
+          v[nt][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off[nt][e], 0, 17));
         }
-      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[nt][e] + acc[mt][nt][e]), rs, off[nt][e], 0, 17);
+    }
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int i = row0 + 128 * wm + 32 * mt + 8 * (e / 4) + 4 * lh + e % 4;
+          const int j = col0 + 128 * wn + 32 * nt + lr;
+          if (i < n && j < n && (!DIAG || i >= j)) S[(int64_t)i * n + j] += acc[mt][nt][e];
+        }
+  }
   if (s_a > 0) {
-    // the previous workgroup (earlier stages of this tile) adds after us
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    // the previous workgroup (earlier stages of this tile) adds after us:
+    // every store of this workgroup has completed before the flag is set
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (tid2 == 0) __hip_atomic_store(sync + g, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid2 == 0) __hip_atomic_store(sync + gw, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// Persistent: workgroup g takes an equal, contiguous range of the
-// (tile, stage) units (tiles in lower-triangle order, stages in token
-// order), so every compute unit gets the same amount of work.  All
-// workgroups are resident (one per compute unit: the LDS stages fill it).
+// Persistent: workgroup g first takes whole tiles in rounds (tile g, g + G,
+// ... while a full round of G tiles remains), so the workgroups of a round
+// walk the token stages in step and share each stage's columns through the
+// L2; the tiles left over (fewer than G) are cut into equal, contiguous
+// ranges of (tile, stage) units, one per workgroup (in lower-triangle tile
+// order, stages in token order).  All workgroups are resident (one per
+// compute unit: the LDS stages fill it).
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 k_stats_mfma(const uint16_t* __restrict__ x, int64_t T, int64_t ld, int n, float* __restrict__ S, int ntiles,
              unsigned* __restrict__ sync, unsigned epoch, uint32_t* __restrict__ flags) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kSB][kSPad];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kSB][kSPad];
+  __shared__ __attribute__((aligned(16))) char As[kSStages * kSSide];
+  __shared__ __attribute__((aligned(16))) char Bs[kSStages * kSSide];
   const int nst = (int)cdiv(T, kSK);
-  const int64_t U = (int64_t)ntiles * nst, G = gridDim.x, g = blockIdx.x;
+  const int G = gridDim.x, gid = blockIdx.x;
+  const int rounds = ntiles / G;
+  for (int rd = 0; rd < rounds; ++rd) {
+    int bi, bj;
+    tri_tile(rd * G + gid, bi, bj);
+    if (bi == bj)
+      stats_segment<true>(x, T, ld, n, S, bi, bj, 0, nst, nst, As, Bs, sync, epoch, flags);
+    else
+      stats_segment<false>(x, T, ld, n, S, bi, bj, 0, nst, nst, As, Bs, sync, epoch, flags);
+  }
+  const int first = rounds * G;
+  const int64_t U = (int64_t)(ntiles - first) * nst;
   const int64_t base = U / G, rem = U % G;
-  const int64_t u0 = g * base + (g < rem ? g : rem), u1 = u0 + base + (g < rem ? 1 : 0);
+  const int64_t u0 = gid * base + (gid < rem ? gid : rem), u1 = u0 + base + (gid < rem ? 1 : 0);
   for (int64_t u = u0; u < u1;) {
-    const int tile = (int)(u / nst), s_a = (int)(u % nst);
+    const int tile = first + (int)(u / nst), s_a = (int)(u % nst);
     const int s_b = (int)((u1 - u) < (int64_t)(nst - s_a) ? s_a + (u1 - u) : nst);
     int bi, bj;
     tri_tile(tile, bi, bj);
@@ -311,10 +368,7 @@ hipError_t launch_stats(const void* x, int dtype, int64_t T, int64_t ld, int n, 
     const int nb2 = (int)cdiv(n, kSB);
     const int ntiles = nb2 * (nb2 + 1) / 2;
     const int64_t units = (int64_t)ntiles * cdiv(T, kSK);
-    // at most two workgroups per tile: a tile's hand-off chain stays one link
-    // long (each link costs a cache write-back and a cold read of the tile)
     int grid = cus < kStatsMaxGroups ? cus : kStatsMaxGroups;
-    if (2 * ntiles < grid) grid = 2 * ntiles;
     if (units < grid) grid = (int)units;
     hipLaunchKernelGGL(k_stats_mfma, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const uint16_t*>(x), T,
                        ld, n, S, ntiles, sync, epoch, flags);
