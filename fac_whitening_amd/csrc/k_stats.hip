@@ -86,8 +86,10 @@ __global__ void __launch_bounds__(256) k_stats_valu(const TX* __restrict__ x, in
 // below the diagonal, one workgroup (4 waves, 2 x 2) per tile.
 //  * X is token-major and stays so in LDS: each side of a stage is 32 token
 //    rows x 256 columns (512 bytes a row), filled by direct global-to-LDS
-//    loads (16 bytes a lane; no registers), four stages deep: three stages
-//    of loads are in flight while one is multiplied.
+//    loads (16 bytes a lane; no registers), five stages deep: four stages
+//    of loads are in flight while one is multiplied.  The LDS pipe, not the
+//    matrix pipe, bounds this loop: the transposing 8-byte reads run at
+//    about 48 bytes a clock per compute unit (16-byte reads about 130).
 //  * The 32x32x16 bf16 MFMA wants 8 consecutive tokens of one column per
 //    lane.  The transposing LDS read (ds_read_b64_tr_b16) gives them: in a
 //    16-lane group, lane j points at 4 columns of token k0 + j / 4, and
@@ -112,7 +114,7 @@ typedef short sshort4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSB = 256;            // output tile
 constexpr int kSK = 32;             // tokens per stage
-constexpr int kSStages = 4;         // LDS stages (three in flight)
+constexpr int kSStages = 5;         // LDS stages (four in flight; 160 KiB)
 constexpr int kSRow = kSB * 2;      // bytes per token row of a side tile
 constexpr int kSSide = kSK * kSRow; // bytes per side and stage (16 KiB)
 constexpr int kOffOOB = (int)0x80000000u;   // an offset past any buffer: the load returns zeros
@@ -169,21 +171,28 @@ __device__ __forceinline__ void stats_segment(const uint16_t* __restrict__ x, in
   }
   // Stage st into LDS buffer buf (stages past T read zeros, no traffic).
   const uint32_t lds_a = (uint32_t)(uintptr_t)(lds_void*)As, lds_b = (uint32_t)(uintptr_t)(lds_void*)Bs;
-  auto issue = [&](int st, int buf) {
+  // buffer descriptor of stage st: base, stride 0, bytes, raw-buffer flags
+  auto stage_rsrc = [&](int st) {
     const int64_t t0 = (int64_t)st * kSK;
     const int64_t rows = T - t0 < kSK ? T - t0 : kSK;
     const uint64_t base = (uint64_t)(uintptr_t)(x + (rows > 0 ? t0 * ld : 0));
-    // buffer descriptor: base, stride 0, bytes, raw-buffer flags
     const sint32x4 rs = {__builtin_amdgcn_readfirstlane((int)(uint32_t)base),
                          __builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32) & 0xFFFF),
                          __builtin_amdgcn_readfirstlane((int)(uint32_t)(rows > 0 ? rows * ld * 2 : 0)),
                          0x00020000};
+    return rs;
+  };
+  // load k of this thread's share of a stage: A side k < 4, B side k - 4
+  auto issue_one = [&](const sint32x4& rs, int buf, int k) {
+    const int q = k & 3;
+    const uint32_t slot = (uint32_t)(buf * kSSide + 64 * (4 * wave + q) * 16);
+    if (k < 4) lds_load16(rs, __builtin_amdgcn_readfirstlane(lds_a + slot), voff_a[q]);
+    else lds_load16(rs, __builtin_amdgcn_readfirstlane(lds_b + slot), voff_b[q]);
+  };
+  auto issue = [&](int st, int buf) {
+    const sint32x4 rs = stage_rsrc(st);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t slot = (uint32_t)(buf * kSSide + 64 * (4 * wave + q) * 16);
-      lds_load16(rs, __builtin_amdgcn_readfirstlane(lds_a + slot), voff_a[q]);
-      if constexpr (!DIAG) lds_load16(rs, __builtin_amdgcn_readfirstlane(lds_b + slot), voff_b[q]);
-    }
+    for (int k = 0; k < (DIAG ? 4 : 8); ++k) issue_one(rs, buf, k);
   };
   constexpr int kLoads = DIAG ? 4 : 8;   // loads per thread per stage
   sfloatx16 acc[4][4];
@@ -215,37 +224,67 @@ __device__ __forceinline__ void stats_segment(const uint16_t* __restrict__ x, in
     const sshort4 v[2] = {lo, hi};
     return __builtin_bit_cast(sbf16x8, v);
   };
-  auto mfma_stage = [&](int buf) {
+  struct Frags {
+    sbf16x8 a[4], b[4];
+  };
+  auto load_frags = [&](Frags& F, int buf, int ks) {
     const char* LA = As + buf * kSSide;
     const char* LB = (DIAG ? As : Bs) + buf * kSSide;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      sbf16x8 fa[4], fb[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        fb[t] = frag(LB, offb[t], ks);
-        fa[t] = frag(LA, offa[t], ks);
-      }
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mt], fb[nt], acc[mt][nt], 0, 0, 0);
+    for (int t = 0; t < 4; ++t) {
+      F.b[t] = frag(LB, offb[t], ks);
+      F.a[t] = frag(LA, offa[t], ks);
     }
   };
-  // Pipeline: stages s_a .. s_a + 2 are requested up front; each iteration
-  // waits for its own stage (the two later ones may stay in flight), syncs,
-  // requests stage st + 3 into the buffer of stage st - 1 and multiplies.
+  // products of row tiles mt0 .. mt1 - 1 with F; after every fourth one the
+  // next load of the stage being prefetched (loads k .. kmax - 1)
+  auto products = [&](const Frags& F, int mt0, int mt1, const sint32x4& lrs, int lbuf, int& k) {
+#pragma unroll
+    for (int mt = mt0; mt < mt1; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.a[mt], F.b[nt], acc[mt][nt], 0, 0, 0);
+        if (nt == 1 && k < kLoads) {
+          issue_one(lrs, lbuf, k);
+          ++k;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
+  // Pipeline (five LDS stages, four in flight): an iteration multiplies
+  // stage st; the operands of its second 16-token step are read while the
+  // first step multiplies; half way through the second step the wave waits
+  // for stage st + 1 and syncs, and reads that stage's first operands under
+  // the last eight products.  The loads of stage st + 4 (into the buffer of
+  // stage st - 1, free since the previous sync) go out one after every
+  // fourth product.
   __syncthreads();   // the previous segment's waves are done with the LDS stages
 #pragma unroll
   for (int p = 0; p < kSStages - 1; ++p) issue(s_a + p, p);
+  // counts of this wave's loads that may stay in flight
+  constexpr int kAheadStart = (kSStages - 2) * kLoads;                 // stage s_a complete
+  constexpr int kAheadMid = 2 * kLoads + (kLoads > 4 ? 6 : kLoads);     // stage st + 1 complete
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (kAheadStart & 0xF) | ((kAheadStart >> 4) << 14));
+  __syncthreads();
+  Frags F0, F1;
+  load_frags(F0, 0, 0);
+  int buf = 0;
   for (int st = s_a; st < s_b; ++st) {
-    const int buf = (st - s_a) & (kSStages - 1);
-    if constexpr (DIAG) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kLoads & 0xF) | ((2 * kLoads >> 4) << 14));
-    else __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kLoads & 0xF) | ((2 * kLoads >> 4) << 14));
+    const sint32x4 lrs = stage_rsrc(st + kSStages - 1);
+    const int lbuf = buf == 0 ? kSStages - 1 : buf - 1;
+    int k = 0;
+    load_frags(F1, buf, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    products(F0, 0, 4, lrs, lbuf, k);
+    products(F1, 0, 2, lrs, lbuf, k);
+    const int nbuf = buf + 1 == kSStages ? 0 : buf + 1;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's reads of buffer buf are done
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (kAheadMid & 0xF) | ((kAheadMid >> 4) << 14));
     __syncthreads();
-    issue(st + kSStages - 1, (buf + kSStages - 1) & (kSStages - 1));
-    mfma_stage(buf);
+    load_frags(F0, nbuf, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    products(F1, 2, 4, lrs, lbuf, k);
+    buf = nbuf;
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);   // drain the loads past the range before the LDS is reused
   const int gw = blockIdx.x, tid2 = threadIdx.x;
