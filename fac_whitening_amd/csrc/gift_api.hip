@@ -175,6 +175,7 @@ WorkLayout work_layout(const gift_layer_desc& g) {
   if (g.transform == GIFT_CHOL_TWOSIDED) w.tmp = take(m * d * 4);
   if (g.transform == GIFT_LOWRANK) {
     w.ppart = take((size_t)cdiv((int64_t)d, kProjChunk) * m * 32 * 8);
+    w.pc = take(m * 32 * 4);
     const size_t lp = (size_t)lp_of(l_of(g));
     w.Y = take(d * lp * 8);
     w.Q = take(d * lp * 8);
@@ -434,7 +435,8 @@ static gift_status unwhiten_multi(gift_layer_t L, const float* Ub, float* d_out,
       const float* U = reinterpret_cast<const float*>(L->state + L->sl.U);
       const float* coef = reinterpret_cast<const float*>(L->state + L->sl.coef);
       GIFT_HIP(gift::launch_lr_project(Ub, d, m, d, U, g.rank, ppart, s));
-      GIFT_HIP(gift::launch_lr_apply(Ub, d, m, d, U, g.rank, ppart, coef, 1, d_out, ldo, GIFT_SCALE_TENSOR, nullptr,
+      GIFT_HIP(gift::launch_lr_apply(Ub, d, m, d, U, g.rank, ppart, reinterpret_cast<float*>(work + L->wl.pc), coef, 1,
+                                     d_out, ldo, GIFT_SCALE_TENSOR, nullptr,
                                      s));
       break;
     }
@@ -546,7 +548,8 @@ static gift_status encode_impl(gift_layer_t L, const float* d_W, int64_t ldw, in
       const float* U = reinterpret_cast<const float*>(L->state + L->sl.U);
       const float* coef = reinterpret_cast<const float*>(L->state + L->sl.coef);
       GIFT_HIP(gift::launch_lr_project(d_W, ldw, m, d, U, g.rank, ppart, s));
-      GIFT_HIP(gift::launch_lr_apply(d_W, ldw, m, d, U, g.rank, ppart, coef, 0, out, d, amax_scaling, wslots, s));
+      GIFT_HIP(gift::launch_lr_apply(d_W, ldw, m, d, U, g.rank, ppart, reinterpret_cast<float*>(work + L->wl.pc), coef,
+                                     0, out, d, amax_scaling, wslots, s));
       X = out;
       ldx = d;
       if (d_resid) GIFT_HIP(gift::launch_amax(X, ldx, m, d, amax_scaling, d_resid, slots, s));

@@ -10,7 +10,7 @@ namespace gift {
 
 constexpr int kBlock = 128;          // per-block scaling tile (128 x 128)
 constexpr int kMaxRank = 64;         // k + p <= 64 for the small dense solvers
-constexpr int kProjChunk = 256;      // columns per partial in the projection X U
+constexpr int kProjChunk = 512;      // columns per partial in the projection X U
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -87,6 +87,7 @@ struct WorkLayout {
   size_t tile = 0;      // fp32 [m][d]: whitened tensor (encode) or reduced U (decode)
   size_t tmp = 0;       // fp32 [m][d]: second buffer (two-sided)
   size_t ppart = 0;     // fp64 [nchunk][m][k]: projection partials
+  size_t pc = 0;        // fp32 [m][k]: their sum times the coefficients
   size_t amax = 0;      // uint32 [nblk]
   // refresh
   size_t Y = 0, Q = 0, Z = 0;   // fp64 [d][l]
@@ -156,8 +157,9 @@ hipError_t launch_dequant_sum(const uint8_t* codes, int64_t code_stride, const f
 // Low-rank transform pieces: partials of X U, then out = alpha X + (P c) U^T.
 hipError_t launch_lr_project(const float* x, int64_t ldx, int m, int d, const float* U, int k,
                              double* ppart, hipStream_t s);
+// (ppart is first reduced into pc: fp32 [m][32] workspace)
 hipError_t launch_lr_apply(const float* x, int64_t ldx, int m, int d, const float* U, int k,
-                           const double* ppart, const float* coef, int which, float* out,
+                           const double* ppart, float* pc, const float* coef, int which, float* out,
                            int64_t ldo, int scaling, uint32_t* amax_slots, hipStream_t s);
 // Column scaling out = x * v[j] (diagonal transform), with optional amax.
 hipError_t launch_diag_apply(const float* x, int64_t ldx, int m, int d, const float* v, float* out,

@@ -7,8 +7,8 @@
 //     P = X U            (m x k, a skinny contraction over d)
 //     out = alpha X + (P diag(c)) U^T
 // Encode uses (alpha, c) = (rho^-1/2, c_enc), decode (rho^1/2, c_dec).
-// The projection is split over column chunks of 256 and the partial
-// products are summed in a fixed order by the consumer (deterministic).
+// The projection is split over column chunks of kProjChunk and the partial
+// products are summed in a fixed order (deterministic).
 // Partials and their sum are float64: with d in the tens of thousands and
 // heavy-tailed rows, P is a long sum whose float32 rounding, amplified by
 // the cancellation between alpha X and the low-rank term, would reach the
@@ -17,74 +17,110 @@
 
 namespace gift {
 
-// part[chunk][row][c] = sum_{j in chunk} x[row][j] * U[j][c]
-//   KP: padded columns of U; CG: column groups per row (CW = KP / CG columns
-//   per thread); RB = 256 / CG rows per workgroup; KC: chunk length.
-//   FULLK: one workgroup walks every chunk of its rows and writes the whole
-//   sum (part has a single chunk); otherwise one chunk per workgroup.
-template <int KP, int CG, int KC, bool FULLK, typename TU, typename TO>
+// part[chunk][row][c] = sum_{j in chunk} x[row][j] * U[j][c] on the fp64
+// matrix cores (v_mfma_f64_16x16x4f64): lane l supplies Aop[l % 16][l / 16]
+// and Bop[l / 16][l % 16], and slot e of lane l holds D[4 e + l / 16][l % 16].
+// A wave owns 32 rows x 32 columns of one chunk (2 x 2 output tiles).  In
+// each 32-column step, lane l loads 8 consecutive values of its row starting
+// at 8 (l / 16) (two 16-byte loads, 128 contiguous bytes per 4 lanes), and
+// k-step s pairs x[row][j + 8 k + s] with U[j + 8 k + s][c] for k = l / 16:
+// a permutation of the contraction index, applied to both operands.  The
+// fp32 inputs are exact in fp64, so every product is exact and only the
+// fp64 accumulation rounds.  x is read from memory once; U (d x 32 fp32)
+// from L2.
+typedef double pdouble4 __attribute__((ext_vector_type(4)));
+constexpr int kProjRowsWave = 32;
+
 __global__ void __launch_bounds__(256) k_project(const float* __restrict__ x, int64_t ldx, int m, int d,
-                                                 const TU* __restrict__ U, TO* __restrict__ part) {
-  constexpr int CW = KP / CG;
-  constexpr int RB = 256 / CG;
-  __shared__ TU Us[KC][KP];
-  __shared__ float Xs[RB][KC + 1];
-  const int tid = threadIdx.x;
-  const int row0 = blockIdx.y * RB;
-  const int r = tid / CG, cg = tid % CG;
-  TO acc[CW];
+                                                 const float* __restrict__ U, double* __restrict__ part) {
+  constexpr int KP = 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lk = lane >> 4;
+  const int row0 = ((int)blockIdx.y * 4 + wave) * kProjRowsWave;
+  if (row0 >= m) return;   // whole wave; the kernel has no barrier
+  const int chunk = blockIdx.x;
+  const int jb = chunk * kProjChunk, je = min(d, jb + kProjChunk);
+  // rows past m are clamped for the loads and not stored
+  const float* xr0 = x + (int64_t)min(row0 + lr, m - 1) * ldx;
+  const float* xr1 = x + (int64_t)min(row0 + 16 + lr, m - 1) * ldx;
+  pdouble4 acc[2][2];
 #pragma unroll
-  for (int c = 0; c < CW; ++c) acc[c] = TO(0);
-  const int c_begin = FULLK ? 0 : (int)blockIdx.x;
-  const int c_end = FULLK ? (int)cdiv(d, KC) : (int)blockIdx.x + 1;
-  for (int chunk = c_begin; chunk < c_end; ++chunk) {
-    const int j0 = chunk * KC;
-    if (FULLK) __syncthreads();
-    for (int i = tid; i < KC * KP; i += 256) {
-      int j = i / KP, c = i % KP;
-      Us[j][c] = (j0 + j < d) ? U[(int64_t)(j0 + j) * KP + c] : TU(0);
-    }
-    for (int i = tid; i < RB * KC / 4; i += 256) {
-      int rr = i / (KC / 4), j = (i % (KC / 4)) * 4;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (row0 + rr < m && j0 + j < d) v = *reinterpret_cast<const float4*>(x + (int64_t)(row0 + rr) * ldx + j0 + j);
-      Xs[rr][j] = v.x;
-      Xs[rr][j + 1] = v.y;
-      Xs[rr][j + 2] = v.z;
-      Xs[rr][j + 3] = v.w;
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int j = 0; j < KC; ++j) {
-      TO xv = (TO)Xs[r][j];
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int c = 0; c < CW; ++c) acc[c] += xv * (TO)Us[j][cg * CW + c];
+    for (int c = 0; c < 2; ++c) acc[h][c] = (pdouble4){0.0, 0.0, 0.0, 0.0};
+  for (int j0 = jb; j0 < je; j0 += 32) {
+    const int j = j0 + 8 * lk;   // d is a multiple of 8: all 8 in range or none
+    float a0[8], a1[8], b0[8], b1[8];
+    if (j < je) {
+      const float4 p0 = *reinterpret_cast<const float4*>(xr0 + j);
+      const float4 p1 = *reinterpret_cast<const float4*>(xr0 + j + 4);
+      const float4 q0 = *reinterpret_cast<const float4*>(xr1 + j);
+      const float4 q1 = *reinterpret_cast<const float4*>(xr1 + j + 4);
+      a0[0] = p0.x; a0[1] = p0.y; a0[2] = p0.z; a0[3] = p0.w;
+      a0[4] = p1.x; a0[5] = p1.y; a0[6] = p1.z; a0[7] = p1.w;
+      a1[0] = q0.x; a1[1] = q0.y; a1[2] = q0.z; a1[3] = q0.w;
+      a1[4] = q1.x; a1[5] = q1.y; a1[6] = q1.z; a1[7] = q1.w;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        b0[s] = U[(int64_t)(j + s) * KP + lr];
+        b1[s] = U[(int64_t)(j + s) * KP + 16 + lr];
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) a0[s] = a1[s] = b0[s] = b1[s] = 0.f;
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const double A0 = a0[s], A1 = a1[s], B0 = b0[s], B1 = b1[s];
+      acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(A0, B0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(A0, B1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(A1, B0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(A1, B1, acc[1][1], 0, 0, 0);
     }
   }
-  if (row0 + r < m) {
-    const int slot = FULLK ? 0 : (int)blockIdx.x;
-    TO* dst = part + ((int64_t)slot * m + row0 + r) * KP + cg * CW;
 #pragma unroll
-    for (int c = 0; c < CW; ++c) dst[c] = acc[c];
-  }
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = row0 + 16 * h + 4 * e + lk;
+      if (row < m) {
+        double* dst = part + ((int64_t)chunk * m + row) * KP + lr;
+        dst[0] = acc[h][0][e];
+        dst[16] = acc[h][1][e];
+      }
+    }
 }
 
 hipError_t launch_lr_project(const float* x, int64_t ldx, int m, int d, const float* U, int k,
                              double* ppart, hipStream_t s) {
   (void)k;
   if (m == 0 || d == 0) return hipSuccess;
-  dim3 grid((unsigned)cdiv(d, kProjChunk), (unsigned)cdiv(m, 32));
-  hipLaunchKernelGGL((k_project<32, 8, kProjChunk, false, float, double>), grid, dim3(256), 0, s, x, ldx, m, d, U,
-                     ppart);
+  dim3 grid((unsigned)cdiv(d, kProjChunk), (unsigned)cdiv(m, 4 * kProjRowsWave));
+  hipLaunchKernelGGL(k_project, grid, dim3(256), 0, s, x, ldx, m, d, U, ppart);
   return hipGetLastError();
 }
 
-// out[i][j] = alpha x[i][j] + sum_t (c_t sum_chunk part[chunk][i][t]) U[j][t]
+// pc[i][t] = fp32(c_t * sum_chunk part[chunk][i][t]): the projection
+// partials summed once, in chunk order, in float64 (then scaled by c and
+// rounded once).
+__global__ void __launch_bounds__(256) k_lr_reduce(const double* __restrict__ part, int nchunk, int m,
+                                                   const float* __restrict__ coef, int which,
+                                                   float* __restrict__ pc) {
+  constexpr int KP = 32;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)m * KP) return;
+  const float* c = coef + (which == 0 ? 0 : KP);
+  double acc = 0.0;
+  for (int ch = 0; ch < nchunk; ++ch) acc += part[(int64_t)ch * m * KP + i];
+  pc[i] = (float)(acc * (double)c[i % KP]);
+}
+
+// out[i][j] = alpha x[i][j] + sum_t pc[i][t] U[j][t]
 // Tile: 16 rows x 256 columns; wave w owns rows 4w..4w+3, lane l columns
 // 4l..4l+3.  Optionally the amax of |out| per 128 x 128 tile (or tensor).
 __global__ void __launch_bounds__(256) k_lr_apply(const float* __restrict__ x, int64_t ldx, int m, int d,
-                                                  const float* __restrict__ U, const double* __restrict__ part,
-                                                  int nchunk, const float* __restrict__ coef, int which,
+                                                  const float* __restrict__ U, const float* __restrict__ pc,
+                                                  const float* __restrict__ coef, int which,
                                                   float* __restrict__ out, int64_t ldo, int scaling,
                                                   uint32_t* __restrict__ slots) {
   constexpr int KP = 32;
@@ -94,7 +130,6 @@ __global__ void __launch_bounds__(256) k_lr_apply(const float* __restrict__ x, i
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col0 = blockIdx.x * 256;
   const int row0 = blockIdx.y * 16;
-  const float* c = coef + (which == 0 ? 0 : KP);
   const float alpha = coef[2 * KP + which];
   // U rows of this column tile, transposed into LDS.
   for (int i = tid; i < 256 * KP / 4; i += 256) {
@@ -106,13 +141,9 @@ __global__ void __launch_bounds__(256) k_lr_apply(const float* __restrict__ x, i
     UsT[t + 2][j] = v.z;
     UsT[t + 3][j] = v.w;
   }
-  // Reduce the projection partials of these 16 rows (fixed chunk order).
   for (int i = tid; i < 16 * KP; i += 256) {
-    int r = i / KP, t = i % KP;
-    double acc = 0.0;
-    if (row0 + r < m)
-      for (int ch = 0; ch < nchunk; ++ch) acc += part[((int64_t)ch * m + row0 + r) * KP + t];
-    Pc[r][t] = (float)(acc * (double)c[t]);
+    const int r = i / KP, t = i % KP;
+    Pc[r][t] = row0 + r < m ? pc[(int64_t)(row0 + r) * KP + t] : 0.f;
   }
   __syncthreads();
   const int col = col0 + lane * 4;
@@ -172,14 +203,16 @@ __global__ void __launch_bounds__(256) k_lr_apply(const float* __restrict__ x, i
 }
 
 hipError_t launch_lr_apply(const float* x, int64_t ldx, int m, int d, const float* U, int k,
-                           const double* ppart, const float* coef, int which, float* out,
+                           const double* ppart, float* pc, const float* coef, int which, float* out,
                            int64_t ldo, int scaling, uint32_t* amax_slots, hipStream_t s) {
   (void)k;
   if (m == 0 || d == 0) return hipSuccess;
+  const int nchunk = (int)cdiv(d, kProjChunk);
+  hipLaunchKernelGGL(k_lr_reduce, dim3((unsigned)cdiv((int64_t)m * 32, 256)), dim3(256), 0, s, ppart, nchunk, m,
+                     coef, which, pc);
   dim3 grid((unsigned)cdiv(d, 256), (unsigned)cdiv(m, 16));
-  int nchunk = (int)cdiv(d, kProjChunk);
-  hipLaunchKernelGGL(k_lr_apply, grid, dim3(256), 0, s, x, ldx, m, d, U, ppart, nchunk, coef, which, out, ldo,
-                     scaling, amax_slots);
+  hipLaunchKernelGGL(k_lr_apply, grid, dim3(256), 0, s, x, ldx, m, d, U, pc, coef, which, out, ldo, scaling,
+                     amax_slots);
   return hipGetLastError();
 }
 
