@@ -116,24 +116,42 @@ __global__ void __launch_bounds__(256) k_lr_reduce(const double* __restrict__ pa
 }
 
 // out[i][j] = alpha x[i][j] + sum_t pc[i][t] U[j][t]
-// Tile: 16 rows x 256 columns; wave w owns rows 4w..4w+3, lane l columns
-// 4l..4l+3.  Optionally the amax of |out| per 128 x 128 tile (or tensor).
+// Tile: 128 rows x 256 columns (U's 256 rows staged once, transposed, in
+// LDS), walked 16 rows at a time; wave w owns rows 4w..4w+3 of each step,
+// lane l columns 4l..4l+3.  The next step's x is loaded while this step's
+// products run.  Optionally the amax of |out| per 128 x 128 tile (or
+// tensor): a tile covers whole amax blocks.
+constexpr int kApplyRows = 128;
+static_assert(kApplyRows == kBlock, "an apply tile covers one row of amax blocks");
+
 __global__ void __launch_bounds__(256) k_lr_apply(const float* __restrict__ x, int64_t ldx, int m, int d,
                                                   const float* __restrict__ U, const float* __restrict__ pc,
                                                   const float* __restrict__ coef, int which,
                                                   float* __restrict__ out, int64_t ldo, int scaling,
                                                   uint32_t* __restrict__ slots) {
-  constexpr int KP = 32;
+  constexpr int KP = 32, STEPS = kApplyRows / 16;
   __shared__ float UsT[KP][256 + 4];
-  __shared__ float Pc[16][KP];
+  __shared__ float Pc[kApplyRows][KP + 4];
   __shared__ uint32_t red[4][2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col0 = blockIdx.x * 256;
-  const int row0 = blockIdx.y * 16;
+  const int row0 = blockIdx.y * kApplyRows;
   const float alpha = coef[2 * KP + which];
-  // U rows of this column tile, transposed into LDS.
+  const int col = col0 + lane * 4;
+  const bool colok = col < d;   // d is a multiple of 8: all 4 columns or none
+  auto load_x = [&](int step, float4* xv) {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int row = row0 + 16 * step + wave * 4 + rr;
+      xv[rr] = (colok && row < m) ? *reinterpret_cast<const float4*>(x + (int64_t)row * ldx + col)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  float4 xcur[4], xnxt[4];
+  load_x(0, xcur);
+  // U rows of this column tile, transposed into LDS; the row block's pc.
   for (int i = tid; i < 256 * KP / 4; i += 256) {
-    int j = i / (KP / 4), t = (i % (KP / 4)) * 4;
+    const int j = i / (KP / 4), t = (i % (KP / 4)) * 4;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (col0 + j < d) v = *reinterpret_cast<const float4*>(U + (int64_t)(col0 + j) * KP + t);
     UsT[t][j] = v.x;
@@ -141,47 +159,60 @@ __global__ void __launch_bounds__(256) k_lr_apply(const float* __restrict__ x, i
     UsT[t + 2][j] = v.z;
     UsT[t + 3][j] = v.w;
   }
-  for (int i = tid; i < 16 * KP; i += 256) {
-    const int r = i / KP, t = i % KP;
-    Pc[r][t] = row0 + r < m ? pc[(int64_t)(row0 + r) * KP + t] : 0.f;
+  for (int i = tid; i < kApplyRows * KP / 4; i += 256) {
+    const int r = i / (KP / 4), t = (i % (KP / 4)) * 4;
+    *reinterpret_cast<float4*>(&Pc[r][t]) = row0 + r < m ? *reinterpret_cast<const float4*>(pc + (int64_t)(row0 + r) * KP + t)
+                                                         : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   __syncthreads();
-  const int col = col0 + lane * 4;
-  float acc[4][4];
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) acc[rr][q] = 0.f;
-#pragma unroll 8
-  for (int t = 0; t < KP; ++t) {
-    float4 u = *reinterpret_cast<const float4*>(&UsT[t][lane * 4]);
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      float p = Pc[wave * 4 + rr][t];
-      acc[rr][0] += p * u.x;
-      acc[rr][1] += p * u.y;
-      acc[rr][2] += p * u.z;
-      acc[rr][3] += p * u.w;
-    }
-  }
   uint32_t mx = 0;
-  if (col < d) {
+  for (int step = 0; step < STEPS; ++step) {
+    if (row0 + 16 * step >= m) break;   // uniform over the workgroup
+    if (step + 1 < STEPS) load_x(step + 1, xnxt);
+    float acc[4][4];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      int row = row0 + wave * 4 + rr;
-      if (row < m) {
-        float4 v = *reinterpret_cast<const float4*>(x + (int64_t)row * ldx + col);
-        float4 o = make_float4(alpha * v.x + acc[rr][0], alpha * v.y + acc[rr][1], alpha * v.z + acc[rr][2],
-                               alpha * v.w + acc[rr][3]);
-        *reinterpret_cast<float4*>(out + (int64_t)row * ldo + col) = o;
-        uint32_t a = __float_as_uint(o.x) & 0x7FFFFFFFu, b = __float_as_uint(o.y) & 0x7FFFFFFFu;
-        uint32_t e = __float_as_uint(o.z) & 0x7FFFFFFFu, f = __float_as_uint(o.w) & 0x7FFFFFFFu;
-        a = a > b ? a : b;
-        e = e > f ? e : f;
-        a = a > e ? a : e;
-        mx = mx > a ? mx : a;
+    for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[rr][q] = 0.f;
+    const int rb = 16 * step + wave * 4;
+#pragma unroll 2
+    for (int t = 0; t < KP; t += 4) {
+      float4 u[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) u[q] = *reinterpret_cast<const float4*>(&UsT[t + q][lane * 4]);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float4 p = *reinterpret_cast<const float4*>(&Pc[rb + rr][t]);
+        const float pv[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[rr][0] += pv[q] * u[q].x;
+          acc[rr][1] += pv[q] * u[q].y;
+          acc[rr][2] += pv[q] * u[q].z;
+          acc[rr][3] += pv[q] * u[q].w;
+        }
       }
     }
+    if (colok) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int row = row0 + rb + rr;
+        if (row < m) {
+          const float4 v = xcur[rr];
+          const float4 o = make_float4(alpha * v.x + acc[rr][0], alpha * v.y + acc[rr][1],
+                                       alpha * v.z + acc[rr][2], alpha * v.w + acc[rr][3]);
+          *reinterpret_cast<float4*>(out + (int64_t)row * ldo + col) = o;
+          uint32_t a = __float_as_uint(o.x) & 0x7FFFFFFFu, b = __float_as_uint(o.y) & 0x7FFFFFFFu;
+          uint32_t e = __float_as_uint(o.z) & 0x7FFFFFFFu, f = __float_as_uint(o.w) & 0x7FFFFFFFu;
+          a = a > b ? a : b;
+          e = e > f ? e : f;
+          a = a > e ? a : e;
+          mx = mx > a ? mx : a;
+        }
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) xcur[rr] = xnxt[rr];
   }
   if (slots) {
     for (int o = 16; o > 0; o >>= 1) {
@@ -210,7 +241,7 @@ hipError_t launch_lr_apply(const float* x, int64_t ldx, int m, int d, const floa
   const int nchunk = (int)cdiv(d, kProjChunk);
   hipLaunchKernelGGL(k_lr_reduce, dim3((unsigned)cdiv((int64_t)m * 32, 256)), dim3(256), 0, s, ppart, nchunk, m,
                      coef, which, pc);
-  dim3 grid((unsigned)cdiv(d, 256), (unsigned)cdiv(m, 16));
+  dim3 grid((unsigned)cdiv(d, 256), (unsigned)cdiv(m, kApplyRows));
   hipLaunchKernelGGL(k_lr_apply, grid, dim3(256), 0, s, x, ldx, m, d, U, pc, coef, which, out, ldo, scaling,
                      amax_slots);
   return hipGetLastError();
