@@ -160,47 +160,134 @@ hipError_t launch_quantize(const float* x, int64_t ld, int m, int d, int fmt, in
 }
 
 // U = (1/R) sum_r s_r dec(q_r), replicas summed in increasing r.
+// A lane owns V consecutive codes of a row (V = 16: one 16-byte load per
+// replica, or 8 when rows are not 16-byte aligned); a wave walks rows of
+// a 32-row band, four replicas' loads in flight at a time.  Codes are
+// decoded two at a time by the hardware OCP FP8 conversion.
+constexpr int kDqRows = 32;
+typedef float dq_float2 __attribute__((ext_vector_type(2)));
+
 template <int FMT>
+__device__ __forceinline__ void dec_word(uint32_t w, float* v) {
+  dq_float2 lo, hi;
+  if constexpr (FMT == 0) {
+    lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  } else {
+    lo = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
+    hi = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, true);
+  }
+  v[0] = lo[0];
+  v[1] = lo[1];
+  v[2] = hi[0];
+  v[3] = hi[1];
+}
+
+template <int V>
+struct CodeVec {
+  uint32_t w[V / 4];
+};
+
+template <int V>
+__device__ __forceinline__ CodeVec<V> load_codes(const uint8_t* p) {
+  CodeVec<V> c;
+  if constexpr (V == 16) {
+    const uint4 q = *reinterpret_cast<const uint4*>(p);
+    c.w[0] = q.x;
+    c.w[1] = q.y;
+    c.w[2] = q.z;
+    c.w[3] = q.w;
+  } else {
+    const uint2 q = *reinterpret_cast<const uint2*>(p);
+    c.w[0] = q.x;
+    c.w[1] = q.y;
+  }
+  return c;
+}
+
+template <int FMT, int V>
+__device__ __forceinline__ void acc_codes(const CodeVec<V>& c, float sc, float* a) {
+#pragma unroll
+  for (int k = 0; k < V / 4; ++k) {
+    float v[4];
+    dec_word<FMT>(c.w[k], v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[4 * k + e] += sc * v[e];
+  }
+}
+
+template <int FMT, int V>
 __global__ void __launch_bounds__(256) k_dequant_sum(const uint8_t* __restrict__ codes, int64_t code_stride,
                                                      const float* __restrict__ scales, int64_t scale_stride,
                                                      int R, int m, int d, int scaling,
                                                      float* __restrict__ out, int64_t ldo, float invR) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col = blockIdx.x * 256 + lane * 4;
-  const int r0 = blockIdx.y * kBlock;
-  const int r1 = min(m, r0 + kBlock);
-  if (col >= d) return;
-  const int slot = scaling == 0 ? 0 : blockIdx.y * (int)cdiv(d, kBlock) + col / kBlock;
+  const int col = blockIdx.x * (64 * V) + lane * V;
+  const int r0 = blockIdx.y * kDqRows;
+  const int r1 = min(m, r0 + kDqRows);
+  if (col >= d) return;   // d is a multiple of V: a lane's codes are all in range
+  const int ncb = (int)cdiv(d, kBlock);
   for (int rr = r0 + wave; rr < r1; rr += 4) {
-    // the sum starts from replica 0's term (not +0), so a lone -0 stays -0
-    const float s0 = scales[slot];
-    const uint32_t q0 = *reinterpret_cast<const uint32_t*>(codes + (int64_t)rr * d + col);
-    float a0 = s0 * dec_fp8<FMT>(q0 & 0xFFu), a1 = s0 * dec_fp8<FMT>((q0 >> 8) & 0xFFu);
-    float a2 = s0 * dec_fp8<FMT>((q0 >> 16) & 0xFFu), a3 = s0 * dec_fp8<FMT>(q0 >> 24);
-    for (int r = 1; r < R; ++r) {
-      const float sc = scales[(int64_t)r * scale_stride + slot];
-      uint32_t c = *reinterpret_cast<const uint32_t*>(codes + (int64_t)r * code_stride + (int64_t)rr * d + col);
-      a0 += sc * dec_fp8<FMT>(c & 0xFFu);
-      a1 += sc * dec_fp8<FMT>((c >> 8) & 0xFFu);
-      a2 += sc * dec_fp8<FMT>((c >> 16) & 0xFFu);
-      a3 += sc * dec_fp8<FMT>(c >> 24);
+    const int slot = scaling == 0 ? 0 : (rr / kBlock) * ncb + col / kBlock;
+    const uint8_t* cp = codes + (int64_t)rr * d + col;
+    float a[V];
+    {
+      // the sum starts from replica 0's term (not +0), so a lone -0 stays -0
+      const float s0 = scales[slot];
+      const CodeVec<V> c = load_codes<V>(cp);
+#pragma unroll
+      for (int k = 0; k < V / 4; ++k) {
+        float v[4];
+        dec_word<FMT>(c.w[k], v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[4 * k + e] = s0 * v[e];
+      }
     }
-    *reinterpret_cast<float4*>(out + (int64_t)rr * ldo + col) = make_float4(a0 * invR, a1 * invR, a2 * invR, a3 * invR);
+    int r = 1;
+    for (; r + 4 <= R; r += 4) {
+      CodeVec<V> c[4];
+      float sc[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        sc[u] = scales[(int64_t)(r + u) * scale_stride + slot];
+        c[u] = load_codes<V>(cp + (int64_t)(r + u) * code_stride);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc_codes<FMT, V>(c[u], sc[u], a);
+    }
+    for (; r < R; ++r)
+      acc_codes<FMT, V>(load_codes<V>(cp + (int64_t)r * code_stride), scales[(int64_t)r * scale_stride + slot], a);
+    float* op = out + (int64_t)rr * ldo + col;
+#pragma unroll
+    for (int k = 0; k < V / 4; ++k)
+      *reinterpret_cast<float4*>(op + 4 * k) =
+          make_float4(a[4 * k] * invR, a[4 * k + 1] * invR, a[4 * k + 2] * invR, a[4 * k + 3] * invR);
   }
+}
+
+template <int FMT, int V>
+static void launch_dq(const uint8_t* codes, int64_t code_stride, const float* scales, int64_t scale_stride, int R,
+                      int m, int d, int scaling, float* out, int64_t ldo, float invR, hipStream_t s) {
+  dim3 grid((unsigned)cdiv(d, 64 * V), (unsigned)cdiv(m, kDqRows));
+  hipLaunchKernelGGL((k_dequant_sum<FMT, V>), grid, dim3(256), 0, s, codes, code_stride, scales, scale_stride, R,
+                     m, d, scaling, out, ldo, invR);
 }
 
 hipError_t launch_dequant_sum(const uint8_t* codes, int64_t code_stride, const float* scales,
                               int64_t scale_stride, int R, int m, int d, int fmt, int scaling,
                               float* out, int64_t ldo, hipStream_t s) {
   if (m == 0 || d == 0) return hipSuccess;
-  dim3 grid((unsigned)cdiv(d, 256), (unsigned)cdiv(m, kBlock));
-  float invR = 1.0f / (float)R;
-  if (fmt == 0)
-    hipLaunchKernelGGL(k_dequant_sum<0>, grid, dim3(256), 0, s, codes, code_stride, scales, scale_stride,
-                       R, m, d, scaling, out, ldo, invR);
-  else
-    hipLaunchKernelGGL(k_dequant_sum<1>, grid, dim3(256), 0, s, codes, code_stride, scales, scale_stride,
-                       R, m, d, scaling, out, ldo, invR);
+  if (d % 8 != 0) return hipErrorInvalidValue;
+  const float invR = 1.0f / (float)R;
+  // 16-byte loads need 16-byte aligned rows in every replica
+  const bool v16 = d % 16 == 0 && (reinterpret_cast<uintptr_t>(codes) & 15u) == 0 && (R == 1 || code_stride % 16 == 0);
+  if (fmt == 0) {
+    if (v16) launch_dq<0, 16>(codes, code_stride, scales, scale_stride, R, m, d, scaling, out, ldo, invR, s);
+    else launch_dq<0, 8>(codes, code_stride, scales, scale_stride, R, m, d, scaling, out, ldo, invR, s);
+  } else {
+    if (v16) launch_dq<1, 16>(codes, code_stride, scales, scale_stride, R, m, d, scaling, out, ldo, invR, s);
+    else launch_dq<1, 8>(codes, code_stride, scales, scale_stride, R, m, d, scaling, out, ldo, invR, s);
+  }
   return hipGetLastError();
 }
 

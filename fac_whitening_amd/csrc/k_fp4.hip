@@ -18,9 +18,10 @@
 // the even column in the low nibble.
 //
 // Tiling: quantiser, 4 lanes per block (one float4 each, a quad reduces the
-// block amax with two shuffles); dequant-sum, 2 lanes per block (8 codes,
-// one 32-bit load per replica).  Consecutive lanes take consecutive columns
-// of a row, so every load and store of a wave is contiguous.
+// block amax with two shuffles); dequant-sum, 32 codes per lane (two
+// blocks, one 16-byte load per replica).  Consecutive lanes take
+// consecutive columns of a row, so every load and store of a wave is
+// contiguous.
 #include "fp8_codec.hpp"
 #include "gift_internal.hpp"
 
@@ -132,38 +133,121 @@ hipError_t launch_quantize_fp4(const float* x, int64_t ld, int m, int d, const u
 
 // U = (1/R) sum_r S_{b,r} dec(q_r), replicas in increasing r (the sum
 // starts from replica 0's term, so a lone -0 stays -0).
+// A lane owns V consecutive codes of a row (V = 32: one 16-byte load per
+// replica, or 16 with 8-byte loads when code rows are not 16-byte
+// aligned); a wave walks the rows of a 32-row band with four replicas'
+// loads in flight.  Codes are decoded a byte (two codes) at a time by the
+// hardware E2M1 conversion with a unit scale, which is exact.
+constexpr int kDq4Rows = 32;
+typedef float fp4_float2 __attribute__((ext_vector_type(2)));
+
+template <int V>
+struct Fp4Vec {
+  uint32_t w[V / 8];
+  uint32_t sc[V / 16];   // E4M3 block scale bytes
+};
+
+template <int V>
+__device__ __forceinline__ Fp4Vec<V> load_fp4(const uint8_t* cp, const uint8_t* sp) {
+  Fp4Vec<V> c;
+  if constexpr (V == 32) {
+    const uint4 q = *reinterpret_cast<const uint4*>(cp);
+    c.w[0] = q.x;
+    c.w[1] = q.y;
+    c.w[2] = q.z;
+    c.w[3] = q.w;
+  } else {
+    const uint2 q = *reinterpret_cast<const uint2*>(cp);
+    c.w[0] = q.x;
+    c.w[1] = q.y;
+  }
+#pragma unroll
+  for (int b = 0; b < V / 16; ++b) c.sc[b] = sp[b];
+  return c;
+}
+
+// a[j] (+)= S_b dec(q_j) for the V codes of one replica; FIRST: replica 0.
+template <int V, bool FIRST>
+__device__ __forceinline__ void acc_fp4(const Fp4Vec<V>& c, float tscale, float* a) {
+#pragma unroll
+  for (int b = 0; b < V / 16; ++b) {
+    const float S = dec_e4m3(c.sc[b]) * tscale;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint32_t w = c.w[2 * b + k];
+      const fp4_float2 v[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0),
+                               __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1),
+                               __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2),
+                               __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3)};
+#pragma unroll
+      for (int by = 0; by < 4; ++by) {
+        const int j = 16 * b + 8 * k + 2 * by;
+        if constexpr (FIRST) {
+          a[j] = S * v[by][0];
+          a[j + 1] = S * v[by][1];
+        } else {
+          a[j] = __builtin_fmaf(S, v[by][0], a[j]);
+          a[j + 1] = __builtin_fmaf(S, v[by][1], a[j + 1]);
+        }
+      }
+    }
+  }
+}
+
+template <int V>
 __global__ void __launch_bounds__(256) k_dequant_sum_fp4(const uint8_t* __restrict__ codes, int64_t code_stride,
                                                          const uint8_t* __restrict__ bscales, int64_t bscale_stride,
                                                          const float* __restrict__ tscales, int R, int m, int d,
                                                          float* __restrict__ out, int64_t ldo, float invR) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int q8 = d >> 3;
-  if (t >= (int64_t)m * q8) return;
-  const int row = (int)(t / q8), col = (int)(t % q8) * 8;
-  const int64_t co = (int64_t)row * (d >> 1) + (col >> 1);
-  const int64_t so = (int64_t)row * (d / kFp4Block) + col / kFp4Block;
-  float acc[8];
-  for (int r = 0; r < R; ++r) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + (int64_t)r * code_stride + co);
-    const float S = dec_e4m3(bscales[(int64_t)r * bscale_stride + so]) * tscales[r];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = blockIdx.x * (64 * V) + lane * V;
+  const int r0 = blockIdx.y * kDq4Rows;
+  const int r1 = min(m, r0 + kDq4Rows);
+  if (col >= d) return;   // d is a multiple of V: a lane's codes are all in range
+  for (int row = r0 + wave; row < r1; row += 4) {
+    const uint8_t* cp = codes + (int64_t)row * (d >> 1) + (col >> 1);
+    const uint8_t* sp = bscales + (int64_t)row * (d / kFp4Block) + col / kFp4Block;
+    float a[V];
+    acc_fp4<V, true>(load_fp4<V>(cp, sp), tscales[0], a);
+    int r = 1;
+    for (; r + 4 <= R; r += 4) {
+      Fp4Vec<V> c[4];
+      float t[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float v = dec_e2m1((w >> (4 * j)) & 0xFu);
-      acc[j] = r == 0 ? S * v : __builtin_fmaf(S, v, acc[j]);
+      for (int u = 0; u < 4; ++u) {
+        t[u] = tscales[r + u];
+        c[u] = load_fp4<V>(cp + (int64_t)(r + u) * code_stride, sp + (int64_t)(r + u) * bscale_stride);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc_fp4<V, false>(c[u], t[u], a);
     }
+    for (; r < R; ++r)
+      acc_fp4<V, false>(load_fp4<V>(cp + (int64_t)r * code_stride, sp + (int64_t)r * bscale_stride), tscales[r], a);
+    float* o = out + (int64_t)row * ldo + col;
+#pragma unroll
+    for (int k = 0; k < V / 4; ++k)
+      *reinterpret_cast<float4*>(o + 4 * k) =
+          make_float4(a[4 * k] * invR, a[4 * k + 1] * invR, a[4 * k + 2] * invR, a[4 * k + 3] * invR);
   }
-  float* o = out + (int64_t)row * ldo + col;
-  *reinterpret_cast<float4*>(o) = make_float4(acc[0] * invR, acc[1] * invR, acc[2] * invR, acc[3] * invR);
-  *reinterpret_cast<float4*>(o + 4) = make_float4(acc[4] * invR, acc[5] * invR, acc[6] * invR, acc[7] * invR);
 }
 
 hipError_t launch_dequant_sum_fp4(const uint8_t* codes, int64_t code_stride, const uint8_t* bscales,
                                   int64_t bscale_stride, const float* tscales, int R, int m, int d, float* out,
                                   int64_t ldo, hipStream_t s) {
-  const int64_t n8 = (int64_t)m * (d / 8);
-  if (n8 == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_dequant_sum_fp4, dim3((unsigned)cdiv(n8, 256)), dim3(256), 0, s, codes, code_stride, bscales,
-                     bscale_stride, tscales, R, m, d, out, ldo, 1.0f / (float)R);
+  if (m == 0 || d == 0) return hipSuccess;
+  if (d % 16 != 0) return hipErrorInvalidValue;
+  const float invR = 1.0f / (float)R;
+  // 16-byte loads need 16-byte aligned code rows in every replica
+  const bool v32 = d % 32 == 0 && (reinterpret_cast<uintptr_t>(codes) & 15u) == 0 && (R == 1 || code_stride % 16 == 0);
+  if (v32) {
+    dim3 grid((unsigned)cdiv(d, 64 * 32), (unsigned)cdiv(m, kDq4Rows));
+    hipLaunchKernelGGL(k_dequant_sum_fp4<32>, grid, dim3(256), 0, s, codes, code_stride, bscales, bscale_stride,
+                       tscales, R, m, d, out, ldo, invR);
+  } else {
+    dim3 grid((unsigned)cdiv(d, 64 * 16), (unsigned)cdiv(m, kDq4Rows));
+    hipLaunchKernelGGL(k_dequant_sum_fp4<16>, grid, dim3(256), 0, s, codes, code_stride, bscales, bscale_stride,
+                       tscales, R, m, d, out, ldo, invR);
+  }
   return hipGetLastError();
 }
 

@@ -20,7 +20,8 @@ FMTS = [("e4m3", 0), ("e5m2", 1)]
 @pytest.fixture(scope="module")
 def fw():
     import fac_whitening_amd as fw
-    return fw
+    yield fw
+    fw.set_fused(True)
 
 
 def _euclid(fw, m, d):
@@ -28,8 +29,10 @@ def _euclid(fw, m, d):
 
 
 @pytest.mark.parametrize("fmt,f", FMTS)
-def test_decode_all_256_codes(fw, fmt, f):
-    print(f"[decode all codes {fmt}]", flush=True)
+@pytest.mark.parametrize("fused", [True, False])
+def test_decode_all_256_codes(fw, fmt, f, fused):
+    print(f"[decode all codes {fmt} fused={fused}]", flush=True)
+    fw.set_fused(fused)
     L = _euclid(fw, 2, 128)
     codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).reshape(2, 128).to(DEV)
     scales = torch.ones(1, 1, dtype=torch.float32, device=DEV)
@@ -112,17 +115,24 @@ def test_quantizer_zero_and_nonfinite(fw):
     assert torch.isnan(out).all()
 
 
-@pytest.mark.parametrize("R", [1, 3, 8])
+@pytest.mark.parametrize("R", [1, 3, 5, 8])
 @pytest.mark.parametrize("scaling,s", [("tensor", 0), ("block", 1)])
-def test_dequant_reduce_matches_oracle(fw, R, scaling, s):
-    print(f"[dequant-reduce R={R} {scaling}]", flush=True)
+@pytest.mark.parametrize("shape", [(150, 400), (37, 408)])
+@pytest.mark.parametrize("fused", [True, False])
+def test_dequant_reduce_matches_oracle(fw, R, scaling, s, shape, fused):
+    """Both routes: the persistent kernel and the standalone dequant-sum
+    (16 codes per lane, or 8 when d is not a multiple of 16)."""
+    print(f"[dequant-reduce R={R} {scaling} {shape} fused={fused}]", flush=True)
+    fw.set_fused(fused)
     rng = np.random.default_rng(30 + R)
-    m, d = 150, 400
+    m, d = shape
     Xs = [(rng.standard_normal((m, d)) * np.exp(rng.standard_normal((1, d)))).astype(np.float32) for _ in range(R)]
     pl = [G.quantize(x, "e4m3", scaling)[:2] for x in Xs]
     ref = G.dequant_reduce([p[0] for p in pl], [p[1] for p in pl], "e4m3", scaling)
     L = _euclid(fw, m, d)
-    codes = torch.from_numpy(np.stack([p[0] for p in pl])).to(DEV)
+    stride = -(-m * d // 16) * 16     # replica rows 16-byte aligned
+    codes = torch.empty(R, stride, dtype=torch.uint8, device=DEV)[:, :m * d].view(R, m, d)
+    codes.copy_(torch.from_numpy(np.stack([p[0] for p in pl])))
     scales = torch.from_numpy(np.stack([p[1].ravel() for p in pl])).to(DEV)
     out = L.decode_reduce(codes, scales, 0, s).cpu().numpy()
     # fp32 sum of R exact products: error <= R ulps of the sum of magnitudes

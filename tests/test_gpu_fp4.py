@@ -105,14 +105,15 @@ def test_fp4_encode_stage_isolated(fw, kind, shape, ef):
     L.close()
 
 
-@pytest.mark.parametrize("R", [1, 4, 16])
-@pytest.mark.parametrize("kind", ["euclid", "lowrank"])
-def test_fp4_decode_reduce(fw, kind, R):
+@pytest.mark.parametrize("R", [1, 4, 6, 16])
+@pytest.mark.parametrize("kind,shape", [("euclid", (200, 1536)), ("euclid", (100, 1008)), ("lowrank", (200, 1536))])
+def test_fp4_decode_reduce(fw, kind, shape, R):
     """The mean of R FP4 payloads mapped back: Euclidean within the fp32
     rounding of the sum; rank-32 with the oracle's factor in the layer state
-    and the oracle's inverse transform."""
-    m, d = 200, 1536
-    print(f"[fp4 decode {kind} R={R}]", flush=True)
+    and the oracle's inverse transform.  d = 1008 (not a multiple of 32)
+    takes the 16-codes-per-lane decoder."""
+    m, d = shape
+    print(f"[fp4 decode {kind} {shape} R={R}]", flush=True)
     rng = np.random.default_rng(17 + R)
     if kind == "lowrank":
         T = 1024
