@@ -93,6 +93,25 @@ __device__ __forceinline__ float dec_fp8(uint32_t c) {
   else return dec_e5m2(c);
 }
 
+// The four codes of a 32-bit word (byte i -> v[i]) by the hardware OCP FP8
+// conversion, two at a time; the same values as dec_fp8.
+typedef float fp8_float2 __attribute__((ext_vector_type(2)));
+template <int FMT>
+__device__ __forceinline__ void dec4_fp8(uint32_t w, float* v) {
+  fp8_float2 lo, hi;
+  if constexpr (FMT == 0) {
+    lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  } else {
+    lo = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
+    hi = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, true);
+  }
+  v[0] = lo[0];
+  v[1] = lo[1];
+  v[2] = hi[0];
+  v[3] = hi[1];
+}
+
 // Scale pair from an amax (as the bit pattern of |x|, ordered as uint32 so
 // NaN > Inf > finite): r = fp32(FMAX / amax) (double division rounded once:
 // the correctly rounded float quotient), s = fp32(amax / FMAX).

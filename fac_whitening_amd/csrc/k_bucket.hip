@@ -217,11 +217,10 @@ __global__ void __launch_bounds__(256) k_bucket_dequant_sum(BucketTable t, const
 #pragma unroll
       for (int h = 0; h < kBH; ++h) {
         const float s = h < 2 ? sa : sb;
+        float v[4];
+        dec4_fp8<FMT>(w[h], v);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float v = dec_fp8<FMT>((w[h] >> (8 * j)) & 0xFFu);
-          acc[h][j] = r == 0 ? s * v : __builtin_fmaf(s, v, acc[h][j]);
-        }
+        for (int j = 0; j < 4; ++j) acc[h][j] = r == 0 ? s * v[j] : __builtin_fmaf(s, v[j], acc[h][j]);
       }
     }
     float* o = out + L.base;

@@ -165,24 +165,6 @@ hipError_t launch_quantize(const float* x, int64_t ld, int m, int d, int fmt, in
 // a 32-row band, four replicas' loads in flight at a time.  Codes are
 // decoded two at a time by the hardware OCP FP8 conversion.
 constexpr int kDqRows = 32;
-typedef float dq_float2 __attribute__((ext_vector_type(2)));
-
-template <int FMT>
-__device__ __forceinline__ void dec_word(uint32_t w, float* v) {
-  dq_float2 lo, hi;
-  if constexpr (FMT == 0) {
-    lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-    hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  } else {
-    lo = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
-    hi = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, true);
-  }
-  v[0] = lo[0];
-  v[1] = lo[1];
-  v[2] = hi[0];
-  v[3] = hi[1];
-}
-
 template <int V>
 struct CodeVec {
   uint32_t w[V / 4];
@@ -210,7 +192,7 @@ __device__ __forceinline__ void acc_codes(const CodeVec<V>& c, float sc, float* 
 #pragma unroll
   for (int k = 0; k < V / 4; ++k) {
     float v[4];
-    dec_word<FMT>(c.w[k], v);
+    dec4_fp8<FMT>(c.w[k], v);
 #pragma unroll
     for (int e = 0; e < 4; ++e) a[4 * k + e] += sc * v[e];
   }
@@ -238,7 +220,7 @@ __global__ void __launch_bounds__(256) k_dequant_sum(const uint8_t* __restrict__
 #pragma unroll
       for (int k = 0; k < V / 4; ++k) {
         float v[4];
-        dec_word<FMT>(c.w[k], v);
+        dec4_fp8<FMT>(c.w[k], v);
 #pragma unroll
         for (int e = 0; e < 4; ++e) a[4 * k + e] = s0 * v[e];
       }
