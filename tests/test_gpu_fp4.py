@@ -144,6 +144,24 @@ def test_fp4_decode_reduce(fw, kind, shape, R):
     L.close()
 
 
+@pytest.mark.parametrize("m,d", [(2, 256), (4, 144)])
+def test_fp4_decode_all_256_bytes(fw, m, d):
+    """Every byte (two E2M1 codes) under unit block and tensor scales
+    decodes to the oracle's values exactly, signed zeros included, with 32
+    codes per lane (d = 256) and 16 (d = 144)."""
+    print(f"[fp4 decode all bytes {m}x{d}]", flush=True)
+    L = fw.Layer(m, d, "euclid", device=DEV)
+    nb = m * d // 2
+    byts = (np.arange(nb) % 256).astype(np.uint8).reshape(m, d // 2)
+    codes = torch.from_numpy(byts).to(DEV)
+    bsc = torch.full((m, d // 16), 0x38, dtype=torch.uint8, device=DEV)   # E4M3 1.0
+    tsc = torch.ones(1, device=DEV)
+    out = L.decode_reduce_fp4(codes, bsc, tsc).cpu().numpy()
+    ref = fp4.decode(fp4.unpack(byts)).astype(np.float32)
+    assert np.array_equal(out, ref) and np.array_equal(np.signbit(out), np.signbit(ref))
+    L.close()
+
+
 def test_fp4_nonfinite(fw):
     """An Inf in the gradient: NaN tensor scale, every block scale 0x7F,
     codes 0, the flag set; the decoded tensor is NaN."""
