@@ -94,19 +94,35 @@ __device__ __forceinline__ void flush_tensor_max(uint32_t v, uint32_t* slot, uin
   __syncthreads();
 }
 
-// amax (as |x| bit patterns) of every scale block into slots (zeroed before).
+// The kBH float4s of this lane in chunk L (zeros past the tensor's end).
+__device__ __forceinline__ void load_lane(const float* __restrict__ g, const BLane& L, float4* v) {
+  const float* x = g + L.base;
+#pragma unroll
+  for (int h = 0; h < kBH; ++h)
+    v[h] = L.live(h) ? *reinterpret_cast<const float4*>(x + L.e0 + 256 * h) : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// amax (as |x| bit patterns) of every scale block into slots (zeroed
+// before).  The next chunk's values are loaded while this chunk is reduced.
 __global__ void __launch_bounds__(256) k_bucket_amax(BucketTable t, const float* __restrict__ g, int block512,
                                                      uint32_t* __restrict__ slots) {
   __shared__ uint32_t red[4];
   BRange r(t);
+  if (r.c >= r.end) return;   // workgroup-uniform
   uint32_t run = 0;   // per tensor: this lane's max over the tensor's chunks so far
-  for (; r.c < r.end;) {
-    const BLane L(t, r);
-    const float* x = g + L.base;
-    float4 v[kBH];
-#pragma unroll
-    for (int h = 0; h < kBH; ++h)
-      v[h] = L.live(h) ? *reinterpret_cast<const float4*>(x + L.e0 + 256 * h) : make_float4(0.f, 0.f, 0.f, 0.f);
+  BLane L(t, r);
+  float4 v[kBH];
+  load_lane(g, L, v);
+  for (;;) {
+    BRange rn = r;
+    const bool newt = rn.advance(t);
+    const bool more = rn.c < rn.end;   // workgroup-uniform
+    BLane Ln = L;
+    float4 vn[kBH];
+    if (more) {
+      Ln = BLane(t, rn);
+      load_lane(g, Ln, vn);
+    }
     if (block512) {
       const uint32_t b0 = wave_umax(max(umax4(v[0]), umax4(v[1])));
       const uint32_t b1 = wave_umax(max(umax4(v[2]), umax4(v[3])));
@@ -115,17 +131,19 @@ __global__ void __launch_bounds__(256) k_bucket_amax(BucketTable t, const float*
         if (L.live(0)) slots[blk] = b0;   // one wave per block: no other writer
         if (L.live(2)) slots[blk + 1] = b1;
       }
-      r.advance(t);
     } else {
 #pragma unroll
       for (int h = 0; h < kBH; ++h) run = max(run, umax4(v[h]));
-      const int i = r.i;
-      const bool last = r.advance(t) || r.c >= r.end;
-      if (last) {   // workgroup-uniform
-        flush_tensor_max(run, slots + t.scale_off[i], red);
+      if (newt || !more) {   // the tensor's last chunk in this range (workgroup-uniform)
+        flush_tensor_max(run, slots + t.scale_off[r.i], red);
         run = 0;
       }
     }
+    if (!more) break;
+    r = rn;
+    L = Ln;
+#pragma unroll
+    for (int h = 0; h < kBH; ++h) v[h] = vn[h];
   }
 }
 
@@ -158,14 +176,22 @@ __global__ void __launch_bounds__(256) k_bucket_quantize(BucketTable t, const fl
                                                          float* __restrict__ scales) {
   const float fmax = fp8_fmax(FMT);
   BRange r(t);
-  for (; r.c < r.end; r.advance(t)) {
-    const BLane L(t, r);
-    const float* x = g + L.base;
+  if (r.c >= r.end) return;
+  // the next chunk's values are loaded while this chunk is encoded
+  BLane L(t, r);
+  float4 v[kBH];
+  load_lane(g, L, v);
+  for (;;) {
+    BRange rn = r;
+    rn.advance(t);
+    const bool more = rn.c < rn.end;   // workgroup-uniform
+    BLane Ln = L;
+    float4 vn[kBH];
+    if (more) {
+      Ln = BLane(t, rn);
+      load_lane(g, Ln, vn);
+    }
     uint8_t* q = codes + L.base;
-    float4 v[kBH];
-#pragma unroll
-    for (int h = 0; h < kBH; ++h)
-      v[h] = L.live(h) ? *reinterpret_cast<const float4*>(x + L.e0 + 256 * h) : make_float4(0.f, 0.f, 0.f, 0.f);
     // the scale of each half of the wave's range (one block each; per
     // tensor both are the tensor's)
 #pragma unroll
@@ -188,6 +214,11 @@ __global__ void __launch_bounds__(256) k_bucket_quantize(BucketTable t, const fl
         if (L.live(h))
           *reinterpret_cast<uint32_t*>(q + L.e0 + 256 * h) = bad ? 0x7F7F7F7Fu : codes4<FMT>(v[h], rr, fmax);
     }
+    if (!more) break;
+    r = rn;
+    L = Ln;
+#pragma unroll
+    for (int h = 0; h < kBH; ++h) v[h] = vn[h];
   }
 }
 
