@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFS = 2500.0
 FP64_PEAK_TFS = 78.6
+FP32_PEAK_TFS = 157.3
 
 
 def parse():
@@ -144,20 +145,27 @@ def main():
     # stream).  Each event adds about 2.5 us to the step, so only the
     # dominant call is bracketed.
     dec_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # batch boundaries: 5 batches of consecutive steps (median, p10, p90)
+    nbat = min(5, args.steps)
+    bounds = [args.steps * j // nbat for j in range(nbat + 1)]
+    bat_ev = {b: torch.cuda.Event(enable_timing=True) for b in bounds}
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    start.record()
+    bat_ev[0].record()
     for i in range(args.steps):
         W, codes, scales, out = sets[i % len(sets)]
         L.encode(W, fw.E4M3, scaling, codes=codes[0], scales=scales[0])
         dec_ev[i][0].record()
         L.decode_reduce(codes, scales, fw.E4M3, scaling, out=out)
         dec_ev[i][1].record()
-    stop.record()
+        if i + 1 in bat_ev:
+            bat_ev[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    start, stop = bat_ev[0], bat_ev[args.steps]
     total_ms = start.elapsed_time(stop)
+    bat_ms = [bat_ev[bounds[j]].elapsed_time(bat_ev[bounds[j + 1]]) / (bounds[j + 1] - bounds[j])
+              for j in range(nbat)]
     t_dec = float(np.mean([a.elapsed_time(b) for a, b in dec_ev]))
     t_enc = total_ms / args.steps - t_dec     # the rest of the step: encode and the event gaps
     ms_per_step = total_ms / args.steps
@@ -180,6 +188,60 @@ def main():
                 "unit_frac": round((enc_bytes + dec_bytes) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "decode_ms": round(t_dec, 5), "rest_of_step_ms": round(t_enc, 5),
                 "alg_bytes_encode": int(enc_bytes), "alg_bytes_decode": int(dec_bytes)}
+
+    # ---- beside the headline: batch spread, the unit with one buffer set
+    # (warm), the per-128x128-block unit, a plain streaming copy (the
+    # achievable HBM ceiling on this machine) and the fp32-equivalent flops
+    def unit_on(sc, c, s_, W, out):
+        L.encode(W, fw.E4M3, sc, codes=c[0], scales=s_[0])
+        L.decode_reduce(c, s_, fw.E4M3, sc, out=out)
+
+    W0, c0, s0, o0 = sets[0]
+    t_warm = _event_ms(torch, lambda: unit_on(scaling, c0, s0, W0, o0), args.steps)
+    other = fw.SCALE_BLOCK128 if scaling == fw.SCALE_TENSOR else fw.SCALE_TENSOR
+    nb_o = fw.nblocks(m, d, other)
+    bsets = []
+    for j in range(len(sets)):
+        c = torch.empty(R, m, d, dtype=torch.uint8, device=dev)
+        s_ = torch.empty(R, nb_o, dtype=torch.float32, device=dev)
+        if j == 0:
+            for r in range(1, R):
+                L.encode(case.W[r], fw.E4M3, other, codes=c[r], scales=s_[r])
+        else:
+            c.copy_(bsets[0][0])
+            s_.copy_(bsets[0][1])
+        bsets.append((c, s_))
+    bturn = [0]
+
+    def unit_other():
+        j = bturn[0] % len(sets)
+        bturn[0] += 1
+        unit_on(other, bsets[j][0], bsets[j][1], sets[j][0], sets[j][3])
+
+    t_other = _event_ms(torch, unit_other, args.steps)
+    del bsets
+    csrc = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+    cdst = torch.empty_like(csrc)
+    t_copy = _event_ms(torch, lambda: torch.neg(csrc, out=cdst), 10)
+    del csrc, cdst
+    copy_gbs = 2.0 * 4 * (64 << 20) / (t_copy * 1e-3) / 1e9
+    unit_detail = {
+        "batches_ms_per_step": {"median": round(float(np.median(bat_ms)), 5),
+                                "p10": round(float(np.percentile(bat_ms, 10)), 5),
+                                "p90": round(float(np.percentile(bat_ms, 90)), 5), "batches": nbat},
+        "warm_one_set": {"ms_per_step": round(t_warm, 5),
+                         "GB_s_of_grad": round(grad_bytes / (t_warm * 1e-3) / 1e9, 1)},
+        ("block128" if other == fw.SCALE_BLOCK128 else "tensor"): {
+            "ms_per_step": round(t_other, 5), "GB_s_of_grad": round(grad_bytes / (t_other * 1e-3) / 1e9, 1),
+            "cache": f"cold ({args.sets} rotating buffer sets)"},
+        "copy_ceiling": {"kernel": "torch.neg, 64 Mi fp32 (256 MiB read + 256 MiB written)",
+                         "GB_s": round(copy_gbs, 1), "frac_of_peak": round(copy_gbs / HBM_PEAK_GBS, 4),
+                         "unit_frac_of_copy": round((enc_bytes + dec_bytes) / (ms_per_step * 1e-3) / 1e9 / copy_gbs,
+                                                    4)},
+        "fp32_equivalent": {"flop_per_elem": 256, "TFLOP_s": round(256.0 * m * d / (ms_per_step * 1e-3) / 1e12, 2),
+                            "frac_of_fp32_peak": round(256.0 * m * d / (ms_per_step * 1e-3) / 1e12 / FP32_PEAK_TFS,
+                                                       4)},
+    }
 
     # the encode alone, without and with error feedback (Algorithm 1: the
     # residual is read and rewritten beside the codes), outside the unit
@@ -215,6 +277,7 @@ def main():
                    "cache": f"cold ({args.sets} rotating buffer sets)"},
         "roofline": roofline,
         "stage_rooflines": stage_rooflines,
+        "unit_detail": unit_detail,
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu:
