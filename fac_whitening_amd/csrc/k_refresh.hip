@@ -189,68 +189,59 @@ __device__ __forceinline__ double rsq_nr(double x) {
 }
 
 // One wave: G (LP x LP, leading l x l used) = L L^T, writes M = L^-T (upper
-// triangular, zero outside l x l) into small[kSmM].  Lane i owns row i of L
-// (left-looking: column j from dot products with the finished columns) and
-// then column i of L^-1 (forward substitution); both live in LDS.  One wave
-// keeps its LDS accesses in program order, so no barrier is needed.  Rows
-// and columns past l are the identity.
+// triangular, zero outside l x l) into small[kSmM].  Lane i keeps row i of
+// L in registers (left-looking: at step j it forms L[i][j] from its own row
+// and row j of L, read from LDS where each lane stores its new element), and
+// then column i of L^-1 (forward substitution against the rows of L in
+// LDS).  Both loops are unrolled over the compile-time size, so every
+// register index is a constant and the LDS reads of a step are broadcasts
+// issued together.  One wave keeps its LDS accesses in program order, so no
+// barrier is needed.  Rows and columns past l are the identity.
 template <int LP>
 __global__ void __launch_bounds__(64) k_chol_inv_small(const double* __restrict__ G, int l,
                                                        double* __restrict__ small, uint32_t* __restrict__ flags) {
-  __shared__ double Ls[LP][LP + 1];   // L, row-major
-  __shared__ double Xs[LP][LP + 1];   // L^-1, Xs[r][c]
-  __shared__ double Dinv[LP];         // 1 / L[j][j]
+  static_assert(LP <= 64, "one lane per row");
+  __shared__ __attribute__((aligned(16))) double Ls[LP][LP + 2];   // L, row-major, rows 16-byte aligned
+  __shared__ double Dinv[LP];                                        // 1 / L[j][j]
   const int i = threadIdx.x;
   const bool own = i < LP;
-  if (own) {
-    double g[LP];   // all loads in flight before the first store
+  const int ir = own ? i : LP - 1;   // lanes past LP load a valid row and never store
+  double row[LP];                    // G[i][q] for q >= j, L[i][q] for q < j
 #pragma unroll
-    for (int q = 0; q < LP; ++q) g[q] = G[i * LP + q];
-#pragma unroll
-    for (int q = 0; q < LP; ++q) Ls[i][q] = (i < l && q < l) ? g[q] : (i == q ? 1.0 : 0.0);
+  for (int q = 0; q < LP; ++q) {
+    const double g = G[ir * LP + q];
+    row[q] = (i < l && q < l) ? g : (i == q ? 1.0 : 0.0);
   }
   bool bad = false;
-  // dot products with four partial sums (short dependency chains)
-  auto dot = [&](const double* x, const double* y, int lo, int hi) {
-    double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
-    int q = lo;
-    for (; q + 4 <= hi; q += 4) {
-      s0 += x[q] * y[q];
-      s1 += x[q + 1] * y[q + 1];
-      s2 += x[q + 2] * y[q + 2];
-      s3 += x[q + 3] * y[q + 3];
-    }
-    for (; q < hi; ++q) s0 += x[q] * y[q];
-    return (s0 + s1) + (s2 + s3);
-  };
+#pragma unroll
   for (int j = 0; j < LP; ++j) {
-    const double r = own ? Ls[i][j] - dot(Ls[i], Ls[j], 0, j) : 0.0;
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};   // four chains
+#pragma unroll
+    for (int q = 0; q < j; ++q) acc[q & 3] += row[q] * Ls[j][q];
+    const double r = row[j] - ((acc[0] + acc[1]) + (acc[2] + acc[3]));
     const double dj = __shfl(r, j, 64);   // the pivot, from lane j
     double rs = rsq_nr(dj);               // 1 / L[j][j]
     if (!(dj > 0.0)) {
       bad = true;
       rs = __longlong_as_double(0x7FF8000000000000LL);
     }
-    if (own) Ls[i][j] = i > j ? r * rs : (i == j ? dj * rs : 0.0);
-    if (i == j) Dinv[j] = rs;
+    row[j] = i > j ? r * rs : (i == j ? dj * rs : 0.0);
+    if (own) Ls[i][j] = row[j];
+    if (i == 0) Dinv[j] = rs;
   }
+  double x[LP];   // column i of L^-1: x[q] = (L^-1)[q][i], zero above the diagonal
+#pragma unroll
   for (int rr = 0; rr < LP; ++rr) {
-    if (own) {
-      double v = rr == i ? 1.0 : 0.0;
-      // v -= sum_{q = i}^{rr - 1} L[rr][q] X[q][i]  (X column i read with stride)
-      double s0 = 0.0, s1 = 0.0;
-      int q = i;
-      for (; q + 2 <= rr; q += 2) {
-        s0 += Ls[rr][q] * Xs[q][i];
-        s1 += Ls[rr][q + 1] * Xs[q + 1][i];
-      }
-      for (; q < rr; ++q) s0 += Ls[rr][q] * Xs[q][i];
-      v -= s0 + s1;
-      Xs[rr][i] = rr >= i ? v * Dinv[rr] : 0.0;
-    }
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int q = 0; q < rr; ++q) acc[q & 3] += Ls[rr][q] * x[q];
+    const double v = (rr == i ? 1.0 : 0.0) - ((acc[0] + acc[1]) + (acc[2] + acc[3]));
+    x[rr] = rr >= i ? v * Dinv[rr] : 0.0;
   }
-  if (own)
-    for (int c = 0; c < LP; ++c) small[kSmM + i * LP + c] = (i < l && c < l) ? Xs[c][i] : 0.0;
+  if (own) {
+#pragma unroll
+    for (int c = 0; c < LP; ++c) small[kSmM + i * LP + c] = (i < l && c < l) ? x[c] : 0.0;
+  }
   if (i == 0 && bad) atomicOr(flags, (uint32_t)GIFT_FLAG_NONFINITE);
 }
 
