@@ -17,11 +17,11 @@
 // magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; no Inf or NaN.  Two codes per byte,
 // the even column in the low nibble.
 //
-// Tiling: quantiser, 4 lanes per block (one float4 each, a quad reduces the
-// block amax with two shuffles); dequant-sum, 32 codes per lane (two
+// Tiling: quantiser, one lane per 16-element block (four float4 loads, the
+// scale arithmetic once per block); dequant-sum, 32 codes per lane (two
 // blocks, one 16-byte load per replica).  Consecutive lanes take
-// consecutive columns of a row, so every load and store of a wave is
-// contiguous.
+// consecutive blocks (or code runs) of a row, so a wave's accesses cover
+// one contiguous range.
 #include "fp8_codec.hpp"
 #include "gift_internal.hpp"
 
@@ -56,6 +56,9 @@ __device__ __forceinline__ float fp4_tscale(uint32_t am) {
   return (float)((double)__uint_as_float(am) / kFp4TscaleDiv);
 }
 
+// One lane per 16-element block: four 16-byte loads, the block amax in
+// registers, the scale arithmetic once per block, one 8-byte code store and
+// one scale byte (consecutive lanes take consecutive blocks of a row).
 template <bool EF>
 __global__ void __launch_bounds__(256) k_quantize_fp4(const float* __restrict__ x, int64_t ld, int m, int d,
                                                       const uint32_t* __restrict__ slot,
@@ -63,36 +66,43 @@ __global__ void __launch_bounds__(256) k_quantize_fp4(const float* __restrict__ 
                                                       uint8_t* __restrict__ codes, uint8_t* __restrict__ bscales,
                                                       float* __restrict__ tscale, float* __restrict__ resid,
                                                       uint32_t* __restrict__ flags) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int q4 = d >> 2;                                   // float4 groups per row
-  const int64_t n4 = (int64_t)m * q4;
-  const bool in = t < n4;                                  // n4 is a multiple of 4: quads are all in or all out
-  const int row = in ? (int)(t / q4) : 0;
-  const int col = in ? (int)(t % q4) * 4 : 0;
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;   // block index, row-major
+  const int bpr = d / kFp4Block;
+  const int64_t nb = (int64_t)m * bpr;
   const uint32_t am_t = amax_in ? (__float_as_uint(amax_in[0]) & 0x7FFFFFFFu) : slot[0];
   const float g = fp4_tscale(am_t);
-  if (t == 0) {
+  if (b == 0) {
     tscale[0] = g;
     if (amax_out) amax_out[0] = __uint_as_float(slot[0]);
     if (am_t >= 0x7F800000u) atomicOr(flags, (uint32_t)GIFT_FLAG_NONFINITE);
   }
-  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (in) {
-    v = *reinterpret_cast<const float4*>(x + (int64_t)row * ld + col);
-    if constexpr (EF) {
-      const float4 e = *reinterpret_cast<const float4*>(resid + (int64_t)row * d + col);
-      v.x += e.x;
-      v.y += e.y;
-      v.z += e.z;
-      v.w += e.w;
+  if (b >= nb) return;
+  const int row = (int)(b / bpr), col = (int)(b % bpr) * kFp4Block;
+  float v[16];
+  const float* src = x + (int64_t)row * ld + col;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float4 q = *reinterpret_cast<const float4*>(src + 4 * k);
+    v[4 * k] = q.x;
+    v[4 * k + 1] = q.y;
+    v[4 * k + 2] = q.z;
+    v[4 * k + 3] = q.w;
+  }
+  float* rp = resid + (int64_t)row * d + col;
+  if constexpr (EF) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float4 e = *reinterpret_cast<const float4*>(rp + 4 * k);
+      v[4 * k] += e.x;
+      v[4 * k + 1] += e.y;
+      v[4 * k + 2] += e.z;
+      v[4 * k + 3] += e.w;
     }
   }
-  // block amax over the quad (|x| bit patterns order like |x|, NaN on top)
-  auto ab = [](float f) { return __float_as_uint(f) & 0x7FFFFFFFu; };
-  uint32_t mx = max(max(ab(v.x), ab(v.y)), max(ab(v.z), ab(v.w)));
-  mx = max(mx, (uint32_t)__shfl_xor((int)mx, 1, 64));
-  mx = max(mx, (uint32_t)__shfl_xor((int)mx, 2, 64));
-  if (!in) return;
+  // block amax (|x| bit patterns order like |x|, NaN on top)
+  uint32_t mx = 0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) mx = max(mx, __float_as_uint(v[k]) & 0x7FFFFFFFu);
   float sig;
   if (g != g) sig = __uint_as_float(0x7FC00000u);
   else if (g == 0.0f) sig = 0.0f;
@@ -101,27 +111,35 @@ __global__ void __launch_bounds__(256) k_quantize_fp4(const float* __restrict__ 
   const float S = dec_e4m3(sc) * g;
   const bool bad = S != S;
   const float r = S > 0.0f ? (float)(1.0 / (double)S) : 0.0f;
-  uint32_t c0 = enc_e2m1(v.x * r), c1 = enc_e2m1(v.y * r), c2 = enc_e2m1(v.z * r), c3 = enc_e2m1(v.w * r);
-  if (bad) c0 = c1 = c2 = c3 = 0u;
-  *reinterpret_cast<uint16_t*>(codes + (int64_t)row * (d >> 1) + (col >> 1)) =
-      (uint16_t)(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
-  if ((col & (kFp4Block - 1)) == 0) {
-    bscales[(int64_t)row * (d / kFp4Block) + col / kFp4Block] = (uint8_t)sc;
-    if (bad && g == g) atomicOr(flags, (uint32_t)GIFT_FLAG_NONFINITE);   // a NaN block under a finite tensor scale
+  uint32_t c[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) c[k] = bad ? 0u : enc_e2m1(v[k] * r);
+  uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    w0 |= c[k] << (4 * k);
+    w1 |= c[8 + k] << (4 * k);
   }
+  *reinterpret_cast<uint2*>(codes + (int64_t)row * (d >> 1) + (col >> 1)) = make_uint2(w0, w1);
+  bscales[b] = (uint8_t)sc;
+  if (bad && g == g) atomicOr(flags, (uint32_t)GIFT_FLAG_NONFINITE);   // a NaN block under a finite tensor scale
   if constexpr (EF) {
     // new residual fp32(u - S dec(q)), the difference rounded once
-    const float4 e = make_float4(__builtin_fmaf(-S, dec_e2m1(c0), v.x), __builtin_fmaf(-S, dec_e2m1(c1), v.y),
-                                 __builtin_fmaf(-S, dec_e2m1(c2), v.z), __builtin_fmaf(-S, dec_e2m1(c3), v.w));
-    *reinterpret_cast<float4*>(resid + (int64_t)row * d + col) = e;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      *reinterpret_cast<float4*>(rp + 4 * k) =
+          make_float4(__builtin_fmaf(-S, dec_e2m1(c[4 * k]), v[4 * k]),
+                      __builtin_fmaf(-S, dec_e2m1(c[4 * k + 1]), v[4 * k + 1]),
+                      __builtin_fmaf(-S, dec_e2m1(c[4 * k + 2]), v[4 * k + 2]),
+                      __builtin_fmaf(-S, dec_e2m1(c[4 * k + 3]), v[4 * k + 3]));
   }
 }
 
 hipError_t launch_quantize_fp4(const float* x, int64_t ld, int m, int d, const uint32_t* slot, const float* amax_in,
                                float* amax_out, uint8_t* codes, uint8_t* bscales, float* tscale, float* resid,
                                uint32_t* flags, hipStream_t s) {
-  const int64_t n4 = (int64_t)m * (d / 4);
-  const unsigned blocks = (unsigned)cdiv(n4 > 0 ? n4 : 1, 256);   // one thread at least: it writes the tensor scale
+  const int64_t nb = (int64_t)m * (d / kFp4Block);
+  const unsigned blocks = (unsigned)cdiv(nb > 0 ? nb : 1, 256);   // one thread at least: it writes the tensor scale
   if (resid)
     hipLaunchKernelGGL(k_quantize_fp4<true>, dim3(blocks), dim3(256), 0, s, x, ld, m, d, slot, amax_in, amax_out,
                        codes, bscales, tscale, resid, flags);
