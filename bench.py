@@ -51,8 +51,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (the multi-GPU reduce-scatter / all-gather "
-              "exchange is a design, not built); use --gpus 1", file=sys.stderr)
+        print("bench.py: runs on one GPU only (the multi-GPU reduce-scatter / all-gather exchange is not "
+              "implemented); use --gpus 1", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
