@@ -41,10 +41,12 @@ def parse():
     p.add_argument("--scaling", default="tensor", choices=["tensor", "block"])
     p.add_argument("--sets", type=int, default=4)
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
-    p.add_argument("--config", default="unit", choices=["unit", "selective", "stress"],
+    p.add_argument("--config", default="unit", choices=["unit", "selective", "stress", "slab"],
                    help="unit: the headline encode + decode unit (default); selective: the whole "
                         "600M-class gradient buffer (168 tensors, 13 rank-32); stress: one step of "
-                        "the 4096 x 16384 stress layer (statistics, refresh, encode, decode R = 16)")
+                        "the 4096 x 16384 stress layer (statistics, refresh, encode, decode R = 16); "
+                        "slab: one GPU's share of the row-slab exchange at R = 8 (the kernels between "
+                        "the collectives, which are not run)")
     return p.parse_args()
 
 
@@ -66,6 +68,8 @@ def main():
         return bench_selective(args, torch, fw, synth, dev)
     if args.config == "stress":
         return bench_stress(args, torch, fw, synth, dev)
+    if args.config == "slab":
+        return bench_slab(args, torch, fw, synth, dev)
     m, d, T, R, k = 1536, 6144, 16384, 8, 32
     scaling = fw.SCALINGS[args.scaling]
     nb = fw.nblocks(m, d, scaling)
@@ -531,6 +535,102 @@ def bench_stress(args, torch, fw, synth, dev):
                                   "unit": "GB/s", "frac": round(alg4 / (t_fp4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                   "alg_bytes": int(alg4),
                                   "work": "encode of replica 0 and decode-reduce of 16 FP4 payloads"}},
+    }
+    print(json.dumps(result), flush=True)
+
+
+def bench_slab(args, torch, fw, synth, dev):
+    """One GPU's share of the row-slab exchange for the 1536 x 6144 rank-32
+    layer at R = 8 GPUs (the multi-GPU design: every GPU encodes its whole
+    gradient in whitened coordinates; an all-to-all gives GPU g the 192-row
+    slab g of all 8 payloads; it dequantises and sums them and requantises
+    the mean in whitened coordinates with one scale shared by all slabs (an
+    AllReduceMax of the slab amax); an all-gather brings every GPU all 8
+    requantised slabs, one tensor with one scale; each unwhitens it, R = 1).
+    Timed: GPU 0's kernels before, between and after the collectives (the
+    encode of its gradient, slab dequant-sum, slab amax, requantise,
+    unwhitening of the gathered tensor, one launch each); the collectives
+    are not run (one GPU): the shared amax and the other slabs come from
+    setup."""
+    m, d, T, R, k = 1536, 6144, 16384, 8, 32
+    rows = m // R
+    case = synth.make_layer(4, device=dev, R=R)
+    L = fw.Layer(m, d, "lowrank", rank=k, oversample=16, power_iters=4, ema_decay=0.0, device=dev)
+    L.accumulate_stats(case.a_steps[0], fw.SIDE_A, commit=True)
+    L.refresh(case.omega)
+    codes = torch.empty(R, m, d, dtype=torch.uint8, device=dev)
+    scales = torch.empty(R, 1, dtype=torch.float32, device=dev)
+    for r in range(R):
+        L.encode(case.W[r], fw.E4M3, fw.SCALE_TENSOR, codes=codes[r], scales=scales[r])
+    Le = fw.Layer(rows, d, "euclid", device=dev)          # slab reduce, amax and requantise
+    mean = torch.empty(rows, d, dtype=torch.float32, device=dev)
+    gathered = torch.empty(1, m, d, dtype=torch.uint8, device=dev)   # the all-gather's result
+    gscale = torch.empty(1, 1, dtype=torch.float32, device=dev)
+    am_local = torch.empty(1, dtype=torch.float32, device=dev)
+    out = torch.empty(m, d, dtype=torch.float32, device=dev)
+    # setup: every slab's mean and amax (the AllReduceMax's inputs), then the
+    # other GPUs' requantised slabs with the shared scale
+    ams = []
+    for g in range(R):
+        Le.decode_reduce(codes[:, g * rows:(g + 1) * rows, :], scales, fw.E4M3, fw.SCALE_TENSOR, out=mean)
+        a = torch.empty(1, dtype=torch.float32, device=dev)
+        Le.encode(mean, fw.E4M3, fw.SCALE_TENSOR, amax_out=a, want_codes=False)
+        ams.append(a)
+    shared = torch.stack(ams).max(dim=0).values
+    for g in range(1, R):
+        Le.decode_reduce(codes[:, g * rows:(g + 1) * rows, :], scales, fw.E4M3, fw.SCALE_TENSOR, out=mean)
+        Le.encode(mean, fw.E4M3, fw.SCALE_TENSOR, amax_in=shared, codes=gathered[0, g * rows:(g + 1) * rows],
+                  scales=gscale[0])
+    slab0 = codes[:, :rows, :]
+
+    def encode_own():   # this GPU's whole gradient, before the all-to-all
+        L.encode(case.W[0], fw.E4M3, fw.SCALE_TENSOR, codes=codes[0], scales=scales[0])
+
+    def reduce():
+        Le.decode_reduce(slab0, scales, fw.E4M3, fw.SCALE_TENSOR, out=mean)
+
+    def requant():
+        Le.encode(mean, fw.E4M3, fw.SCALE_TENSOR, amax_out=am_local, want_codes=False)   # into the AllReduceMax
+        Le.encode(mean, fw.E4M3, fw.SCALE_TENSOR, amax_in=shared, codes=gathered[0, :rows], scales=gscale[0])
+
+    def unwhiten():
+        L.decode_reduce(gathered, gscale, fw.E4M3, fw.SCALE_TENSOR, out=out)
+
+    def step():
+        encode_own()
+        reduce()
+        requant()
+        unwhiten()
+
+    steps = max(1, args.steps)
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    ms = _event_ms(torch, step, steps)
+    t_encode = _event_ms(torch, encode_own, steps)
+    t_reduce = _event_ms(torch, reduce, steps)
+    t_requant = _event_ms(torch, requant, steps)
+    t_unwhiten = _event_ms(torch, unwhiten, steps)
+    torch.cuda.synchronize()
+    assert L.flags() == 0 and Le.flags() == 0
+    n_slab, n = rows * d, m * d
+    alg = ((4.0 * n + n + d * 32 * 4) + (R * n_slab + 4.0 * n_slab) + (4.0 * n_slab) + (4.0 * n_slab + n_slab)
+           + (n + 4.0 * n + d * 32 * 4))
+    ingress = 2 * (R - 1) * n_slab            # FP8 bytes in per GPU: all-to-all + all-gather
+    result = {
+        "metric": "row-slab exchange, one GPU's kernels: GB/s of the fp32 gradient (1536x6144, r=32, R=8)",
+        "value": round(4.0 * n / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic (the unit's layer and payloads), warm",
+        "config": {"workload": f"GPU 0 of {R}: slab of {rows} rows x {d}, E4M3, one requantisation scale "
+                               "shared by the slabs", "rows_per_gpu": rows, "replicas": R},
+        "stages_ms": {"encode_own": round(t_encode, 5), "slab_dequant_sum": round(t_reduce, 5), "slab_amax_and_requantise": round(t_requant, 5),
+                      "unwhiten_gathered": round(t_unwhiten, 5)},
+        "roofline": {"bound": "hbm", "achieved": round(alg / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "alg_bytes": int(alg)},
+        "exchange": {"fp8_ingress_bytes_per_gpu": int(ingress),
+                     "fp32_ring_allreduce_ingress_bytes_per_gpu": int(2 * (R - 1) * 4 * n_slab),
+                     "note": "not run: one GPU"},
     }
     print(json.dumps(result), flush=True)
 
