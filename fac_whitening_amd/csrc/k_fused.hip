@@ -741,10 +741,31 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
           for (int e = 0; e < 4; ++e) x[i][4 * grp + e] = c[e];
         }
       }
+      if constexpr (!ENC) {
+        // decode: the column block's three sub-tiles are final; store them
+        // from the registers while the next block's products run (two
+        // 16-byte stores per sub-tile and lane: row 16 rb + lr, columns
+        // c .. c + 3 and c + 16 .. c + 19)
+        const auto orr = make_rsrc(a.out, ((int64_t)(m - 1) * a.ldo + d) * 4);
+#pragma unroll
+        for (int rb = 0; rb < 3; ++rb) {
+          const int i = q * 3 + rb;
+          const int row = row0 + 16 * rb + lr, c = col0 + 32 * SUB_CB(i) + 4 * lg;
+          const int o = (int)(((int64_t)row * a.ldo + c) * 4);
+          const int32x4 v0 = {__float_as_int(x[i][0]), __float_as_int(x[i][1]), __float_as_int(x[i][2]),
+                              __float_as_int(x[i][3])};
+          const int32x4 v1 = {__float_as_int(x[i][4]), __float_as_int(x[i][5]), __float_as_int(x[i][6]),
+                              __float_as_int(x[i][7])};
+          __builtin_amdgcn_raw_buffer_store_b128(v0, orr, (row < m && c < d) ? o : kOff, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(v1, orr, (row < m && c + 16 < d) ? o + 64 : kOff, 0, 0);
+        }
+      }
     }
   }
 
   }   // LR
+
+  if constexpr (LR && !ENC) return;   // the decode stored its sub-tiles above
 
   if (!enc) {
     // ---- decode: store W^ --------------------------------------------------
