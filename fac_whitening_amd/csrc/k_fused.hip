@@ -367,37 +367,37 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
     // the projection operands first: loads complete in order, so the
     // projection of a row block then waits for that block's data only
     if constexpr (LR) load_uops(a.ub, d, cbg0, uo);
-    int32x4 v[2 * kCPT];   // chunks 6 rb .. 6 rb + 5 hold row block rb
-#pragma unroll
-    for (int j = 0; j < 2 * kCPT; ++j) {
-      const int q = tid + 512 * j, r = q / 192, c = (q % 192) * 4;
-      const bool ok = row0 + r < m && col0 + c < d;
-      v[j] = __builtin_amdgcn_raw_buffer_load_b128(wr, ok ? (int)(((int64_t)(row0 + r) * a.ldw + col0 + c) * 4) : kOff,
-                                                   0, 0);
-    }
     if constexpr (LR) {
-      // each 16-row block is staged, read back in the sub-tile layout and
-      // projected as soon as it lands, while the later blocks stream in
+      // each lane loads its sub-tiles directly (row 16 rb + lr, columns
+      // c .. c + 3 and c + 16 .. c + 19), row block by row block; loads
+      // complete in order, so the projection of a row block waits for that
+      // block only while the later blocks stream in
 #pragma unroll
-      for (int rb = 0; rb < 3; ++rb) {
-#pragma unroll
-        for (int j = 6 * rb; j < 6 * rb + 6; ++j) {
-          const int q = tid + 512 * j, r = q / 192, c = (q % 192) * 4;
-          *reinterpret_cast<int32x4*>(smem + r * kTilePad + c) = v[j];
-        }
-        __syncthreads();
+      for (int rb = 0; rb < 3; ++rb)
 #pragma unroll
         for (int q = 0; q < 3; ++q) {
-          const float* src = smem + (rb * 16 + lr) * kTilePad + (wave + 8 * q) * 32 + 4 * lg;
-          const float4 v0 = *reinterpret_cast<const float4*>(src);
-          const float4 v1 = *reinterpret_cast<const float4*>(src + 16);
+          const int row = row0 + 16 * rb + lr, c = col0 + 32 * (wave + 8 * q) + 4 * lg;
+          const int o = (int)(((int64_t)row * a.ldw + c) * 4);
+          const int32x4 v0 = __builtin_amdgcn_raw_buffer_load_b128(wr, (row < m && c < d) ? o : kOff, 0, 0);
+          const int32x4 v1 = __builtin_amdgcn_raw_buffer_load_b128(wr, (row < m && c + 16 < d) ? o + 64 : kOff, 0, 0);
           float* xi = x[q * 3 + rb];
-          xi[0] = v0.x; xi[1] = v0.y; xi[2] = v0.z; xi[3] = v0.w;
-          xi[4] = v1.x; xi[5] = v1.y; xi[6] = v1.z; xi[7] = v1.w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            xi[e] = __int_as_float(v0[e]);
+            xi[4 + e] = __int_as_float(v1[e]);
+          }
         }
-        project_rb(rb);
-      }
+#pragma unroll
+      for (int rb = 0; rb < 3; ++rb) project_rb(rb);
     } else {
+      int32x4 v[2 * kCPT];
+#pragma unroll
+      for (int j = 0; j < 2 * kCPT; ++j) {
+        const int q = tid + 512 * j, r = q / 192, c = (q % 192) * 4;
+        const bool ok = row0 + r < m && col0 + c < d;
+        v[j] = __builtin_amdgcn_raw_buffer_load_b128(wr, ok ? (int)(((int64_t)(row0 + r) * a.ldw + col0 + c) * 4) : kOff,
+                                                     0, 0);
+      }
 #pragma unroll
       for (int j = 0; j < 2 * kCPT; ++j) {
         const int q = tid + 512 * j, r = q / 192, c = (q % 192) * 4;
