@@ -1,5 +1,5 @@
 // Flat gradient buckets: the Euclidean FP8 codec over many tensors in one
-// launch per phase (GIFT 阅读笔记, Algorithm 1 lines 3-8: Scale,
+// launch per phase (GIFT 阅读笔记, Algorithm 1, the Euclidean branch: Scale,
 // AllReduceMax, Q, AllReduceSum, Dequantize / N for every layer outside the
 // selected set).  Scales per tensor, or per 512 consecutive elements of a
 // tensor (the per-block Euclidean baseline of the experiment setup, block

@@ -56,7 +56,7 @@ enum {
 
 /* Change of coordinates applied before quantisation ([Note] Algorithm 1). */
 enum gift_transform {
-  GIFT_EUCLID = 0,          /* none: the Euclidean FP8 baseline ([Note] Algorithm 1, lines 3-8) */
+  GIFT_EUCLID = 0,          /* none: the Euclidean FP8 baseline ([Note] Algorithm 1, the Euclidean branch) */
   GIFT_DIAG = 1,            /* T_A = diag((A_ii + lam)^-1/2) ([Note] §简化二, Table II "diagonal") */
   GIFT_LOWRANK = 2,         /* T_A = U diag((Lt)^-1/2 - rho^-1/2) U^T + rho^-1/2 I, rank k
                                ([Note] §简化二, Eq. (17); the form is this library's reading) */
@@ -170,8 +170,8 @@ gift_status gift_refresh_factors(gift_layer_t layer, const float* d_omega, void*
                                  size_t work_bytes, gift_stream_t stream);
 
 /* ---------------------------------------------------------------------------
- * Encode one replica's gradient ([Note] Algorithm 1, lines 10-13 without
- * error feedback (see gift_encode_ef); Euclidean lines 4-6):
+ * Encode one replica's gradient ([Note] Algorithm 1, the geometry branch without
+ * error feedback (see gift_encode_ef); the Euclidean branch's scale and quantise):
  *   W~ = W T_A (two-sided: L_G^-1 W T_A), amax per tensor or per 128x128
  *   tile (edge tiles: their valid region), r = fp32(FMAX / amax),
  *   code = FP8(fp32(w~ * r)) with round-to-nearest-even (ties to the even
@@ -193,7 +193,7 @@ gift_status gift_encode(gift_layer_t layer, const float* d_W, int64_t ldw, int32
                         size_t work_bytes, gift_stream_t stream);
 
 /* ---------------------------------------------------------------------------
- * Encode with error feedback ([Note] Algorithm 1, lines 10-15: the
+ * Encode with error feedback ([Note] Algorithm 1, the geometry branch with its error-feedback steps: the
  * residual of the previous step is added in the whitened coordinates):
  *   U~ = fp32(W~ + R), amax, scale and codes of U~ exactly as gift_encode
  *   computes them for W~, then R <- fp32(U~ - s dec(code)) (the difference
@@ -214,8 +214,9 @@ gift_status gift_encode_ef(gift_layer_t layer, const float* d_W, int64_t ldw, in
                            void* d_work, size_t work_bytes, gift_stream_t stream);
 
 /* ---------------------------------------------------------------------------
- * Decode-reduce R replica payloads ([Note] Eq. (1) and Algorithm 1, lines
- * 20-22; the payloads of R workers held in one GPU's memory):
+ * Decode-reduce R replica payloads ([Note] Eq. (1) and Algorithm 1, the
+ * geometry branch's AllReduceSum, Dequantize / N and map back; the payloads
+ * of R workers held in one GPU's memory):
  *   U = (1/R) sum_{r=0..R-1} s_r dec(q_r) (fp32, r in increasing order),
  *   W^ = U T_A^-1 (two-sided: L_G U L_A^T), written as fp32.
  * d_codes:      replica r at d_codes + r * code_stride (bytes), [d_out][d_in]
@@ -273,7 +274,7 @@ gift_status gift_decode_reduce_fp4(gift_layer_t layer, const uint8_t* d_codes, i
 
 /* ---------------------------------------------------------------------------
  * Flat gradient buckets: the Euclidean FP8 path of every layer outside the
- * selected set ([Note] Algorithm 1, lines 3-8) over a whole buffer of
+ * selected set ([Note] Algorithm 1, the Euclidean branch) over a whole buffer of
  * tensors, one launch per phase.
  *
  * A bucket describes n tensors of h_numel[i] fp32 elements (each a multiple
@@ -295,7 +296,7 @@ gift_status gift_decode_reduce_fp4(gift_layer_t layer, const uint8_t* d_codes, i
  * gift_bucket_sizes: total elements, number of scales, and the workspace
  *   bytes gift_bucket_encode needs for a local amax.
  * gift_bucket_amax: d_amax_out fp32 [nscales] = the amax of every scale
- *   block (for the AllReduceMax of Algorithm 1, line 5).
+ *   block (for the AllReduceMax of Algorithm 1's Euclidean branch).
  * gift_bucket_encode: codes uint8 [numel] and scales fp32 [nscales] with the
  *   shared amax d_amax_in (NULL: the local one, computed first into d_work);
  *   d_amax_out NULL or fp32 [nscales] receives the local amax.
@@ -319,7 +320,7 @@ gift_status gift_bucket_decode_reduce(gift_bucket_t bucket, const uint8_t* d_cod
                                       const float* d_scales, int64_t scale_stride, int32_t R,
                                       int32_t fmt, float* d_out, gift_stream_t stream);
 
-/* Scale-sync schedule ([Note] Algorithm 1, lines 16-19): the geometry-aware
+/* Scale-sync schedule ([Note] Algorithm 1, its scale-sync step): the geometry-aware
  * layers quantise with their local scale and, on a scale-sync step, with the
  * scale shared across workers (the AllReduceMax of the local amaxes: an
  * amax-only gift_encode / gift_encode_ef per replica, then the call with

@@ -47,7 +47,7 @@ R9  Knee (Note §简化三, "the layers before the sharp drop"): cut after the
     ratio; 0/0 counts as 1; ties go to the smallest i).
 R10 EMA of A (not on the pages): the first commit sets A to the batch
     statistics, later commits A <- beta A + (1 - beta) A_batch.
-R11 Error feedback (Note 算法 1, lines 11-15): the residual is added to the
+R11 Error feedback (Note 算法 1, its error-feedback steps): the residual is added to the
     whitened tensor in float32 (U~ = fp32(W~ + R)), U~ is scaled and
     quantised, and the new residual is the float32 rounding of
     U~ - s dec(q) (one rounding of the exact difference).  The whitened
@@ -323,7 +323,7 @@ def dequant_reduce(codes_list, scales_list, fmt: str, scaling: str) -> np.ndarra
 
 
 # ---------------------------------------------------------------------------
-# Flat buckets of Euclidean tensors (Algorithm 1, lines 3-8; R13)
+# Flat buckets of Euclidean tensors (Algorithm 1, the Euclidean branch; R13)
 # ---------------------------------------------------------------------------
 
 FLAT_BLOCK = 512
@@ -516,7 +516,7 @@ def encode(W, T, fmt: str, scaling: str, L_G=None, amax_in=None):
 
 
 def encode_ef(W, T, R, fmt: str, scaling: str, L_G=None, amax_in=None):
-    """[Note] Algorithm 1 with error feedback (lines 10-15, R11): whiten,
+    """[Note] Algorithm 1 with error feedback (the geometry branch, R11): whiten,
     add the residual, scale, quantise, and carry the quantisation error of
     U~ to the next step.  R is the float32 residual [m][d] of the previous
     step (zeros at the first).  Returns dict(whitened, u_tilde, codes,
@@ -528,7 +528,7 @@ def encode_ef(W, T, R, fmt: str, scaling: str, L_G=None, amax_in=None):
 
 
 def error_feedback(Wt, R, fmt: str, scaling: str, amax_in=None):
-    """The error-feedback step of [Note] Algorithm 1 (lines 11-15, R11) on
+    """The error-feedback step of [Note] Algorithm 1 (its error-feedback steps, R11) on
     an already whitened float32 tensor Wt: U~ = fp32(Wt + R), scale and
     quantise U~, new residual fp32(U~ - s dec(q)).  Returns dict(u_tilde,
     codes, scales, amax, residual)."""

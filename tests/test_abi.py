@@ -66,7 +66,7 @@ def test_host_side_checks_without_gpu():
 
 
 def test_scale_sync_schedule():
-    """Algorithm 1, lines 16-19: local scales by default, a shared scale on
+    """Algorithm 1, its scale-sync step: local scales by default, a shared scale on
     every period-th step from step 0; period <= 0 never syncs."""
     import fac_whitening_amd as fw
     assert [fw.scale_sync_due(t, 4) for t in range(9)] == [True, False, False, False, True, False, False, False, True]

@@ -2,7 +2,7 @@
 whole buffer of tensors in one launch per phase, per tensor or per 512
 elements, against the oracle.
 
-Pages: GIFT 阅读笔记 Algorithm 1, lines 3-8 (local amax, AllReduceMax, one
+Pages: GIFT 阅读笔记 Algorithm 1, the Euclidean branch (local amax, AllReduceMax, one
 shared scale, quantise, AllReduceSum, dequantise, divide by N) for every
 layer outside the selected set; the per-block Euclidean baseline with block
 size 512 (experiment setup; reading R13 of the oracle).

@@ -456,7 +456,7 @@ def test_layer_scores_mean_over_steps():
 
 
 # ---------------------------------------------------------------------------
-# Error feedback ([Note] 算法 1, lines 11-15; reading R11)
+# Error feedback ([Note] 算法 1, its error-feedback steps; reading R11)
 # ---------------------------------------------------------------------------
 
 def _spacing(y, fmt):
