@@ -361,7 +361,8 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
     }
   };
 
-  // ---- stream the tile in (flat, coalesced) and stage it in LDS --------------
+  // ---- stream the tile in: the rank-k encode straight into the sub-tile
+  // registers, the other kernels flat and coalesced through LDS -------------
   if constexpr (ENC) {
     const auto wr = make_rsrc(a.W, ((int64_t)(m - 1) * a.ldw + d) * 4);
     // the projection operands first: loads complete in order, so the
