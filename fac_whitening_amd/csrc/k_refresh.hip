@@ -175,13 +175,8 @@ __global__ void __launch_bounds__(256) k_gram_parts(const double* __restrict__ X
   }
 }
 
-// 1 / x and 1 / sqrt(x) from the hardware estimates and two Newton steps
-// each (about one ulp: the rotations stay orthogonal to rounding).
-__device__ __forceinline__ double rcp_nr(double x) {
-  double r = __builtin_amdgcn_rcp(x);
-  r = r * (2.0 - x * r);
-  return r * (2.0 - x * r);
-}
+// 1 / sqrt(x) from the hardware estimate and two Newton steps (about one
+// ulp: the rotations stay orthogonal to rounding).
 __device__ __forceinline__ double rsq_nr(double x) {
   double y = __builtin_amdgcn_rsq(x);
   y = y * (1.5 - 0.5 * x * y * y);
@@ -272,22 +267,25 @@ __global__ void __launch_bounds__(256) k_right_small(const double* __restrict__ 
   for (int c = 0; c < CPT; ++c) out[(int64_t)i * NC + g * CPT + c] = (TO)acc[c];
 }
 
-// Jacobi rotation annihilating B[p][q] (Golub & Van Loan, Alg. 8.5.1):
-// tau = (aqq - app) / (2 apq), t = sign(tau) / (|tau| + sqrt(1 + tau^2)),
-// c = 1 / sqrt(1 + t^2), s = t c.
+// Jacobi rotation annihilating B[p][q] (Golub & Van Loan, Alg. 8.5.1): with
+// d = aqq - app and a = 2 apq, t = tan(theta) = sg a / (|d| + sqrt(d^2 + a^2))
+// (sg = sign(d), t = sign(a) at d = 0: |t| = 1 there, either root
+// annihilates), c = 1 / sqrt(1 + t^2), s = t c.  Taken without a division:
+// with h = |d| + sqrt(d^2 + a^2), c = h / sqrt(h^2 + a^2) and
+// s = sg a / sqrt(h^2 + a^2).  d and a are first scaled by one power of two
+// so that no square overflows or underflows.  Caller: apq != 0.
 __device__ __forceinline__ void jacobi_rot(double app, double aqq, double apq, double& c, double& s) {
-  const double tau = (aqq - app) * rcp_nr(2.0 * apq);
-  const double at = fabs(tau);
-  double t;
-  if (at > 1e150) {
-    t = 0.5 * rcp_nr(tau);   // sqrt(1 + tau^2) = |tau| to double precision
-  } else {
-    const double u = 1.0 + tau * tau;
-    t = rcp_nr(at + u * rsq_nr(u));
-    if (tau < 0.0) t = -t;
-  }
-  c = rsq_nr(1.0 + t * t);
-  s = t * c;
+  double d = aqq - app, a = 2.0 * apq;
+  int e;
+  (void)frexp(fmax(fabs(d), fabs(a)), &e);
+  d = ldexp(d, -e);
+  a = ldexp(a, -e);   // max(|d|, |a|) in [0.5, 1)
+  const double h2 = fma(d, d, a * a);
+  const double h = fabs(d) + h2 * rsq_nr(h2);
+  const double num = d < 0.0 ? -a : a;
+  const double r = rsq_nr(fma(h, h, num * num));
+  c = h * r;
+  s = num * r;
 }
 
 // One workgroup: B (Q^T A Q, LP x LP, leading l x l used) symmetrised;
