@@ -334,6 +334,53 @@ def test_invariant_payload_is_quarter_of_fp32():
 
 
 # ---------------------------------------------------------------------------
+# Damping (reading R2: lam = 1e-3 tr(A) / n of the undamped statistics)
+# ---------------------------------------------------------------------------
+
+def test_damping_hand_values():
+    """lam = rel * tr(A) / n, from the diagonal only, written out by hand."""
+    assert G.damping(np.diag([1.0, 2.0, 3.0, 4.0])) == pytest.approx(2.5e-3, rel=1e-15)
+    assert G.damping(np.diag([1.0, 2.0, 3.0, 4.0]), rel=0.5) == pytest.approx(1.25, rel=1e-15)
+    # off-diagonal entries do not enter; n is the matrix order
+    assert G.damping(np.array([[2.0, 1.0], [1.0, 4.0]])) == pytest.approx(3e-3, rel=1e-15)
+    assert G.damping(np.full((3, 3), 7.0)) == pytest.approx(7e-3, rel=1e-15)
+
+
+def test_damping_enters_the_transforms_on_the_undamped_trace():
+    """The diagonal and Cholesky transforms of A = c I (d = 8) with the
+    damping written out by hand: lam = 1e-3 * (8 c) / 8 = 1e-3 c, so
+    T_A = (c + 1e-3 c)^-1/2 I.  A lam taken from the damped trace, or over
+    a wrong count, moves T_A by more than the tolerance."""
+    d, c = 8, 4.0
+    A = c * np.eye(d)
+    lam = G.damping(A)
+    assert lam == pytest.approx(4e-3, rel=1e-15)
+    want = (c * 1.001) ** -0.5
+    for kind in ("diag", "chol"):
+        T, Tinv, _ = G.build_transform(kind, A=A, lam=lam)
+        np.testing.assert_allclose(T, want * np.eye(d), rtol=1e-14, atol=0)
+        np.testing.assert_allclose(Tinv, np.eye(d) / want, rtol=1e-14, atol=0)
+
+
+def test_damping_on_a_spiked_lowrank_factor():
+    """A = Q diag(sigma) Q^T with k spikes and a flat tail c: the rank-k
+    factor with lam = 1e-3 tr(A) / d (tr(A) = sum sigma, computed from the
+    spectrum, not from A) gives rho = c + lam, Lt = sigma_k + lam and
+    T_A = (A + lam I)^-1/2 exactly."""
+    rng = np.random.default_rng(21)
+    d, k = 64, 6
+    A, Q, sig = _spiked(d, k, rng, c=0.02)
+    lam_hand = 1e-3 * float(sig.sum()) / d
+    assert G.damping(A) == pytest.approx(lam_hand, rel=1e-12)
+    f = G.lowrank_factor(A, rng.standard_normal((d, k + 8)), k, 4, G.damping(A))
+    assert f["rho"] == pytest.approx(0.02 + lam_hand, rel=1e-10)
+    np.testing.assert_allclose(f["lam_t"], sig[:k] + lam_hand, rtol=1e-10)
+    T, _ = G.transform_lowrank(f)
+    ref = (Q * (sig + lam_hand) ** -0.5) @ Q.T
+    np.testing.assert_allclose(T, ref, atol=1e-10 * np.abs(ref).max())
+
+
+# ---------------------------------------------------------------------------
 # Quantiser and reduction
 # ---------------------------------------------------------------------------
 
@@ -357,6 +404,48 @@ def test_quantize_blocks_bruteforce():
             tile = np.abs(X[bi * 128:(bi + 1) * 128, bj * 128:(bj + 1) * 128])
             ii, jj = np.unravel_index(np.argmax(tile), tile.shape)
             assert codes[bi * 128 + ii, bj * 128 + jj] & 0x7F == 0x7E
+
+
+def _e4m3_finite_values():
+    """Non-negative finite E4M3 values from the bit layout (bias 7, 3
+    mantissa bits; exponent 15 with mantissa 7 is NaN)."""
+    v = [m * 2.0 ** -9 for m in range(8)]
+    v += [(8 + m) * 2.0 ** (e - 10) for e in range(1, 16) for m in range(8) if not (e == 15 and m == 7)]
+    return np.array(v)
+
+
+def test_block_dequantize_exact_on_ragged_tiles():
+    """Per-128x128 round trip on a ragged 200 x 300 tensor (tiles of
+    128/72 rows and 128/128/44 columns): tile (i, j) holds E4M3 values
+    times 2^e_ij with one element at +-448 * 2^e_ij, every e_ij different.
+    Then r = 2^-e_ij and s = 2^e_ij exactly, every code is exact, and
+    dequantize() must give the tensor back bit for bit; a transposed or
+    shifted tile-to-scale map, or an edge tile read with the wrong extent,
+    scales some element by the wrong power of two."""
+    rng = np.random.default_rng(22)
+    m, d = 200, 300
+    vals = _e4m3_finite_values()
+    vals = vals[vals <= 448]
+    ex = np.array([[-7, 3, 11], [5, -2, 0]])
+    X = np.empty((m, d), np.float32)
+    for i in range(2):
+        for j in range(3):
+            rs, cs = slice(128 * i, min(m, 128 * i + 128)), slice(128 * j, min(d, 128 * j + 128))
+            h, w = rs.stop - rs.start, cs.stop - cs.start
+            v = rng.choice(vals, (h, w)) * rng.choice([-1.0, 1.0], (h, w))
+            v[h // 2, w // 3] = 448.0 * (-1) ** (i + j)
+            X[rs, cs] = v * 2.0 ** ex[i, j]
+    codes, scales, am = G.quantize(X, "e4m3", "block")
+    np.testing.assert_array_equal(scales, (2.0 ** ex).astype(np.float32))
+    np.testing.assert_array_equal(am, 448.0 * 2.0 ** ex)
+    back = G.dequantize(codes, scales, "e4m3", "block")
+    np.testing.assert_array_equal(back, X.astype(np.float64))
+    # the reduction of R copies of the same payload is that payload
+    U = G.dequant_reduce([codes] * 4, [scales] * 4, "e4m3", "block")
+    np.testing.assert_array_equal(U, X.astype(np.float64))
+    # and a transposed scale grid (2 x 3 -> 3 x 2 read back row-major) fails
+    bad = np.ascontiguousarray(scales.T).reshape(2, 3)
+    assert not np.array_equal(G.dequantize(codes, bad, "e4m3", "block"), back)
 
 
 def test_quantize_zero_and_nonfinite():
