@@ -11,7 +11,10 @@ separately, as is the encode alone, without and with error feedback
 Timed region: W untimed warmup steps, then K steps bracketed by
 torch.cuda.synchronize(); the input buffers rotate over 4 independent sets
 (W, 8 payloads, output: 604 MB in all, more than twice the 256 MB Infinity
-Cache) so each step reads inputs that are not cache-resident.
+Cache) so each step reads inputs that are not cache-resident.  The kernel
+durations behind `roofline` come from a second pass over the same K steps
+with HIP events around every call (event pairs lengthen the stream, so they
+stay out of the pass that `value` is measured on).
 
 Prints one JSON line (the metric, roofline of the dominant kernel, the oracle
 timed on the host cores as a baseline).
@@ -144,12 +147,8 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    # timed region: HIP events around every call of the dominant kernel
-    # (decode-reduce), on the stream the kernels use (torch's current
-    # stream).  Each event adds about 2.5 us to the step, so only the
-    # dominant call is bracketed.
-    dec_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    # batch boundaries: 5 batches of consecutive steps (median, p10, p90)
+    # Timed region: K steps back to back, with events only at the 5 batch
+    # boundaries (median, p10, p90); `value` comes from it.
     nbat = min(5, args.steps)
     bounds = [args.steps * j // nbat for j in range(nbat + 1)]
     bat_ev = {b: torch.cuda.Event(enable_timing=True) for b in bounds}
@@ -157,22 +156,31 @@ def main():
     wall0 = time.perf_counter()
     bat_ev[0].record()
     for i in range(args.steps):
-        W, codes, scales, out = sets[i % len(sets)]
-        L.encode(W, fw.E4M3, scaling, codes=codes[0], scales=scales[0])
-        dec_ev[i][0].record()
-        L.decode_reduce(codes, scales, fw.E4M3, scaling, out=out)
-        dec_ev[i][1].record()
+        step(i)
         if i + 1 in bat_ev:
             bat_ev[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    start, stop = bat_ev[0], bat_ev[args.steps]
-    total_ms = start.elapsed_time(stop)
+    total_ms = bat_ev[0].elapsed_time(bat_ev[args.steps])
     bat_ms = [bat_ev[bounds[j]].elapsed_time(bat_ev[bounds[j + 1]]) / (bounds[j + 1] - bounds[j])
               for j in range(nbat)]
-    t_dec = float(np.mean([a.elapsed_time(b) for a, b in dec_ev]))
-    t_enc = total_ms / args.steps - t_dec     # the rest of the step: encode and the event gaps
     ms_per_step = total_ms / args.steps
+    # Kernel durations: the same K steps again with HIP events around every
+    # encode and decode call, on the stream they run on (torch's current
+    # stream).  An event pair adds a few microseconds to the stream, so this
+    # pass is kept apart from the one `value` comes from.
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(args.steps):
+        W, codes, scales, out = sets[i % len(sets)]
+        L.encode(W, fw.E4M3, scaling, codes=codes[0], scales=scales[0])
+        evs[2 * i + 1].record()
+        L.decode_reduce(codes, scales, fw.E4M3, scaling, out=out)
+        evs[2 * i + 2].record()
+    torch.cuda.synchronize()
+    t_enc = float(np.mean([evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(args.steps)]))
+    t_dec = float(np.mean([evs[2 * i + 1].elapsed_time(evs[2 * i + 2]) for i in range(args.steps)]))
     grad_bytes = 4.0 * m * d
     value = grad_bytes / (ms_per_step * 1e-3) / 1e9         # GB/s of fp32 gradient
 
@@ -190,7 +198,8 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(kernel, args.scaling),
                 "kernel": kernel,
                 "unit_frac": round((enc_bytes + dec_bytes) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                "decode_ms": round(t_dec, 5), "rest_of_step_ms": round(t_enc, 5),
+                "decode_ms": round(t_dec, 5), "encode_ms": round(t_enc, 5),
+                "durations": "mean of event pairs around every call in a second pass over the K steps",
                 "alg_bytes_encode": int(enc_bytes), "alg_bytes_decode": int(dec_bytes)}
 
     # ---- beside the headline: batch spread, the unit with one buffer set
@@ -285,7 +294,7 @@ def main():
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(case, L, R, m, d, args.scaling)
+        result["cpu_baseline"] = cpu_baseline(case, L.buffers()["A"], R, m, d, args.scaling)
     print(json.dumps(result), flush=True)
 
 
@@ -635,36 +644,83 @@ def bench_slab(args, torch, fw, synth, dev):
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(case, L, R, m, d, scaling, budget_s=10.0, max_units=30):
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(case, A_gpu, R, m, d, scaling, budget_s=10.0, max_units=30):
     """The oracle (numpy fp64) on the same unit: encode of one replica +
     decode-reduce of R payloads, with the oracle's own dense T_A (built from
     the GPU's A outside the timed part).  Whole units are repeated until
-    about `budget_s` seconds of CPU work have run (at most `max_units`)."""
+    about `budget_s` seconds of CPU work have run (at most `max_units`), with
+    the BLAS threads numpy has; then one whole unit with one BLAS thread, and
+    each stage of the path on its own (statistics on a 2048-token sample
+    scaled to the layer's 16384 tokens, refresh, whiten, quantise,
+    decode-reduce)."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import gift as G
-    A = L.buffers()["A"].double().cpu().numpy()
+    A = A_gpu.double().cpu().numpy()
+    omega = case.omega.cpu().numpy()
     lam = G.damping(A)
-    T, Tinv = G.transform_lowrank(G.lowrank_factor(A, case.omega.cpu().numpy(), 32, 4, lam))
+    T, Tinv = G.transform_lowrank(G.lowrank_factor(A, omega, 32, 4, lam))
     Ws = [w.cpu().numpy() for w in case.W]
     pre = [G.encode(Ws[r], T, "e4m3", scaling) for r in range(1, R)]
-    units = 0
-    t0 = time.perf_counter()
-    while True:
+
+    def unit():
         e0 = G.encode(Ws[0], T, "e4m3", scaling)
         G.decode_reduce([e0["codes"]] + [p["codes"] for p in pre], [e0["scales"]] + [p["scales"] for p in pre],
                         Tinv, "e4m3", scaling)
+
+    units = 0
+    t0 = time.perf_counter()
+    while True:
+        unit()
         units += 1
         t = time.perf_counter() - t0
         if t >= budget_s or units >= max_units:
             break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": round(units * 4.0 * m * d / t / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+
+    def once(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    grad_gb = 4.0 * m * d / 1e9
+    with threadpool_limits(limits=1):
+        t1 = once(unit)
+    a = case.a_steps[0]
+    T_tok = a.shape[0]
+    sample = a[:2048].float().cpu().numpy()
+    enc0 = G.encode(Ws[0], T, "e4m3", scaling)
+    stages = {
+        "stats_ms": once(lambda: G.second_moment(sample)) * 1e3 * (T_tok / sample.shape[0]),
+        "refresh_ms": once(lambda: G.lowrank_factor(A, omega, 32, 4, lam)) * 1e3,
+        "whiten_ms": once(lambda: G.whiten(Ws[0], T)) * 1e3,
+        "quantise_ms": once(lambda: G.quantize(enc0["whitened"], "e4m3", scaling)) * 1e3,
+        "decode_reduce_ms": once(lambda: G.decode_reduce([enc0["codes"]] + [p["codes"] for p in pre],
+                                                         [enc0["scales"]] + [p["scales"] for p in pre], Tinv,
+                                                         "e4m3", scaling)) * 1e3,
+    }
+    return {"value": round(units * grad_gb / t, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{units} full units (encode 1 replica + decode-reduce 8) at 1536x6144, numpy fp64 "
                       "with dense T_A, BLAS threads as listed",
-            "seconds": round(t, 3), "affinity_cpus": len(os.sched_getaffinity(0))}
+            "seconds": round(t, 3), "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": _cpu_model(),
+            "one_thread": {"value": round(grad_gb / t1, 4), "unit": "GB/s", "seconds": round(t1, 3),
+                           "sample": "1 full unit, BLAS limited to 1 thread"},
+            "stages_ms": {k: round(v, 1) for k, v in stages.items()},
+            "stages_note": "one run each with the BLAS threads above; statistics timed on 2048 of the 16384 "
+                           "tokens and scaled"}
 
 
 def kernel_source_sha():

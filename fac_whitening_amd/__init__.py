@@ -45,7 +45,7 @@ EXPORTS = [
     "gift_profiler_workspace_bytes", "gift_profile_step", "gift_select_layers", "gift_status_string",
     "gift_last_hip_error", "gift_set_fused", "gift_bucket_table_bytes", "gift_bucket_create",
     "gift_bucket_destroy", "gift_bucket_sizes", "gift_bucket_flags", "gift_bucket_amax", "gift_bucket_encode",
-    "gift_bucket_decode_reduce", "gift_scale_sync_due",
+    "gift_bucket_decode_reduce", "gift_scale_sync_due", "gift_set_max_resident", "gift_layer_route",
 ]
 
 
@@ -91,6 +91,8 @@ _sig("gift_select_layers", _i32, _vp, _i32, _P(ctypes.c_double), _P(_i32), _P(_i
 _sig("gift_status_string", ctypes.c_char_p, _i32)
 _sig("gift_last_hip_error", _i32)
 _sig("gift_set_fused", _i32, _i32)
+_sig("gift_set_max_resident", _i32, _i32)
+_sig("gift_layer_route", _i32, _vp, _i32, _i64, _i32, _P(_i32))
 _sig("gift_bucket_table_bytes", _sz, _i32)
 _sig("gift_bucket_create", _i32, _i32, _P(_i64), _i32, _vp, _sz, _vp, _P(_vp))
 _sig("gift_bucket_destroy", _i32, _vp)
@@ -106,6 +108,12 @@ def set_fused(enable: bool) -> bool:
     """Select the persistent single-launch rank-k kernels (True, default) or
     the multi-kernel path (False); returns the previous setting."""
     return bool(_lib.gift_set_fused(1 if enable else 0))
+
+
+def set_max_resident(max_groups: int) -> int:
+    """Cap the workgroups persistent launches may count on being resident at
+    once (0: the device's own limit); returns the previous cap."""
+    return int(_lib.gift_set_max_resident(int(max_groups)))
 
 
 class GiftError(RuntimeError):
@@ -214,6 +222,14 @@ class Layer:
                 cnt *= s
             out[n] = self.state[off:off + 4 * cnt].view(torch.float32).view(*shapes[n])
         return out
+
+    def route(self, op: str, ld=None, R: int = 1) -> str:
+        """'fused' or 'multi': the route gift_encode (op='encode') or
+        gift_decode_reduce (op='decode') takes for this layer now."""
+        f = _i32()
+        _check(_lib.gift_layer_route(self._h, 0 if op == "encode" else 1, self.d if ld is None else ld, R,
+                                     ctypes.byref(f)), "gift_layer_route")
+        return "fused" if f.value else "multi"
 
     def mark_ready(self, stream=None):
         _check(_lib.gift_layer_mark_ready(self._h, _stream(stream)), "gift_layer_mark_ready")

@@ -11,6 +11,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -99,19 +100,91 @@ int device_cus() {
   return cache[dev];
 }
 
-// The fused path keeps every tile resident (one 512-thread workgroup per
-// compute unit at most), so it is taken when the tiles fit on the device.
-// The Euclidean codec takes the same kernels without the transform.
-bool fused_ok(const gift_layer_desc& g) {
+int g_max_resident = 0;   // gift_set_max_resident (0: the device's own limit)
+
+// Workgroups the persistent kernels may count on being resident at once.
+int resident_limit(int device_limit) {
+  if (device_limit <= 0) return 0;
+  return g_max_resident > 0 && g_max_resident < device_limit ? g_max_resident : device_limit;
+}
+
+// Buffer resources of the fused kernels address up to 2 GiB from a base
+// with 32-bit offsets (an offset of 2^31 marks a dropped access), so every
+// span they touch must stay below 2^31 bytes.
+bool span_ok(int m, int d, int64_t ld) {
+  const int64_t lim = (int64_t)1 << 31;
+  return ((int64_t)(m - 1) * ld + d) * 4 < lim && (int64_t)m * d * 4 < lim;
+}
+
+// The fused path keeps every tile resident (its workgroups wait on one
+// another), so it is taken when all tiles fit on the device at once (the
+// occupancy of the fused kernels times the compute units, or the cap set by
+// gift_set_max_resident) and the buffers fit the 32-bit offsets.  The
+// Euclidean codec takes the same kernels without the transform.
+bool fused_ok(const gift_layer_desc& g, int64_t ld) {
   if (!g_fused_enabled || (g.transform != GIFT_LOWRANK && g.transform != GIFT_EUCLID)) return false;
+  if (!span_ok(g.d_out, g.d_in, ld)) return false;
   const int64_t tiles = (int64_t)fused_groups(g) * fused_cg(g);
-  const int cus = device_cus();
-  return cus > 0 && tiles <= cus;
+  const int cap = resident_limit(gift::fused_resident_groups());
+  return cap > 0 && tiles <= cap;
 }
 
 }  // namespace
 
 namespace gift {
+
+int max_resident_cap() { return g_max_resident; }
+
+// Device-wide order of the persistent launches.  Two persistent kernels
+// that shared the device could each hold part of it while waiting for their
+// own workgroups that have no room to start.  Launches on one stream are
+// ordered by the stream; when a persistent launch comes on a different
+// stream than the previous one on this device, the new stream first waits
+// for the old one (an event recorded on it now, after everything it was
+// given).  Nothing is added while one stream carries every call.  Streams
+// under graph capture are left alone.
+namespace {
+struct PersistentOrder {
+  std::mutex mu;
+  hipStream_t last[64] = {};
+  bool used[64] = {};
+  hipEvent_t ev[64] = {};
+};
+PersistentOrder g_order;
+
+bool capturing(hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(s, &st) == hipSuccess && st != hipStreamCaptureStatusNone;
+}
+}  // namespace
+
+hipError_t order_persistent(hipStream_t s) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipSuccess;
+  std::lock_guard<std::mutex> lock(g_order.mu);
+  if (g_order.used[dev] && g_order.last[dev] != s && !capturing(s)) {
+    hipStream_t prev = g_order.last[dev];
+    if (!g_order.ev[dev]) {
+      e = hipEventCreateWithFlags(&g_order.ev[dev], hipEventDisableTiming);
+      if (e != hipSuccess) return e;
+    }
+    if (!capturing(prev) && hipEventRecord(g_order.ev[dev], prev) == hipSuccess) {
+      e = hipStreamWaitEvent(s, g_order.ev[dev], 0);
+      if (e != hipSuccess) return e;
+    } else {
+      // the previous stream is no longer valid (destroyed) or is being
+      // captured: order against everything on the device instead
+      (void)hipGetLastError();
+      e = hipDeviceSynchronize();
+      if (e != hipSuccess) return e;
+    }
+  }
+  g_order.last[dev] = s;
+  g_order.used[dev] = true;
+  return hipSuccess;
+}
 
 StateLayout state_layout(const gift_layer_desc& g) {
   StateLayout s;
@@ -218,6 +291,20 @@ int32_t gift_set_fused(int32_t enable) {
   const int32_t old = g_fused_enabled;
   g_fused_enabled = enable ? 1 : 0;
   return old;
+}
+
+int32_t gift_set_max_resident(int32_t max_groups) {
+  const int32_t old = g_max_resident;
+  g_max_resident = max_groups > 0 ? max_groups : 0;
+  return old;
+}
+
+gift_status gift_layer_route(gift_layer_t L, int32_t op, int64_t ld, int32_t R, int32_t* h_fused) {
+  if (!L || !h_fused || (op != 0 && op != 1) || ld < L->desc.d_in) return GIFT_ERR_INVALID_ARG;
+  bool f = fused_ok(L->desc, ld);
+  if (op == 1) f = f && R >= 1 && R <= 64;
+  *h_fused = f ? 1 : 0;
+  return GIFT_OK;
 }
 
 size_t gift_payload_bytes(int32_t d_out, int32_t d_in, int32_t scaling) {
@@ -487,7 +574,7 @@ static gift_status encode_impl(gift_layer_t L, const float* d_W, int64_t ldw, in
   // FP4 takes the amax per tensor; its block amax is taken by the quantiser
   const int amax_scaling = fp4 ? GIFT_SCALE_TENSOR : scaling;
   const int64_t nb = nblk(m, d, amax_scaling);
-  if (fused_ok(g) && !fp4) {
+  if (fused_ok(g, ldw) && !fp4) {
     gift::FusedArgs a{};
     a.mode = 0;
     a.m = m;
@@ -516,12 +603,18 @@ static gift_status encode_impl(gift_layer_t L, const float* d_W, int64_t ldw, in
     a.whitened = d_whitened;
     a.resid = d_resid;
     const int grid = fused_groups(g) * a.CG;
-    hipError_t e = gift::launch_fused(a, grid, s);
+    hipError_t e = gift::order_persistent(s);
     if (e != hipSuccess) {
       --L->counters[5];
       return hip_fail(e);
     }
-    return GIFT_OK;
+    e = gift::launch_fused(a, grid, s);
+    if (e == hipSuccess) return GIFT_OK;
+    --L->counters[5];
+    // the runtime could not make the grid co-resident: nothing ran, take
+    // the multi-kernel route
+    if (e != hipErrorCooperativeLaunchTooLarge) return hip_fail(e);
+    (void)hipGetLastError();
   }
   GIFT_HIP(gift::launch_fill_u32(slots, 0u, (size_t)nb, s));
   const float* X = d_W;
@@ -631,12 +724,7 @@ gift_status gift_decode_reduce(gift_layer_t L, const uint8_t* d_codes, int64_t c
   if (!L->ready) return GIFT_ERR_NOT_READY;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* work = static_cast<char*>(d_work);
-  if (g.transform == GIFT_EUCLID && !(fused_ok(g) && R <= 64)) {
-    GIFT_HIP(gift::launch_dequant_sum(d_codes, code_stride, d_scales, scale_stride, R, m, d, fmt, scaling, d_out, ldo,
-                                      s));
-    return GIFT_OK;
-  }
-  if (fused_ok(g) && R <= 64) {   // the kernel stages up to 64 replicas' scales
+  if (fused_ok(g, ldo) && R <= 64) {   // the kernel stages up to 64 replicas' scales
     gift::FusedArgs a{};
     a.mode = 1;
     a.m = m;
@@ -663,11 +751,20 @@ gift_status gift_decode_reduce(gift_layer_t L, const uint8_t* d_codes, int64_t c
     a.out = d_out;
     a.ldo = ldo;
     const int grid = fused_groups(g) * a.CG;
-    hipError_t e = gift::launch_fused(a, grid, s);
+    hipError_t e = gift::order_persistent(s);
     if (e != hipSuccess) {
       --L->counters[6];
       return hip_fail(e);
     }
+    e = gift::launch_fused(a, grid, s);
+    if (e == hipSuccess) return GIFT_OK;
+    --L->counters[6];
+    if (e != hipErrorCooperativeLaunchTooLarge) return hip_fail(e);
+    (void)hipGetLastError();   // not co-resident: nothing ran; multi-kernel route
+  }
+  if (g.transform == GIFT_EUCLID) {
+    GIFT_HIP(gift::launch_dequant_sum(d_codes, code_stride, d_scales, scale_stride, R, m, d, fmt, scaling, d_out, ldo,
+                                      s));
     return GIFT_OK;
   }
   float* Ub = reinterpret_cast<float*>(work + L->wl.tile);

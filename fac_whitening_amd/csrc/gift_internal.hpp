@@ -61,7 +61,18 @@ struct FusedArgs {
   float* out;
   int64_t ldo;
 };
+// Cooperative launch of a fused kernel (every workgroup resident at once, or
+// hipErrorCooperativeLaunchTooLarge and nothing runs).
 hipError_t launch_fused(const FusedArgs& args, int grid, hipStream_t s);
+// Workgroups of the fused kernels the current device holds at once (0: unknown).
+int fused_resident_groups();
+// Upper bound on co-resident workgroups that the persistent kernels may
+// assume (gift_set_max_resident; 0 = none).
+int max_resident_cap();
+// Orders a persistent launch on stream s after the previous persistent
+// launch of the library on this device, when that one went to another
+// stream (see gift_api.hip).
+hipError_t order_persistent(hipStream_t s);
 hipError_t launch_pack_u(const float* U, int d, void* ub, void* ua, hipStream_t s);
 
 // Refresh products Y = A X (A symmetric d x d): each workgroup takes 256
@@ -173,6 +184,9 @@ hipError_t launch_diag_apply(const float* x, int64_t ldx, int m, int d, const fl
 constexpr int kStatsMaxGroups = 1024;
 hipError_t launch_stats(const void* x, int dtype, int64_t T, int64_t ld, int n, float* S, unsigned* sync,
                         unsigned epoch, uint32_t* flags, int cus, hipStream_t s);
+// Workgroups of the matrix-core statistics kernel the current device holds
+// at once (0: unknown).
+int stats_resident_groups();
 hipError_t launch_commit(float* S, float* A, int n, double inv_count, float beta, int first,
                          hipStream_t s);
 

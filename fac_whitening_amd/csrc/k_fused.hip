@@ -53,25 +53,16 @@ __device__ __forceinline__ unsigned long long ld_dev64(const unsigned long long*
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Wait (one thread) until *p - target >= 0 in wrap-around arithmetic.
-__device__ __forceinline__ void wait_reach(const unsigned* p, unsigned target, unsigned* flags) {
-  int spins = 0;
-  while ((int)(ld_dev(p) - target) < 0) {
-    if (++spins > kSpinLimit) {
-      atomicOr(flags, (unsigned)GIFT_FLAG_SPIN_TIMEOUT);
-      break;
-    }
-  }
-}
-
 // Wait until the 64-bit word carries `epoch` in its upper half; return it.
+// A wait that runs out sets the sticky flag and *bad (an LDS word).
 __device__ __forceinline__ unsigned long long wait_tag(const unsigned long long* p, unsigned epoch,
-                                                       unsigned* flags) {
+                                                       unsigned* flags, int* bad) {
   unsigned long long v = ld_dev64(p);
   int spins = 0;
   while ((unsigned)(v >> 32) != epoch) {
     if (++spins > kSpinLimit) {
       atomicOr(flags, (unsigned)GIFT_FLAG_SPIN_TIMEOUT);
+      *bad = 1;
       break;
     }
     v = ld_dev64(p);
@@ -298,6 +289,11 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
   __shared__ float srs[12];               // reciprocal scales of those blocks
   __shared__ float sss[12];               // and their scales (error feedback)
   __shared__ uint32_t sam[12];            // the amax bits they come from
+  // Set when a bounded wait of this workgroup ran out (a partner never
+  // published).  Its results are then poisoned, not left silently wrong:
+  // the encode publishes a NaN amax (every code 0x7F and a NaN scale follow)
+  // and writes 0x7F codes, the decode writes NaN.
+  __shared__ int s_bad;
   // cp[rb][wave]: the row block's partials lie in the first 5.5 tile rows
   // (rb 0), the next 5.5 (rb 1), ...
   float (*cp)[8][16][33] = reinterpret_cast<float (*)[8][16][33]>(smem);
@@ -315,6 +311,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
   const int cbg0 = (col0 >> 5) + wave;   // this wave's first 32-column block
   const unsigned tag = (a.epoch << 1) | (enc ? 0u : 1u);
   if (tid < 16) wmax[tid] = 0u;
+  if (tid == 0) s_bad = 0;
   // PIPE: the projection of each 16-row block runs as soon as the block is
   // in (the rank-k encode; the rank-k decode with a compile-time replica
   // count of at most 8 streams the replicas block by block: at 16 the
@@ -668,6 +665,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
           if (ok) break;
           if (++spins > kSpinLimit) {
             atomicOr(a.flags, (unsigned)GIFT_FLAG_SPIN_TIMEOUT);
+            s_bad = 1;
             break;
           }
         }
@@ -695,6 +693,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
       if (ok) break;
       if (++spins > kSpinLimit) {
         atomicOr(a.flags, (unsigned)GIFT_FLAG_SPIN_TIMEOUT);
+        s_bad = 1;
         break;
       }
     }
@@ -708,6 +707,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
 
   // ---- reconstruction X~ = alpha X + (P c) U^T ------------------------------
   {
+    const bool bad = s_bad != 0;   // uniform: every wait of the exchange is before the barrier
     const float alpha = a.coef[64 + (enc ? 0 : 1)];
     bf16x8 ph[3], pm[3], pl[3];
 #pragma unroll
@@ -751,6 +751,10 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
 #pragma unroll
         for (int rb = 0; rb < 3; ++rb) {
           const int i = q * 3 + rb;
+          if (bad) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[i][e] = __builtin_nanf("");
+          }
           const int row = row0 + 16 * rb + lr, c = col0 + 32 * SUB_CB(i) + 4 * lg;
           const int o = (int)(((int64_t)row * a.ldo + c) * 4);
           const int32x4 v0 = {__float_as_int(x[i][0]), __float_as_int(x[i][1]), __float_as_int(x[i][2]),
@@ -873,6 +877,10 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
   }
   if (tid < 16) blk[tid >> 3][tid & 7] = 0u;
   __syncthreads();
+  if (s_bad) {   // uniform here: a partner of the exchange never published
+    if (tid < 16) wmax[tid] = 0x7FC00000u;   // NaN bits order above every |x|
+    __syncthreads();
+  }
   const bool need_sync = a.amax_in == nullptr || a.amax_out != nullptr;
   if (need_sync) {
     unsigned long long* pub = a.apub;
@@ -904,7 +912,10 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
             for (int j = 0; j < 4; ++j) ok = ok && (unsigned)(w[j] >> 32) == a.epoch;
             if (__all(ok)) break;
             if (++spins > kSpinLimit) {
-              if (lane == 0) atomicOr(a.flags, (unsigned)GIFT_FLAG_SPIN_TIMEOUT);
+              if (lane == 0) {
+                atomicOr(a.flags, (unsigned)GIFT_FLAG_SPIN_TIMEOUT);
+                s_bad = 1;
+              }
               break;
             }
           }
@@ -926,7 +937,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
       for (int t = tid; t < nr * 12; t += 512) {
         const int rr = r_lo + t / 12, e = t % 12;
         const int h = rr * a.CG + cgi;
-        const unsigned long long w = wait_tag(pub + (int64_t)h * kApub + e, a.epoch, a.flags);
+        const unsigned long long w = wait_tag(pub + (int64_t)h * kApub + e, a.epoch, a.flags, &s_bad);
         const int brow = (rr * TR) / kBlock + e / 6;   // global block row of that entry
         const int slot_r = brow - rb0;
         if (slot_r >= 0 && slot_r < 2 && (uint32_t)w) atomicMax(&blk[slot_r][e % 6], (uint32_t)w);
@@ -956,14 +967,16 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
       sam[tid] = am;
       const bool leader = a.scaling == 0 ? g == 0 : (br * kBlock >= row0 && bc * kBlock >= col0);
       if (leader) {
-        if (a.scales) a.scales[slot] = sc;
-        if (a.amax_out) a.amax_out[slot] = __uint_as_float(local);
+        const bool bad = s_bad != 0;
+        if (a.scales) a.scales[slot] = bad ? __builtin_nanf("") : sc;
+        if (a.amax_out) a.amax_out[slot] = bad ? __builtin_nanf("") : __uint_as_float(local);
         if (am >= 0x7F800000u) atomicOr(a.flags, (unsigned)GIFT_FLAG_NONFINITE);
       }
     }
   }
   __syncthreads();   // the tile memory now receives the codes
   if (!a.codes) return;
+  const bool bad = s_bad != 0;
 #pragma unroll
   for (int i = 0; i < NSUB; ++i) {
     if (!live[i / 3]) continue;
@@ -973,7 +986,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
     const float r = srs[e];
     const uint32_t am = sam[e];
     uint32_t q0, q1;
-    if (am >= 0x7F800000u) {
+    if (am >= 0x7F800000u || bad) {
       q0 = q1 = 0x7F7F7F7Fu;
     } else if (lmax[i] >= 0x7F800000u) {
       // a non-finite element under a finite shared amax: exact integer path
@@ -1058,60 +1071,97 @@ __global__ void __launch_bounds__(512) k_euclid_decode(FusedArgs a) {
   fused_body<FMT, false, RC, SC, false>(a);
 }
 
+// Persistent launches.  The workgroups of these kernels wait on words that
+// other workgroups of the same launch publish, so every workgroup of the grid
+// must be resident at once: the host takes this route only when the grid
+// fits the kernels' occupancy (fused_resident_groups) and orders its
+// persistent launches device-wide, so two of them never share the device.
+// (A cooperative launch would have the runtime guarantee co-residency, but
+// it measured about 18 us more per launch than the 25-35 us kernels.)
+template <typename K>
+static hipError_t persistent_launch(K kernel, int grid, const FusedArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int FMT, int SC, bool LR>
-static void launch_decode(const FusedArgs& args, dim3 gd, dim3 bd, hipStream_t s) {
+static hipError_t launch_decode(const FusedArgs& a, int grid, hipStream_t s) {
   if constexpr (LR) {
-    switch (args.R) {
-      case 4: hipLaunchKernelGGL((k_rank_decode<FMT, 4, SC>), gd, bd, 0, s, args); break;
-      case 8: hipLaunchKernelGGL((k_rank_decode<FMT, 8, SC>), gd, bd, 0, s, args); break;
-      case 16: hipLaunchKernelGGL((k_rank_decode<FMT, 16, SC>), gd, bd, 0, s, args); break;
-      default: hipLaunchKernelGGL((k_rank_decode<FMT, 0, SC>), gd, bd, 0, s, args); break;
+    switch (a.R) {
+      case 4: return persistent_launch(k_rank_decode<FMT, 4, SC>, grid, a, s);
+      case 8: return persistent_launch(k_rank_decode<FMT, 8, SC>, grid, a, s);
+      case 16: return persistent_launch(k_rank_decode<FMT, 16, SC>, grid, a, s);
+      default: return persistent_launch(k_rank_decode<FMT, 0, SC>, grid, a, s);
     }
   } else {
-    switch (args.R) {
-      case 4: hipLaunchKernelGGL((k_euclid_decode<FMT, 4, SC>), gd, bd, 0, s, args); break;
-      case 8: hipLaunchKernelGGL((k_euclid_decode<FMT, 8, SC>), gd, bd, 0, s, args); break;
-      case 16: hipLaunchKernelGGL((k_euclid_decode<FMT, 16, SC>), gd, bd, 0, s, args); break;
-      default: hipLaunchKernelGGL((k_euclid_decode<FMT, 0, SC>), gd, bd, 0, s, args); break;
+    switch (a.R) {
+      case 4: return persistent_launch(k_euclid_decode<FMT, 4, SC>, grid, a, s);
+      case 8: return persistent_launch(k_euclid_decode<FMT, 8, SC>, grid, a, s);
+      case 16: return persistent_launch(k_euclid_decode<FMT, 16, SC>, grid, a, s);
+      default: return persistent_launch(k_euclid_decode<FMT, 0, SC>, grid, a, s);
     }
   }
 }
 
 template <int FMT, bool LR>
-static void launch_decode(const FusedArgs& args, dim3 gd, dim3 bd, hipStream_t s) {
-  if (args.scaling == 0)
-    launch_decode<FMT, 0, LR>(args, gd, bd, s);
-  else
-    launch_decode<FMT, 1, LR>(args, gd, bd, s);
+static hipError_t launch_decode(const FusedArgs& a, int grid, hipStream_t s) {
+  return a.scaling == 0 ? launch_decode<FMT, 0, LR>(a, grid, s) : launch_decode<FMT, 1, LR>(a, grid, s);
 }
 
-hipError_t launch_fused(const FusedArgs& args, int grid, hipStream_t s) {
-  const dim3 gd((unsigned)grid), bd(512);
-  if (args.mode == 0) {
+hipError_t launch_fused(const FusedArgs& a, int grid, hipStream_t s) {
+  hipError_t e;
+  if (a.mode == 0) {
     // kernel by transform, error feedback and format
-    const int which = (args.lr ? 4 : 0) + (args.resid ? 2 : 0) + (args.fmt == 0 ? 0 : 1);
+    const int which = (a.lr ? 4 : 0) + (a.resid ? 2 : 0) + (a.fmt == 0 ? 0 : 1);
     switch (which) {
-      case 0: hipLaunchKernelGGL(k_euclid_encode<0>, gd, bd, 0, s, args); break;
-      case 1: hipLaunchKernelGGL(k_euclid_encode<1>, gd, bd, 0, s, args); break;
-      case 2: hipLaunchKernelGGL(k_euclid_encode_ef<0>, gd, bd, 0, s, args); break;
-      case 3: hipLaunchKernelGGL(k_euclid_encode_ef<1>, gd, bd, 0, s, args); break;
-      case 4: hipLaunchKernelGGL(k_rank_encode<0>, gd, bd, 0, s, args); break;
-      case 5: hipLaunchKernelGGL(k_rank_encode<1>, gd, bd, 0, s, args); break;
-      case 6: hipLaunchKernelGGL(k_rank_encode_ef<0>, gd, bd, 0, s, args); break;
-      default: hipLaunchKernelGGL(k_rank_encode_ef<1>, gd, bd, 0, s, args); break;
+      case 0: e = persistent_launch(k_euclid_encode<0>, grid, a, s); break;
+      case 1: e = persistent_launch(k_euclid_encode<1>, grid, a, s); break;
+      case 2: e = persistent_launch(k_euclid_encode_ef<0>, grid, a, s); break;
+      case 3: e = persistent_launch(k_euclid_encode_ef<1>, grid, a, s); break;
+      case 4: e = persistent_launch(k_rank_encode<0>, grid, a, s); break;
+      case 5: e = persistent_launch(k_rank_encode<1>, grid, a, s); break;
+      case 6: e = persistent_launch(k_rank_encode_ef<0>, grid, a, s); break;
+      default: e = persistent_launch(k_rank_encode_ef<1>, grid, a, s); break;
     }
-  } else if (args.lr) {
-    if (args.fmt == 0)
-      launch_decode<0, true>(args, gd, bd, s);
-    else
-      launch_decode<1, true>(args, gd, bd, s);
+  } else if (a.fmt == 0) {
+    e = a.lr ? launch_decode<0, true>(a, grid, s) : launch_decode<0, false>(a, grid, s);
   } else {
-    if (args.fmt == 0)
-      launch_decode<0, false>(args, gd, bd, s);
-    else
-      launch_decode<1, false>(args, gd, bd, s);
+    e = a.lr ? launch_decode<1, true>(a, grid, s) : launch_decode<1, false>(a, grid, s);
   }
-  return hipGetLastError();
+  return e;
+}
+
+// Workgroups of the fused kernels that the current device can hold at once:
+// the smallest occupancy of any variant (one query per kernel) times the
+// compute units; 0 if a query fails.
+int fused_resident_groups() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev]) return cache[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
+  const void* kernels[] = {
+      reinterpret_cast<const void*>(k_rank_encode<0>), reinterpret_cast<const void*>(k_rank_encode<1>),
+      reinterpret_cast<const void*>(k_rank_encode_ef<0>), reinterpret_cast<const void*>(k_rank_encode_ef<1>),
+      reinterpret_cast<const void*>(k_euclid_encode<0>), reinterpret_cast<const void*>(k_euclid_encode<1>),
+      reinterpret_cast<const void*>(k_euclid_encode_ef<0>), reinterpret_cast<const void*>(k_euclid_encode_ef<1>),
+#define GIFT_DEC(F, S)                                                                                      \
+  reinterpret_cast<const void*>(k_rank_decode<F, 4, S>), reinterpret_cast<const void*>(k_rank_decode<F, 8, S>), \
+      reinterpret_cast<const void*>(k_rank_decode<F, 16, S>), reinterpret_cast<const void*>(k_rank_decode<F, 0, S>), \
+      reinterpret_cast<const void*>(k_euclid_decode<F, 4, S>), reinterpret_cast<const void*>(k_euclid_decode<F, 8, S>), \
+      reinterpret_cast<const void*>(k_euclid_decode<F, 16, S>), reinterpret_cast<const void*>(k_euclid_decode<F, 0, S>)
+      GIFT_DEC(0, 0), GIFT_DEC(0, 1), GIFT_DEC(1, 0), GIFT_DEC(1, 1)
+#undef GIFT_DEC
+  };
+  int per_cu = 1 << 30;
+  for (const void* k : kernels) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, 512, 0) != hipSuccess) return 0;
+    per_cu = n < per_cu ? n : per_cu;
+  }
+  cache[dev] = per_cu * cus;
+  return cache[dev];
 }
 
 }  // namespace gift

@@ -295,18 +295,25 @@ __device__ __forceinline__ void stats_segment(const uint16_t* __restrict__ x, in
   // release / acquire (on this multi-die device those write back and
   // invalidate a whole L2 and stall every other workgroup on it).
   const bool shared = s_a > 0 || s_b < nst;
+  // a hand-over that never came (a wait that ran out) poisons this part of
+  // the tile with NaN, so the committed A, and the factor, show it
+  bool late = false;
   if (s_b < nst) {
-    // the next workgroup holds the later stages of this tile: it adds first
-    if (tid2 == 0) {
+    // the next workgroup holds the later stages of this tile: it adds first.
+    // Lane 0 of every wave polls, so each wave knows the outcome itself.
+    int out = 0;
+    if ((tid2 & 63) == 0) {
       int spins = 0;
       while (__hip_atomic_load(sync + gw + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
         if (++spins > kStatsSpinLimit) {
           atomicOr(flags, (uint32_t)GIFT_FLAG_SPIN_TIMEOUT);
+          out = 1;
           break;
         }
         __builtin_amdgcn_s_sleep(2);
       }
     }
+    late = __builtin_amdgcn_readfirstlane(out) != 0;
     __syncthreads();
   }
   // S += acc: register v of MFMA tile (mt, nt) is element
@@ -335,7 +342,8 @@ __device__ __forceinline__ void stats_segment(const uint16_t* __restrict__ x, in
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[nt][e] + acc[mt][nt][e]), rs, off[nt][e], 0, 17);
+          __builtin_amdgcn_raw_buffer_store_b32(
+              __float_as_uint(late ? __builtin_nanf("") : v[nt][e] + acc[mt][nt][e]), rs, off[nt][e], 0, 17);
     }
   } else {
 #pragma unroll
@@ -398,6 +406,21 @@ k_stats_mfma(const uint16_t* __restrict__ x, int64_t T, int64_t ld, int n, float
   }
 }
 
+int stats_resident_groups() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (!cache[dev]) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k_stats_mfma), 256, 0) !=
+        hipSuccess)
+      return 0;
+    cache[dev] = cus * per_cu;
+  }
+  return cache[dev];
+}
+
 hipError_t launch_stats(const void* x, int dtype, int64_t T, int64_t ld, int n, float* S, unsigned* sync,
                         unsigned epoch, uint32_t* flags, int cus, hipStream_t s) {
   if (T == 0 || n == 0) return hipSuccess;
@@ -407,8 +430,16 @@ hipError_t launch_stats(const void* x, int dtype, int64_t T, int64_t ld, int n, 
     const int nb2 = (int)cdiv(n, kSB);
     const int ntiles = nb2 * (nb2 + 1) / 2;
     const int64_t units = (int64_t)ntiles * cdiv(T, kSK);
+    // workgroups that share a tile wait on one another: the grid is at most
+    // what the device holds at once (the kernel's occupancy times the
+    // compute units, or the gift_set_max_resident cap)
     int grid = cus < kStatsMaxGroups ? cus : kStatsMaxGroups;
+    const int res = stats_resident_groups(), cap = max_resident_cap();
+    if (res > 0 && res < grid) grid = res;
+    if (cap > 0 && cap < grid) grid = cap;
     if (units < grid) grid = (int)units;
+    const hipError_t e = order_persistent(s);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_stats_mfma, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const uint16_t*>(x), T,
                        ld, n, S, ntiles, sync, epoch, flags);
   } else if (dtype == GIFT_BF16)

@@ -364,16 +364,50 @@ gift_status gift_select_layers(gift_profiler_t prof, int32_t max_select, double*
  * ------------------------------------------------------------------------- */
 const char* gift_status_string(gift_status s);
 int32_t gift_last_hip_error(void);
-/* Process-wide choice of the GIFT_LOWRANK kernels: nonzero (the default)
- * uses the single-launch persistent kernels whenever every 48 x 768 tile of
- * the gradient fits on the device at once (one 512-thread workgroup per
- * compute unit); zero always uses the multi-kernel path (project, apply,
- * amax, quantise / dequantise-sum, project, apply).  Both give results
- * within the same tolerances; the persistent kernels keep the tile in
- * registers and read the gradient once.  Returns the previous setting.
+/* Process-wide choice of the GIFT_LOWRANK and GIFT_EUCLID kernels: nonzero
+ * (the default) uses the single-launch persistent kernels whenever every
+ * 48 x 768 tile of the gradient can be resident on the device at once and
+ * each buffer they address spans less than 2 GiB; zero always uses the
+ * multi-kernel path (project, apply, amax, quantise / dequantise-sum,
+ * project, apply).  Both give results within the same tolerances; the
+ * persistent kernels keep the tile in registers and read the gradient
+ * once.  Returns the previous setting.
+ *
+ * Persistent kernels (the fused encode / decode and the matrix-core
+ * statistics kernel): their workgroups wait on words that other workgroups
+ * of the same launch publish, so the whole grid must be resident at once.
+ *   - The fused route is taken only when the grid fits the device (the
+ *     kernels' occupancy times the compute units, or the bound set by
+ *     gift_set_max_resident); otherwise the multi-kernel path runs (same
+ *     results).  The statistics grid never exceeds that bound.
+ *   - The library orders its persistent launches device-wide: a persistent
+ *     call on a stream other than the previous one's first waits for that
+ *     stream (an event recorded on it at the time of the call; nothing is
+ *     added while one stream carries every call; streams under graph
+ *     capture are not ordered).  Two libgift persistent kernels therefore
+ *     never share the device.  Kernels of other software that also wait on
+ *     their own workgroups must not run beside them.
+ *   - Every wait is bounded.  A wait that runs out sets
+ *     GIFT_FLAG_SPIN_TIMEOUT (read with gift_layer_flags) and poisons the
+ *     result instead of leaving it silently wrong: the encode then gives a
+ *     NaN amax / scale and 0x7F codes, the decode NaN, the statistics NaN
+ *     in A (and so a NaN factor and GIFT_FLAG_NONFINITE at refresh).
  * Calls on one layer must be ordered on one stream (the persistent kernels
  * exchange epoch-tagged words through the layer state). */
 int32_t gift_set_fused(int32_t enable);
+/* Process-wide upper bound on the workgroups that a persistent launch may
+ * count on being resident at once (0, the default: the device's own limit,
+ * from the occupancy of the kernels times the compute units).  For callers
+ * that keep part of the device busy with work of their own, and for tests
+ * of the route choice.  The fused encode / decode are taken only when all
+ * their tiles fit under the bound; the statistics kernel shrinks its grid to
+ * it.  Returns the previous value. */
+int32_t gift_set_max_resident(int32_t max_groups);
+/* Which route gift_encode (op = 0, rows of W at leading dimension ld) or
+ * gift_decode_reduce (op = 1, output leading dimension ld, R replicas)
+ * would take for this layer under the current settings: *h_fused = 1 for
+ * the single-launch persistent kernels, 0 for the multi-kernel path. */
+gift_status gift_layer_route(gift_layer_t layer, int32_t op, int64_t ld, int32_t R, int32_t* h_fused);
 
 #ifdef __cplusplus
 }
