@@ -46,6 +46,7 @@ EXPORTS = [
     "gift_last_hip_error", "gift_set_fused", "gift_bucket_table_bytes", "gift_bucket_create",
     "gift_bucket_destroy", "gift_bucket_sizes", "gift_bucket_flags", "gift_bucket_amax", "gift_bucket_encode",
     "gift_bucket_decode_reduce", "gift_scale_sync_due", "gift_set_max_resident", "gift_layer_route",
+    "gift_bucket_encode_static",
 ]
 
 
@@ -100,6 +101,7 @@ _sig("gift_bucket_sizes", _i32, _vp, _P(_i64), _P(_i64), _P(_sz))
 _sig("gift_bucket_flags", _i32, _vp, _vp, _P(ctypes.c_uint32))
 _sig("gift_bucket_amax", _i32, _vp, _vp, _vp, _vp)
 _sig("gift_bucket_encode", _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp)
+_sig("gift_bucket_encode_static", _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp)
 _sig("gift_bucket_decode_reduce", _i32, _vp, _vp, _i64, _vp, _i64, _i32, _i32, _vp, _vp)
 _sig("gift_scale_sync_due", _i32, _i64, _i32)
 
@@ -426,6 +428,19 @@ class Bucket:
         _check(_lib.gift_bucket_encode(self._h, _ptr(grad), FORMATS.get(fmt, fmt), _ptr(amax_in), _ptr(amax_out),
                                        _ptr(codes), _ptr(scales), _ptr(self.work), self.work_bytes, _stream(stream)),
                "gift_bucket_encode")
+        return codes, scales
+
+    def encode_static(self, grad, fmt=E4M3, amax_in=None, amax_out=None, codes=None, scales=None, stream=None):
+        """gift_bucket_encode_static: the encode without a workspace (the
+        library's per-device scratch array holds the amax slots)."""
+        self._grad(grad)
+        if codes is None:
+            codes = torch.empty(self.numel, dtype=torch.uint8, device=grad.device)
+        if scales is None:
+            scales = torch.empty(self.nscales, dtype=torch.float32, device=grad.device)
+        _check(_lib.gift_bucket_encode_static(self._h, _ptr(grad), FORMATS.get(fmt, fmt), _ptr(amax_in),
+                                              _ptr(amax_out), _ptr(codes), _ptr(scales), _stream(stream)),
+               "gift_bucket_encode_static")
         return codes, scales
 
     def decode_reduce(self, codes, scales, fmt=E4M3, out=None, stream=None):

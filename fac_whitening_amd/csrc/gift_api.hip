@@ -83,6 +83,37 @@ int64_t nblk(int m, int d, int scaling) {
 
 int g_fused_enabled = 1;
 
+// Scratch of gift_bucket_encode_static: the amax slots of one bucket, in a
+// file-scope device array (each device that runs the library holds its own
+// copy until the process ends).  Host code never passes the array's name to
+// a kernel: it takes the device address once per device with
+// hipGetSymbolAddress and uses that.
+constexpr size_t kStaticScratchBytes = (size_t)1 << 20;   // 262144 amax slots
+static __device__ __align__(256) uint32_t scratch[kStaticScratchBytes / 4];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on each device); nullptr and the HIP error on failure.
+void* scratch_address(hipError_t* err) {
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= 64) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
 // Workgroups of the fused rank-k kernels for this shape.
 int fused_groups(const gift_layer_desc& g) { return (int)gift::cdiv(g.d_out, gift::kFusedTR); }
 int fused_cg(const gift_layer_desc& g) { return (int)gift::cdiv(g.d_in, gift::kFusedTC); }
@@ -987,6 +1018,28 @@ gift_status gift_bucket_encode(gift_bucket_t B, const float* d_grad, int32_t fmt
   const int cus = device_cus();
   uint32_t* slots = static_cast<uint32_t*>(d_work);
   if (local) {
+    GIFT_HIP(gift::launch_fill_u32(slots, 0u, (size_t)B->nscales, s));
+    GIFT_HIP(gift::launch_bucket_amax(B->t, d_grad, blk, slots, cus, s));
+  }
+  GIFT_HIP(gift::launch_bucket_quantize(B->t, d_grad, fmt, blk, slots, d_amax_in, d_amax_out, d_codes, d_scales, cus,
+                                        s));
+  return GIFT_OK;
+}
+
+gift_status gift_bucket_encode_static(gift_bucket_t B, const float* d_grad, int32_t fmt, const float* d_amax_in,
+                                      float* d_amax_out, uint8_t* d_codes, float* d_scales, gift_stream_t stream) {
+  if (!B || !d_grad || !d_codes || !d_scales || !aligned16(d_grad) || !aligned16(d_codes)) return GIFT_ERR_INVALID_ARG;
+  if (fmt != GIFT_E4M3 && fmt != GIFT_E5M2) return GIFT_ERR_INVALID_ARG;
+  const bool local = !d_amax_in || d_amax_out;
+  if (local && (size_t)B->nscales * 4 > kStaticScratchBytes) return GIFT_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int blk = B->scaling == GIFT_SCALE_BLOCK512;
+  const int cus = device_cus();
+  uint32_t* slots = nullptr;
+  if (local) {
+    hipError_t e = hipSuccess;
+    slots = static_cast<uint32_t*>(scratch_address(&e));
+    if (!slots) return hip_fail(e);
     GIFT_HIP(gift::launch_fill_u32(slots, 0u, (size_t)B->nscales, s));
     GIFT_HIP(gift::launch_bucket_amax(B->t, d_grad, blk, slots, cus, s));
   }

@@ -316,6 +316,20 @@ gift_status gift_bucket_amax(gift_bucket_t bucket, const float* d_grad, float* d
 gift_status gift_bucket_encode(gift_bucket_t bucket, const float* d_grad, int32_t fmt,
                                const float* d_amax_in, float* d_amax_out, uint8_t* d_codes,
                                float* d_scales, void* d_work, size_t work_bytes, gift_stream_t stream);
+/* gift_bucket_encode_static: gift_bucket_encode without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ * It allocates nothing: the local amax slots live in a scratch array of
+ * 1 MiB compiled into the library (one per device, held until the process
+ * ends), so a bucket may have at most 262144 scales when the local amax is
+ * needed (d_amax_in NULL or d_amax_out given); more gives GIFT_ERR_WORKSPACE
+ * with nothing enqueued.  Codes and scales equal gift_bucket_encode's.
+ * Every call on a device shares that device's array (the slots are cleared
+ * at the start of each call): calls that overlap in time on one device,
+ * from different streams or threads, race and must not be issued. */
+gift_status gift_bucket_encode_static(gift_bucket_t bucket, const float* d_grad, int32_t fmt,
+                                      const float* d_amax_in, float* d_amax_out, uint8_t* d_codes,
+                                      float* d_scales, gift_stream_t stream);
 gift_status gift_bucket_decode_reduce(gift_bucket_t bucket, const uint8_t* d_codes, int64_t code_stride,
                                       const float* d_scales, int64_t scale_stride, int32_t R,
                                       int32_t fmt, float* d_out, gift_stream_t stream);
