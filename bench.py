@@ -44,12 +44,16 @@ def parse():
     p.add_argument("--scaling", default="tensor", choices=["tensor", "block"])
     p.add_argument("--sets", type=int, default=4)
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
-    p.add_argument("--config", default="unit", choices=["unit", "selective", "stress", "slab"],
+    p.add_argument("--config", default="unit",
+                   choices=["unit", "selective", "stress", "slab", "ablation", "fidelity"],
                    help="unit: the headline encode + decode unit (default); selective: the whole "
                         "600M-class gradient buffer (168 tensors, 13 rank-32); stress: one step of "
                         "the 4096 x 16384 stress layer (statistics, refresh, encode, decode R = 16); "
                         "slab: one GPU's share of the row-slab exchange at R = 8 (the kernels between "
-                        "the collectives, which are not run)")
+                        "the collectives, which are not run); ablation: the 1536 x 6144 layer with every "
+                        "transform (two-sided K-FAC, input-side Cholesky, rank-32, diagonal, Euclidean): "
+                        "statistics, refresh, encode + decode-reduce times and fidelity; fidelity: the decoded "
+                        "mean of every configuration against the fp32 mean gradient")
     return p.parse_args()
 
 
@@ -73,6 +77,10 @@ def main():
         return bench_stress(args, torch, fw, synth, dev)
     if args.config == "slab":
         return bench_slab(args, torch, fw, synth, dev)
+    if args.config == "ablation":
+        return bench_ablation(args, torch, fw, synth, dev)
+    if args.config == "fidelity":
+        return bench_fidelity(args, torch, fw, synth, dev)
     m, d, T, R, k = 1536, 6144, 16384, 8, 32
     scaling = fw.SCALINGS[args.scaling]
     nb = fw.nblocks(m, d, scaling)
@@ -278,6 +286,12 @@ def main():
     torch.cuda.synchronize()
     assert L.flags() == 0
 
+    # fidelity of the headline layer's decoded mean against the fp32 mean of
+    # the 8 replicas: GIFT rank-32 (local scales) and the Euclidean baseline
+    # (shared amax), per tensor and per 128 x 128 block
+    LE = fw.Layer(m, d, "euclid", device=dev)
+    fid = fidelity_rows(torch, fw, case.W, L.buffers()["A"], {"gift_rank32": L, "euclid": LE})
+    del LE
     result = {
         "metric": "GIFT encode+decode GB/s of fp32 grad (1536\u00d76144, r=32); % of HBM peak",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -291,6 +305,7 @@ def main():
         "roofline": roofline,
         "stage_rooflines": stage_rooflines,
         "unit_detail": unit_detail,
+        "fidelity": fid,
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu:
@@ -641,6 +656,175 @@ def bench_slab(args, torch, fw, synth, dev):
                      "fp32_ring_allreduce_ingress_bytes_per_gpu": int(2 * (R - 1) * 4 * n_slab),
                      "note": "not run: one GPU"},
     }
+    print(json.dumps(result), flush=True)
+
+
+
+# ---------------------------------------------------------------------------
+# Fidelity of the decoded mean ("GIFT 阅读笔记", §简化一 Eq. (15): RelL2, Cos,
+# MaxErr, MSE against the uncompressed mean; the A-metric error of
+# §核心想法 Eq. (6) with G = I: sqrt(tr(E A E^T) / tr(W A W^T)), A the
+# undamped input statistics).  Measurement code, in float64 on the device.
+# ---------------------------------------------------------------------------
+
+def fidelity(torch, W_hat, W_ref, A=None):
+    Wh, g = W_hat.double(), W_ref.double()
+    e = Wh - g
+    out = {"RelL2": (e.norm() / g.norm()).item(),
+           "Cos": ((Wh * g).sum() / (Wh.norm() * g.norm())).item(),
+           "MaxErr": e.abs().max().item(), "MSE": (e * e).mean().item()}
+    if A is not None:
+        Ad = A.double()
+        out["ARel"] = float(((e @ Ad) * e).sum().item() / ((g @ Ad) * g).sum().item()) ** 0.5
+    return {k: float(f"{v:.5g}") for k, v in out.items()}
+
+
+def decoded_mean(torch, fw, L, Ws, fmt, scaling, shared_amax=False):
+    """Encode every replica with layer L and decode-reduce them.  With
+    shared_amax the replicas quantise with the max of their local amaxes (the
+    AllReduceMax of the Euclidean branch of Algorithm 1), else each with its
+    own (the geometry branch's local scale)."""
+    m, d = Ws[0].shape
+    nb = fw.nblocks(m, d, scaling)
+    amax_in = None
+    if shared_amax:
+        am = torch.empty(len(Ws), nb, dtype=torch.float32, device=Ws[0].device)
+        for r, W in enumerate(Ws):
+            L.encode(W, fmt, scaling, amax_out=am[r], want_codes=False)
+        amax_in = am.max(0).values.contiguous()
+    codes = torch.empty(len(Ws), m, d, dtype=torch.uint8, device=Ws[0].device)
+    scales = torch.empty(len(Ws), nb, dtype=torch.float32, device=Ws[0].device)
+    for r, W in enumerate(Ws):
+        L.encode(W, fmt, scaling, amax_in=amax_in, codes=codes[r], scales=scales[r])
+    out = L.decode_reduce(codes, scales, fmt, scaling)
+    del codes
+    return out
+
+
+def variant_layer(torch, fw, kind, m, d, a, dl, omega, ema=0.0, a_steps=None):
+    L = fw.Layer(m, d, kind, rank=32, oversample=16, power_iters=4, ema_decay=ema, device=a.device)
+    if kind != "euclid":
+        for x in (a_steps or [a]):
+            L.accumulate_stats(x, fw.SIDE_A, commit=True)
+    if kind == "twosided":
+        L.accumulate_stats(dl, fw.SIDE_G, commit=True)
+    L.refresh(omega)
+    return L
+
+
+def fidelity_rows(torch, fw, Ws, A, layers, fmts=("e4m3",), scalings=("tensor", "block")):
+    """{variant: {format/scaling: metrics}} for the given layers (kind -> L)."""
+    Wbar = torch.stack([w.double() for w in Ws]).mean(0)
+    rows = {}
+    for kind, L in layers.items():
+        rows[kind] = {}
+        for fm in fmts:
+            for sc in scalings:
+                out = decoded_mean(torch, fw, L, Ws, fw.FORMATS[fm], fw.SCALINGS[sc], shared_amax=kind == "euclid")
+                rows[kind][f"{fm}/{sc}"] = fidelity(torch, out, Wbar, A)
+                del out
+    return rows
+
+
+def bench_ablation(args, torch, fw, synth, dev):
+    """The two-sided K-FAC ablation on one 1536 x 6144 fc2 layer: A (6144^2)
+    and G (1536^2) from T = 16384 bf16 tokens, E4M3 per 128 x 128 block,
+    R = 8, every transform.  Times the statistics, each refresh (blocked fp64
+    Cholesky and triangular inverse for the full variants, subspace
+    iteration for rank 32), the encode of one replica and the decode-reduce
+    of the 8 payloads, and scores each decoded mean against the fp32 mean
+    gradient."""
+    case = synth.make_layer(4, device=dev)
+    m, d = case.cfg["m"], case.cfg["d"]
+    a, dl = case.a_steps[0], case.delta_steps[0]
+    f, s = fw.E4M3, fw.SCALE_BLOCK128
+    nb = fw.nblocks(m, d, s)
+    reps = 5
+    scratch = fw.Layer(16, d, "diag", device=dev)
+    t_stats_a = _event_ms(torch, lambda: scratch.accumulate_stats(a, fw.SIDE_A), reps)
+    del scratch
+    layers, variants = {}, {}
+    for kind in ("twosided", "chol", "lowrank", "diag", "euclid"):
+        L = variant_layer(torch, fw, kind, m, d, a, dl, case.omega)
+        t_ref = _event_ms(torch, lambda: L.refresh(case.omega), 3) if kind != "euclid" else 0.0
+        codes = torch.empty(len(case.W), m, d, dtype=torch.uint8, device=dev)
+        scales = torch.empty(len(case.W), nb, dtype=torch.float32, device=dev)
+        for r, W in enumerate(case.W):
+            L.encode(W, f, s, codes=codes[r], scales=scales[r])
+        out = torch.empty(m, d, dtype=torch.float32, device=dev)
+        t_enc = _event_ms(torch, lambda: L.encode(case.W[0], f, s, codes=codes[0], scales=scales[0]), reps)
+        t_dec = _event_ms(torch, lambda: L.decode_reduce(codes, scales, f, s, out=out), reps)
+        torch.cuda.synchronize()
+        assert L.flags() == 0, kind
+        variants[kind] = {"refresh_ms": round(t_ref, 4), "encode_ms": round(t_enc, 5), "decode_ms": round(t_dec, 5),
+                          "route": L.route("encode") if kind in ("lowrank", "euclid") else "multi"}
+        layers[kind] = L
+        del codes, out
+    if "twosided" in layers:
+        scratch = fw.Layer(m, 16, "twosided", device=dev)
+        variants["twosided"]["stats_G_ms"] = round(
+            _event_ms(torch, lambda: scratch.accumulate_stats(dl, fw.SIDE_G), reps), 4)
+        del scratch
+    A = layers["chol"].buffers()["A"]
+    fid = fidelity_rows(torch, fw, case.W, A, layers, scalings=("block", "tensor"))
+    for kind in variants:
+        variants[kind]["fidelity"] = fid[kind]
+    chol_flop = 2.0 * d ** 3 / 3.0                      # factor d^3/3 + triangular inverse d^3/3
+    apply_flop = 2.0 * m * d * d / 2.0                   # W L^-T: a triangular product
+    result = {
+        "metric": "two-sided K-FAC ablation, 1536x6144 fc2 layer: per-variant times and fidelity",
+        "n_gpus": 1, "dtype": "f32", "data": "synthetic (a ~ N(0, Q_A diag(i^-1.5) Q_A^T), delta ~ "
+        "N(0, Q_G diag(j^-1) Q_G^T), bf16, T=16384; W_r = delta_r^T a_r / T)",
+        "config": {"workload": "fc2 1536x6144, A 6144^2 and G 1536^2 from 16384 bf16 tokens, E4M3 per 128x128 "
+                               "block (fidelity also per tensor), R=8", "replicas": len(case.W)},
+        "stats_A_ms": round(t_stats_a, 4),
+        "variants": variants,
+        "flops": {"cholesky_and_inverse_A": chol_flop, "triangular_apply_each_way": apply_flop},
+        "fidelity_note": "decoded mean of the 8 replicas against their fp32 mean; Euclidean with the shared "
+                         "amax (AllReduceMax), the others with local scales; ARel uses the undamped A",
+    }
+    print(json.dumps(result), flush=True)
+
+
+def bench_fidelity(args, torch, fw, synth, dev):
+    """Fidelity of every configuration's decoded mean against the fp32 mean
+    of its replicas (the synthetic analogue of Tables I and II)."""
+    res = {}
+    t0 = time.time()
+    # tiny: 64 x 256, fp32 activations, R = 4; every input-side variant
+    c1 = synth.make_layer(1, device=dev)
+    lay = {k: variant_layer(torch, fw, k, 64, 256, c1.a_steps[0], c1.delta_steps[0], c1.omega)
+           for k in ("euclid", "diag", "lowrank", "chol", "twosided")}
+    res["tiny_64x256_r4"] = fidelity_rows(torch, fw, c1.W, lay["chol"].buffers()["A"], lay)
+    del lay
+    # 300M fc2: 1024 x 4096, 4 EMA steps (beta 0.95), R = 8
+    c2 = synth.make_layer(2, device=dev)
+    lay = {k: variant_layer(torch, fw, k, 1024, 4096, c2.a_steps[-1], None, c2.omega, ema=0.95, a_steps=c2.a_steps)
+           for k in ("euclid", "lowrank")}
+    res["fc2_300m_1024x4096_r8"] = fidelity_rows(torch, fw, c2.W, lay["lowrank"].buffers()["A"], lay)
+    del lay, c2
+    # 600M fc2 (the metric layer and the ablation): every variant
+    c4 = synth.make_layer(4, device=dev)
+    lay = {k: variant_layer(torch, fw, k, 1536, 6144, c4.a_steps[0], c4.delta_steps[0], c4.omega)
+           for k in ("euclid", "diag", "lowrank", "chol", "twosided")}
+    res["fc2_600m_1536x6144_r8"] = fidelity_rows(torch, fw, c4.W, lay["chol"].buffers()["A"], lay)
+    del lay, c4
+    torch.cuda.empty_cache()
+    # stress: 4096 x 16384, Student-t gradients with outlier columns, R = 16
+    m, d, Ttok = 4096, 16384, 8192
+    a = synth.stress_activations(Ttok, d, 0, dev)
+    om = synth.omega(d, 48, synth.seed_for(5, synth.ROLE_OMEGA), dev)
+    Ws = [synth.stress_gradient(m, d, 0, r, dev) for r in range(16)]
+    lay = {k: variant_layer(torch, fw, k, m, d, a, None, om) for k in ("euclid", "lowrank")}
+    res["stress_4096x16384_r16"] = fidelity_rows(torch, fw, Ws, lay["lowrank"].buffers()["A"], lay,
+                                                 fmts=("e5m2", "e4m3"), scalings=("block",))
+    del lay, Ws, a
+    result = {"metric": "fidelity of the decoded mean against the fp32 mean gradient, every configuration",
+              "n_gpus": 1, "data": "synthetic, seeded", "seconds": round(time.time() - t0, 1),
+              "note": "RelL2, Cos, MaxErr, MSE (Eq. (15)) and ARel = sqrt(tr(E A E^T) / tr(W A W^T)) with the "
+                      "layer's undamped A; Euclidean quantises with the shared amax (AllReduceMax), the other "
+                      "variants with local scales; keys are format/scaling",
+              "fidelity": res}
     print(json.dumps(result), flush=True)
 
 

@@ -564,8 +564,9 @@ def metrics(W_hat, W_ref, A=None) -> dict:
     if A is not None:
         E = _f64(W_hat) - _f64(W_ref)
         Wr = _f64(W_ref)
-        out["ARel"] = float(np.sqrt(np.einsum("ij,jk,ik->", E, A, E)
-                                    / np.einsum("ij,jk,ik->", Wr, A, Wr)))
+        A = _f64(A)
+        # tr(X A X^T) as the sum of (X A) * X over all entries
+        out["ARel"] = float(np.sqrt(np.sum((E @ A) * E) / np.sum((Wr @ A) * Wr)))
     return out
 
 
