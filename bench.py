@@ -769,8 +769,8 @@ def bench_ablation(args, torch, fw, synth, dev):
     fid = fidelity_rows(torch, fw, case.W, A, layers, scalings=("block", "tensor"))
     for kind in variants:
         variants[kind]["fidelity"] = fid[kind]
-    chol_flop = 2.0 * d ** 3 / 3.0                      # factor d^3/3 + triangular inverse d^3/3
-    apply_flop = 2.0 * m * d * d / 2.0                   # W L^-T: a triangular product
+    chol_flop = 2.0 * (2.0 * d ** 3 / 3.0)              # factor d^3/3 + triangular inverse d^3/3 multiply-adds
+    apply_flop = 2.0 * m * d * d / 2.0                   # W L^-T: a triangular product, m d^2 / 2 multiply-adds
     result = {
         "metric": "two-sided K-FAC ablation, 1536x6144 fc2 layer: per-variant times and fidelity",
         "n_gpus": 1, "dtype": "f32", "data": "synthetic (a ~ N(0, Q_A diag(i^-1.5) Q_A^T), delta ~ "
@@ -780,6 +780,10 @@ def bench_ablation(args, torch, fw, synth, dev):
         "stats_A_ms": round(t_stats_a, 4),
         "variants": variants,
         "flops": {"cholesky_and_inverse_A": chol_flop, "triangular_apply_each_way": apply_flop},
+        "fp64_fraction": {"cholesky_refresh": round(chol_flop / (variants["chol"]["refresh_ms"] * 1e-3) / 1e12
+                                                    / FP64_PEAK_TFS, 4),
+                          "triangular_apply_encode": round(apply_flop / (variants["chol"]["encode_ms"] * 1e-3) / 1e12
+                                                           / FP64_PEAK_TFS, 4)},
         "fidelity_note": "decoded mean of the 8 replicas against their fp32 mean; Euclidean with the shared "
                          "amax (AllReduceMax), the others with local scales; ARel uses the undamped A",
     }
