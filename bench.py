@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--scaling", default="tensor", choices=["tensor", "block"])
     p.add_argument("--sets", type=int, default=4)
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    p.add_argument("--layers", type=int, default=24,
+                   help="selective: decoder layers of the 600M-class model (24: the stated shapes, 906M "
+                        "parameters; 16: 604M, the stated total)")
     p.add_argument("--config", default="unit",
                    choices=["unit", "selective", "stress", "slab", "ablation", "fidelity"],
                    help="unit: the headline encode + decode unit (default); selective: the whole "
@@ -344,7 +347,7 @@ def bench_selective(args, torch, fw, synth, dev):
     t0 = time.time()
     state_gift = 0
     gift_items, eu = [], []
-    for k, (l, name, mo, di, alpha, gift) in enumerate(synth.selective_tensors()):
+    for k, (l, name, mo, di, alpha, gift) in enumerate(synth.selective_tensors(args.layers)):
         seed = lambda r, l=l, name=name: synth.seed_for(3, synth.ROLE_A, l * 8 + list(synth.SELECTIVE_SHAPES).index(name),
                                                         r)
         if not gift:
@@ -409,6 +412,15 @@ def bench_selective(args, torch, fw, synth, dev):
             L.encode(W0, f, s, codes=codes[0], scales=scales[0])
             L.decode_reduce(codes, scales, f, s, out=out)
 
+    # the same rank-32 layers as one group: one launch encodes all of them,
+    # one launch decode-reduces them
+    group = fw.Group([dict(layer=L, W=W0, codes=codes[0], scales=scales[0], rcodes=codes, rscales=scales, out=out)
+                      for L, W0, codes, scales, out in gift_items], R, f, s, device=dev)
+
+    def gift_group():
+        group.encode()
+        group.decode_reduce()
+
     def euclid_bucket():
         B.encode(g0, f, amax_in=amax, amax_out=am0, codes=codes_eu[0], scales=scales_eu[0])
         B.decode_reduce(codes_eu, scales_eu, f, out=out_eu)
@@ -431,6 +443,8 @@ def bench_selective(args, torch, fw, synth, dev):
             L.encode(W, f, s, amax_in=a_in, amax_out=a_out, codes=c[0], scales=sc[0])
             L.decode_reduce(c, sc, f, s, out=o)
 
+    # (the grouped launch measured slower than one launch per layer and
+    # phase: the step keeps the per-layer launches; both are reported)
     def step():
         euclid_bucket()
         gift_layers()
@@ -438,6 +452,7 @@ def bench_selective(args, torch, fw, synth, dev):
     steps = max(1, min(args.steps, 20))
     ms = _event_ms(torch, step, steps)
     ms_gift = _event_ms(torch, gift_layers, steps)
+    ms_group = _event_ms(torch, gift_group, steps)
     ms_bucket = _event_ms(torch, euclid_bucket, steps)
     ms_per_tensor = _event_ms(torch, euclid_per_tensor, steps)
     ms_512 = _event_ms(torch, euclid_bucket_512, steps)
@@ -465,7 +480,8 @@ def bench_selective(args, torch, fw, synth, dev):
         "data": "synthetic (direct Gaussian gradients, bf16 power-law activations for the rank-32 layers)",
         "config": {"workload": "600M-class selective: 24 layers x {q,k,v,o 1536x1536, fc1/fc3 6144x1536, "
                                "fc2 1536x6144}; fc2 of layers 0-12 rank-32, the rest Euclidean; E4M3 per "
-                               "tensor; R=8", "tensors": len(eu) + len(gift_items), "rank32_tensors": len(gift_items),
+                               "tensor; R=8", "layers": args.layers, "tensors": len(eu) + len(gift_items),
+                   "rank32_tensors": len(gift_items),
                    "params": n},
         "roofline": {"bound": "hbm", "achieved": round(alg / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -474,12 +490,28 @@ def bench_selective(args, torch, fw, synth, dev):
             "euclid_bucket": stage(ms_bucket, alg_eu, "155 Euclidean tensors, one bucket: 3 launches"),
             "euclid_per_tensor": stage(ms_per_tensor, alg_eu, "the same with one launch per tensor and phase"),
             "euclid_bucket_block512": stage(ms_512, alg_512, "per-block Euclidean baseline, 512-element blocks"),
-            "rank32_layers": stage(ms_gift, alg_gift, "13 rank-32 fc2 layers, fused encode + decode each"),
+            "rank32_group": stage(ms_group, alg_gift, f"{len(gift_items)} rank-32 fc2 layers as one group: one "
+                                  "launch for the encodes, one for the decode-reduces"),
+            "rank32_per_layer": stage(ms_gift, alg_gift, f"the same layers, fused encode + decode one layer "
+                                      "at a time (2 launches per layer)"),
         },
-        "memory": {"grad_bytes": int(grad_bytes), "rank32_state_bytes": int(state_gift),
-                   "state_over_grad": round(state_gift / grad_bytes, 4)},
+        "memory": memory_report(gift_items, grad_bytes, state_gift),
     }
     print(json.dumps(result), flush=True)
+
+
+def memory_report(gift_items, grad_bytes, state_gift):
+    """Memory of the geometry-aware layers beside the gradient buffer: as the
+    pages count it ("GIFT 阅读笔记", 实验结果 / 内存开销: the rank-32 factor and
+    the error-feedback buffer of the selected layers), and this library's
+    whole layer state (which keeps the d x d statistics and their window
+    accumulator for the subspace iteration)."""
+    factor = sum(W0.shape[1] * 32 * 4 + 68 * 4 for _, W0, *_ in gift_items)   # U_k and the coefficients
+    ef = sum(4 * W0.numel() for _, W0, *_ in gift_items)                      # fp32 residual per layer
+    return {"grad_bytes": int(grad_bytes),
+            "pages_terms": {"factor_bytes": int(factor), "error_feedback_bytes": int(ef),
+                            "over_grad": round((factor + ef) / grad_bytes, 4)},
+            "library_state_bytes": int(state_gift), "library_state_over_grad": round(state_gift / grad_bytes, 4)}
 
 
 def bench_stress(args, torch, fw, synth, dev):

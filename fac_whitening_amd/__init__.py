@@ -46,8 +46,16 @@ EXPORTS = [
     "gift_last_hip_error", "gift_set_fused", "gift_bucket_table_bytes", "gift_bucket_create",
     "gift_bucket_destroy", "gift_bucket_sizes", "gift_bucket_flags", "gift_bucket_amax", "gift_bucket_encode",
     "gift_bucket_decode_reduce", "gift_scale_sync_due", "gift_set_max_resident", "gift_layer_route",
-    "gift_bucket_encode_static",
+    "gift_bucket_encode_static", "gift_group_table_bytes", "gift_group_create", "gift_group_destroy",
+    "gift_group_encode", "gift_group_decode_reduce",
 ]
+
+
+class GroupItem(ctypes.Structure):
+    _fields_ = [("layer", ctypes.c_void_p), ("d_W", ctypes.c_void_p), ("ldw", ctypes.c_int64),
+                ("d_codes", ctypes.c_void_p), ("d_scales", ctypes.c_void_p), ("d_rcodes", ctypes.c_void_p),
+                ("code_stride", ctypes.c_int64), ("d_rscales", ctypes.c_void_p), ("scale_stride", ctypes.c_int64),
+                ("d_out", ctypes.c_void_p), ("ldo", ctypes.c_int64)]
 
 
 class LayerDesc(ctypes.Structure):
@@ -104,6 +112,11 @@ _sig("gift_bucket_encode", _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _
 _sig("gift_bucket_encode_static", _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp)
 _sig("gift_bucket_decode_reduce", _i32, _vp, _vp, _i64, _vp, _i64, _i32, _i32, _vp, _vp)
 _sig("gift_scale_sync_due", _i32, _i64, _i32)
+_sig("gift_group_table_bytes", _sz, _i32)
+_sig("gift_group_create", _i32, _i32, _P(GroupItem), _i32, _i32, _i32, _vp, _sz, _vp, _P(_vp))
+_sig("gift_group_destroy", _i32, _vp)
+_sig("gift_group_encode", _i32, _vp, _vp)
+_sig("gift_group_decode_reduce", _i32, _vp, _vp)
 
 
 def set_fused(enable: bool) -> bool:
@@ -464,6 +477,48 @@ class Bucket:
     def close(self):
         if getattr(self, "_h", None):
             _lib.gift_bucket_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Group:
+    """Grouped rank-k layers (gift_group_*): one launch encodes all of them,
+    one launch decode-reduces all of them.  items: a list of dicts with the
+    layer (a Layer), W, codes, scales (this worker's payload), rcodes
+    [R][m][d], rscales [R][nblk] (the payloads to decode) and out."""
+
+    def __init__(self, items, R, fmt=E4M3, scaling=SCALE_TENSOR, device="cuda", stream=None):
+        n = len(items)
+        arr = (GroupItem * n)()
+        self._keep = items
+        for k, it in enumerate(items):
+            L = it["layer"]
+            rc, rs = it["rcodes"], it["rscales"]
+            arr[k] = GroupItem(L.handle, it["W"].data_ptr(), it["W"].stride(0), it["codes"].data_ptr(),
+                               it["scales"].data_ptr(), rc.data_ptr(), rc.stride(0) if R > 1 else L.m * L.d,
+                               rs.data_ptr(), rs.stride(0) if R > 1 else rs.shape[-1], it["out"].data_ptr(),
+                               it["out"].stride(0))
+        tb = int(_lib.gift_group_table_bytes(n))
+        self.table = _alloc(tb, device)
+        h = _vp()
+        _check(_lib.gift_group_create(n, arr, R, FORMATS.get(fmt, fmt), SCALINGS.get(scaling, scaling),
+                                      _ptr(self.table), tb, _stream(stream), ctypes.byref(h)), "gift_group_create")
+        self._h = h
+
+    def encode(self, stream=None):
+        _check(_lib.gift_group_encode(self._h, _stream(stream)), "gift_group_encode")
+
+    def decode_reduce(self, stream=None):
+        _check(_lib.gift_group_decode_reduce(self._h, _stream(stream)), "gift_group_decode_reduce")
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.gift_group_destroy(self._h)
             self._h = None
 
     def __del__(self):

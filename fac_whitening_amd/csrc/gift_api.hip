@@ -35,6 +35,12 @@ struct gift_bucket {
   gift::BucketTable t{};
 };
 
+struct gift_group {
+  int32_t n = 0, R = 0, fmt = 0, scaling = 0, grid = 0;
+  std::vector<gift_layer_t> layers;
+  gift::FusedArgs* table = nullptr;   // device: n encode entries, then n decode entries
+};
+
 struct gift_profiler {
   int32_t n_layers, fmt, scaling;
   uint64_t* counts;
@@ -829,6 +835,122 @@ gift_status gift_decode_reduce_fp4(gift_layer_t L, const uint8_t* d_codes, int64
                                         s));
   return unwhiten_multi(L, Ub, d_out, ldo, work, s);
 }
+
+// ---------------------------------------------------------------------------
+// Grouped rank-k layers (one launch per phase)
+// ---------------------------------------------------------------------------
+
+size_t gift_group_table_bytes(int32_t n) {
+  if (n < 1 || n > gift::kMaxGroup) return 0;
+  return gift::align256((size_t)2 * n * sizeof(gift::FusedArgs));
+}
+
+gift_status gift_group_create(int32_t n, const gift_group_item* items, int32_t R, int32_t fmt, int32_t scaling,
+                              void* d_table, size_t table_bytes, gift_stream_t stream, gift_group_t* out) {
+  if (n < 1 || n > gift::kMaxGroup || !items || !out || !d_table || (reinterpret_cast<uintptr_t>(d_table) & 255u))
+    return GIFT_ERR_INVALID_ARG;
+  if (fmt != GIFT_E4M3 && fmt != GIFT_E5M2) return GIFT_ERR_INVALID_ARG;
+  if (scaling != GIFT_SCALE_TENSOR && scaling != GIFT_SCALE_BLOCK128) return GIFT_ERR_INVALID_ARG;
+  if (R < 1 || R > 64) return GIFT_ERR_INVALID_ARG;
+  if (table_bytes < gift_group_table_bytes(n)) return GIFT_ERR_WORKSPACE;
+  std::vector<gift::FusedArgs> host((size_t)2 * n);
+  int grid = 0;
+  for (int i = 0; i < n; ++i) {
+    const gift_group_item& it = items[i];
+    gift_layer_t L = it.layer;
+    if (!L || L->desc.transform != GIFT_LOWRANK) return GIFT_ERR_INVALID_ARG;
+    const gift_layer_desc& g = L->desc;
+    const int m = g.d_out, d = g.d_in;
+    const int64_t nb = nblk(m, d, scaling);
+    if (!it.d_W || !aligned16(it.d_W) || it.ldw < d || it.ldw % 4 != 0) return GIFT_ERR_INVALID_ARG;
+    if (!it.d_codes || !aligned16(it.d_codes) || !it.d_scales) return GIFT_ERR_INVALID_ARG;
+    if (!it.d_rcodes || !aligned16(it.d_rcodes) || !it.d_rscales || !it.d_out || !aligned16(it.d_out))
+      return GIFT_ERR_INVALID_ARG;
+    if (it.ldo < d || it.ldo % 4 != 0) return GIFT_ERR_INVALID_ARG;
+    if (R > 1 && (it.code_stride < (int64_t)m * d || it.code_stride % 16 != 0 || it.scale_stride < nb))
+      return GIFT_ERR_INVALID_ARG;
+    // every layer of the group runs on the fused kernels
+    if (!fused_ok(g, it.ldw) || !fused_ok(g, it.ldo)) return GIFT_ERR_UNSUPPORTED;
+    for (int j = 0; j < i; ++j)
+      if (items[j].layer == L) return GIFT_ERR_INVALID_ARG;   // one entry per layer (one epoch per call)
+    gift::FusedArgs& e = host[(size_t)i];
+    e.mode = 0;
+    e.m = m;
+    e.d = d;
+    e.CG = fused_cg(g);
+    e.fmt = fmt;
+    e.scaling = scaling;
+    e.lr = 1;
+    e.W = it.d_W;
+    e.ldw = it.ldw;
+    e.ub = reinterpret_cast<const uint4*>(L->state + L->sl.ub);
+    e.ua = reinterpret_cast<const uint4*>(L->state + L->sl.ua);
+    e.coef = reinterpret_cast<const float*>(L->state + L->sl.coef);
+    e.xpub = reinterpret_cast<unsigned long long*>(L->state + L->sl.xpub);
+    e.apub = reinterpret_cast<unsigned long long*>(L->state + L->sl.apub);
+    e.flags = reinterpret_cast<uint32_t*>(L->state + L->sl.flags);
+    e.codes = it.d_codes;
+    e.scales = it.d_scales;
+    gift::FusedArgs& dd = host[(size_t)(n + i)];
+    dd = e;
+    dd.mode = 1;
+    dd.W = nullptr;
+    dd.codes = nullptr;
+    dd.scales = nullptr;
+    dd.R = R;
+    dd.qcodes = it.d_rcodes;
+    dd.code_stride = R > 1 ? it.code_stride : (int64_t)m * d;
+    dd.qscales = it.d_rscales;
+    dd.scale_stride = R > 1 ? it.scale_stride : nb;
+    dd.invR = 1.0f / (float)R;
+    dd.out = it.d_out;
+    dd.ldo = it.ldo;
+    grid = std::max(grid, fused_groups(g) * e.CG);
+  }
+  gift_group* G = new (std::nothrow) gift_group;
+  if (!G) return GIFT_ERR_INVALID_ARG;
+  G->n = n;
+  G->R = R;
+  G->fmt = fmt;
+  G->scaling = scaling;
+  G->grid = grid;
+  G->table = static_cast<gift::FusedArgs*>(d_table);
+  for (int i = 0; i < n; ++i) G->layers.push_back(items[i].layer);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(d_table, host.data(), host.size() * sizeof(gift::FusedArgs), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);   // the host copy source must outlive the transfer
+  if (e != hipSuccess) {
+    delete G;
+    return hip_fail(e);
+  }
+  *out = G;
+  return GIFT_OK;
+}
+
+gift_status gift_group_destroy(gift_group_t G) {
+  delete G;
+  return GIFT_OK;
+}
+
+static gift_status group_call(gift_group_t G, int decode, gift_stream_t stream) {
+  if (!G) return GIFT_ERR_INVALID_ARG;
+  for (gift_layer_t L : G->layers)
+    if (!L->ready) return GIFT_ERR_NOT_READY;
+  gift::GroupEpochs ep{};
+  for (int i = 0; i < G->n; ++i) ep.v[i] = (unsigned)(++G->layers[(size_t)i]->counters[decode ? 6 : 5]);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = gift::order_persistent(s);
+  if (e == hipSuccess)
+    e = gift::launch_group(G->table + (decode ? G->n : 0), G->n, ep, decode, G->fmt, G->scaling, G->R, G->grid, s);
+  if (e != hipSuccess) {
+    for (int i = 0; i < G->n; ++i) --G->layers[(size_t)i]->counters[decode ? 6 : 5];
+    return hip_fail(e);
+  }
+  return GIFT_OK;
+}
+
+gift_status gift_group_encode(gift_group_t G, gift_stream_t stream) { return group_call(G, 0, stream); }
+gift_status gift_group_decode_reduce(gift_group_t G, gift_stream_t stream) { return group_call(G, 1, stream); }
 
 // ---------------------------------------------------------------------------
 // Profiler

@@ -66,6 +66,14 @@ struct FusedArgs {
 hipError_t launch_fused(const FusedArgs& args, int grid, hipStream_t s);
 // Workgroups of the fused kernels the current device holds at once (0: unknown).
 int fused_resident_groups();
+// Grouped launch of several rank-k layers (table: device array of n
+// FusedArgs, epochs by value).
+constexpr int kMaxGroup = 32;
+struct GroupEpochs {
+  unsigned v[kMaxGroup];
+};
+hipError_t launch_group(const FusedArgs* table, int n, const GroupEpochs& ep, int decode, int fmt, int scaling, int R,
+                        int grid, hipStream_t s);
 // Upper bound on co-resident workgroups that the persistent kernels may
 // assume (gift_set_max_resident; 0 = none).
 int max_resident_cap();

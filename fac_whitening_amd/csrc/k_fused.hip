@@ -278,7 +278,7 @@ constexpr int kXPT = kXW / 512;     // of them per thread (3)
 // tile schedule, amax all-gather and quantiser without the projection,
 // exchange and reconstruction).
 template <int FMT, bool ENC, int RC, int SC, bool LR, bool EF = false>
-__device__ __forceinline__ void fused_body(const FusedArgs& a) {
+__device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, const int G, const unsigned epoch) {
   // The staged tile (fp32, padded rows); after it has been read into
   // registers the same memory holds the per-wave projection partials and the
   // projection of the tile rows, and finally the outgoing tile.
@@ -298,8 +298,9 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
   // (rb 0), the next 5.5 (rb 1), ...
   float (*cp)[8][16][33] = reinterpret_cast<float (*)[8][16][33]>(smem);
   float (*pf)[33] = reinterpret_cast<float (*)[33]>(smem + 8 * 3 * 16 * 33);
-  const int G = gridDim.x;
-  const int g = blockIdx.x, rg = g / a.CG, cgi = g % a.CG;
+  // g: this workgroup's tile, G: the tiles of the layer (the grid of a
+  // single-layer launch)
+  const int rg = g / a.CG, cgi = g % a.CG;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
   const int lr = lane & 15, lg = lane >> 4;
@@ -309,7 +310,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
   const int nbd = (int)cdiv(d, kBlock);
   const int rb0 = row0 / kBlock, cb0 = col0 / kBlock;
   const int cbg0 = (col0 >> 5) + wave;   // this wave's first 32-column block
-  const unsigned tag = (a.epoch << 1) | (enc ? 0u : 1u);
+  const unsigned tag = (epoch << 1) | (enc ? 0u : 1u);
   if (tid < 16) wmax[tid] = 0u;
   if (tid == 0) s_bad = 0;
   // PIPE: the projection of each 16-row block runs as soon as the block is
@@ -884,7 +885,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
   const bool need_sync = a.amax_in == nullptr || a.amax_out != nullptr;
   if (need_sync) {
     unsigned long long* pub = a.apub;
-    const unsigned long long etag = (unsigned long long)a.epoch << 32;
+    const unsigned long long etag = (unsigned long long)epoch << 32;
     // the tag makes each word self-validating: no ordering with other data
     // is needed.  The words are published with atomic exchanges, which take
     // effect at the device's coherence point at once.
@@ -909,7 +910,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
             }
             bool ok = true;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ok = ok && (unsigned)(w[j] >> 32) == a.epoch;
+            for (int j = 0; j < 4; ++j) ok = ok && (unsigned)(w[j] >> 32) == epoch;
             if (__all(ok)) break;
             if (++spins > kSpinLimit) {
               if (lane == 0) {
@@ -937,7 +938,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
       for (int t = tid; t < nr * 12; t += 512) {
         const int rr = r_lo + t / 12, e = t % 12;
         const int h = rr * a.CG + cgi;
-        const unsigned long long w = wait_tag(pub + (int64_t)h * kApub + e, a.epoch, a.flags, &s_bad);
+        const unsigned long long w = wait_tag(pub + (int64_t)h * kApub + e, epoch, a.flags, &s_bad);
         const int brow = (rr * TR) / kBlock + e / 6;   // global block row of that entry
         const int slot_r = brow - rb0;
         if (slot_r >= 0 && slot_r < 2 && (uint32_t)w) atomicMax(&blk[slot_r][e % 6], (uint32_t)w);
@@ -1048,27 +1049,43 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a) {
 // replica count 4, 8, 16 (0: any count up to 64) and scaling.
 template <int FMT>
 __global__ void __launch_bounds__(512) k_rank_encode(FusedArgs a) {
-  fused_body<FMT, true, 0, -1, true>(a);
+  fused_body<FMT, true, 0, -1, true>(a, blockIdx.x, gridDim.x, a.epoch);
 }
 template <int FMT>
 __global__ void __launch_bounds__(512) k_rank_encode_ef(FusedArgs a) {
-  fused_body<FMT, true, 0, -1, true, true>(a);
+  fused_body<FMT, true, 0, -1, true, true>(a, blockIdx.x, gridDim.x, a.epoch);
 }
 template <int FMT, int RC, int SC>
 __global__ void __launch_bounds__(512) k_rank_decode(FusedArgs a) {
-  fused_body<FMT, false, RC, SC, true>(a);
+  fused_body<FMT, false, RC, SC, true>(a, blockIdx.x, gridDim.x, a.epoch);
 }
 template <int FMT>
 __global__ void __launch_bounds__(512) k_euclid_encode(FusedArgs a) {
-  fused_body<FMT, true, 0, -1, false>(a);
+  fused_body<FMT, true, 0, -1, false>(a, blockIdx.x, gridDim.x, a.epoch);
 }
 template <int FMT>
 __global__ void __launch_bounds__(512) k_euclid_encode_ef(FusedArgs a) {
-  fused_body<FMT, true, 0, -1, false, true>(a);
+  fused_body<FMT, true, 0, -1, false, true>(a, blockIdx.x, gridDim.x, a.epoch);
 }
 template <int FMT, int RC, int SC>
 __global__ void __launch_bounds__(512) k_euclid_decode(FusedArgs a) {
-  fused_body<FMT, false, RC, SC, false>(a);
+  fused_body<FMT, false, RC, SC, false>(a, blockIdx.x, gridDim.x, a.epoch);
+}
+
+// Grouped launch: several rank-k layers one after another in one persistent
+// launch (one per phase).  Workgroup g takes tile g of each layer in turn
+// (layers with fewer tiles skip it) and moves on as soon as its part of a
+// layer is done, so the tail of one layer overlaps the loads of the next in
+// other workgroups.  Each layer's exchange words and amax words live in its
+// own state, tagged with its own call epoch (passed by value).
+template <int FMT, bool ENC, int RC, int SC>
+__global__ void __launch_bounds__(512) k_rank_group(const FusedArgs* __restrict__ table, int n, GroupEpochs ep) {
+  for (int L = 0; L < n; ++L) {
+    const FusedArgs& a = table[L];
+    const int tiles = (int)cdiv(a.m, TR) * a.CG;
+    if ((int)blockIdx.x < tiles) fused_body<FMT, ENC, RC, SC, true>(a, blockIdx.x, tiles, ep.v[L]);
+    __syncthreads();   // the LDS of this layer is free before the next one
+  }
 }
 
 // Persistent launches.  The workgroups of these kernels wait on words that
@@ -1129,6 +1146,36 @@ hipError_t launch_fused(const FusedArgs& a, int grid, hipStream_t s) {
     e = a.lr ? launch_decode<1, true>(a, grid, s) : launch_decode<1, false>(a, grid, s);
   }
   return e;
+}
+
+template <int FMT, int SC>
+static void launch_group_decode(const FusedArgs* table, int n, const GroupEpochs& ep, int R, int grid,
+                                hipStream_t s) {
+  const dim3 gd((unsigned)grid), bd(512);
+  switch (R) {
+    case 4: hipLaunchKernelGGL((k_rank_group<FMT, false, 4, SC>), gd, bd, 0, s, table, n, ep); break;
+    case 8: hipLaunchKernelGGL((k_rank_group<FMT, false, 8, SC>), gd, bd, 0, s, table, n, ep); break;
+    case 16: hipLaunchKernelGGL((k_rank_group<FMT, false, 16, SC>), gd, bd, 0, s, table, n, ep); break;
+    default: hipLaunchKernelGGL((k_rank_group<FMT, false, 0, SC>), gd, bd, 0, s, table, n, ep); break;
+  }
+}
+
+hipError_t launch_group(const FusedArgs* table, int n, const GroupEpochs& ep, int decode, int fmt, int scaling, int R,
+                        int grid, hipStream_t s) {
+  const dim3 gd((unsigned)grid), bd(512);
+  if (!decode) {
+    if (fmt == 0)
+      hipLaunchKernelGGL((k_rank_group<0, true, 0, -1>), gd, bd, 0, s, table, n, ep);
+    else
+      hipLaunchKernelGGL((k_rank_group<1, true, 0, -1>), gd, bd, 0, s, table, n, ep);
+  } else if (fmt == 0) {
+    if (scaling == 0) launch_group_decode<0, 0>(table, n, ep, R, grid, s);
+    else launch_group_decode<0, 1>(table, n, ep, R, grid, s);
+  } else {
+    if (scaling == 0) launch_group_decode<1, 0>(table, n, ep, R, grid, s);
+    else launch_group_decode<1, 1>(table, n, ep, R, grid, s);
+  }
+  return hipGetLastError();
 }
 
 // Workgroups of the fused kernels that the current device can hold at once:

@@ -334,6 +334,51 @@ gift_status gift_bucket_decode_reduce(gift_bucket_t bucket, const uint8_t* d_cod
                                       const float* d_scales, int64_t scale_stride, int32_t R,
                                       int32_t fmt, float* d_out, gift_stream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Grouped rank-k layers ([Note] Algorithm 1: every step encodes, reduces and
+ * maps back each selected layer; §实验设置: 13 fc2 layers take the rank-32
+ * path): the encodes of several GIFT_LOWRANK layers in one launch, and their
+ * decode-reduces in one launch, on the single-launch kernels (every layer
+ * must take the fused route: gift_layer_route gives 1 for its ld's).  Each
+ * layer is the same computation as gift_encode / gift_decode_reduce with
+ * the local amax (results bit-identical to those calls); a workgroup moves
+ * to its tile of the next layer as soon as its part of a layer is done.
+ *
+ * A group binds fixed buffers, given per layer in gift_group_item:
+ *   d_W, ldw:            fp32 [d_out][ldw] gradient to encode
+ *   d_codes, d_scales:   this worker's payload (written by the encode)
+ *   d_rcodes, code_stride, d_rscales, scale_stride: the R payloads to decode
+ *                        (replica r at + r * stride, as gift_decode_reduce)
+ *   d_out, ldo:          fp32 [d_out][ldo] decoded mean
+ * gift_group_create: n <= 32 distinct layers, one format / scaling / R for
+ * all; d_table = caller-owned device memory of gift_group_table_bytes(n)
+ * bytes, 256-byte aligned; the call copies the launch table into it and
+ * synchronises `stream`.  GIFT_ERR_UNSUPPORTED if a layer cannot take the
+ * fused route.  The layers may be refreshed later; encode / decode return
+ * GIFT_ERR_NOT_READY while any of them has no factor.  Calls on a group and
+ * on its layers must be ordered on one stream.
+ * ------------------------------------------------------------------------- */
+typedef struct gift_group* gift_group_t;
+typedef struct gift_group_item {
+  gift_layer_t layer;
+  const float* d_W;
+  int64_t ldw;
+  uint8_t* d_codes;
+  float* d_scales;
+  const uint8_t* d_rcodes;
+  int64_t code_stride;
+  const float* d_rscales;
+  int64_t scale_stride;
+  float* d_out;
+  int64_t ldo;
+} gift_group_item;
+size_t gift_group_table_bytes(int32_t n);
+gift_status gift_group_create(int32_t n, const gift_group_item* items, int32_t R, int32_t fmt, int32_t scaling,
+                              void* d_table, size_t table_bytes, gift_stream_t stream, gift_group_t* out);
+gift_status gift_group_destroy(gift_group_t group);
+gift_status gift_group_encode(gift_group_t group, gift_stream_t stream);
+gift_status gift_group_decode_reduce(gift_group_t group, gift_stream_t stream);
+
 /* Scale-sync schedule ([Note] Algorithm 1, its scale-sync step): the geometry-aware
  * layers quantise with their local scale and, on a scale-sync step, with the
  * scale shared across workers (the AllReduceMax of the local amaxes: an
