@@ -292,7 +292,7 @@ WorkLayout work_layout(const gift_layer_desc& g) {
     w.Z = take(d * lp * 8);
     w.small = take((64 + 64 * 64 + 64) * 8);
     w.gpart = take(((size_t)cdiv((int64_t)d, kGramRows) + 1) * lp * lp * 8);   // partials + their sum
-    w.apart = take((size_t)aq_splits((int)d) * d * lp * 8);
+    w.apart = take(std::max((size_t)aq_splits((int)d) * d * lp * 8, (size_t)aq32_splits((int)d) * d * lp * 4));
   }
   if (g.transform == GIFT_CHOL_INPUT || g.transform == GIFT_CHOL_TWOSIDED) {
     const size_t n = g.transform == GIFT_CHOL_TWOSIDED ? std::max(d, m) : d;

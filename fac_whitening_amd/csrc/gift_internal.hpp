@@ -85,17 +85,29 @@ hipError_t launch_pack_u(const float* U, int d, void* ub, void* ua, hipStream_t 
 
 // Refresh products Y = A X (A symmetric d x d): each workgroup takes 256
 // columns of A and a range of its rows; the partial sums of the ranges are
-// added in a fixed order.  At least ~2 workgroups per compute unit.
+// added in a fixed order.  At most 512 workgroups (two per compute unit, the
+// fp64 kernel's occupancy), so that they run in one even round.
 constexpr int kAqCols = 256;
 __host__ __device__ inline int aq_rows_per_split(int d) {
   const int cb = (int)cdiv(d, kAqCols);
-  int splits = (int)cdiv(512, cb);
+  int splits = 512 / cb;   // at most two workgroups per compute unit: one even round
   const int max_splits = (int)cdiv(d, 64);
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
   return (int)cdiv(cdiv(d, splits), 32) * 32;
 }
 __host__ __device__ inline int aq_splits(int d) { return (int)cdiv(d, aq_rows_per_split(d)); }
+// The fp32 products: workgroups of 64 columns, row ranges (multiples of 64
+// rows) split so that there are about 768 workgroups (three per compute unit).
+__host__ __device__ inline int aq32_rows_per_split(int d) {
+  const int cb = (int)cdiv(d, 64);
+  int splits = (int)cdiv(768, cb);
+  const int max_splits = (int)cdiv(d, 64);
+  if (splits > max_splits) splits = max_splits;
+  if (splits < 1) splits = 1;
+  return (int)cdiv(cdiv(d, splits), 64) * 64;
+}
+__host__ __device__ inline int aq32_splits(int d) { return (int)cdiv(d, aq32_rows_per_split(d)); }
 constexpr int kGramRows = 64;   // rows per partial of the l x l Gram products
 
 // Offsets (bytes) inside the per-call workspace.  Regions overlap between
@@ -112,7 +124,7 @@ struct WorkLayout {
   size_t Y = 0, Q = 0, Z = 0;   // fp64 [d][l]
   size_t small = 0;             // fp64 scratch for the l x l solvers
   size_t gpart = 0;             // fp64 [nchunk][l][l]
-  size_t apart = 0;             // fp64 [splits][d][l]: partials of A X
+  size_t apart = 0;             // partials of A X: fp64 [splits][d][l] or fp32 [splits32][d][l]
   size_t chol = 0;              // fp64 [n][n] (Cholesky variants)
   size_t chol2 = 0;             // fp64 [n][n]
   size_t total = 0;

@@ -11,7 +11,8 @@
 // pass between products, two (CholeskyQR2) for the Rayleigh-Ritz basis; the
 // l x l eigenproblem is solved by cyclic two-sided Jacobi (Golub & Van Loan,
 // §8.5) in fp64 in one wave, with parallel (round-robin) ordering.  The
-// products A X run on the fp64 matrix cores.
+// first two products A X of the iteration run on the fp32 matrix cores, the
+// later ones and the Rayleigh-Ritz product Z = A Q on the fp64 ones.
 // A is read as fp32; every other quantity is fp64 until the basis U and the
 // coefficient vectors are written as fp32.
 #include "gift_internal.hpp"
@@ -54,6 +55,7 @@ __global__ void k_omega64(const float* __restrict__ om, int d, int l, int lp, do
 // workgroup (b, s) owns columns 256 b + 64 w .. + 63 of A; A is read from
 // memory once, X (a few MB) from L2.  A's fp32 values are exact in fp64.
 typedef double double4v __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 template <int LP>
 __global__ void __launch_bounds__(256) k_aq(const float* __restrict__ A, int d, const double* __restrict__ X,
@@ -116,6 +118,105 @@ __global__ void __launch_bounds__(256) k_aq(const float* __restrict__ A, int d, 
         const int row = i0 + 16 * mt + 4 * e + lk;
         if (row < d) part[((int64_t)blockIdx.y * d + row) * LP + 16 * nt + lm] = acc[mt][nt][e];
       }
+}
+
+// The same product on the fp32 matrix cores (v_mfma_f32_16x16x4f32, twice
+// the fp64 rate) for the products of the subspace iteration, whose errors
+// only perturb the basis that the next product and orthonormalisation
+// carry on (the Rayleigh-Ritz product keeps fp64).  X is rounded to fp32 on
+// load; A's fp32 values are exact; sums are fp32.  Workgroup (b, s) owns 64
+// columns of A and row range s; its 4 waves take a quarter of the range
+// each and their accumulators are added in LDS in wave order.  Slot e of
+// lane l holds D[4 (l / 16) + e][l % 16].  The partials of the ranges are
+// fp32 and summed in fp64 by k_sum_parts32.
+template <int LP>
+__global__ void __launch_bounds__(256) k_aq32(const float* __restrict__ A, int d, const double* __restrict__ X,
+                                              int jrows, float* __restrict__ part) {
+  constexpr int NT = LP / 16;
+  constexpr int KB = 4;   // 4-row k-steps per block (16 rows)
+  __shared__ floatx4 red[3][4][NT][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lm = lane & 15, lk = lane >> 4;
+  const int i0 = blockIdx.x * 64;
+  const int js = blockIdx.y * jrows, je = min(d, js + jrows);
+  const int qr = jrows / 4;
+  const int j0 = min(je, js + wave * qr), j1 = min(je, j0 + qr);
+  int ic[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) ic[mt] = min(i0 + 16 * mt + lm, d - 1);   // clamped: loads stay in bounds
+  floatx4 acc[4][NT];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = (floatx4){0.f, 0.f, 0.f, 0.f};
+  struct Blk {
+    float a[KB][4];
+    double b[KB][NT];
+  };
+  auto load = [&](int jb, Blk& t) {
+#pragma unroll
+    for (int ks = 0; ks < KB; ++ks) {
+      const int jr = min(jb + 4 * ks + lk, d - 1);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) t.a[ks][mt] = A[(int64_t)jr * d + ic[mt]];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) t.b[ks][nt] = X[(int64_t)jr * LP + 16 * nt + lm];
+    }
+  };
+  auto compute = [&](int jb, const Blk& t) {
+#pragma unroll
+    for (int ks = 0; ks < KB; ++ks) {
+      const bool in = jb + 4 * ks + lk < j1;   // rows past the range contribute zero
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const float av = in ? t.a[ks][mt] : 0.f;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, (float)t.b[ks][nt], acc[mt][nt], 0, 0, 0);
+      }
+    }
+  };
+  if (j0 < j1) {
+    Blk cur, nxt;
+    load(j0, cur);
+    for (int jb = j0; jb < j1; jb += 4 * KB) {
+      if (jb + 4 * KB < j1) load(jb + 4 * KB, nxt);   // in flight while this block computes
+      compute(jb, cur);
+      cur = nxt;
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) red[wave - 1][mt][nt][lane] = acc[mt][nt];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        floatx4 v = acc[mt][nt];
+#pragma unroll
+        for (int w = 0; w < 3; ++w) v += red[w][mt][nt][lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = i0 + 16 * mt + 4 * lk + e;
+          if (row < d) part[((int64_t)blockIdx.y * d + row) * LP + 16 * nt + lm] = v[e];
+        }
+      }
+  }
+}
+
+// out[e] = sum_p part[p][e] in fp64, in order p = 0, 1, ... (deterministic)
+__global__ void __launch_bounds__(256) k_sum_parts32(const float* __restrict__ part, int nparts, int64_t n,
+                                                     double* __restrict__ out) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  double s = 0.0;
+  for (int p = 0; p < nparts; ++p) s += (double)part[(int64_t)p * n + e];
+  out[e] = s;
 }
 
 // out[e] = sum_{p < nparts} part[p][e], in order p = 0, 1, ... (deterministic)
@@ -504,10 +605,17 @@ static hipError_t refresh_lowrank_lp(const float* A, int d, int k, int l, int q,
   double* gsum = gpart + (int64_t)nchG * LP * LP;      // the summed l x l matrix
   const int jrows = aq_rows_per_split(d), nsplit = aq_splits(d);
   const int64_t ny = (int64_t)d * LP;
-  auto product = [&](const double* X, double* out) {   // out = A X
+  auto product = [&](const double* X, double* out) {   // out = A X (fp64 matrix cores)
     hipLaunchKernelGGL((k_aq<LP>), dim3((unsigned)cdiv(d, kAqCols), (unsigned)nsplit), dim3(256), 0, s, A, d, X,
                        jrows, apart);
     hipLaunchKernelGGL(k_sum_parts, dim3((unsigned)cdiv(ny, 256)), dim3(256), 0, s, apart, nsplit, ny, out);
+  };
+  const int jrows32 = aq32_rows_per_split(d), nsplit32 = aq32_splits(d);
+  auto product32 = [&](const double* X, double* out) {   // out = A X (fp32 matrix cores, fp64 result)
+    float* p32 = reinterpret_cast<float*>(apart);
+    hipLaunchKernelGGL((k_aq32<LP>), dim3((unsigned)cdiv(d, 64), (unsigned)nsplit32), dim3(256), 0, s, A, d, X,
+                       jrows32, p32);
+    hipLaunchKernelGGL(k_sum_parts32, dim3((unsigned)cdiv(ny, 256)), dim3(256), 0, s, p32, nsplit32, ny, out);
   };
   auto gram = [&](const double* X, const double* Y2) {  // gsum = X^T Y2
     hipLaunchKernelGGL((k_gram_parts<LP>), dim3(nchG), dim3(256), 0, s, X, Y2, d, gpart);
@@ -528,13 +636,19 @@ static hipError_t refresh_lowrank_lp(const float* A, int d, int k, int l, int q,
       src = out;
     }
   };
-  product(Q, Y);                      // Y = A Omega
+  // The first two products on the fp32 matrix cores: what their rounding
+  // does to the basis is contracted by every exact (fp64) product after
+  // them; the last products before the Rayleigh-Ritz step stay fp64.
+  product32(Q, Y);                    // Y = A Omega
   for (int it = 0; it < q; ++it) {
     orth(Y, Q, 1);                    // Q = orth(Y)
-    product(Q, Y);                    // Y = A Q
+    if (it == 0 && q >= 3)
+      product32(Q, Y);                // Y = A Q
+    else
+      product(Q, Y);
   }
   orth(Y, Q, 2);                      // Q = orth(Y)
-  product(Q, Z);                      // Z = A Q
+  product(Q, Z);                      // Z = A Q (fp64: the Rayleigh-Ritz matrix and the Ritz values)
   gram(Q, Z);
   hipLaunchKernelGGL((k_jacobi_coef<LP>), dim3(1), dim3(256), 0, s, gsum, l, k, d, damping_rel, small, coef, flags);
   hipLaunchKernelGGL((k_right_small<LP, 32, float>), dim3((unsigned)cdiv((int64_t)d * 4, 256)), dim3(256), 0, s, Q,
