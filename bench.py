@@ -12,9 +12,10 @@ Timed region: W untimed warmup steps, then K steps bracketed by
 torch.cuda.synchronize(); the input buffers rotate over 4 independent sets
 (W, 8 payloads, output: 604 MB in all, more than twice the 256 MB Infinity
 Cache) so each step reads inputs that are not cache-resident.  The kernel
-durations behind `roofline` come from a second pass over the same K steps
-with HIP events around every call (event pairs lengthen the stream, so they
-stay out of the pass that `value` is measured on).
+durations behind `roofline` come from K encode calls and then K
+decode-reduce calls back to back over the same buffer sets, each batch
+between one pair of HIP events (event pairs around single calls would
+lengthen them, and they stay out of the pass `value` is measured on).
 
 Prints one JSON line (the metric, roofline of the dominant kernel, the oracle
 timed on the host cores as a baseline).
@@ -176,22 +177,31 @@ def main():
     bat_ms = [bat_ev[bounds[j]].elapsed_time(bat_ev[bounds[j + 1]]) / (bounds[j + 1] - bounds[j])
               for j in range(nbat)]
     ms_per_step = total_ms / args.steps
-    # Kernel durations: the same K steps again with HIP events around every
-    # encode and decode call, on the stream they run on (torch's current
-    # stream).  An event pair adds a few microseconds to the stream, so this
-    # pass is kept apart from the one `value` comes from.
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
-    torch.cuda.synchronize()
-    evs[0].record()
-    for i in range(args.steps):
-        W, codes, scales, out = sets[i % len(sets)]
+    # Kernel durations: K encode calls back to back, then K decode-reduce
+    # calls back to back, over the same rotating buffer sets, each batch
+    # bracketed by one pair of HIP events on the stream the kernels run on
+    # (torch's current stream): the average launch-to-launch duration of
+    # each kernel, without the few microseconds an event pair adds to a call.
+    def batch_ms(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(args.steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    def enc_only(i):
+        W, codes, scales, _ = sets[i % len(sets)]
         L.encode(W, fw.E4M3, scaling, codes=codes[0], scales=scales[0])
-        evs[2 * i + 1].record()
+
+    def dec_only(i):
+        _, codes, scales, out = sets[i % len(sets)]
         L.decode_reduce(codes, scales, fw.E4M3, scaling, out=out)
-        evs[2 * i + 2].record()
-    torch.cuda.synchronize()
-    t_enc = float(np.mean([evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(args.steps)]))
-    t_dec = float(np.mean([evs[2 * i + 1].elapsed_time(evs[2 * i + 2]) for i in range(args.steps)]))
+
+    t_enc = batch_ms(enc_only)
+    t_dec = batch_ms(dec_only)
     grad_bytes = 4.0 * m * d
     value = grad_bytes / (ms_per_step * 1e-3) / 1e9         # GB/s of fp32 gradient
 
@@ -210,7 +220,7 @@ def main():
                 "kernel": kernel,
                 "unit_frac": round((enc_bytes + dec_bytes) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "decode_ms": round(t_dec, 5), "encode_ms": round(t_enc, 5),
-                "durations": "mean of event pairs around every call in a second pass over the K steps",
+                "durations": "K calls of each kernel back to back over the rotating sets, one event pair per batch",
                 "alg_bytes_encode": int(enc_bytes), "alg_bytes_decode": int(dec_bytes)}
 
     # ---- beside the headline: batch spread, the unit with one buffer set
@@ -944,12 +954,18 @@ def cpu_baseline(case, A_gpu, R, m, d, scaling, budget_s=10.0, max_units=30):
 
 
 def kernel_source_sha():
-    """Hash of the sources the fused kernels are built from."""
+    """Hash of the sources the fused kernels are built from: k_fused.hip,
+    fp8_codec.hpp and the FusedArgs declaration of gift_internal.hpp."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("k_fused.hip", "fp8_codec.hpp", "gift_internal.hpp"):
-        with open(os.path.join(ROOT, "fac_whitening_amd", "csrc", f), "rb") as fh:
+    csrc = os.path.join(ROOT, "fac_whitening_amd", "csrc")
+    for f in ("k_fused.hip", "fp8_codec.hpp"):
+        with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
+    with open(os.path.join(csrc, "gift_internal.hpp")) as fh:
+        text = fh.read()
+    i = text.index("struct FusedArgs {")
+    h.update(text[i:text.index("};", i)].encode())
     return h.hexdigest()
 
 
