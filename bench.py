@@ -340,8 +340,9 @@ def _event_ms(torch, fn, reps):
 
 
 def bench_selective(args, torch, fw, synth, dev):
-    """Whole-buffer encode + decode-reduce of the 600M-class deployment: 168
-    weight gradients (906M fp32 values, 3.62 GB), the fc2 gradients of 13
+    """Whole-buffer encode + decode-reduce of the 600M-class deployment (the
+    figures below are for the default 24 layers; --layers 16 gives the
+    604M-parameter buffer): 168 weight gradients (906M fp32 values, 3.62 GB), the fc2 gradients of 13
     layers rank-32 whitened, the other 155 Euclidean; E4M3 per tensor,
     R = 8 (replicas 1..7 encoded in setup).  One step = worker 0's share:
     the 155 Euclidean tensors as one flat bucket (local amax and quantise
@@ -488,16 +489,16 @@ def bench_selective(args, torch, fw, synth, dev):
         "value": round(grad_bytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": "f32",
         "data": "synthetic (direct Gaussian gradients, bf16 power-law activations for the rank-32 layers)",
-        "config": {"workload": "600M-class selective: 24 layers x {q,k,v,o 1536x1536, fc1/fc3 6144x1536, "
-                               "fc2 1536x6144}; fc2 of layers 0-12 rank-32, the rest Euclidean; E4M3 per "
-                               "tensor; R=8", "layers": args.layers, "tensors": len(eu) + len(gift_items),
+        "config": {"workload": f"600M-class selective: {args.layers} layers x {{q,k,v,o 1536x1536, fc1/fc3 "
+                               f"6144x1536, fc2 1536x6144}}; fc2 of {len(gift_items)} layers rank-32, the rest "
+                               "Euclidean; E4M3 per tensor; R=8", "layers": args.layers, "tensors": len(eu) + len(gift_items),
                    "rank32_tensors": len(gift_items),
                    "params": n},
         "roofline": {"bound": "hbm", "achieved": round(alg / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "alg_bytes": int(alg)},
         "stages": {
-            "euclid_bucket": stage(ms_bucket, alg_eu, "155 Euclidean tensors, one bucket: 3 launches"),
+            "euclid_bucket": stage(ms_bucket, alg_eu, f"{len(eu)} Euclidean tensors, one bucket: 3 launches"),
             "euclid_per_tensor": stage(ms_per_tensor, alg_eu, "the same with one launch per tensor and phase"),
             "euclid_bucket_block512": stage(ms_512, alg_512, "per-block Euclidean baseline, 512-element blocks"),
             "rank32_group": stage(ms_group, alg_gift, f"{len(gift_items)} rank-32 fc2 layers as one group: one "
