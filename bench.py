@@ -358,13 +358,15 @@ def bench_selective(args, torch, fw, synth, dev):
     t0 = time.time()
     state_gift = 0
     gift_items, eu = [], []
+    shared_work = None   # one workspace for every rank-32 layer (their windows commit in one call each)
     for k, (l, name, mo, di, alpha, gift) in enumerate(synth.selective_tensors(args.layers)):
         seed = lambda r, l=l, name=name: synth.seed_for(3, synth.ROLE_A, l * 8 + list(synth.SELECTIVE_SHAPES).index(name),
                                                         r)
         if not gift:
             eu.append((mo, di, alpha, seed))
             continue
-        L = fw.Layer(mo, di, "lowrank", device=dev)
+        L = fw.Layer(mo, di, "lowrank", device=dev, transient_stats=True, workspace=shared_work)
+        shared_work = L.work
         a = synth.gaussian_rows(Ttok, di, alpha, None, synth.seed_for(3, synth.ROLE_A, l, 0, 1), dev, torch.bfloat16)
         L.accumulate_stats(a, fw.SIDE_A, commit=True)
         del a
@@ -506,23 +508,25 @@ def bench_selective(args, torch, fw, synth, dev):
             "rank32_per_layer": stage(ms_gift, alg_gift, f"the same layers, fused encode + decode one layer "
                                       "at a time (2 launches per layer)"),
         },
-        "memory": memory_report(gift_items, grad_bytes, state_gift),
+        "memory": memory_report(gift_items, grad_bytes, state_gift, shared_work.numel()),
     }
     print(json.dumps(result), flush=True)
 
 
-def memory_report(gift_items, grad_bytes, state_gift):
+def memory_report(gift_items, grad_bytes, state_gift, work_bytes):
     """Memory of the geometry-aware layers beside the gradient buffer: as the
     pages count it ("GIFT 阅读笔记", 实验结果 / 内存开销: the rank-32 factor and
     the error-feedback buffer of the selected layers), and this library's
-    whole layer state (which keeps the d x d statistics and their window
-    accumulator for the subspace iteration)."""
+    whole layer state (the committed d x d statistics the subspace iteration
+    reads, the packed factor, the exchange words; the layers keep no window
+    sum: each window is accumulated in the one workspace they share)."""
     factor = sum(W0.shape[1] * 32 * 4 + 68 * 4 for _, W0, *_ in gift_items)   # U_k and the coefficients
     ef = sum(4 * W0.numel() for _, W0, *_ in gift_items)                      # fp32 residual per layer
     return {"grad_bytes": int(grad_bytes),
             "pages_terms": {"factor_bytes": int(factor), "error_feedback_bytes": int(ef),
                             "over_grad": round((factor + ef) / grad_bytes, 4)},
-            "library_state_bytes": int(state_gift), "library_state_over_grad": round(state_gift / grad_bytes, 4)}
+            "library_state_bytes": int(state_gift), "library_state_over_grad": round(state_gift / grad_bytes, 4),
+            "shared_workspace_bytes": int(work_bytes)}
 
 
 def bench_stress(args, torch, fw, synth, dev):

@@ -30,6 +30,7 @@ E4M3, E5M2, E2M1 = 0, 1, 2
 SCALE_TENSOR, SCALE_BLOCK128, SCALE_BLOCK16, SCALE_BLOCK512 = 0, 1, 2, 3
 BF16, FP32 = 0, 1
 SIDE_A, SIDE_G = 0, 1
+LAYER_TRANSIENT_STATS = 1   # statistics windows committed in one call, S in the workspace
 FLAG_NONFINITE, FLAG_SPIN_TIMEOUT = 1, 2
 TRANSFORMS = {"euclid": EUCLID, "diag": DIAG, "lowrank": LOWRANK, "chol": CHOL_INPUT, "twosided": CHOL_TWOSIDED}
 FORMATS = {"e4m3": E4M3, "e5m2": E5M2}
@@ -61,7 +62,7 @@ class GroupItem(ctypes.Structure):
 class LayerDesc(ctypes.Structure):
     _fields_ = [("d_out", ctypes.c_int32), ("d_in", ctypes.c_int32), ("transform", ctypes.c_int32),
                 ("rank", ctypes.c_int32), ("oversample", ctypes.c_int32), ("power_iters", ctypes.c_int32),
-                ("ema_decay", ctypes.c_float), ("damping_rel", ctypes.c_float)]
+                ("ema_decay", ctypes.c_float), ("damping_rel", ctypes.c_float), ("flags", ctypes.c_int32)]
 
 
 _vp, _sz, _i32, _i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
@@ -83,7 +84,7 @@ _sig("gift_layer_set_counters", _i32, _vp, _P(_i64))
 _sig("gift_layer_flags", _i32, _vp, _vp, _P(ctypes.c_uint32))
 _sig("gift_layer_buffers", _i32, _vp, *[_P(_vp)] * 8)
 _sig("gift_layer_mark_ready", _i32, _vp, _vp)
-_sig("gift_accumulate_stats", _i32, _vp, _i32, _vp, _i32, _i64, _i64, _i32, _vp)
+_sig("gift_accumulate_stats", _i32, _vp, _i32, _vp, _i32, _i64, _i64, _i32, _vp, _sz, _vp)
 _sig("gift_commit_stats", _i32, _vp, _i32, _vp)
 _sig("gift_refresh_factors", _i32, _vp, _vp, _vp, _sz, _vp)
 _sig("gift_encode", _i32, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp)
@@ -172,9 +173,10 @@ class Layer:
 
     def __init__(self, d_out: int, d_in: int, transform="lowrank", rank: int = 32, oversample: int = 16,
                  power_iters: int = 4, ema_decay: float = 0.0, damping_rel: float = 1e-3, device="cuda",
-                 stream=None, workspace=None):
+                 stream=None, workspace=None, transient_stats: bool = False):
         tr = TRANSFORMS[transform] if isinstance(transform, str) else int(transform)
-        self.desc = LayerDesc(d_out, d_in, tr, rank, oversample, power_iters, ema_decay, damping_rel)
+        self.desc = LayerDesc(d_out, d_in, tr, rank, oversample, power_iters, ema_decay, damping_rel,
+                              LAYER_TRANSIENT_STATS if transient_stats else 0)
         sb, wb = _sz(), _sz()
         _check(_lib.gift_layer_state_bytes(ctypes.byref(self.desc), ctypes.byref(sb), ctypes.byref(wb)),
                "gift_layer_state_bytes")
@@ -255,7 +257,7 @@ class Layer:
         if x.dtype not in (torch.bfloat16, torch.float32) or x.dim() != 2 or x.stride(1) != 1:
             raise ValueError("x must be a row-major [T][n] bf16 or fp32 tensor")
         _check(_lib.gift_accumulate_stats(self._h, side, _ptr(x), dtype, x.shape[0], x.stride(0), int(commit),
-                                          _stream(stream)), "gift_accumulate_stats")
+                                          _ptr(self.work), self.work_bytes, _stream(stream)), "gift_accumulate_stats")
 
     def commit_stats(self, side: int = SIDE_A, stream=None):
         _check(_lib.gift_commit_stats(self._h, side, _stream(stream)), "gift_commit_stats")

@@ -75,6 +75,7 @@ bool desc_ok(const gift_layer_desc* d) {
   if (d->transform < GIFT_EUCLID || d->transform > GIFT_CHOL_TWOSIDED) return false;
   if (!(d->ema_decay >= 0.0f && d->ema_decay < 1.0f)) return false;
   if (!(d->damping_rel >= 0.0f) || !std::isfinite(d->damping_rel)) return false;
+  if (d->flags & ~(int32_t)GIFT_LAYER_TRANSIENT_STATS) return false;   // unknown flag bits
   if (d->transform == GIFT_LOWRANK) {
     if (d->rank < 1 || d->rank > 32 || d->rank > d->d_in) return false;
     if (d->oversample < 0 || d->power_iters < 0 || d->power_iters > 64) return false;
@@ -234,14 +235,15 @@ StateLayout state_layout(const gift_layer_desc& g) {
   const size_t d = (size_t)g.d_in, m = (size_t)g.d_out;
   const bool stats_a = g.transform != GIFT_EUCLID;
   const bool stats_g = g.transform == GIFT_CHOL_TWOSIDED;
+  const bool keep_s = (g.flags & GIFT_LAYER_TRANSIENT_STATS) == 0;   // window sums in the state
   s.flags = take(256);
   if (stats_a) {
-    s.S_A = take(d * d * 4);
+    if (keep_s) s.S_A = take(d * d * 4);
     s.A = take(d * d * 4);
     s.ssync = take(kStatsMaxGroups * 4);   // statistics: one grow-only flag per workgroup
   }
   if (stats_g) {
-    s.S_G = take(m * m * 4);
+    if (keep_s) s.S_G = take(m * m * 4);
     s.G = take(m * m * 4);
   }
   if (g.transform == GIFT_LOWRANK) {
@@ -300,6 +302,11 @@ WorkLayout work_layout(const gift_layer_desc& g) {
     w.chol2 = take(n * n * 8 + 256);   // + the damping scalar
   }
   w.total = std::max<size_t>(off, 256);
+  if ((g.flags & GIFT_LAYER_TRANSIENT_STATS) && g.transform != GIFT_EUCLID) {
+    const size_t n = g.transform == GIFT_CHOL_TWOSIDED ? std::max(d, m) : d;
+    w.stats = 0;
+    w.total = std::max(w.total, align256(n * n * 4));
+  }
   return w;
 }
 
@@ -441,16 +448,14 @@ gift_status gift_layer_mark_ready(gift_layer_t L, gift_stream_t stream) {
 // Statistics
 // ---------------------------------------------------------------------------
 
-gift_status gift_commit_stats(gift_layer_t L, int32_t side, gift_stream_t stream) {
-  if (!L || (side != GIFT_SIDE_A && side != GIFT_SIDE_G)) return GIFT_ERR_INVALID_ARG;
+// A (or G) from the window sum S (in the state or, for a transient-statistics
+// layer, in the workspace).
+static gift_status commit_window(gift_layer_t L, int32_t side, const float* S, gift_stream_t stream) {
   const gift_layer_desc& g = L->desc;
-  if (g.transform == GIFT_EUCLID) return GIFT_ERR_INVALID_ARG;
-  if (side == GIFT_SIDE_G && g.transform != GIFT_CHOL_TWOSIDED) return GIFT_ERR_INVALID_ARG;
   int64_t& tokens = L->counters[side];
   int64_t& commits = L->counters[2 + side];
   if (tokens <= 0) return GIFT_ERR_NOT_READY;
   const int n = side == GIFT_SIDE_A ? g.d_in : g.d_out;
-  float* S = reinterpret_cast<float*>(L->state + (side == GIFT_SIDE_A ? L->sl.S_A : L->sl.S_G));
   float* A = reinterpret_cast<float*>(L->state + (side == GIFT_SIDE_A ? L->sl.A : L->sl.G));
   GIFT_HIP(gift::launch_commit(S, A, n, 1.0 / (double)tokens, g.ema_decay, commits == 0 ? 1 : 0,
                                static_cast<hipStream_t>(stream)));
@@ -459,8 +464,18 @@ gift_status gift_commit_stats(gift_layer_t L, int32_t side, gift_stream_t stream
   return GIFT_OK;
 }
 
+gift_status gift_commit_stats(gift_layer_t L, int32_t side, gift_stream_t stream) {
+  if (!L || (side != GIFT_SIDE_A && side != GIFT_SIDE_G)) return GIFT_ERR_INVALID_ARG;
+  const gift_layer_desc& g = L->desc;
+  if (g.transform == GIFT_EUCLID) return GIFT_ERR_INVALID_ARG;
+  if (side == GIFT_SIDE_G && g.transform != GIFT_CHOL_TWOSIDED) return GIFT_ERR_INVALID_ARG;
+  if (g.flags & GIFT_LAYER_TRANSIENT_STATS) return GIFT_ERR_INVALID_ARG;   // commits inside accumulate
+  return commit_window(L, side, reinterpret_cast<const float*>(L->state + (side == GIFT_SIDE_A ? L->sl.S_A : L->sl.S_G)),
+                       stream);
+}
+
 gift_status gift_accumulate_stats(gift_layer_t L, int32_t side, const void* d_x, int32_t dtype, int64_t T,
-                                  int64_t ld, int32_t commit, gift_stream_t stream) {
+                                  int64_t ld, int32_t commit, void* d_work, size_t work_bytes, gift_stream_t stream) {
   if (!L || (side != GIFT_SIDE_A && side != GIFT_SIDE_G)) return GIFT_ERR_INVALID_ARG;
   const gift_layer_desc& g = L->desc;
   if (g.transform == GIFT_EUCLID) return GIFT_ERR_INVALID_ARG;
@@ -472,17 +487,28 @@ gift_status gift_accumulate_stats(gift_layer_t L, int32_t side, const void* d_x,
     if (!d_x || !aligned16(d_x) || ld < n) return GIFT_ERR_INVALID_ARG;
     if (ld % (dtype == GIFT_BF16 ? 8 : 4) != 0) return GIFT_ERR_INVALID_ARG;
   }
+  const bool transient = (g.flags & GIFT_LAYER_TRANSIENT_STATS) != 0;
+  const bool opens = L->counters[side] == 0;   // the first call of a window stores its sums
+  float* S;
+  if (transient) {
+    // one call per window: accumulate into the workspace and commit
+    if (!commit || !opens || T == 0) return GIFT_ERR_INVALID_ARG;
+    if (!d_work || (reinterpret_cast<uintptr_t>(d_work) & 255u)) return GIFT_ERR_INVALID_ARG;
+    if (work_bytes < L->wl.total) return GIFT_ERR_WORKSPACE;
+    S = reinterpret_cast<float*>(static_cast<char*>(d_work) + L->wl.stats);
+  } else {
+    S = reinterpret_cast<float*>(L->state + (side == GIFT_SIDE_A ? L->sl.S_A : L->sl.S_G));
+  }
   if (commit && L->counters[side] + T <= 0) return GIFT_ERR_NOT_READY;
-  float* S = reinterpret_cast<float*>(L->state + (side == GIFT_SIDE_A ? L->sl.S_A : L->sl.S_G));
   if (T > 0) {
     unsigned* ssync = reinterpret_cast<unsigned*>(L->state + L->sl.ssync);
     uint32_t* flags = reinterpret_cast<uint32_t*>(L->state + L->sl.flags);
     const unsigned epoch = (unsigned)(++L->counters[7]);
-    GIFT_HIP(gift::launch_stats(d_x, dtype, T, ld, n, S, ssync, epoch, flags, device_cus(),
+    GIFT_HIP(gift::launch_stats(d_x, dtype, T, ld, n, S, ssync, epoch, flags, device_cus(), opens,
                                 static_cast<hipStream_t>(stream)));
   }
   L->counters[side] += T;
-  if (commit) return gift_commit_stats(L, side, stream);
+  if (commit) return commit_window(L, side, S, stream);
   return GIFT_OK;
 }
 

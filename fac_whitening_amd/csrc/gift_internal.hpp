@@ -127,6 +127,9 @@ struct WorkLayout {
   size_t apart = 0;             // partials of A X: fp64 [splits][d][l] or fp32 [splits32][d][l]
   size_t chol = 0;              // fp64 [n][n] (Cholesky variants)
   size_t chol2 = 0;             // fp64 [n][n]
+  // statistics of a GIFT_LAYER_TRANSIENT_STATS layer: the window sum S,
+  // fp32 [n][n] (aliases the areas above: no other call runs meanwhile)
+  size_t stats = 0;
   size_t total = 0;
 };
 
@@ -202,12 +205,13 @@ hipError_t launch_diag_apply(const float* x, int64_t ldx, int m, int d, const fl
 // the workgroups sharing a tile add into S in a fixed order, handing over
 // through `sync` (grow-only, one word per workgroup) at `epoch`.
 constexpr int kStatsMaxGroups = 1024;
+// overwrite: the call opens a window, so its sums are stored, not added
 hipError_t launch_stats(const void* x, int dtype, int64_t T, int64_t ld, int n, float* S, unsigned* sync,
-                        unsigned epoch, uint32_t* flags, int cus, hipStream_t s);
+                        unsigned epoch, uint32_t* flags, int cus, bool overwrite, hipStream_t s);
 // Workgroups of the matrix-core statistics kernel the current device holds
 // at once (0: unknown).
 int stats_resident_groups();
-hipError_t launch_commit(float* S, float* A, int n, double inv_count, float beta, int first,
+hipError_t launch_commit(const float* S, float* A, int n, double inv_count, float beta, int first,
                          hipStream_t s);
 
 // Refresh (rank-k).

@@ -25,9 +25,11 @@ __device__ __forceinline__ void tri_tile(int idx, int& bi, int& bj) {
 // VALU tiling: 64 x 64 output tile per workgroup, 32 tokens per LDS stage,
 // 4 x 4 outputs per thread; fp32 sums over 256-token chunks folded into fp64
 // (keeps the relative error of A near the fp32 storage rounding).
+// overwrite: the first call of a window stores the sums instead of adding
+// them to S (which then needs no clearing between windows).
 template <typename TX>
 __global__ void __launch_bounds__(256) k_stats_valu(const TX* __restrict__ x, int64_t T, int64_t ld, int n,
-                                                    float* __restrict__ S) {
+                                                    float* __restrict__ S, int overwrite) {
   __shared__ float Ai[32][64 + 4];
   __shared__ float Aj[32][64 + 4];
   int bi, bj;
@@ -76,7 +78,8 @@ __global__ void __launch_bounds__(256) k_stats_valu(const TX* __restrict__ x, in
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       int j = bj * 64 + tx * 4 + q;
-      if (j < n) S[(int64_t)i * n + j] = (float)((double)S[(int64_t)i * n + j] + acc64[p][q]);
+      if (j < n)
+        S[(int64_t)i * n + j] = overwrite ? (float)acc64[p][q] : (float)((double)S[(int64_t)i * n + j] + acc64[p][q]);
     }
   }
 }
@@ -152,7 +155,7 @@ template <bool DIAG>
 __device__ __forceinline__ void stats_segment(const uint16_t* __restrict__ x, int64_t T, int64_t ld, int n,
                                               float* __restrict__ S, int bi, int bj, int s_a, int s_b, int nst,
                                               char* As, char* Bs, unsigned* __restrict__ sync, unsigned epoch,
-                                              uint32_t* __restrict__ flags) {
+                                              uint32_t* __restrict__ flags, bool overwrite) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -316,9 +319,12 @@ __device__ __forceinline__ void stats_segment(const uint16_t* __restrict__ x, in
     late = __builtin_amdgcn_readfirstlane(out) != 0;
     __syncthreads();
   }
-  // S += acc: register v of MFMA tile (mt, nt) is element
+  // S += acc (S = acc for the first writer of a tile when the call opens a
+  // window: the workgroup holding the tile's last stages, which adds first):
+  // register v of MFMA tile (mt, nt) is element
   // (8 (v / 4) + 4 (lane / 32) + v % 4, lane % 32) of the 32 x 32 tile
   const int lr = lane & 31, lh = lane >> 5;
+  const bool store_only = overwrite && s_b == nst;
   if (shared) {
     // device-coherent loads and stores (sc0 sc1), 64 loads in flight per
     // row block; elements outside the output go to an offset past the end
@@ -336,7 +342,7 @@ __device__ __forceinline__ void stats_segment(const uint16_t* __restrict__ x, in
           const int j = col0 + 128 * wn + 32 * nt + lr;
           const bool ok = i < n && j < n && (!DIAG || i >= j);
           off[nt][e] = ok ? (int)(uint32_t)(((int64_t)i * n + j) * 4) : (int)nbytes;
-          v[nt][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off[nt][e], 0, 17));
+          v[nt][e] = store_only ? 0.f : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off[nt][e], 0, 17));
         }
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
@@ -354,7 +360,8 @@ __device__ __forceinline__ void stats_segment(const uint16_t* __restrict__ x, in
         for (int e = 0; e < 16; ++e) {
           const int i = row0 + 128 * wm + 32 * mt + 8 * (e / 4) + 4 * lh + e % 4;
           const int j = col0 + 128 * wn + 32 * nt + lr;
-          if (i < n && j < n && (!DIAG || i >= j)) S[(int64_t)i * n + j] += acc[mt][nt][e];
+          if (i < n && j < n && (!DIAG || i >= j))
+            S[(int64_t)i * n + j] = store_only ? acc[mt][nt][e] : S[(int64_t)i * n + j] + acc[mt][nt][e];
         }
   }
   if (s_a > 0) {
@@ -375,7 +382,7 @@ __device__ __forceinline__ void stats_segment(const uint16_t* __restrict__ x, in
 // compute unit: the LDS stages fill it).
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 k_stats_mfma(const uint16_t* __restrict__ x, int64_t T, int64_t ld, int n, float* __restrict__ S, int ntiles,
-             unsigned* __restrict__ sync, unsigned epoch, uint32_t* __restrict__ flags) {
+             unsigned* __restrict__ sync, unsigned epoch, uint32_t* __restrict__ flags, int overwrite) {
   __shared__ __attribute__((aligned(16))) char As[kSStages * kSSide];
   __shared__ __attribute__((aligned(16))) char Bs[kSStages * kSSide];
   const int nst = (int)cdiv(T, kSK);
@@ -385,9 +392,9 @@ k_stats_mfma(const uint16_t* __restrict__ x, int64_t T, int64_t ld, int n, float
     int bi, bj;
     tri_tile(rd * G + gid, bi, bj);
     if (bi == bj)
-      stats_segment<true>(x, T, ld, n, S, bi, bj, 0, nst, nst, As, Bs, sync, epoch, flags);
+      stats_segment<true>(x, T, ld, n, S, bi, bj, 0, nst, nst, As, Bs, sync, epoch, flags, overwrite != 0);
     else
-      stats_segment<false>(x, T, ld, n, S, bi, bj, 0, nst, nst, As, Bs, sync, epoch, flags);
+      stats_segment<false>(x, T, ld, n, S, bi, bj, 0, nst, nst, As, Bs, sync, epoch, flags, overwrite != 0);
   }
   const int first = rounds * G;
   const int64_t U = (int64_t)(ntiles - first) * nst;
@@ -399,9 +406,9 @@ k_stats_mfma(const uint16_t* __restrict__ x, int64_t T, int64_t ld, int n, float
     int bi, bj;
     tri_tile(tile, bi, bj);
     if (bi == bj)
-      stats_segment<true>(x, T, ld, n, S, bi, bj, s_a, s_b, nst, As, Bs, sync, epoch, flags);
+      stats_segment<true>(x, T, ld, n, S, bi, bj, s_a, s_b, nst, As, Bs, sync, epoch, flags, overwrite != 0);
     else
-      stats_segment<false>(x, T, ld, n, S, bi, bj, s_a, s_b, nst, As, Bs, sync, epoch, flags);
+      stats_segment<false>(x, T, ld, n, S, bi, bj, s_a, s_b, nst, As, Bs, sync, epoch, flags, overwrite != 0);
     u += s_b - s_a;
   }
 }
@@ -422,7 +429,7 @@ int stats_resident_groups() {
 }
 
 hipError_t launch_stats(const void* x, int dtype, int64_t T, int64_t ld, int n, float* S, unsigned* sync,
-                        unsigned epoch, uint32_t* flags, int cus, hipStream_t s) {
+                        unsigned epoch, uint32_t* flags, int cus, bool overwrite, hipStream_t s) {
   if (T == 0 || n == 0) return hipSuccess;
   int nb = (int)cdiv(n, 64);
   unsigned tiles = (unsigned)(nb * (nb + 1) / 2);
@@ -441,19 +448,20 @@ hipError_t launch_stats(const void* x, int dtype, int64_t T, int64_t ld, int n, 
     const hipError_t e = order_persistent(s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_stats_mfma, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const uint16_t*>(x), T,
-                       ld, n, S, ntiles, sync, epoch, flags);
+                       ld, n, S, ntiles, sync, epoch, flags, overwrite ? 1 : 0);
   } else if (dtype == GIFT_BF16)
     hipLaunchKernelGGL(k_stats_valu<__hip_bfloat16>, dim3(tiles), dim3(256), 0, s,
-                       static_cast<const __hip_bfloat16*>(x), T, ld, n, S);
+                       static_cast<const __hip_bfloat16*>(x), T, ld, n, S, overwrite ? 1 : 0);
   else
     hipLaunchKernelGGL(k_stats_valu<float>, dim3(tiles), dim3(256), 0, s, static_cast<const float*>(x), T, ld,
-                       n, S);
+                       n, S, overwrite ? 1 : 0);
   return hipGetLastError();
 }
 
 // A = first ? S/count : beta A + (1 - beta) S/count  (fp64 arithmetic, fp32
-// storage), for the lower-triangle tile (bi, bj) and its mirror; S <- 0.
-__global__ void __launch_bounds__(256) k_commit(float* __restrict__ S, float* __restrict__ A, int n,
+// storage), for the lower-triangle tile (bi, bj) and its mirror.  S is left
+// as it is: the next window's first call overwrites it.
+__global__ void __launch_bounds__(256) k_commit(const float* __restrict__ S, float* __restrict__ A, int n,
                                                 double inv_count, double beta, int first) {
   __shared__ float tile[64][65];
   int bi, bj;
@@ -471,7 +479,6 @@ __global__ void __launch_bounds__(256) k_commit(float* __restrict__ S, float* __
         v = (float)a;
         A[o] = v;
       }
-      S[o] = 0.f;   // the upper half of diagonal tiles is accumulated but unused
     }
     tile[r][c] = v;
   }
@@ -484,7 +491,7 @@ __global__ void __launch_bounds__(256) k_commit(float* __restrict__ S, float* __
   }
 }
 
-hipError_t launch_commit(float* S, float* A, int n, double inv_count, float beta, int first, hipStream_t s) {
+hipError_t launch_commit(const float* S, float* A, int n, double inv_count, float beta, int first, hipStream_t s) {
   if (n == 0) return hipSuccess;
   int nb = (int)cdiv(n, 64);
   unsigned tiles = (unsigned)(nb * (nb + 1) / 2);

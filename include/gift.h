@@ -88,13 +88,25 @@ typedef struct gift_layer_desc {
   int32_t power_iters; /* q: re-orthonormalised products after Y = A Omega */
   float ema_decay;     /* beta in [0, 1): A <- beta A + (1 - beta) A_batch  */
   float damping_rel;   /* lam = damping_rel * tr(A) / d (also for G)       */
+  int32_t flags;       /* GIFT_LAYER_* bits, 0 for none                    */
 } gift_layer_desc;
+
+/* Layer flags.
+ * GIFT_LAYER_TRANSIENT_STATS: every statistics window is accumulated and
+ *   committed in one gift_accumulate_stats call (commit nonzero, nothing
+ *   pending).  The window's running sum S then lives in the caller's
+ *   workspace for the duration of that call, and the state holds only the
+ *   committed A (and G): d_in^2 (+ d_out^2) fp32 less per layer, which is
+ *   what lets many layers share one workspace.  Any other statistics call
+ *   on such a layer returns GIFT_ERR_INVALID_ARG. */
+enum { GIFT_LAYER_TRANSIENT_STATS = 1 };
 
 /* ---------------------------------------------------------------------------
  * Layer state.
  * gift_layer_state_bytes: bytes of the caller-owned device state buffer for
- * this layer (statistics A [and G], their EMA, the factor, flags) and the
- * largest workspace any call on this layer needs.  Both are multiples of 256.
+ * this layer (the window sums S_A [and S_G] unless GIFT_LAYER_TRANSIENT_STATS,
+ * the committed A [and G], the factor, flags) and the largest workspace any
+ * call on this layer needs.  Both are multiples of 256.
  * gift_layer_create: binds `d_state` (>= state_bytes, 256-byte aligned) to a
  * new host handle; enqueues the zeroing of the state on `stream`.
  * The state is plain device memory: copying it (and the handle's host
@@ -139,15 +151,23 @@ gift_status gift_layer_mark_ready(gift_layer_t layer, gift_stream_t stream);
  *
  * gift_accumulate_stats: S_side += x^T x for x = d_x [T][ld] (dtype bf16 or
  * fp32, the first n columns used, n = d_in for side A, d_out for side G),
- * and adds T to the side's pending-token count.  If `commit` is nonzero the
- * window is then committed in the same launch (see gift_commit_stats).
- * T may be 0 (no-op unless commit).
+ * and adds T to the side's pending-token count; the first call of a window
+ * (nothing pending) stores x^T x instead.  If `commit` is nonzero the
+ * window is then committed in the same call (see gift_commit_stats).
+ * T may be 0 (no-op unless commit).  d_work / work_bytes: the layer's
+ * workspace (>= its workspace_bytes); read only for layers created with
+ * GIFT_LAYER_TRANSIENT_STATS, where S lives there for the call (commit must
+ * be nonzero, T > 0 and nothing pending), otherwise it may be NULL.
  * gift_commit_stats: A_batch = S / count; A = A_batch on the first commit,
- * else A = beta A + (1 - beta) A_batch; S = 0, count = 0.  GIFT_ERR_NOT_READY
- * if no tokens are pending.
+ * else A = beta A + (1 - beta) A_batch; count = 0 (S keeps its contents
+ * until the next window's first call replaces them).  GIFT_ERR_NOT_READY
+ * if no tokens are pending; GIFT_ERR_INVALID_ARG on a
+ * GIFT_LAYER_TRANSIENT_STATS layer (its windows commit inside
+ * gift_accumulate_stats).
  * ------------------------------------------------------------------------- */
 gift_status gift_accumulate_stats(gift_layer_t layer, int32_t side, const void* d_x, int32_t dtype,
-                                  int64_t T, int64_t ld, int32_t commit, gift_stream_t stream);
+                                  int64_t T, int64_t ld, int32_t commit, void* d_work, size_t work_bytes,
+                                  gift_stream_t stream);
 gift_status gift_commit_stats(gift_layer_t layer, int32_t side, gift_stream_t stream);
 
 /* ---------------------------------------------------------------------------

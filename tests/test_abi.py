@@ -46,6 +46,18 @@ def test_host_side_checks_without_gpu():
                 fw.LayerDesc(1536, 6144, fw.LOWRANK, 32, 16, 4, 1.0, 1e-3),     # beta = 1
                 fw.LayerDesc(1536, 6144, fw.LOWRANK, 32, 16, 4, 0.0, -1.0)]:    # damping < 0
         assert lib.gift_layer_state_bytes(ctypes.byref(bad), ctypes.byref(sb), ctypes.byref(wb)) == 1
+    # transient statistics: the window sums leave the state (d^2 fp32, and
+    # m^2 more for the two-sided variant) and the workspace holds one of them
+    for tr, n_s in ((fw.LOWRANK, 6144 * 6144 * 4), (fw.CHOL_TWOSIDED, (6144 * 6144 + 1536 * 1536) * 4)):
+        base = fw.LayerDesc(1536, 6144, tr, 32, 16, 4, 0.0, 1e-3)
+        tra = fw.LayerDesc(1536, 6144, tr, 32, 16, 4, 0.0, 1e-3, fw.LAYER_TRANSIENT_STATS)
+        sb2, wb2 = ctypes.c_size_t(), ctypes.c_size_t()
+        assert lib.gift_layer_state_bytes(ctypes.byref(base), ctypes.byref(sb), ctypes.byref(wb)) == 0
+        assert lib.gift_layer_state_bytes(ctypes.byref(tra), ctypes.byref(sb2), ctypes.byref(wb2)) == 0
+        assert sb.value - sb2.value == n_s
+        assert wb2.value >= max(wb.value, 6144 * 6144 * 4)
+    unknown = fw.LayerDesc(1536, 6144, fw.LOWRANK, 32, 16, 4, 0.0, 1e-3, 2)   # unknown flag bit
+    assert lib.gift_layer_state_bytes(ctypes.byref(unknown), ctypes.byref(sb), ctypes.byref(wb)) == 1
     # payload = 1 byte per element + one fp32 scale per tile
     assert fw.payload_bytes(1536, 6144, fw.SCALE_TENSOR) == 1536 * 6144 + 4
     assert fw.payload_bytes(1536, 6144, fw.SCALE_BLOCK128) == 1536 * 6144 + 4 * 12 * 48
