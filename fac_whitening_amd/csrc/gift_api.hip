@@ -250,8 +250,8 @@ StateLayout state_layout(const gift_layer_desc& g) {
     s.U = take(d * 32 * 4);
     s.coef = take(68 * 4);
     const size_t ncb = (size_t)cdiv((int64_t)d, 32);
-    s.ub = take(ncb * 6 * 1024);
-    s.ua = take(ncb * 6 * 1024);
+    s.ub = take(ncb * kUPackBytes);
+    s.ua = take(ncb * kUPackBytes);
     // tagged projection partials [tiles][48 x 32], then the row-group sums
     // [row groups][48 x 32]
     s.xpub = take((size_t)fused_groups(g) * (fused_cg(g) + 1) * kFusedTR * 32 * 8);

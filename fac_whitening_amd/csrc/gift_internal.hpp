@@ -28,6 +28,9 @@ struct StateLayout {
 
 // Fused rank-k kernel geometry (48 x 768 tiles, 8 waves).
 constexpr int kFusedTR = 48, kFusedTC = 768;
+// Packed U_k operands per 32-column block and operand order: 2 groups x 2
+// f16 pieces x 64 lanes x 16 bytes.
+constexpr int kUPackBytes = 2 * 2 * 64 * 16;
 // Per-tensor amax words of the fused encode: kAmaxCopies copies of the
 // [tiles] array, each on its own 4 KiB page(s), so that no single memory
 // channel serves every workgroup's reads.

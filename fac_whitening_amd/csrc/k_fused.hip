@@ -13,13 +13,18 @@
 //    packed U operand a wave loads serves three sub-tiles.
 //  * In a sub-tile, lane l holds row l % 16 and columns 4 g .. 4 g + 3 and
 //    16 + 4 g .. 16 + 4 g + 3 (g = l / 16).  These eight values are the A
-//    operand of the projection MFMA (16x16x32 bf16, with U_k's rows permuted
-//    the same way) and, unchanged, the accumulator (C layout) of the
+//    operand of the projection MFMA (16x16x32 f16, with U_k's rows permuted
+//    the same way) and have the layout of the result (D layout) of the
 //    reconstruction MFMA that computes the transposed sub-tile.
-//  * fp32 accuracy from bf16 MFMA: each operand is split into three bf16
-//    pieces (x = h + m + l, each the RNE bf16 of the previous residual) and
-//    the six products h*h, h*m, m*h, h*l, l*h, m*m are accumulated in fp32;
-//    what is dropped is below 2^-26 of each product.
+//  * Near-fp32 products from f16 MFMA: every row of an operand is scaled
+//    by a power of two that puts its largest magnitude in [2^14, 2^15)
+//    (U_k, whose entries are at most 1, by 2^14), split into two f16 pieces
+//    (x = h + l, h the RNE f16 of x, l that of the residual), and the three
+//    products l*h, h*l, h*h are accumulated in fp32; the sums are scaled
+//    back exactly (ldexp).  Piece rounding and the dropped l*l term stay
+//    below about 3 * 2^-22 of each product; entries far below their row's
+//    largest lose relative precision in the f16 subnormal range, but never
+//    more than about 2^-40 of that largest entry.
 //  * P needs whole rows: the workgroups of one row group (same 48 rows)
 //    publish their partial P as epoch-tagged words in the layer state; each
 //    sums one slice of the partials in column-group order and publishes the
@@ -41,7 +46,7 @@
 
 namespace gift {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSpinLimit = 1 << 20;
@@ -72,15 +77,25 @@ __device__ __forceinline__ unsigned long long wait_tag(const unsigned long long*
 
 __device__ __forceinline__ uint32_t absbits_f(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
 
-__device__ __forceinline__ void split3(float x, __bf16& h, __bf16& m, __bf16& l) {
-  h = (__bf16)x;
-  const float r1 = x - (float)h;
-  m = (__bf16)r1;
-  const float r2 = r1 - (float)m;
-  l = (__bf16)r2;
+// x = h + l + (a residual below 2^-22 |x| in the f16 normal range): h the
+// RNE f16 of x, l that of x - h (exact in fp32).
+__device__ __forceinline__ void split2(float x, _Float16& h, _Float16& l) {
+  h = (_Float16)x;
+  l = (_Float16)(x - (float)h);
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+// Scale exponent of a row whose largest magnitude is mx: 2^e mx lies in
+// [2^14, 2^15) (e clamped to [-126, 127]; 0 for a zero or non-finite mx,
+// whose row then carries its zeros, Inf or NaN through unchanged).
+__device__ __forceinline__ int row_exp(float mx) {
+  const uint32_t b = __float_as_uint(mx);
+  if (mx == 0.0f || (b & 0x7F800000u) == 0x7F800000u) return 0;
+  const int ex = (int)((b >> 23) & 0xFF) - 127;   // floor(log2 mx); -127 for subnormal mx
+  const int e = 14 - ex;
+  return e < -126 ? -126 : (e > 127 ? 127 : e);
+}
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+constexpr int kUExp = 14;   // U_k's pieces are of 2^14 U_k
 
 // Buffer resources: loads outside [0, bytes) return 0 and stores there are
 // dropped, so edge tiles need no branches around their memory operations
@@ -103,6 +118,7 @@ __device__ __forceinline__ int perm_col(int g, int j) { return j < 4 ? 4 * g + j
 //       slot j -> U[32 cb + perm_col(g, j)][n + 16 half]
 //   ua[cb][grp][piece][lane]: reconstruction A operand:
 //       slot j -> U[32 cb + 16 grp + n][8 g + j]
+// Pieces: the two f16 pieces of 2^14 U (split2).
 // ---------------------------------------------------------------------------
 __global__ void k_pack_u(const float* __restrict__ U, int d, uint4* __restrict__ ub, uint4* __restrict__ ua) {
   const int ncb = (int)cdiv(d, 32);
@@ -110,7 +126,7 @@ __global__ void k_pack_u(const float* __restrict__ U, int d, uint4* __restrict__
   if (t >= ncb * 2 * 2 * 64) return;
   const int lane = t & 63, half = (t >> 6) & 1, which = (t >> 7) & 1, cb = t >> 8;
   const int n = lane & 15, g = lane >> 4;
-  __bf16 h[8], m[8], l[8];
+  _Float16 h[8], l[8];
   for (int j = 0; j < 8; ++j) {
     int col, k;
     if (which == 0) {
@@ -121,12 +137,11 @@ __global__ void k_pack_u(const float* __restrict__ U, int d, uint4* __restrict__
       k = 8 * g + j;
     }
     const float v = col < d ? U[(int64_t)col * 32 + k] : 0.0f;
-    split3(v, h[j], m[j], l[j]);
+    split2(v * pow2f(kUExp), h[j], l[j]);
   }
-  uint4* dst = (which == 0 ? ub : ua) + ((int64_t)(cb * 2 + half) * 3) * 64 + lane;
+  uint4* dst = (which == 0 ? ub : ua) + ((int64_t)(cb * 2 + half) * 2) * 64 + lane;
   dst[0] = __builtin_bit_cast(uint4, h);
-  dst[64] = __builtin_bit_cast(uint4, m);
-  dst[128] = __builtin_bit_cast(uint4, l);
+  dst[64] = __builtin_bit_cast(uint4, l);
 }
 
 hipError_t launch_pack_u(const float* U, int d, void* ub, void* ua, hipStream_t s) {
@@ -232,20 +247,20 @@ __device__ __forceinline__ void accum_codes(float (*acc)[16], float* acct, const
 // [column block q][half or group][piece], read through a buffer resource
 // so that blocks past the last column read zeros instead of memory.
 struct UOps {
-  bf16x8 u[3][2][3];
+  half8 u[3][2][2];
 };
 
 __device__ __forceinline__ void load_uops(const uint4* packed, int d, int cbg0, UOps& o) {
-  const auto rs = make_rsrc(packed, cdiv(d, 32) * 6 * 1024);
+  const auto rs = make_rsrc(packed, cdiv(d, 32) * kUPackBytes);
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int q = 0; q < 3; ++q)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int p = 0; p < 3; ++p) {
-        const int off = ((((cbg0 + 8 * q) * 2 + h) * 3 + p) * 64 + lane) * 16;
-        o.u[q][h][p] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+      for (int p = 0; p < 2; ++p) {
+        const int off = ((((cbg0 + 8 * q) * 2 + h) * 2 + p) * 64 + lane) * 16;
+        o.u[q][h][p] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
       }
 }
 
@@ -324,39 +339,56 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
 #pragma unroll
   for (int q = 0; q < 3; ++q) live[q] = col0 + (wave + 8 * q) * 32 < d;
   UOps uo;
-  // projection P = X U of row block rb (this wave's partial, 16 rows x 32)
+  // projection P = X U of row block rb (this wave's partial, 16 rows x 32),
+  // in units of 2^(xe[rb] + 14) for row 16 rb + (lane % 16): the row's scale
+  // exponent over this wave's three column blocks (the four lanes of a row
+  // agree through the two shuffles), U_k's pieces carrying 2^14
   floatx4 pacc[3][2];
+  int xe[3];
 #pragma unroll
   for (int rb = 0; rb < 3; ++rb)
 #pragma unroll
     for (int h = 0; h < 2; ++h) pacc[rb][h] = (floatx4){0.f, 0.f, 0.f, 0.f};
   auto project_rb = [&](int rb) {
+    float mx = 0.f;
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+      if (live[q]) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(x[q * 3 + rb][j]));
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    xe[rb] = row_exp(mx);
+    const float sc = pow2f(xe[rb]);
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
       if (!live[q]) continue;
       const int i = q * 3 + rb;
-      bf16x8 xh, xm, xl;
+      half8 xh, xl;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        __bf16 h, mm, l;
-        split3(x[i][j], h, mm, l);
+        _Float16 h, l;
+        split2(x[i][j] * sc, h, l);
         xh[j] = h;
-        xm[j] = mm;
         xl[j] = l;
       }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const bf16x8* u = uo.u[q][h];
+        const half8* u = uo.u[q][h];
         floatx4 c = pacc[rb][h];
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xm, u[1], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, u[2], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, u[0], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, u[1], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xm, u[0], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, u[0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl, u[0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, u[1], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, u[0], c, 0, 0, 0);
         pacc[rb][h] = c;
       }
     }
+  };
+  // slot e of pacc[rb][h] is row 4 (lane / 16) + e of the block: its scale
+  // exponent is that of the lane holding the row
+  auto unscaled = [&](int rb, int h, int e) {
+    const int er = __shfl(xe[rb], 4 * lg + e, 64);
+    return __builtin_ldexpf(pacc[rb][h][e], -(er + kUExp));
   };
 
   // ---- stream the tile in: the rank-k encode straight into the sub-tile
@@ -496,7 +528,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
-              for (int e = 0; e < 4; ++e) cp[b][wave][4 * lg + e][lr + 16 * h] = pacc[b][h][e];
+              for (int e = 0; e < 4; ++e) cp[b][wave][4 * lg + e][lr + 16 * h] = unscaled(b, h, e);
         }
       }
     }
@@ -619,7 +651,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) cp[rb][wave][4 * lg + e][lr + 16 * h] = pacc[rb][h][e];
+      for (int e = 0; e < 4; ++e) cp[rb][wave][4 * lg + e][lr + 16 * h] = unscaled(rb, h, e);
   __syncthreads();
   // sum the 8 waves (fixed order) and publish this tile's partial: word
   // e = 32 row + k of the tile, one atomic exchange each (it takes effect at
@@ -710,15 +742,25 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
   {
     const bool bad = s_bad != 0;   // uniform: every wait of the exchange is before the barrier
     const float alpha = a.coef[64 + (enc ? 0 : 1)];
-    bf16x8 ph[3], pm[3], pl[3];
+    // P c of row 16 rb + (lane % 16), 8 rank entries per lane: scaled by the
+    // row's exponent (over its 32 entries, which the four lanes of the row
+    // hold) and split into two f16 pieces
+    half8 ph[3], pl[3];
+    int pe[3];
 #pragma unroll
     for (int rb = 0; rb < 3; ++rb) {
+      float mx = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(pf[rb * 16 + lr][8 * lg + j]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      pe[rb] = row_exp(mx);
+      const float sc = pow2f(pe[rb]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        __bf16 h, mm, l;
-        split3(pf[rb * 16 + lr][8 * lg + j], h, mm, l);
+        _Float16 h, l;
+        split2(pf[rb * 16 + lr][8 * lg + j] * sc, h, l);
         ph[rb][j] = h;
-        pm[rb][j] = mm;
         pl[rb][j] = l;
       }
     }
@@ -727,20 +769,18 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
       if (!live[q]) continue;
 #pragma unroll
       for (int grp = 0; grp < 2; ++grp) {
-        const bf16x8 uh = uo.u[q][grp][0], um = uo.u[q][grp][1], ul = uo.u[q][grp][2];
+        const half8 uh = uo.u[q][grp][0], ul = uo.u[q][grp][1];
 #pragma unroll
         for (int rb = 0; rb < 3; ++rb) {
           const int i = q * 3 + rb;
-          floatx4 c = (floatx4){alpha * x[i][4 * grp], alpha * x[i][4 * grp + 1], alpha * x[i][4 * grp + 2],
-                                alpha * x[i][4 * grp + 3]};
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(um, pm[rb], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uh, pl[rb], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ul, ph[rb], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uh, pm[rb], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(um, ph[rb], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uh, ph[rb], c, 0, 0, 0);
+          floatx4 c = (floatx4){0.f, 0.f, 0.f, 0.f};
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ul, ph[rb], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(uh, pl[rb], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(uh, ph[rb], c, 0, 0, 0);
+          // slot e is the lane's own row: alpha x + the product scaled back
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x[i][4 * grp + e] = c[e];
+          for (int e = 0; e < 4; ++e)
+            x[i][4 * grp + e] = __builtin_fmaf(alpha, x[i][4 * grp + e], __builtin_ldexpf(c[e], -(pe[rb] + kUExp)));
         }
       }
       if constexpr (!ENC) {
