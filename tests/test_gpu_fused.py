@@ -170,3 +170,30 @@ def test_fused_decode_compiled_replica_counts(fw, R, scaling, shape):
     err = rel_fro(out.cpu().numpy(), ref)
     assert err <= 1e-5, f"decode rel err {err:.3e}"
     assert L.flags() == 0
+
+
+@pytest.mark.parametrize("k", [-80, -40, 40, 90])
+def test_fused_scale_invariance_by_powers_of_two(fw, k):
+    """Every scale inside the fused kernels is a power of two (the row scales
+    of the two-piece f16 products, 2^14 on U_k, the FP8 scale pair), so
+    W 2^k must give the same codes with every scale times 2^k, and the
+    decode of those payloads exactly 2^k times the decode at k = 0, down to
+    gradients near 1e-30 and up to 1e24."""
+    m, d, R = 200, 1544, 3
+    print(f"[fused scale invariance 2^{k}]", flush=True)
+    Ws, fac = _case(m, d, R, 11)
+    L = _layer_with_factor(fw, m, d, fac)
+    fw.set_fused(True)
+    for scaling in (fw.SCALE_TENSOR, fw.SCALE_BLOCK128):
+        base_c, base_s, sc_c, sc_s = [], [], [], []
+        for W in Ws:
+            Wt = torch.from_numpy(W).to(DEV)
+            c0, s0 = L.encode(Wt, fw.E4M3, scaling)
+            c1, s1 = L.encode(Wt * 2.0 ** k, fw.E4M3, scaling)
+            assert torch.equal(c0, c1)
+            assert torch.equal(s1, s0 * 2.0 ** k)
+            base_c.append(c0); base_s.append(s0); sc_c.append(c1); sc_s.append(s1)
+        o0 = L.decode_reduce(torch.stack(base_c), torch.stack(base_s), fw.E4M3, scaling)
+        o1 = L.decode_reduce(torch.stack(sc_c), torch.stack(sc_s), fw.E4M3, scaling)
+        assert torch.equal(o1, o0 * 2.0 ** k)
+    assert L.flags() == 0
