@@ -170,7 +170,7 @@ hipError_t launch_dequant_sum_fp4(const uint8_t* codes, int64_t code_stride, con
 // Flat gradient buckets (Euclidean codec over many tensors, one launch per
 // phase).  Prefix tables in device memory, n + 1 entries each.
 struct BucketTable {
-  const int64_t* chunk_start;   // first 2048-element chunk of each tensor
+  const int64_t* chunk_start;   // first 4096-element chunk of each tensor
   const int64_t* elem_off;      // first element of each tensor in the flat buffer
   const int64_t* scale_off;     // first scale of each tensor
   int n;
