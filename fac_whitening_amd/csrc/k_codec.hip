@@ -247,12 +247,70 @@ __global__ void __launch_bounds__(256) k_dequant_sum(const uint8_t* __restrict__
   }
 }
 
+// The same with a compile-time replica count RC: a 32-row band lies in one
+// 128-row block row, so each lane's scale of every replica is read once
+// per band (not once per row, behind that row's code loads), and the RC
+// code loads of a row are all in flight together.
+template <int FMT, int V, int RC>
+__global__ void __launch_bounds__(256) k_dequant_sum_rc(const uint8_t* __restrict__ codes, int64_t code_stride,
+                                                        const float* __restrict__ scales, int64_t scale_stride,
+                                                        int m, int d, int scaling, float* __restrict__ out,
+                                                        int64_t ldo, float invR) {
+  static_assert(kBlock % kDqRows == 0, "a band lies in one block row");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = blockIdx.x * (64 * V) + lane * V;
+  const int r0 = blockIdx.y * kDqRows;
+  const int r1 = min(m, r0 + kDqRows);
+  if (col >= d) return;   // d is a multiple of V: a lane's codes are all in range
+  const int ncb = (int)cdiv(d, kBlock);
+  const int slot = scaling == 0 ? 0 : (r0 / kBlock) * ncb + col / kBlock;
+  float sc[RC];
+#pragma unroll
+  for (int r = 0; r < RC; ++r) sc[r] = scales[(int64_t)r * scale_stride + slot];
+  for (int rr = r0 + wave; rr < r1; rr += 4) {
+    const uint8_t* cp = codes + (int64_t)rr * d + col;
+    CodeVec<V> c[RC];
+#pragma unroll
+    for (int r = 0; r < RC; ++r) c[r] = load_codes<V>(cp + (int64_t)r * code_stride);
+    float a[V];
+#pragma unroll
+    for (int k = 0; k < V / 4; ++k) {   // from replica 0's term (not +0), so a lone -0 stays -0
+      float v[4];
+      dec4_fp8<FMT>(c[0].w[k], v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[4 * k + e] = sc[0] * v[e];
+    }
+#pragma unroll
+    for (int r = 1; r < RC; ++r) acc_codes<FMT, V>(c[r], sc[r], a);
+    float* op = out + (int64_t)rr * ldo + col;
+#pragma unroll
+    for (int k = 0; k < V / 4; ++k)
+      *reinterpret_cast<float4*>(op + 4 * k) =
+          make_float4(a[4 * k] * invR, a[4 * k + 1] * invR, a[4 * k + 2] * invR, a[4 * k + 3] * invR);
+  }
+}
+
 template <int FMT, int V>
 static void launch_dq(const uint8_t* codes, int64_t code_stride, const float* scales, int64_t scale_stride, int R,
                       int m, int d, int scaling, float* out, int64_t ldo, float invR, hipStream_t s) {
   dim3 grid((unsigned)cdiv(d, 64 * V), (unsigned)cdiv(m, kDqRows));
-  hipLaunchKernelGGL((k_dequant_sum<FMT, V>), grid, dim3(256), 0, s, codes, code_stride, scales, scale_stride, R,
-                     m, d, scaling, out, ldo, invR);
+  switch (R) {
+    case 4:
+      hipLaunchKernelGGL((k_dequant_sum_rc<FMT, V, 4>), grid, dim3(256), 0, s, codes, code_stride, scales,
+                         scale_stride, m, d, scaling, out, ldo, invR);
+      break;
+    case 8:
+      hipLaunchKernelGGL((k_dequant_sum_rc<FMT, V, 8>), grid, dim3(256), 0, s, codes, code_stride, scales,
+                         scale_stride, m, d, scaling, out, ldo, invR);
+      break;
+    case 16:
+      hipLaunchKernelGGL((k_dequant_sum_rc<FMT, V, 16>), grid, dim3(256), 0, s, codes, code_stride, scales,
+                         scale_stride, m, d, scaling, out, ldo, invR);
+      break;
+    default:
+      hipLaunchKernelGGL((k_dequant_sum<FMT, V>), grid, dim3(256), 0, s, codes, code_stride, scales, scale_stride, R,
+                         m, d, scaling, out, ldo, invR);
+  }
 }
 
 hipError_t launch_dequant_sum(const uint8_t* codes, int64_t code_stride, const float* scales,
