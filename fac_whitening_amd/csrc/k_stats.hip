@@ -151,11 +151,11 @@ __device__ __forceinline__ void lds_load16(sint32x4 rsrc, uint32_t lds, int voff
 // the workgroup holding the later stages adds first and raises its flag;
 // the one holding the earlier stages (its range ends inside the tile) waits
 // for the next workgroup's flag before adding.  Deterministic, no workspace.
-template <bool DIAG>
+template <bool DIAG, bool OW>
 __device__ __forceinline__ void stats_segment(const uint16_t* __restrict__ x, int64_t T, int64_t ld, int n,
                                               float* __restrict__ S, int bi, int bj, int s_a, int s_b, int nst,
                                               char* As, char* Bs, unsigned* __restrict__ sync, unsigned epoch,
-                                              uint32_t* __restrict__ flags, bool overwrite) {
+                                              uint32_t* __restrict__ flags) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -324,7 +324,9 @@ __device__ __forceinline__ void stats_segment(const uint16_t* __restrict__ x, in
   // register v of MFMA tile (mt, nt) is element
   // (8 (v / 4) + 4 (lane / 32) + v % 4, lane % 32) of the 32 x 32 tile
   const int lr = lane & 31, lh = lane >> 5;
-  const bool store_only = overwrite && s_b == nst;
+  const bool store_only = OW && s_b == nst;
+  // (the old value is loaded in either case and dropped when the sums are
+  // stored: the same code as for adding, whose registers this loop fits)
   if (shared) {
     // device-coherent loads and stores (sc0 sc1), 64 loads in flight per
     // row block; elements outside the output go to an offset past the end
@@ -342,14 +344,15 @@ __device__ __forceinline__ void stats_segment(const uint16_t* __restrict__ x, in
           const int j = col0 + 128 * wn + 32 * nt + lr;
           const bool ok = i < n && j < n && (!DIAG || i >= j);
           off[nt][e] = ok ? (int)(uint32_t)(((int64_t)i * n + j) * 4) : (int)nbytes;
-          v[nt][e] = store_only ? 0.f : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off[nt][e], 0, 17));
+          v[nt][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off[nt][e], 0, 17));
         }
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
           __builtin_amdgcn_raw_buffer_store_b32(
-              __float_as_uint(late ? __builtin_nanf("") : v[nt][e] + acc[mt][nt][e]), rs, off[nt][e], 0, 17);
+              __float_as_uint(late ? __builtin_nanf("") : (store_only ? acc[mt][nt][e] : v[nt][e] + acc[mt][nt][e])),
+              rs, off[nt][e], 0, 17);
     }
   } else {
 #pragma unroll
@@ -360,8 +363,10 @@ __device__ __forceinline__ void stats_segment(const uint16_t* __restrict__ x, in
         for (int e = 0; e < 16; ++e) {
           const int i = row0 + 128 * wm + 32 * mt + 8 * (e / 4) + 4 * lh + e % 4;
           const int j = col0 + 128 * wn + 32 * nt + lr;
-          if (i < n && j < n && (!DIAG || i >= j))
-            S[(int64_t)i * n + j] = store_only ? acc[mt][nt][e] : S[(int64_t)i * n + j] + acc[mt][nt][e];
+          if (i < n && j < n && (!DIAG || i >= j)) {
+            const float old = S[(int64_t)i * n + j];
+            S[(int64_t)i * n + j] = store_only ? acc[mt][nt][e] : old + acc[mt][nt][e];
+          }
         }
   }
   if (s_a > 0) {
@@ -380,9 +385,13 @@ __device__ __forceinline__ void stats_segment(const uint16_t* __restrict__ x, in
 // ranges of (tile, stage) units, one per workgroup (in lower-triangle tile
 // order, stages in token order).  All workgroups are resident (one per
 // compute unit: the LDS stages fill it).
+// OW: the call opens a window (the first writer of each tile stores its
+// sums instead of adding them); a separate kernel, so that the adding form
+// keeps its own register allocation.
+template <bool OW>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 k_stats_mfma(const uint16_t* __restrict__ x, int64_t T, int64_t ld, int n, float* __restrict__ S, int ntiles,
-             unsigned* __restrict__ sync, unsigned epoch, uint32_t* __restrict__ flags, int overwrite) {
+             unsigned* __restrict__ sync, unsigned epoch, uint32_t* __restrict__ flags) {
   __shared__ __attribute__((aligned(16))) char As[kSStages * kSSide];
   __shared__ __attribute__((aligned(16))) char Bs[kSStages * kSSide];
   const int nst = (int)cdiv(T, kSK);
@@ -392,9 +401,9 @@ k_stats_mfma(const uint16_t* __restrict__ x, int64_t T, int64_t ld, int n, float
     int bi, bj;
     tri_tile(rd * G + gid, bi, bj);
     if (bi == bj)
-      stats_segment<true>(x, T, ld, n, S, bi, bj, 0, nst, nst, As, Bs, sync, epoch, flags, overwrite != 0);
+      stats_segment<true, OW>(x, T, ld, n, S, bi, bj, 0, nst, nst, As, Bs, sync, epoch, flags);
     else
-      stats_segment<false>(x, T, ld, n, S, bi, bj, 0, nst, nst, As, Bs, sync, epoch, flags, overwrite != 0);
+      stats_segment<false, OW>(x, T, ld, n, S, bi, bj, 0, nst, nst, As, Bs, sync, epoch, flags);
   }
   const int first = rounds * G;
   const int64_t U = (int64_t)(ntiles - first) * nst;
@@ -406,9 +415,9 @@ k_stats_mfma(const uint16_t* __restrict__ x, int64_t T, int64_t ld, int n, float
     int bi, bj;
     tri_tile(tile, bi, bj);
     if (bi == bj)
-      stats_segment<true>(x, T, ld, n, S, bi, bj, s_a, s_b, nst, As, Bs, sync, epoch, flags, overwrite != 0);
+      stats_segment<true, OW>(x, T, ld, n, S, bi, bj, s_a, s_b, nst, As, Bs, sync, epoch, flags);
     else
-      stats_segment<false>(x, T, ld, n, S, bi, bj, s_a, s_b, nst, As, Bs, sync, epoch, flags, overwrite != 0);
+      stats_segment<false, OW>(x, T, ld, n, S, bi, bj, s_a, s_b, nst, As, Bs, sync, epoch, flags);
     u += s_b - s_a;
   }
 }
@@ -420,7 +429,7 @@ int stats_resident_groups() {
   if (!cache[dev]) {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k_stats_mfma), 256, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k_stats_mfma<false>), 256, 0) !=
         hipSuccess)
       return 0;
     cache[dev] = cus * per_cu;
@@ -447,8 +456,12 @@ hipError_t launch_stats(const void* x, int dtype, int64_t T, int64_t ld, int n, 
     if (units < grid) grid = (int)units;
     const hipError_t e = order_persistent(s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_stats_mfma, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const uint16_t*>(x), T,
-                       ld, n, S, ntiles, sync, epoch, flags, overwrite ? 1 : 0);
+    if (overwrite)
+      hipLaunchKernelGGL(k_stats_mfma<true>, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const uint16_t*>(x),
+                         T, ld, n, S, ntiles, sync, epoch, flags);
+    else
+      hipLaunchKernelGGL(k_stats_mfma<false>, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const uint16_t*>(x),
+                         T, ld, n, S, ntiles, sync, epoch, flags);
   } else if (dtype == GIFT_BF16)
     hipLaunchKernelGGL(k_stats_valu<__hip_bfloat16>, dim3(tiles), dim3(256), 0, s,
                        static_cast<const __hip_bfloat16*>(x), T, ld, n, S, overwrite ? 1 : 0);
