@@ -109,7 +109,9 @@ constexpr int kOff = (int)0x80000000u;   // an offset past any buffer used here
 // kept from the caches' normal replacement they leave the U_k operands and
 // exchange words their place: 57.5 -> 52.3 us per unit at 1536 x 6144).  The
 // gradient loads and the decode's fp32 stores stay normal (non-temporal
-// there measured slower).
+// there measured slower).  With error feedback the residual's stores are
+// non-temporal too (it is next read a whole step later: 33.9 -> 33.0 us for
+// the encode with its residual); its loads stay normal (measured slower).
 constexpr int kNT = 2;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
@@ -1076,8 +1078,8 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
       }
       const int row = row0 + rbl * 16 + lr, c = col0 + cbl * 32 + 4 * lg;
       const int o = (row * d + c) * 4;
-      __builtin_amdgcn_raw_buffer_store_b128(o0, rr, (row < m && c < d) ? o : kOff, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b128(o1, rr, (row < m && c + 16 < d) ? o + 64 : kOff, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(o0, rr, (row < m && c < d) ? o : kOff, 0, kNT);
+      __builtin_amdgcn_raw_buffer_store_b128(o1, rr, (row < m && c + 16 < d) ? o + 64 : kOff, 0, kNT);
     }
   }
   __syncthreads();
