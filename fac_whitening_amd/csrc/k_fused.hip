@@ -94,6 +94,29 @@ __device__ __forceinline__ int row_exp(float mx) {
   const int e = 14 - ex;
   return e < -126 ? -126 : (e > 127 ? 127 : e);
 }
+// Maximum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the lanes holding
+// one row of a sub-tile), with the VALU's row swaps (v_permlane32_swap
+// exchanges the two 32-lane halves, v_permlane16_swap neighbouring 16-lane
+// rows) instead of the LDS permute path.
+__device__ __forceinline__ float rowmax4(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+// Maximum over the wave, in every lane: rotations inside each 16-lane row
+// (DPP row_ror 8, 4, 2, 1), then the row swaps.
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));
+  v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));
+  v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xF, 0xF, false));
+  v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xF, 0xF, false));
+  const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = umax32(p[0], p[1]);
+  const auto q = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return umax32(q[0], q[1]);
+}
 __device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
 constexpr int kUExp = 14;   // U_k's pieces are of 2^14 U_k
 
@@ -284,8 +307,8 @@ __device__ __forceinline__ unsigned long long tagged(unsigned tag, float v) {
 constexpr int kXW = TR * 32;        // projection words per tile (1536)
 constexpr int kXPT = kXW / 512;     // of them per thread (3)
 
-// SC: the decode's scaling (0 per tensor, 1 per block) as a compile-time
-// constant (-1: read at run time).  Per tensor, each replica's scale is one
+// SC: the scaling (0 per tensor, 1 per block) as a compile-time constant
+// (-1: read at run time).  Per tensor, each replica's scale is one
 // uniform word read in the replica loop; per block the scales of the tile's
 // blocks are staged in LDS first.
 // RC > 0: the decode's replica count is a compile-time constant and the
@@ -334,6 +357,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
   const int nbd = (int)cdiv(d, kBlock);
   const int rb0 = row0 / kBlock, cb0 = col0 / kBlock;
   const int cbg0 = (col0 >> 5) + wave;   // this wave's first 32-column block
+  const bool pts = SC >= 0 ? SC == 0 : a.scaling == 0;   // one scale for the whole tensor
   const unsigned tag = (epoch << 1) | (enc ? 0u : 1u);
   if (tid < 16) wmax[tid] = 0u;
   if (tid == 0) s_bad = 0;
@@ -366,9 +390,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
 #pragma unroll
         for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(x[q * 3 + rb][j]));
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    xe[rb] = row_exp(mx);
+    xe[rb] = row_exp(rowmax4(mx));
     const float sc = pow2f(xe[rb]);
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
@@ -551,12 +573,12 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
       const bool ok = row0 + r < m && col0 + c < d;
       off[j] = ok ? (row0 + r) * d + col0 + c : kOff;
       hi[j] = col0 + c + 8 < d;
-      sidx[j] = (a.scaling == 0 || !ok) ? 0 : ((row0 + r) / kBlock - rb0) * 6 + (col0 + c) / kBlock - cb0;
+      sidx[j] = (pts || !ok) ? 0 : ((row0 + r) / kBlock - rb0) * 6 + (col0 + c) / kBlock - cb0;
     }
     const int ft = kDTail + 8 * tid, rt = ft / TC, ct = ft % TC;
     const bool okt = row0 + rt < m && col0 + ct < d;
     const int offt = okt ? (row0 + rt) * d + col0 + ct : kOff;
-    const int sidxt = (a.scaling == 0 || !okt) ? 0 : ((row0 + rt) / kBlock - rb0) * 6 + (col0 + ct) / kBlock - cb0;
+    const int sidxt = (pts || !okt) ? 0 : ((row0 + rt) / kBlock - rb0) * 6 + (col0 + ct) / kBlock - cb0;
     float acc[kDCPT][16], acct[8];
     CodeBuf b0, b1, b2;
     constexpr bool PT = SC == 0;
@@ -761,9 +783,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
       float mx = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(pf[rb * 16 + lr][8 * lg + j]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      pe[rb] = row_exp(mx);
+      pe[rb] = row_exp(rowmax4(mx));
       const float sc = pow2f(pe[rb]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -895,14 +915,11 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
   // 128-row blocks (rb0, rb0 + 1); columns col0 .. col0 + 767 in the six
   // 128-column blocks cb0 .. cb0 + 5 (col0 is a multiple of 768).  Local
   // amax of this tile per block entry (2 x 6), or per tensor (entry 0).
-  if (a.scaling == 0) {
+  if (pts) {
     uint32_t v = 0;
 #pragma unroll
     for (int i = 0; i < NSUB; ++i) v = v > lmax[i] ? v : lmax[i];
-    for (int o = 32; o > 0; o >>= 1) {
-      const uint32_t u = (uint32_t)__shfl_xor((int)v, o, 64);
-      v = v > u ? v : u;
-    }
+    v = wave_umax(v);
     if (lane == 0) wmax[8 + wave] = v;
     __syncthreads();
     if (tid == 0) {
@@ -914,11 +931,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
   } else {
 #pragma unroll
     for (int i = 0; i < NSUB; ++i) {
-      uint32_t v = lmax[i];
-      for (int o = 32; o > 0; o >>= 1) {
-        const uint32_t u = (uint32_t)__shfl_xor((int)v, o, 64);
-        v = v > u ? v : u;
-      }
+      const uint32_t v = wave_umax(lmax[i]);
       if (lane == 0 && live[i / 3] && v != 0u) {
         const int e = ((row0 + SUB_RB(i) * 16) / kBlock - rb0) * 6 + (col0 + SUB_CB(i) * 32) / kBlock - cb0;
         atomicMax(&wmax[e], v);
@@ -938,7 +951,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
     // the tag makes each word self-validating: no ordering with other data
     // is needed.  The words are published with atomic exchanges, which take
     // effect at the device's coherence point at once.
-    if (a.scaling == 0) {
+    if (pts) {
       // per tensor: one word per workgroup, written into kAmaxCopies copies
       // of a compact array (lane c of wave 0 writes copy c); workgroup g
       // reads copy g % kAmaxCopies with one wave, a few coalesced loads per
@@ -972,10 +985,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
 #pragma unroll
           for (int j = 0; j < 4; ++j) v = v > (uint32_t)w[j] ? v : (uint32_t)w[j];
         }
-        for (int o = 32; o > 0; o >>= 1) {
-          const uint32_t u = (uint32_t)__shfl_xor((int)v, o, 64);
-          v = v > u ? v : u;
-        }
+        v = wave_umax(v);
         if (lane == 0) blk[0][0] = v;
       }
     } else {
@@ -999,7 +1009,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
   // the workgroup holding a block's top-left sub-tile writes its scale and
   // local amax
   const float fmax = fp8_fmax(FMT);
-  if (tid < 12 && (a.scaling != 0 || tid == 0)) {
+  if (tid < 12 && (!pts || tid == 0)) {
     const int br = rb0 + tid / 6, bc = cb0 + tid % 6;
     // blocks rb0 and cb0 .. cb0 + 5 always meet the tile; rb0 + 1 may not
     const bool inside = br * kBlock < m && bc * kBlock < d && br * kBlock < row0 + TR;
@@ -1007,7 +1017,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
     sss[tid] = 0.0f;
     sam[tid] = 0u;
     if (inside) {
-      const int slot = a.scaling == 0 ? 0 : br * nbd + bc;
+      const int slot = pts ? 0 : br * nbd + bc;
       const uint32_t local = blk[tid / 6][tid % 6];
       const uint32_t am = a.amax_in ? absbits_f(a.amax_in[slot]) : local;
       float r, sc;
@@ -1015,7 +1025,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
       srs[tid] = r;
       sss[tid] = sc;
       sam[tid] = am;
-      const bool leader = a.scaling == 0 ? g == 0 : (br * kBlock >= row0 && bc * kBlock >= col0);
+      const bool leader = pts ? g == 0 : (br * kBlock >= row0 && bc * kBlock >= col0);
       if (leader) {
         const bool bad = s_bad != 0;
         if (a.scales) a.scales[slot] = bad ? __builtin_nanf("") : sc;
@@ -1027,46 +1037,32 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
   __syncthreads();   // the tile memory now receives the codes
   if (!a.codes) return;
   const bool bad = s_bad != 0;
+  // hardware conversion of 8 finite values (clamped to the format's range:
+  // saturating RNE)
+  auto hw8 = [&](const float* xi, float r, uint32_t& q0, uint32_t& q1) {
+    float y[8];
 #pragma unroll
-  for (int i = 0; i < NSUB; ++i) {
-    if (!live[i / 3]) continue;
-    const int rbl = SUB_RB(i), cbl = SUB_CB(i);
-    const int e = a.scaling == 0 ? 0
-                                 : ((row0 + rbl * 16) / kBlock - rb0) * 6 + (col0 + cbl * 32) / kBlock - cb0;
-    const float r = srs[e];
-    const uint32_t am = sam[e];
-    uint32_t q0, q1;
-    if (am >= 0x7F800000u || bad) {
-      q0 = q1 = 0x7F7F7F7Fu;
-    } else if (lmax[i] >= 0x7F800000u) {
-      // a non-finite element under a finite shared amax: exact integer path
-      uint32_t e[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) e[j] = enc_fp8<FMT>(x[i][j] * r);
-      q0 = e[0] | (e[1] << 8) | (e[2] << 16) | (e[3] << 24);
-      q1 = e[4] | (e[5] << 8) | (e[6] << 16) | (e[7] << 24);
+    for (int j = 0; j < 8; ++j) y[j] = __builtin_amdgcn_fmed3f(xi[j] * r, fmax, -fmax);
+    if constexpr (FMT == 0) {
+      q0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+      q0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)q0, true);
+      q1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+      q1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], (int)q1, true);
     } else {
-      float y[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) y[j] = __builtin_amdgcn_fmed3f(x[i][j] * r, fmax, -fmax);
-      if constexpr (FMT == 0) {
-        q0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-        q0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)q0, true);
-        q1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
-        q1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], (int)q1, true);
-      } else {
-        q0 = __builtin_amdgcn_cvt_pk_bf8_f32(y[0], y[1], 0, false);
-        q0 = __builtin_amdgcn_cvt_pk_bf8_f32(y[2], y[3], (int)q0, true);
-        q1 = __builtin_amdgcn_cvt_pk_bf8_f32(y[4], y[5], 0, false);
-        q1 = __builtin_amdgcn_cvt_pk_bf8_f32(y[6], y[7], (int)q1, true);
-      }
+      q0 = __builtin_amdgcn_cvt_pk_bf8_f32(y[0], y[1], 0, false);
+      q0 = __builtin_amdgcn_cvt_pk_bf8_f32(y[2], y[3], (int)q0, true);
+      q1 = __builtin_amdgcn_cvt_pk_bf8_f32(y[4], y[5], 0, false);
+      q1 = __builtin_amdgcn_cvt_pk_bf8_f32(y[6], y[7], (int)q1, true);
     }
+  };
+  // the codes into the tile memory; with error feedback the new residual
+  // fp32(U~ - s dec(q)), the difference rounded once
+  auto emit = [&](int i, uint32_t q0, uint32_t q1, float sc) {
+    const int rbl = SUB_RB(i), cbl = SUB_CB(i);
     uint8_t* cs = reinterpret_cast<uint8_t*>(smem) + (rbl * 16 + lr) * (TC + 16) + cbl * 32 + 4 * lg;
     *reinterpret_cast<uint32_t*>(cs) = q0;
     *reinterpret_cast<uint32_t*>(cs + 16) = q1;
     if constexpr (EF) {
-      // new residual fp32(U~ - s dec(q)), the difference rounded once
-      const float sc = sss[e];
       float dv[8];
       dec4<FMT>(q0, dv);
       dec4<FMT>(q1, dv + 4);
@@ -1080,6 +1076,45 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
       const int o = (row * d + c) * 4;
       __builtin_amdgcn_raw_buffer_store_b128(o0, rr, (row < m && c < d) ? o : kOff, 0, kNT);
       __builtin_amdgcn_raw_buffer_store_b128(o1, rr, (row < m && c + 16 < d) ? o + 64 : kOff, 0, kNT);
+    }
+  };
+  // Per tensor with a finite amax and no non-finite element in the wave's
+  // sub-tiles (the usual case, one uniform test): one scale pair for every
+  // sub-tile and no per-sub-tile branches.
+  bool nonfin = false;
+#pragma unroll
+  for (int i = 0; i < NSUB; ++i) nonfin = nonfin || lmax[i] >= 0x7F800000u;
+  if (pts && !bad && sam[0] < 0x7F800000u && !__any(nonfin)) {
+    const float r = srs[0], sc = sss[0];
+#pragma unroll
+    for (int i = 0; i < NSUB; ++i) {
+      if (!live[i / 3]) continue;
+      uint32_t q0, q1;
+      hw8(x[i], r, q0, q1);
+      emit(i, q0, q1, sc);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NSUB; ++i) {
+      if (!live[i / 3]) continue;
+      const int rbl = SUB_RB(i), cbl = SUB_CB(i);
+      const int e = pts ? 0 : ((row0 + rbl * 16) / kBlock - rb0) * 6 + (col0 + cbl * 32) / kBlock - cb0;
+      const float r = srs[e];
+      const uint32_t am = sam[e];
+      uint32_t q0, q1;
+      if (am >= 0x7F800000u || bad) {
+        q0 = q1 = 0x7F7F7F7Fu;
+      } else if (lmax[i] >= 0x7F800000u) {
+        // a non-finite element under a finite shared amax: exact integer path
+        uint32_t e8[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e8[j] = enc_fp8<FMT>(x[i][j] * r);
+        q0 = e8[0] | (e8[1] << 8) | (e8[2] << 16) | (e8[3] << 24);
+        q1 = e8[4] | (e8[5] << 8) | (e8[6] << 16) | (e8[7] << 24);
+      } else {
+        hw8(x[i], r, q0, q1);
+      }
+      emit(i, q0, q1, sss[e]);
     }
   }
   __syncthreads();
@@ -1096,25 +1131,25 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
 // One kernel per direction, transform and format (distinct names in
 // traces); the encode also with error feedback (_ef), the decode per
 // replica count 4, 8, 16 (0: any count up to 64) and scaling.
-template <int FMT>
+template <int FMT, int SC>
 __global__ void __launch_bounds__(512) k_rank_encode(FusedArgs a) {
-  fused_body<FMT, true, 0, -1, true>(a, blockIdx.x, gridDim.x, a.epoch);
+  fused_body<FMT, true, 0, SC, true>(a, blockIdx.x, gridDim.x, a.epoch);
 }
-template <int FMT>
+template <int FMT, int SC>
 __global__ void __launch_bounds__(512) k_rank_encode_ef(FusedArgs a) {
-  fused_body<FMT, true, 0, -1, true, true>(a, blockIdx.x, gridDim.x, a.epoch);
+  fused_body<FMT, true, 0, SC, true, true>(a, blockIdx.x, gridDim.x, a.epoch);
 }
 template <int FMT, int RC, int SC>
 __global__ void __launch_bounds__(512) k_rank_decode(FusedArgs a) {
   fused_body<FMT, false, RC, SC, true>(a, blockIdx.x, gridDim.x, a.epoch);
 }
-template <int FMT>
+template <int FMT, int SC>
 __global__ void __launch_bounds__(512) k_euclid_encode(FusedArgs a) {
-  fused_body<FMT, true, 0, -1, false>(a, blockIdx.x, gridDim.x, a.epoch);
+  fused_body<FMT, true, 0, SC, false>(a, blockIdx.x, gridDim.x, a.epoch);
 }
-template <int FMT>
+template <int FMT, int SC>
 __global__ void __launch_bounds__(512) k_euclid_encode_ef(FusedArgs a) {
-  fused_body<FMT, true, 0, -1, false, true>(a, blockIdx.x, gridDim.x, a.epoch);
+  fused_body<FMT, true, 0, SC, false, true>(a, blockIdx.x, gridDim.x, a.epoch);
 }
 template <int FMT, int RC, int SC>
 __global__ void __launch_bounds__(512) k_euclid_decode(FusedArgs a) {
@@ -1174,21 +1209,26 @@ static hipError_t launch_decode(const FusedArgs& a, int grid, hipStream_t s) {
   return a.scaling == 0 ? launch_decode<FMT, 0, LR>(a, grid, s) : launch_decode<FMT, 1, LR>(a, grid, s);
 }
 
+template <int SC>
+static hipError_t launch_encode(const FusedArgs& a, int grid, hipStream_t s) {
+  // kernel by transform, error feedback and format
+  const int which = (a.lr ? 4 : 0) + (a.resid ? 2 : 0) + (a.fmt == 0 ? 0 : 1);
+  switch (which) {
+    case 0: return persistent_launch(k_euclid_encode<0, SC>, grid, a, s);
+    case 1: return persistent_launch(k_euclid_encode<1, SC>, grid, a, s);
+    case 2: return persistent_launch(k_euclid_encode_ef<0, SC>, grid, a, s);
+    case 3: return persistent_launch(k_euclid_encode_ef<1, SC>, grid, a, s);
+    case 4: return persistent_launch(k_rank_encode<0, SC>, grid, a, s);
+    case 5: return persistent_launch(k_rank_encode<1, SC>, grid, a, s);
+    case 6: return persistent_launch(k_rank_encode_ef<0, SC>, grid, a, s);
+    default: return persistent_launch(k_rank_encode_ef<1, SC>, grid, a, s);
+  }
+}
+
 hipError_t launch_fused(const FusedArgs& a, int grid, hipStream_t s) {
   hipError_t e;
   if (a.mode == 0) {
-    // kernel by transform, error feedback and format
-    const int which = (a.lr ? 4 : 0) + (a.resid ? 2 : 0) + (a.fmt == 0 ? 0 : 1);
-    switch (which) {
-      case 0: e = persistent_launch(k_euclid_encode<0>, grid, a, s); break;
-      case 1: e = persistent_launch(k_euclid_encode<1>, grid, a, s); break;
-      case 2: e = persistent_launch(k_euclid_encode_ef<0>, grid, a, s); break;
-      case 3: e = persistent_launch(k_euclid_encode_ef<1>, grid, a, s); break;
-      case 4: e = persistent_launch(k_rank_encode<0>, grid, a, s); break;
-      case 5: e = persistent_launch(k_rank_encode<1>, grid, a, s); break;
-      case 6: e = persistent_launch(k_rank_encode_ef<0>, grid, a, s); break;
-      default: e = persistent_launch(k_rank_encode_ef<1>, grid, a, s); break;
-    }
+    e = a.scaling == 0 ? launch_encode<0>(a, grid, s) : launch_encode<1>(a, grid, s);
   } else if (a.fmt == 0) {
     e = a.lr ? launch_decode<0, true>(a, grid, s) : launch_decode<0, false>(a, grid, s);
   } else {
@@ -1213,10 +1253,13 @@ hipError_t launch_group(const FusedArgs* table, int n, const GroupEpochs& ep, in
                         int grid, hipStream_t s) {
   const dim3 gd((unsigned)grid), bd(512);
   if (!decode) {
-    if (fmt == 0)
-      hipLaunchKernelGGL((k_rank_group<0, true, 0, -1>), gd, bd, 0, s, table, n, ep);
-    else
-      hipLaunchKernelGGL((k_rank_group<1, true, 0, -1>), gd, bd, 0, s, table, n, ep);
+    if (fmt == 0) {
+      if (scaling == 0) hipLaunchKernelGGL((k_rank_group<0, true, 0, 0>), gd, bd, 0, s, table, n, ep);
+      else hipLaunchKernelGGL((k_rank_group<0, true, 0, 1>), gd, bd, 0, s, table, n, ep);
+    } else {
+      if (scaling == 0) hipLaunchKernelGGL((k_rank_group<1, true, 0, 0>), gd, bd, 0, s, table, n, ep);
+      else hipLaunchKernelGGL((k_rank_group<1, true, 0, 1>), gd, bd, 0, s, table, n, ep);
+    }
   } else if (fmt == 0) {
     if (scaling == 0) launch_group_decode<0, 0>(table, n, ep, R, grid, s);
     else launch_group_decode<0, 1>(table, n, ep, R, grid, s);
@@ -1238,10 +1281,13 @@ int fused_resident_groups() {
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
   const void* kernels[] = {
-      reinterpret_cast<const void*>(k_rank_encode<0>), reinterpret_cast<const void*>(k_rank_encode<1>),
-      reinterpret_cast<const void*>(k_rank_encode_ef<0>), reinterpret_cast<const void*>(k_rank_encode_ef<1>),
-      reinterpret_cast<const void*>(k_euclid_encode<0>), reinterpret_cast<const void*>(k_euclid_encode<1>),
-      reinterpret_cast<const void*>(k_euclid_encode_ef<0>), reinterpret_cast<const void*>(k_euclid_encode_ef<1>),
+#define GIFT_ENC(S)                                                                                       \
+  reinterpret_cast<const void*>(k_rank_encode<0, S>), reinterpret_cast<const void*>(k_rank_encode<1, S>),      \
+      reinterpret_cast<const void*>(k_rank_encode_ef<0, S>), reinterpret_cast<const void*>(k_rank_encode_ef<1, S>), \
+      reinterpret_cast<const void*>(k_euclid_encode<0, S>), reinterpret_cast<const void*>(k_euclid_encode<1, S>),  \
+      reinterpret_cast<const void*>(k_euclid_encode_ef<0, S>), reinterpret_cast<const void*>(k_euclid_encode_ef<1, S>)
+      GIFT_ENC(0), GIFT_ENC(1),
+#undef GIFT_ENC
 #define GIFT_DEC(F, S)                                                                                      \
   reinterpret_cast<const void*>(k_rank_decode<F, 4, S>), reinterpret_cast<const void*>(k_rank_decode<F, 8, S>), \
       reinterpret_cast<const void*>(k_rank_decode<F, 16, S>), reinterpret_cast<const void*>(k_rank_decode<F, 0, S>), \
