@@ -305,6 +305,13 @@ __device__ __forceinline__ unsigned long long tagged(unsigned tag, float v) {
 }
 
 constexpr int kXW = TR * 32;        // projection words per tile (1536)
+// Output staging of the rank-k decode: two 48 x 256 fp32 slabs, row stride
+// kStagePad floats; the first over the per-wave partials (8 x 3 x 16 x 33
+// floats), the second after the gathered projection (48 x 33 floats).
+constexpr int kStagePad = 260;
+constexpr int kStageB = 8 * 3 * 16 * 33 + 48 * 33 + 80;
+static_assert(TR * kStagePad <= 8 * 3 * 16 * 33, "first output slab over the partials");
+static_assert(kStageB % 4 == 0 && kStageB + TR * kStagePad <= TR * kTilePad, "second output slab inside the tile");
 constexpr int kXPT = kXW / 512;     // of them per thread (3)
 
 // SC: the scaling (0 per tensor, 1 per block) as a compile-time constant
@@ -793,9 +800,10 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
         pl[rb][j] = l;
       }
     }
-#pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      if (!live[q]) continue;
+    // the three sub-tiles of column block q (this wave's columns
+    // col0 + 32 (wave + 8 q) ..) made final in the registers
+    auto recon_q = [&](int q) {
+      if (!live[q]) return;
 #pragma unroll
       for (int grp = 0; grp < 2; ++grp) {
         const half8 uh = uo.u[q][grp][0], ul = uo.u[q][grp][1];
@@ -812,29 +820,57 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
             x[i][4 * grp + e] = __builtin_fmaf(alpha, x[i][4 * grp + e], __builtin_ldexpf(c[e], -(pe[rb] + kUExp)));
         }
       }
-      if constexpr (!ENC) {
-        // decode: the column block's three sub-tiles are final; store them
-        // from the registers while the next block's products run (two
-        // 16-byte stores per sub-tile and lane: row 16 rb + lr, columns
-        // c .. c + 3 and c + 16 .. c + 19)
-        const auto orr = make_rsrc(a.out, ((int64_t)(m - 1) * a.ldo + d) * 4);
+    };
+    if constexpr (ENC) {
+#pragma unroll
+      for (int q = 0; q < 3; ++q) recon_q(q);
+    } else {
+      // Decode: the output leaves through LDS so that every store
+      // instruction of a wave writes 1 KB of one row (256 columns) instead
+      // of 64 bytes of 16 rows.  Column block q of all 8 waves is the 48 x
+      // 256 slab at columns col0 + 256 q; slabs alternate between two
+      // buffers (the partials' area and the space after the gathered
+      // projection), and the products of the next slab run while the
+      // previous one is stored.
+      float* stg[2] = {smem, smem + kStageB};
+      auto stage = [&](int q) {
+        float* b = stg[q & 1];
 #pragma unroll
         for (int rb = 0; rb < 3; ++rb) {
           const int i = q * 3 + rb;
+          float* dst = b + (16 * rb + lr) * kStagePad + 32 * wave + 4 * lg;
           if (bad) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[i][e] = __builtin_nanf("");
           }
-          const int row = row0 + 16 * rb + lr, c = col0 + 32 * SUB_CB(i) + 4 * lg;
-          const int o = (int)(((int64_t)row * a.ldo + c) * 4);
-          const int32x4 v0 = {__float_as_int(x[i][0]), __float_as_int(x[i][1]), __float_as_int(x[i][2]),
-                              __float_as_int(x[i][3])};
-          const int32x4 v1 = {__float_as_int(x[i][4]), __float_as_int(x[i][5]), __float_as_int(x[i][6]),
-                              __float_as_int(x[i][7])};
-          __builtin_amdgcn_raw_buffer_store_b128(v0, orr, (row < m && c < d) ? o : kOff, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b128(v1, orr, (row < m && c + 16 < d) ? o + 64 : kOff, 0, 0);
+          *reinterpret_cast<float4*>(dst) = make_float4(x[i][0], x[i][1], x[i][2], x[i][3]);
+          *reinterpret_cast<float4*>(dst + 16) = make_float4(x[i][4], x[i][5], x[i][6], x[i][7]);
         }
-      }
+      };
+      const auto orr = make_rsrc(a.out, ((int64_t)(m - 1) * a.ldo + d) * 4);
+      auto drain = [&](int q) {
+        const float* b = stg[q & 1];
+#pragma unroll
+        for (int j = 0; j < 6; ++j) {
+          const int f = tid + 512 * j, r = f >> 6, c = (f & 63) * 4;
+          const int32x4 v = *reinterpret_cast<const int32x4*>(b + r * kStagePad + c);
+          const int row = row0 + r, col = col0 + 256 * q + c;
+          __builtin_amdgcn_raw_buffer_store_b128(
+              v, orr, (row < m && col < d) ? (int)(((int64_t)row * a.ldo + col) * 4) : kOff, 0, 0);
+        }
+      };
+      recon_q(0);
+      stage(0);
+      __syncthreads();
+      recon_q(1);
+      drain(0);
+      stage(1);
+      __syncthreads();
+      recon_q(2);
+      drain(1);
+      stage(2);
+      __syncthreads();
+      drain(2);
     }
   }
 
