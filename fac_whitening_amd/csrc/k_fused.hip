@@ -131,8 +131,10 @@ constexpr int kOff = (int)0x80000000u;   // an offset past any buffer used here
 // decode's code loads are non-temporal (each byte is touched once per call;
 // kept from the caches' normal replacement they leave the U_k operands and
 // exchange words their place: 57.5 -> 52.3 us per unit at 1536 x 6144).  The
-// gradient loads and the decode's fp32 stores stay normal (non-temporal
-// there measured slower).  With error feedback the residual's stores are
+// rank-k decode's fp32 stores, whole 1 KB row segments, are non-temporal as
+// well (50.3 -> 48.2 us per unit; while they were 64-byte pieces of 16 rows
+// it measured slower).  The gradient loads stay normal (non-temporal there
+// measured slower).  With error feedback the residual's stores are
 // non-temporal too (it is next read a whole step later: 33.9 -> 33.0 us for
 // the encode with its residual); its loads stay normal (measured slower).
 constexpr int kNT = 2;
@@ -856,7 +858,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
           const int32x4 v = *reinterpret_cast<const int32x4*>(b + r * kStagePad + c);
           const int row = row0 + r, col = col0 + 256 * q + c;
           __builtin_amdgcn_raw_buffer_store_b128(
-              v, orr, (row < m && col < d) ? (int)(((int64_t)row * a.ldo + col) * 4) : kOff, 0, 0);
+              v, orr, (row < m && col < d) ? (int)(((int64_t)row * a.ldo + col) * 4) : kOff, 0, kNT);
         }
       };
       recon_q(0);
