@@ -292,7 +292,10 @@ __global__ void __launch_bounds__(256) k_bucket_quantize(BucketTable t, const fl
 
 // U = (1/R) sum_r s_r dec(q_r), replicas in increasing r (from replica 0's
 // term, so a lone -0 stays -0).  RC: the replica count when known at
-// compile time (0: R at run time).
+// compile time (0: R at run time).  The code loads and the fp32 stores are
+// non-temporal (each byte is touched once: 3.24 -> 3.16 ms for the 155
+// tensors of the 600M-class bucket at R = 8).
+constexpr int kNTb = 2;
 template <int FMT, int RC>
 __global__ void __launch_bounds__(256) k_bucket_dequant_sum(BucketTable t, const uint8_t* __restrict__ codes,
                                                             int64_t code_stride, const float* __restrict__ scales,
@@ -312,7 +315,7 @@ __global__ void __launch_bounds__(256) k_bucket_dequant_sum(BucketTable t, const
       const float sb = L.block_live(1) ? cld(scales, uidx64((int64_t)r * scale_stride + s1)) : 0.0f;
       uint32_t w[kBH];
 #pragma unroll
-      for (int h = 0; h < kBH; ++h) w[h] = __builtin_amdgcn_raw_buffer_load_b32(qs, L.off + 256 * h, 0, 0);
+      for (int h = 0; h < kBH; ++h) w[h] = __builtin_amdgcn_raw_buffer_load_b32(qs, L.off + 256 * h, 0, kNTb);
 #pragma unroll
       for (int h = 0; h < kBH; ++h) {
         const float s = h < 2 ? sa : sb;
@@ -328,7 +331,7 @@ __global__ void __launch_bounds__(256) k_bucket_dequant_sum(BucketTable t, const
       __builtin_amdgcn_raw_buffer_store_b128(
           __builtin_bit_cast(int32x4_b, make_float4(acc[h][0] * invR, acc[h][1] * invR, acc[h][2] * invR,
                                                     acc[h][3] * invR)),
-          os, 4 * (L.off + 256 * h), 0, 0);
+          os, 4 * (L.off + 256 * h), 0, kNTb);
   }
 }
 
