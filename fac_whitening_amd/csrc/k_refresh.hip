@@ -219,35 +219,46 @@ __global__ void __launch_bounds__(256) k_sum_parts32(const float* __restrict__ p
   out[e] = s;
 }
 
-// out[e] = sum_{p < nparts} part[p][e], in order p = 0, 1, ... (deterministic)
+// out[e] = sum_{p < nparts} part[p][e], in order p = 0, 1, ... (deterministic).
+// Sixteen independent loads in flight per thread, added in order: the l x l
+// Gram sums have few elements (2304 threads) and many partials, so the
+// load latency, not the bytes, sets their time.
 __global__ void __launch_bounds__(256) k_sum_parts(const double* __restrict__ part, int nparts, int64_t n,
                                                    double* __restrict__ out) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= n) return;
+  constexpr int U = 16;
   double s = 0.0;
   int p = 0;
-  for (; p + 4 <= nparts; p += 4) {   // four independent loads in flight, summed in order
-    const double v0 = part[(int64_t)p * n + e], v1 = part[(int64_t)(p + 1) * n + e];
-    const double v2 = part[(int64_t)(p + 2) * n + e], v3 = part[(int64_t)(p + 3) * n + e];
-    s += v0;
-    s += v1;
-    s += v2;
-    s += v3;
+  for (; p + U <= nparts; p += U) {
+    double v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = part[(int64_t)(p + u) * n + e];
+#pragma unroll
+    for (int u = 0; u < U; ++u) s += v[u];
   }
   for (; p < nparts; ++p) s += part[(int64_t)p * n + e];
   out[e] = s;
 }
 
-// part[ch][a][b] = sum_{i in rows of chunk ch} X[i][a] Y[i][b]  (fp64, LP <= 64)
+// part[ch][a][b] = sum_{i in rows of chunk ch} X[i][a] Y[i][b]  (fp64, LP a
+// multiple of 16, at most 64), each entry summed over the chunk's rows in
+// order.  Thread (ta, tb) of the 16 x 16 grid owns the BS x BS block of
+// entries a = BS ta + u, b = BS tb + v (BS = LP / 16): per row it reads BS
+// values of X and BS of Y from LDS for BS^2 products.
 template <int LP>
 __global__ void __launch_bounds__(256) k_gram_parts(const double* __restrict__ X, const double* __restrict__ Y,
                                                     int d, double* __restrict__ part) {
+  static_assert(LP % 16 == 0 && LP <= 64, "16 x 16 thread blocks");
+  constexpr int BS = LP / 16;
   __shared__ double Xs[32][LP];
   __shared__ double Ys[32][LP];
-  constexpr int PER = (LP * LP + 255) / 256;
-  double acc[PER];
+  const int ta = threadIdx.x >> 4, tb = threadIdx.x & 15;
+  double acc[BS][BS];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.0;
+  for (int u = 0; u < BS; ++u)
+#pragma unroll
+    for (int v = 0; v < BS; ++v) acc[u][v] = 0.0;
   const int r0 = blockIdx.x * kGramRows;
   for (int s0 = r0; s0 < min(d, r0 + kGramRows); s0 += 32) {
     for (int e = threadIdx.x; e < 32 * LP; e += 256) {
@@ -257,23 +268,33 @@ __global__ void __launch_bounds__(256) k_gram_parts(const double* __restrict__ X
       Ys[rr][c] = ok ? Y[(int64_t)(s0 + rr) * LP + c] : 0.0;
     }
     __syncthreads();
+#pragma unroll 4
+    for (int rr = 0; rr < 32; ++rr) {
+      double xa[BS], yb[BS];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      int o = threadIdx.x + e * 256;
-      if (o < LP * LP) {
-        int a = o / LP, b = o % LP;
-        double s = acc[e];
-        for (int rr = 0; rr < 32; ++rr) s += Xs[rr][a] * Ys[rr][b];
-        acc[e] = s;
-      }
+      for (int u = 0; u < BS; ++u) xa[u] = Xs[rr][BS * ta + u];
+#pragma unroll
+      for (int v = 0; v < BS; ++v) yb[v] = Ys[rr][BS * tb + v];
+#pragma unroll
+      for (int u = 0; u < BS; ++u)
+#pragma unroll
+        for (int v = 0; v < BS; ++v) acc[u][v] += xa[u] * yb[v];
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    int o = threadIdx.x + e * 256;
-    if (o < LP * LP) part[(int64_t)blockIdx.x * LP * LP + o] = acc[e];
-  }
+  for (int u = 0; u < BS; ++u)
+#pragma unroll
+    for (int v = 0; v < BS; ++v)
+      part[(int64_t)blockIdx.x * LP * LP + (BS * ta + u) * LP + BS * tb + v] = acc[u][v];
+}
+
+// v of lane j (j uniform) in every lane, through two v_readlane (no LDS
+// round trip).
+__device__ __forceinline__ double lane_bcast(double v, int j) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)b, j), hi = __builtin_amdgcn_readlane((int)(b >> 32), j);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
 }
 
 // 1 / sqrt(x) from the hardware estimate and two Newton steps (about one
@@ -315,7 +336,7 @@ __global__ void __launch_bounds__(64) k_chol_inv_small(const double* __restrict_
 #pragma unroll
     for (int q = 0; q < j; ++q) acc[q & 3] += row[q] * Ls[j][q];
     const double r = row[j] - ((acc[0] + acc[1]) + (acc[2] + acc[3]));
-    const double dj = __shfl(r, j, 64);   // the pivot, from lane j
+    const double dj = lane_bcast(r, j);   // the pivot, from lane j
     double rs = rsq_nr(dj);               // 1 / L[j][j]
     if (!(dj > 0.0)) {
       bad = true;
@@ -358,11 +379,13 @@ __global__ void __launch_bounds__(256) k_right_small(const double* __restrict__ 
   double acc[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) acc[c] = 0.0;
-#pragma unroll 8
-  for (int a = 0; a < LP; ++a) {
-    const double x = X[(int64_t)i * LP + a];
+  double xr[LP];   // the whole row in flight at once
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) acc[c] += x * Ms[a][g * CPT + c];
+  for (int a = 0; a < LP; ++a) xr[a] = X[(int64_t)i * LP + a];
+#pragma unroll
+  for (int a = 0; a < LP; ++a) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) acc[c] += xr[a] * Ms[a][g * CPT + c];
   }
 #pragma unroll
   for (int c = 0; c < CPT; ++c) out[(int64_t)i * NC + g * CPT + c] = (TO)acc[c];
