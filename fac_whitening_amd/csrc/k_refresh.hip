@@ -61,7 +61,7 @@ template <int LP>
 __global__ void __launch_bounds__(256) k_aq(const float* __restrict__ A, int d, const double* __restrict__ X,
                                             int jrows, double* __restrict__ part) {
   constexpr int NT = LP / 16;    // output column tiles
-  constexpr int KB = 4;          // 4-row k-steps per block (16 rows)
+  constexpr int KB = 6;          // 4-row k-steps per block (24 rows; 4 and 8 measured slower)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lm = lane & 15, lk = lane >> 4;
   const int i0 = blockIdx.x * kAqCols + wave * 64;

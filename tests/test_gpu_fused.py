@@ -143,6 +143,40 @@ def test_fused_shared_amax(fw, scaling):
     assert torch.equal(local2, local)
 
 
+@pytest.mark.parametrize("scaling", ["tensor", "block"])
+def test_fused_nonfinite_rows_under_shared_amax(fw, scaling):
+    """A finite shared amax (Algorithm 1's AllReduceMax) with Inf and NaN in
+    a few rows of this worker's gradient: the whitening spreads them along
+    their rows, so the waves holding those rows quantise element by element
+    (exact integer encoder: Inf saturates, NaN -> 0x7F with its sign) while
+    every other wave of the launch takes the uniform finite path.  Codes
+    and scales bit-exact against the oracle's quantiser on the GPU's own
+    whitened tensor (reading R4)."""
+    m, d = 200, 1544
+    print(f"[fused non-finite rows, shared amax, {scaling}]", flush=True)
+    fw.set_fused(True)
+    Ws, fac = _case(m, d, 1, seed=13)
+    L = _layer_with_factor(fw, m, d, fac)
+    s = fw.SCALINGS[scaling]
+    nb = fw.nblocks(m, d, s)
+    W = torch.from_numpy(Ws[0]).to(DEV)
+    local = torch.empty(nb, device=DEV)
+    L.encode(W, 0, s, amax_out=local)
+    shared = local * 1.25
+    W[37, 100] = float("inf")
+    W[150, 901] = float("-inf")
+    W[151, 5] = float("nan")
+    whit = torch.empty(m, d, device=DEV)
+    c, sc = L.encode(W, 0, s, amax_in=shared, whitened=whit)
+    wh = whit.cpu().numpy()
+    bad_rows = ~np.isfinite(wh).all(axis=1)
+    assert bad_rows[[37, 150, 151]].all() and bad_rows.sum() < m // 4
+    cq, sq, _ = G.quantize(wh, "e4m3", scaling,
+                           amax_in=shared.cpu().numpy().astype(np.float64).reshape(G.nblocks(m, d, scaling)))
+    assert np.array_equal(c.cpu().numpy(), cq)
+    assert np.array_equal(sc.cpu().numpy(), sq.ravel())
+
+
 @pytest.mark.parametrize("R", [4, 8])
 @pytest.mark.parametrize("scaling", ["tensor", "block"])
 @pytest.mark.parametrize("shape", [(200, 1544), (1536, 6144)])
