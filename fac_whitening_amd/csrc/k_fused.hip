@@ -1309,8 +1309,8 @@ hipError_t launch_group(const FusedArgs* table, int n, const GroupEpochs& ep, in
 }
 
 // Workgroups of the fused kernels that the current device can hold at once:
-// the smallest occupancy of any variant (one query per kernel) times the
-// compute units; 0 if a query fails.
+// the smallest occupancy of any variant, single-layer and grouped (one query
+// per kernel), times the compute units; 0 if a query fails.
 int fused_resident_groups() {
   static int cache[64] = {0};
   int dev = 0;
@@ -1331,8 +1331,15 @@ int fused_resident_groups() {
       reinterpret_cast<const void*>(k_rank_decode<F, 16, S>), reinterpret_cast<const void*>(k_rank_decode<F, 0, S>), \
       reinterpret_cast<const void*>(k_euclid_decode<F, 4, S>), reinterpret_cast<const void*>(k_euclid_decode<F, 8, S>), \
       reinterpret_cast<const void*>(k_euclid_decode<F, 16, S>), reinterpret_cast<const void*>(k_euclid_decode<F, 0, S>)
-      GIFT_DEC(0, 0), GIFT_DEC(0, 1), GIFT_DEC(1, 0), GIFT_DEC(1, 1)
+      GIFT_DEC(0, 0), GIFT_DEC(0, 1), GIFT_DEC(1, 0), GIFT_DEC(1, 1),
 #undef GIFT_DEC
+  // the grouped launches of the same bodies
+#define GIFT_GRP(F, S)                                                                                         \
+  reinterpret_cast<const void*>(k_rank_group<F, true, 0, S>), reinterpret_cast<const void*>(k_rank_group<F, false, 4, S>), \
+      reinterpret_cast<const void*>(k_rank_group<F, false, 8, S>),                                                \
+      reinterpret_cast<const void*>(k_rank_group<F, false, 16, S>), reinterpret_cast<const void*>(k_rank_group<F, false, 0, S>)
+      GIFT_GRP(0, 0), GIFT_GRP(0, 1), GIFT_GRP(1, 0), GIFT_GRP(1, 1)
+#undef GIFT_GRP
   };
   int per_cu = 1 << 30;
   for (const void* k : kernels) {
