@@ -11,8 +11,9 @@
 // pass between products, two (CholeskyQR2) for the Rayleigh-Ritz basis; the
 // l x l eigenproblem is solved by cyclic two-sided Jacobi (Golub & Van Loan,
 // §8.5) in fp64 in one wave, with parallel (round-robin) ordering.  The
-// first two products A X of the iteration run on the fp32 matrix cores, the
-// later ones and the Rayleigh-Ritz product Z = A Q on the fp64 ones.
+// products A X of the iteration but the last run on the fp32 matrix cores
+// (fp32 partial sums over row ranges, added in fp64), the last one and the
+// Rayleigh-Ritz product Z = A Q on the fp64 ones.
 // A is read as fp32; every other quantity is fp64 until the basis U and the
 // coefficient vectors are written as fp32.
 #include "gift_internal.hpp"
@@ -659,13 +660,19 @@ static hipError_t refresh_lowrank_lp(const float* A, int d, int k, int l, int q,
       src = out;
     }
   };
-  // The first two products on the fp32 matrix cores: what their rounding
-  // does to the basis is contracted by every exact (fp64) product after
-  // them; the last products before the Rayleigh-Ritz step stay fp64.
+  // The products of the iteration but the last on the fp32 matrix cores:
+  // their rounding only perturbs the span that the next (exact) product and
+  // orthonormalisation carry on.  The last product before the Rayleigh-Ritz
+  // basis and the Rayleigh-Ritz product stay fp64.  (Measured on the
+  // heavy-tailed 4096 x 16384 stress layer against the oracle's whitening
+  // with the factor of the same A: with every product of the iteration in
+  // fp32, codes near zero moved by up to 9 E5M2 steps; with all but the last
+  // in fp32 the codes agree exactly as with fp64 products after the first
+  // two.)
   product32(Q, Y);                    // Y = A Omega
   for (int it = 0; it < q; ++it) {
     orth(Y, Q, 1);                    // Q = orth(Y)
-    if (it == 0 && q >= 3)
+    if (it + 1 < q)
       product32(Q, Y);                // Y = A Q
     else
       product(Q, Y);
