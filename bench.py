@@ -35,6 +35,11 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFS = 2500.0
 FP64_PEAK_TFS = 78.6
 FP32_PEAK_TFS = 157.3
+# The refresh's six A X products: the last one of the subspace iteration and
+# the Rayleigh-Ritz product on the fp64 matrix cores, the other four on the
+# fp32 ones.  Its peak is the rate at which the six would run, each at its
+# own unit's peak.
+REFRESH_PEAK_TFS = 6.0 / (2.0 / FP64_PEAK_TFS + 4.0 / FP32_PEAK_TFS)
 
 
 def parse():
@@ -124,9 +129,10 @@ def main():
                   "peak": BF16_PEAK_TFS, "unit": "TFLOP/s",
                   "frac": round(stats_flop / t_stats_ms / 1e9 / BF16_PEAK_TFS, 4),
                   "work": "A += a^T a, 16384 bf16 tokens x 6144 (triangle flops)"},
-        "refresh": {"ms": round(t_refresh_ms, 4), "bound": "fp64",
-                    "achieved": round(refresh_flop / t_refresh_ms / 1e9, 2), "peak": FP64_PEAK_TFS,
-                    "unit": "TFLOP/s", "frac": round(refresh_flop / t_refresh_ms / 1e9 / FP64_PEAK_TFS, 4),
+        "refresh": {"ms": round(t_refresh_ms, 4), "bound": "mfma",
+                    "achieved": round(refresh_flop / t_refresh_ms / 1e9, 2), "peak": round(REFRESH_PEAK_TFS, 1),
+                    "unit": "TFLOP/s", "frac": round(refresh_flop / t_refresh_ms / 1e9 / REFRESH_PEAK_TFS, 4),
+                    "peak_note": "2 products at the fp64 matrix peak, 4 at the fp32 matrix peak",
                     "hbm_frac": round(refresh_bytes / (t_refresh_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                     "work": "rank-32 subspace iteration (q = 4, l = 48) on the 6144 x 6144 A"},
     }
@@ -600,8 +606,8 @@ def bench_stress(args, torch, fw, synth, dev):
         "stage_rooflines": {
             "stats": {"achieved": round(stats_flop / t_stats / 1e9, 1), "peak": BF16_PEAK_TFS, "unit": "TFLOP/s",
                       "frac": round(stats_flop / t_stats / 1e9 / BF16_PEAK_TFS, 4)},
-            "refresh": {"achieved": round(refresh_flop / t_refresh / 1e9, 2), "peak": FP64_PEAK_TFS,
-                        "unit": "TFLOP/s", "frac": round(refresh_flop / t_refresh / 1e9 / FP64_PEAK_TFS, 4)},
+            "refresh": {"achieved": round(refresh_flop / t_refresh / 1e9, 2), "peak": round(REFRESH_PEAK_TFS, 1),
+                        "unit": "TFLOP/s", "frac": round(refresh_flop / t_refresh / 1e9 / REFRESH_PEAK_TFS, 4)},
             "encode_decode_fp4": {"achieved": round(alg4 / (t_fp4 * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                                   "unit": "GB/s", "frac": round(alg4 / (t_fp4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                   "alg_bytes": int(alg4),
