@@ -177,6 +177,38 @@ def test_fused_nonfinite_rows_under_shared_amax(fw, scaling):
     assert np.array_equal(sc.cpu().numpy(), sq.ravel())
 
 
+@pytest.mark.parametrize("R", [1, 16, 64, 65])
+@pytest.mark.parametrize("scaling", ["tensor", "block"])
+def test_fused_decode_replica_count_extremes(fw, R, scaling):
+    """One replica (the run-time count), 16 (compiled, whole-tile order), 64
+    (the most whose scales the persistent decode stages) and 65 (past it:
+    the multi-kernel route) on a ragged multi-tile shape, against the
+    oracle's decode-reduce of the same payloads (Algorithm 1: dequantise,
+    average over the R workers, map back)."""
+    m, d = 100, 1000
+    print(f"[fused decode R={R} {scaling}]", flush=True)
+    fw.set_fused(True)
+    _, fac = _case(m, d, 1, seed=17)
+    _, Tinv = G.transform_lowrank(fac)
+    L = _layer_with_factor(fw, m, d, fac)
+    s = fw.SCALINGS[scaling]
+    nb = fw.nblocks(m, d, s)
+    rng = np.random.default_rng(100 + R)
+    cs = (np.arange(1, d + 1) ** -0.5).astype(np.float32)
+    codes = torch.empty(R, m, d, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(R, nb, dtype=torch.float32, device=DEV)
+    for r in range(R):
+        w = (rng.standard_normal((m, d)).astype(np.float32) * cs * (1.0 + 0.05 * r)).astype(np.float32)
+        L.encode(torch.from_numpy(w).to(DEV), 0, s, codes=codes[r], scales=scales[r])
+    out = L.decode_reduce(codes, scales, 0, s)
+    bm, bd = G.nblocks(m, d, scaling)
+    ref = G.decode_reduce([codes[r].cpu().numpy() for r in range(R)],
+                          [scales[r].cpu().numpy().reshape(bm, bd) for r in range(R)], Tinv, "e4m3", scaling)
+    err = rel_fro(out.cpu().numpy(), ref)
+    assert err <= 1e-5, f"decode rel err {err:.3e}"
+    assert L.flags() == 0
+
+
 @pytest.mark.parametrize("R", [4, 8])
 @pytest.mark.parametrize("scaling", ["tensor", "block"])
 @pytest.mark.parametrize("shape", [(200, 1544), (1536, 6144)])
