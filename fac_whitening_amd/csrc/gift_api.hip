@@ -637,14 +637,17 @@ static gift_status encode_impl(gift_layer_t L, const float* d_W, int64_t ldw, in
   // FP4 takes the amax per tensor; its block amax is taken by the quantiser
   const int amax_scaling = fp4 ? GIFT_SCALE_TENSOR : scaling;
   const int64_t nb = nblk(m, d, amax_scaling);
-  if (fused_ok(g, ldw) && !fp4) {
+  // the fused kernels take FP8 and, without error feedback, FP4 (rank-k and
+  // Euclidean transforms)
+  const bool fused_fp4 = fp4 && !d_resid && (g.transform == GIFT_LOWRANK || g.transform == GIFT_EUCLID);
+  if (fused_ok(g, ldw) && (!fp4 || fused_fp4)) {
     gift::FusedArgs a{};
     a.mode = 0;
     a.m = m;
     a.d = d;
     a.CG = fused_cg(g);
     a.fmt = fmt;
-    a.scaling = scaling;
+    a.scaling = fp4 ? GIFT_SCALE_TENSOR : scaling;   // FP4: the tensor amax (block scales in the quantiser)
 
     a.epoch = (unsigned)(++L->counters[5]);
     a.W = d_W;
@@ -663,6 +666,8 @@ static gift_status encode_impl(gift_layer_t L, const float* d_W, int64_t ldw, in
     a.amax_out = d_amax_out;
     a.codes = d_codes;
     a.scales = d_scales;
+    a.bscales = d_bscales;
+    a.tscale = d_tscale;
     a.whitened = d_whitened;
     a.resid = d_resid;
     const int grid = fused_groups(g) * a.CG;
@@ -851,6 +856,42 @@ gift_status gift_decode_reduce_fp4(gift_layer_t L, const uint8_t* d_codes, int64
   if (!L->ready) return GIFT_ERR_NOT_READY;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* work = static_cast<char*>(d_work);
+  // the fused rank-k decode streams 4 or 8 replicas' FP4 payloads
+  if (g.transform == GIFT_LOWRANK && (R == 4 || R == 8) && fused_ok(g, ldo)) {
+    gift::FusedArgs a{};
+    a.mode = 1;
+    a.m = m;
+    a.d = d;
+    a.CG = fused_cg(g);
+    a.fmt = GIFT_E2M1;
+    a.scaling = GIFT_SCALE_TENSOR;
+    a.R = R;
+    a.epoch = (unsigned)(++L->counters[6]);
+    a.lr = 1;
+    a.ub = reinterpret_cast<const uint4*>(L->state + L->sl.ub);
+    a.ua = reinterpret_cast<const uint4*>(L->state + L->sl.ua);
+    a.coef = reinterpret_cast<const float*>(L->state + L->sl.coef);
+    a.xpub = reinterpret_cast<unsigned long long*>(L->state + L->sl.xpub);
+    a.flags = reinterpret_cast<uint32_t*>(L->state + L->sl.flags);
+    a.qcodes = d_codes;
+    a.code_stride = R > 1 ? code_stride : (int64_t)m * d / 2;
+    a.qbscales = d_bscales;
+    a.bscale_stride = R > 1 ? bscale_stride : (int64_t)m * d / 16;
+    a.qtscales = d_tscales;
+    a.invR = 1.0f / (float)R;
+    a.out = d_out;
+    a.ldo = ldo;
+    const int grid = fused_groups(g) * a.CG;
+    hipError_t e = gift::order_persistent(s);
+    if (e != hipSuccess) {
+      --L->counters[6];
+      return hip_fail(e);
+    }
+    e = gift::launch_fused(a, grid, s);
+    if (e == hipSuccess) return GIFT_OK;
+    --L->counters[6];
+    return hip_fail(e);
+  }
   if (g.transform == GIFT_EUCLID) {
     GIFT_HIP(gift::launch_dequant_sum_fp4(d_codes, code_stride, d_bscales, bscale_stride, d_tscales, R, m, d, d_out,
                                           ldo, s));

@@ -54,18 +54,23 @@ struct FusedArgs {
   float* amax_out;
   uint8_t* codes;
   float* scales;
+  uint8_t* bscales;           // FP4 encode: E4M3 block scale codes [m][d / 16]
+  float* tscale;              // FP4 encode: the tensor scale [1]
   float* whitened;
   float* resid;               // error feedback: fp32 [m][d] residual, read and rewritten (NULL: none)
   const uint8_t* qcodes;
   int64_t code_stride;
   const float* qscales;
   int64_t scale_stride;
+  const uint8_t* qbscales;    // FP4 decode: block scale codes of replica r at r * bscale_stride
+  int64_t bscale_stride;
+  const float* qtscales;      // FP4 decode: tensor scales [R]
   float invR;
   float* out;
   int64_t ldo;
 };
-// Cooperative launch of a fused kernel (every workgroup resident at once, or
-// hipErrorCooperativeLaunchTooLarge and nothing runs).
+// Persistent launch of a fused kernel; the caller has checked that the grid
+// fits the kernels' occupancy (fused_resident_groups).
 hipError_t launch_fused(const FusedArgs& args, int grid, hipStream_t s);
 // Workgroups of the fused kernels the current device holds at once (0: unknown).
 int fused_resident_groups();

@@ -27,35 +27,6 @@
 
 namespace gift {
 
-constexpr int kFp4Block = 16;
-constexpr double kFp4TscaleDiv = 6.0 * 448.0;
-
-// E2M1 code of y: the magnitude is the number of decision points below |y|,
-// with the midpoints 0.25, 1.25, 2.5, 5 going down (to the even codes 0, 2,
-// 4, 6) and 0.75, 1.75, 3.5 going up (to 2, 4, 6).  +-Inf saturates to 7;
-// NaN gives +0.
-__device__ __forceinline__ uint32_t enc_e2m1(float y) {
-  const float a = __builtin_fabsf(y);
-  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
-  const uint32_t sign = (a == a) ? (__float_as_uint(y) >> 28) & 0x8u : 0u;
-  return c | sign;
-}
-
-// Value of an E2M1 code: magnitudes 0 and 1 are 0 and 0.5; k >= 2 is
-// (1 + (k & 1) / 2) 2^((k >> 1) - 1), built as a float bit pattern.
-__device__ __forceinline__ float dec_e2m1(uint32_t c) {
-  const uint32_t k = c & 7u;
-  const float v = k < 2u ? 0.5f * (float)k : __uint_as_float((((k >> 1) + 126u) << 23) | ((k & 1u) << 22));
-  return __uint_as_float(__float_as_uint(v) | ((c & 8u) << 28));
-}
-
-// g from the tensor amax (bit pattern of |x|): NaN for a non-finite amax.
-__device__ __forceinline__ float fp4_tscale(uint32_t am) {
-  if (am >= 0x7F800000u) return __uint_as_float(0x7FC00000u);
-  if (am == 0u) return 0.0f;
-  return (float)((double)__uint_as_float(am) / kFp4TscaleDiv);
-}
-
 // One lane per 16-element block: four 16-byte loads, the block amax in
 // registers, the scale arithmetic once per block, one 8-byte code store and
 // one scale byte (consecutive lanes take consecutive blocks of a row).

@@ -105,6 +105,13 @@ __device__ __forceinline__ float rowmax4(float v) {
   return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 __device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+// The same over |x| bit patterns (NaN above Inf above every finite value).
+__device__ __forceinline__ uint32_t rowumax4(uint32_t v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = umax32(p[0], p[1]);
+  const auto q = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return umax32(q[0], q[1]);
+}
 // Maximum over the wave, in every lane: rotations inside each 16-lane row
 // (DPP row_ror 8, 4, 2, 1), then the row swaps.
 __device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
@@ -210,6 +217,17 @@ __device__ __forceinline__ void dec4(uint32_t w, float* v) {
   v[3] = hi[1];
 }
 
+// Decode the 8 E2M1 codes of one 32-bit word (the low nibble of each byte
+// first) by the hardware conversion with a unit scale, which is exact.
+__device__ __forceinline__ void dec8_fp4(uint32_t w, float* v) {
+  const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  v[0] = p0[0]; v[1] = p0[1]; v[2] = p1[0]; v[3] = p1[1];
+  v[4] = p2[0]; v[5] = p2[1]; v[6] = p3[0]; v[7] = p3[1];
+}
+
 // Sub-tile i of wave w: column block cb = w + 8 (i / 3), row block rb = i % 3.
 #define SUB_RB(i) ((i) % 3)
 #define SUB_CB(i) (wave + 8 * ((i) / 3))
@@ -237,6 +255,15 @@ struct Unit {
   int32x4 v;    // 16 codes
   int32x2 t;    // 8 codes
 };
+// The same unit of an FP4 payload: 16 and 8 E2M1 codes and the E4M3 scale
+// codes of the blocks they lie in.
+struct Unit4 {
+  int32x2 v;
+  int t;
+  uint32_t sa, sb;
+};
+template <bool B, class T, class F> struct pick_t { using type = T; };
+template <class T, class F> struct pick_t<false, T, F> { using type = F; };
 
 struct CodeBuf {
   int32x4 v[kDCPT];
@@ -307,6 +334,7 @@ __device__ __forceinline__ unsigned long long tagged(unsigned tag, float v) {
 }
 
 constexpr int kXW = TR * 32;        // projection words per tile (1536)
+constexpr int kFp4Pad = TC / 2 + 16;  // LDS row stride (bytes) of a tile's FP4 codes
 // Output staging of the rank-k decode: two 48 x 256 fp32 slabs, row stride
 // kStagePad floats; the first over the per-wave partials (8 x 3 x 16 x 33
 // floats), the second after the gathered projection (48 x 33 floats).
@@ -485,15 +513,25 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
     const int fA = 16 * tid, rA = fA / TC, cA = fA % TC;
     const int fB = 8192 + 8 * tid, rB = fB / TC, cB = fB % TC;
     const bool hiA = col0 + cA + 8 < d;   // the upper 8 codes of chunk A lie inside the row
+    // FP8: code offsets (bytes) and the staged-scale entries; FP4 (d a
+    // multiple of 16, so chunk A is one whole scale block): code offsets
+    // (two codes a byte) and the offsets of the two blocks' scale bytes
     int offA[3], offB[3], sA[3], sB[3];
 #pragma unroll
     for (int rb = 0; rb < 3; ++rb) {
       const int ra = row0 + 16 * rb + rA, rbw = row0 + 16 * rb + rB;
       const bool okA = ra < m && col0 + cA < d, okB = rbw < m && col0 + cB < d;
-      offA[rb] = okA ? ra * d + col0 + cA : kOff;
-      offB[rb] = okB ? rbw * d + col0 + cB : kOff;
-      sA[rb] = (PT || !okA) ? 0 : (ra / kBlock - rb0) * 6 + (col0 + cA) / kBlock - cb0;
-      sB[rb] = (PT || !okB) ? 0 : (rbw / kBlock - rb0) * 6 + (col0 + cB) / kBlock - cb0;
+      if constexpr (FMT == 2) {
+        offA[rb] = okA ? (ra * d + col0 + cA) >> 1 : kOff;
+        offB[rb] = okB ? (rbw * d + col0 + cB) >> 1 : kOff;
+        sA[rb] = okA ? ra * (d / kFp4Block) + (col0 + cA) / kFp4Block : kOff;
+        sB[rb] = okB ? rbw * (d / kFp4Block) + (col0 + cB) / kFp4Block : kOff;
+      } else {
+        offA[rb] = okA ? ra * d + col0 + cA : kOff;
+        offB[rb] = okB ? rbw * d + col0 + cB : kOff;
+        sA[rb] = (PT || !okA) ? 0 : (ra / kBlock - rb0) * 6 + (col0 + cA) / kBlock - cb0;
+        sB[rb] = (PT || !okB) ? 0 : (rbw / kBlock - rb0) * 6 + (col0 + cB) / kBlock - cb0;
+      }
     }
     if constexpr (!PT) {
       // the last wave stages the block scales before its code stream starts
@@ -507,13 +545,24 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
     }
     // the projection operands first (loads complete in order)
     load_uops(a.ub, d, cbg0, uo);
-    Unit buf[kPipeDepth];
-    auto issue = [&](int u, Unit& U) {
+    using UnitT = typename pick_t<FMT == 2, Unit4, Unit>::type;
+    UnitT buf[kPipeDepth];
+    auto issue = [&](int u, UnitT& U) {
       const int rb = u / RC, r = u % RC;
       const bool in = u < NU;
-      const auto q = make_rsrc(a.qcodes + (in ? (int64_t)r * a.code_stride : 0), in ? (int64_t)m * d : 0);
-      U.v = __builtin_amdgcn_raw_buffer_load_b128(q, in ? offA[rb < 3 ? rb : 2] : kOff, 0, kNT);
-      U.t = __builtin_amdgcn_raw_buffer_load_b64(q, in ? offB[rb < 3 ? rb : 2] : kOff, 0, kNT);
+      if constexpr (FMT == 2) {
+        const auto q = make_rsrc(a.qcodes + (in ? (int64_t)r * a.code_stride : 0), in ? (int64_t)m * d / 2 : 0);
+        const auto qs = make_rsrc(a.qbscales + (in ? (int64_t)r * a.bscale_stride : 0),
+                                  in ? (int64_t)m * d / kFp4Block : 0);
+        U.v = __builtin_amdgcn_raw_buffer_load_b64(q, in ? offA[rb < 3 ? rb : 2] : kOff, 0, kNT);
+        U.t = __builtin_amdgcn_raw_buffer_load_b32(q, in ? offB[rb < 3 ? rb : 2] : kOff, 0, kNT);
+        U.sa = __builtin_amdgcn_raw_buffer_load_b8(qs, in ? sA[rb < 3 ? rb : 2] : kOff, 0, 0);
+        U.sb = __builtin_amdgcn_raw_buffer_load_b8(qs, in ? sB[rb < 3 ? rb : 2] : kOff, 0, 0);
+      } else {
+        const auto q = make_rsrc(a.qcodes + (in ? (int64_t)r * a.code_stride : 0), in ? (int64_t)m * d : 0);
+        U.v = __builtin_amdgcn_raw_buffer_load_b128(q, in ? offA[rb < 3 ? rb : 2] : kOff, 0, kNT);
+        U.t = __builtin_amdgcn_raw_buffer_load_b64(q, in ? offB[rb < 3 ? rb : 2] : kOff, 0, kNT);
+      }
     };
 #pragma unroll
     for (int u = 0; u < kPipeDepth; ++u) issue(u, buf[u]);
@@ -523,15 +572,26 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int rb = u / RC, r = u % RC;
-      Unit& U = buf[u % kPipeDepth];
+      UnitT& U = buf[u % kPipeDepth];
       {
-        const float sa = PT ? a.qscales[(int64_t)r * a.scale_stride] : ssc[r][sA[rb]];
-        const float sb = PT ? sa : ssc[r][sB[rb]];
-        float va[16], vb[8];
+        float sa, sb, va[16], vb[8];
+        if constexpr (FMT == 2) {
+          // S_b = fp32(dec(sc_b) g_r); the E2M1 codes converted exactly by
+          // the hardware (unit scale), the low nibble the even column
+          const float gr = a.qtscales[r];
+          sa = dec_e4m3(U.sa) * gr;
+          sb = dec_e4m3(U.sb) * gr;
+          dec8_fp4((uint32_t)U.v[0], va);
+          dec8_fp4((uint32_t)U.v[1], va + 8);
+          dec8_fp4((uint32_t)U.t, vb);
+        } else {
+          sa = PT ? a.qscales[(int64_t)r * a.scale_stride] : ssc[r][sA[rb]];
+          sb = PT ? sa : ssc[r][sB[rb]];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) dec4<FMT>((w < 2 || hiA) ? (uint32_t)U.v[w] : 0u, va + 4 * w);
-        dec4<FMT>((uint32_t)U.t[0], vb);
-        dec4<FMT>((uint32_t)U.t[1], vb + 4);
+          for (int w = 0; w < 4; ++w) dec4<FMT>((w < 2 || hiA) ? (uint32_t)U.v[w] : 0u, va + 4 * w);
+          dec4<FMT>((uint32_t)U.t[0], vb);
+          dec4<FMT>((uint32_t)U.t[1], vb + 4);
+        }
 #pragma unroll
         for (int k = 0; k < 16; ++k) accA[k] = r == 0 ? sa * va[k] : accA[k] + sa * va[k];
 #pragma unroll
@@ -1047,7 +1107,21 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
   // the workgroup holding a block's top-left sub-tile writes its scale and
   // local amax
   const float fmax = fp8_fmax(FMT);
-  if (tid < 12 && (!pts || tid == 0)) {
+  if constexpr (FMT == 2) {
+    // FP4: the tensor scale g = fp32(amax_T / 2688) from the tensor amax
+    // (local, or the shared one); the block scales follow per 16 elements
+    if (tid == 0) {
+      const uint32_t local = blk[0][0];
+      const bool bad = s_bad != 0;
+      const uint32_t am = bad ? 0x7FC00000u : (a.amax_in ? absbits_f(a.amax_in[0]) : local);
+      sss[0] = fp4_tscale(am);
+      if (g == 0) {
+        if (a.tscale) a.tscale[0] = sss[0];
+        if (a.amax_out) a.amax_out[0] = bad ? __builtin_nanf("") : __uint_as_float(local);
+        if (am >= 0x7F800000u) atomicOr(a.flags, (unsigned)GIFT_FLAG_NONFINITE);
+      }
+    }
+  } else if (tid < 12 && (!pts || tid == 0)) {
     const int br = rb0 + tid / 6, bc = cb0 + tid % 6;
     // blocks rb0 and cb0 .. cb0 + 5 always meet the tile; rb0 + 1 may not
     const bool inside = br * kBlock < m && bc * kBlock < d && br * kBlock < row0 + TR;
@@ -1116,6 +1190,47 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
       __builtin_amdgcn_raw_buffer_store_b128(o1, rr, (row < m && c + 16 < d) ? o + 64 : kOff, 0, kNT);
     }
   };
+  if constexpr (FMT == 2) {
+    // FP4: a sub-tile row's 32 columns are two 16-element blocks, each held
+    // by the four lanes of the row (columns 4 lg .. 4 lg + 3 of it); their
+    // amax over |x| bits (NaN on top), sig = fp32(amax_b / 6g), the E4M3
+    // block scale, r_b = fp32(1 / S_b), and four E2M1 codes per lane and
+    // block into the tile memory (rows of 384 bytes, the even column in the
+    // low nibble).  A NaN block (or tensor) scale gives zero codes.
+    const float gt = sss[0];
+    const int bpr = d / kFp4Block;
+#pragma unroll
+    for (int i = 0; i < NSUB; ++i) {
+      if (!live[i / 3]) continue;
+      const int rbl = SUB_RB(i), cbl = SUB_CB(i);
+      const int row = row0 + rbl * 16 + lr;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t mb = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) mb = umax32(mb, absbits_f(x[i][4 * h + k]));
+        mb = rowumax4(mb);
+        float sig;
+        if (gt != gt) sig = __builtin_nanf("");
+        else if (gt == 0.0f) sig = 0.0f;
+        else sig = (float)((double)__uint_as_float(mb) / (6.0 * (double)gt));
+        const uint32_t sc = enc_e4m3(sig);
+        const float S = dec_e4m3(sc) * gt;
+        const bool bb = S != S;
+        const float rb_ = S > 0.0f ? (float)(1.0 / (double)S) : 0.0f;
+        uint32_t w = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w |= (bb ? 0u : enc_e2m1(x[i][4 * h + k] * rb_)) << (4 * k);
+        const int cb = cbl * 32 + 16 * h;   // the block's first column in the tile
+        *reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(smem) + (rbl * 16 + lr) * kFp4Pad + (cb >> 1) +
+                                     2 * lg) = (uint16_t)w;
+        if (lg == 0 && row < m && col0 + cb < d) {
+          a.bscales[(int64_t)row * bpr + (col0 + cb) / kFp4Block] = (uint8_t)sc;
+          if (bb && gt == gt) atomicOr(a.flags, (unsigned)GIFT_FLAG_NONFINITE);
+        }
+      }
+    }
+  } else {
   // Per tensor with a finite amax and no non-finite element in the wave's
   // sub-tiles (the usual case, one uniform test): one scale pair for every
   // sub-tile and no per-sub-tile branches.
@@ -1155,7 +1270,22 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
       emit(i, q0, q1, sss[e]);
     }
   }
+  }   // FP8
   __syncthreads();
+  if constexpr (FMT == 2) {
+    // FP4 codes: 48 rows of 384 bytes, in 8-byte pieces (16 columns each)
+    const auto cr = make_rsrc(a.codes, (int64_t)m * (d / 2));
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      const int q = tid + 512 * j;
+      if (q >= TR * (TC / 16)) break;
+      const int r = q / (TC / 16), c16 = q % (TC / 16);
+      const bool ok = row0 + r < m && col0 + 16 * c16 < d;
+      const int32x2 v = *reinterpret_cast<const int32x2*>(reinterpret_cast<const uint8_t*>(smem) + r * kFp4Pad + 8 * c16);
+      __builtin_amdgcn_raw_buffer_store_b64(v, cr, ok ? ((row0 + r) * d + col0) / 2 + 8 * c16 : kOff, 0, kNT);
+    }
+    return;
+  }
   const auto cr = make_rsrc(a.codes, (int64_t)m * d);
 #pragma unroll
   for (int j = 0; j < kCPT; ++j) {
@@ -1265,7 +1395,18 @@ static hipError_t launch_encode(const FusedArgs& a, int grid, hipStream_t s) {
 
 hipError_t launch_fused(const FusedArgs& a, int grid, hipStream_t s) {
   hipError_t e;
-  if (a.mode == 0) {
+  if (a.fmt == 2) {
+    // FP4 (tensor amax, 16-element block scales): the encode without error
+    // feedback; the rank-k decode at 4 or 8 replicas
+    if (a.mode == 0) {
+      if (a.resid) return hipErrorInvalidValue;
+      e = a.lr ? persistent_launch(k_rank_encode<2, 0>, grid, a, s) : persistent_launch(k_euclid_encode<2, 0>, grid, a, s);
+    } else {
+      if (!a.lr || (a.R != 4 && a.R != 8)) return hipErrorInvalidValue;
+      e = a.R == 4 ? persistent_launch(k_rank_decode<2, 4, 0>, grid, a, s)
+                   : persistent_launch(k_rank_decode<2, 8, 0>, grid, a, s);
+    }
+  } else if (a.mode == 0) {
     e = a.scaling == 0 ? launch_encode<0>(a, grid, s) : launch_encode<1>(a, grid, s);
   } else if (a.fmt == 0) {
     e = a.lr ? launch_decode<0, true>(a, grid, s) : launch_decode<0, false>(a, grid, s);
@@ -1338,8 +1479,11 @@ int fused_resident_groups() {
   reinterpret_cast<const void*>(k_rank_group<F, true, 0, S>), reinterpret_cast<const void*>(k_rank_group<F, false, 4, S>), \
       reinterpret_cast<const void*>(k_rank_group<F, false, 8, S>),                                                \
       reinterpret_cast<const void*>(k_rank_group<F, false, 16, S>), reinterpret_cast<const void*>(k_rank_group<F, false, 0, S>)
-      GIFT_GRP(0, 0), GIFT_GRP(0, 1), GIFT_GRP(1, 0), GIFT_GRP(1, 1)
+      GIFT_GRP(0, 0), GIFT_GRP(0, 1), GIFT_GRP(1, 0), GIFT_GRP(1, 1),
 #undef GIFT_GRP
+      // the FP4 payload
+      reinterpret_cast<const void*>(k_rank_encode<2, 0>), reinterpret_cast<const void*>(k_euclid_encode<2, 0>),
+      reinterpret_cast<const void*>(k_rank_decode<2, 4, 0>), reinterpret_cast<const void*>(k_rank_decode<2, 8, 0>)
   };
   int per_cu = 1 << 30;
   for (const void* k : kernels) {
