@@ -1196,7 +1196,12 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
     // amax over |x| bits (NaN on top), sig = fp32(amax_b / 6g), the E4M3
     // block scale, r_b = fp32(1 / S_b), and four E2M1 codes per lane and
     // block into the tile memory (rows of 384 bytes, the even column in the
-    // low nibble).  A NaN block (or tensor) scale gives zero codes.
+    // low nibble).  A NaN block (or tensor) scale gives zero codes.  The
+    // codes come from the hardware conversion at unit scale, which rounds
+    // as the encoder does (to nearest, ties to the even code, saturating at
+    // 6, both signs of zero kept) for every non-NaN input; a NaN product,
+    // which it would saturate, is replaced by +0 first, the encoder's code
+    // for NaN.
     const float gt = sss[0];
     const int bpr = d / kFp4Block;
 #pragma unroll
@@ -1217,10 +1222,16 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
         const uint32_t sc = enc_e4m3(sig);
         const float S = dec_e4m3(sc) * gt;
         const bool bb = S != S;
-        const float rb_ = S > 0.0f ? (float)(1.0 / (double)S) : 0.0f;
-        uint32_t w = 0;
+        const float rb_ = S > 0.0f ? 1.0f / S : 0.0f;
+        float y[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) w |= (bb ? 0u : enc_e2m1(x[i][4 * h + k] * rb_)) << (4 * k);
+        for (int k = 0; k < 4; ++k) {
+          const float t = x[i][4 * h + k] * rb_;
+          y[k] = t == t ? t : 0.0f;
+        }
+        uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[0], y[1], 1.0f, 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], 1.0f, 1);
+        w = bb ? 0u : w;
         const int cb = cbl * 32 + 16 * h;   // the block's first column in the tile
         *reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(smem) + (rbl * 16 + lr) * kFp4Pad + (cb >> 1) +
                                      2 * lg) = (uint16_t)w;

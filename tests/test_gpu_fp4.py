@@ -183,6 +183,42 @@ def test_fp4_nonfinite(fw):
     L.close()
 
 
+@pytest.mark.parametrize("kind", ["euclid", "lowrank"])
+@pytest.mark.parametrize("share", ["finite", "zero"])
+def test_fp4_nonfinite_under_shared_amax(fw, kind, share):
+    """Inf, -Inf and NaN elements at 1536 x 6144 (the persistent encode)
+    under a finite shared amax (1.5x the finite local one) or a zero one:
+    codes, block scales and tensor scale bit for bit against the oracle on
+    the GPU's own W~.  An Inf block saturates its scale and its own codes;
+    a NaN block takes the NaN scale and zero codes; under a zero amax every
+    code is a signed zero (an Inf times the zero reciprocal gives +0).  The
+    flag is raised exactly where a finite tensor scale meets a NaN block
+    scale."""
+    m, d = 1536, 6144
+    print(f"[fp4 non-finite {kind} shared amax {share}]", flush=True)
+    rng = np.random.default_rng(91)
+    L = _layer(fw, kind, m, d, seed=5)
+    w = _grad(m, d, rng)
+    finite_amax = float(np.abs(w).max())
+    w[3, 17] = np.inf
+    w[700, 6000] = -np.inf
+    w[1535, 40] = np.nan
+    w[48, 767] = np.inf                       # the last column of a tile
+    amax_in = torch.tensor([1.5 * finite_amax if share == "finite" else 0.0], dtype=torch.float32, device=DEV)
+    wh = torch.empty(m, d, device=DEV)
+    codes, bsc, tsc = L.encode_fp4(torch.from_numpy(w).to(DEV), amax_in=amax_in, whitened=wh)
+    torch.cuda.synchronize()
+    ref = G.quantize_fp4(wh.cpu().numpy(), amax_in=amax_in.cpu().numpy())
+    assert np.array_equal(codes.cpu().numpy(), fp4.pack(ref["codes"]))
+    assert np.array_equal(bsc.cpu().numpy(), ref["bscales"])
+    assert tsc.item() == ref["tscale"]
+    flag = bool(np.isfinite(ref["tscale"])) and bool(((ref["bscales"] & 0x7F) == 0x7F).any())
+    assert bool(L.flags() & fw.FLAG_NONFINITE) == flag
+    if share == "finite":
+        assert flag
+    L.close()
+
+
 def test_fp4_argument_checks(fw):
     """d_in not a multiple of 16 and E2M1 through the FP8 call are refused
     before anything is enqueued."""
