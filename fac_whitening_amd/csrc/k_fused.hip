@@ -41,6 +41,8 @@
 //  * Tags derive from per-direction call counters that only grow, so
 //    nothing is reset between calls.  Every wait is bounded; a timeout sets
 //    GIFT_FLAG_SPIN_TIMEOUT and the kernel still exits.
+#include <type_traits>
+
 #include "fp8_codec.hpp"
 #include "gift_internal.hpp"
 
@@ -105,12 +107,17 @@ __device__ __forceinline__ float rowmax4(float v) {
   return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 __device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
-// The same over |x| bit patterns (NaN above Inf above every finite value).
-__device__ __forceinline__ uint32_t rowumax4(uint32_t v) {
-  const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  v = umax32(p[0], p[1]);
-  const auto q = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  return umax32(q[0], q[1]);
+// 4 x 4 transpose over the lanes of a row: with r[k] of lane l + 16 s
+// called M[s][k] (l < 16), afterwards r[k] of lane l + 16 s holds M[k][s].
+// Two stages of row swaps on register pairs: the 32-lane halves of (r0, r2)
+// and (r1, r3), then the neighbouring 16-lane rows of (r0, r1) and (r2, r3).
+__device__ __forceinline__ void quad_transpose(uint32_t (&r)[4]) {
+  auto p = __builtin_amdgcn_permlane32_swap(r[0], r[2], false, false);
+  auto q = __builtin_amdgcn_permlane32_swap(r[1], r[3], false, false);
+  r[0] = p[0]; r[2] = p[1]; r[1] = q[0]; r[3] = q[1];
+  p = __builtin_amdgcn_permlane16_swap(r[0], r[1], false, false);
+  q = __builtin_amdgcn_permlane16_swap(r[2], r[3], false, false);
+  r[0] = p[0]; r[1] = p[1]; r[2] = q[0]; r[3] = q[1];
 }
 // Maximum over the wave, in every lane: rotations inside each 16-lane row
 // (DPP row_ror 8, 4, 2, 1), then the row swaps.
@@ -1191,56 +1198,87 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
     }
   };
   if constexpr (FMT == 2) {
-    // FP4: a sub-tile row's 32 columns are two 16-element blocks, each held
-    // by the four lanes of the row (columns 4 lg .. 4 lg + 3 of it); their
-    // amax over |x| bits (NaN on top), sig = fp32(amax_b / 6g), the E4M3
-    // block scale, r_b = fp32(1 / S_b), and four E2M1 codes per lane and
-    // block into the tile memory (rows of 384 bytes, the even column in the
-    // low nibble).  A NaN block (or tensor) scale gives zero codes.  The
+    // FP4: a sub-tile row's 32 columns are two 16-element blocks (block
+    // j = 2 i + h of sub-tile i), each held by the four lanes of the row,
+    // columns 4 lg .. 4 lg + 3 of it.  Blocks go in groups of four: each
+    // lane forms its partial amax over |x| bits (NaN on top) of the four,
+    // a transpose over the row's lanes hands lane lg the four partials of
+    // the group's block lg, and that lane alone forms the block amax, sig =
+    // fp32(amax_b / 6g), the E4M3 block scale (which it stores) and r_b =
+    // fp32(1 / S_b), NaN for a NaN block scale.  A transpose of the r_b,
+    // replicated, gives every lane of the row the group's four.  The E2M1
     // codes come from the hardware conversion at unit scale, which rounds
     // as the encoder does (to nearest, ties to the even code, saturating at
-    // 6, both signs of zero kept) for every non-NaN input; a NaN product,
-    // which it would saturate, is replaced by +0 first, the encoder's code
-    // for NaN.
+    // 6, both signs of zero kept) for every non-NaN input; where a product
+    // x r_b can be NaN in the wave (a non-finite x, an infinite or NaN r_b)
+    // NaN products are set to +0 first, the encoder's code for NaN and
+    // the zero codes of a NaN block scale.  Four codes per lane and block
+    // go into the tile memory (rows of 384 bytes, the even column in the
+    // low nibble).
     const float gt = sss[0];
     const int bpr = d / kFp4Block;
+    constexpr int NG = (2 * NSUB + 3) / 4;
+    float rbs[NG][4];
+    bool risky = false;
 #pragma unroll
-    for (int i = 0; i < NSUB; ++i) {
-      if (!live[i / 3]) continue;
-      const int rbl = SUB_RB(i), cbl = SUB_CB(i);
-      const int row = row0 + rbl * 16 + lr;
+    for (int g4 = 0; g4 < NG; ++g4) {
+      uint32_t r[4];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int k = 0; k < 4; ++k) {
+        const int j = 4 * g4 + k;
         uint32_t mb = 0;
+        if (j < 2 * NSUB) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) mb = umax32(mb, absbits_f(x[i][4 * h + k]));
-        mb = rowumax4(mb);
-        float sig;
-        if (gt != gt) sig = __builtin_nanf("");
-        else if (gt == 0.0f) sig = 0.0f;
-        else sig = (float)((double)__uint_as_float(mb) / (6.0 * (double)gt));
-        const uint32_t sc = enc_e4m3(sig);
-        const float S = dec_e4m3(sc) * gt;
-        const bool bb = S != S;
-        const float rb_ = S > 0.0f ? 1.0f / S : 0.0f;
-        float y[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float t = x[i][4 * h + k] * rb_;
-          y[k] = t == t ? t : 0.0f;
+          for (int e = 0; e < 4; ++e) mb = umax32(mb, absbits_f(x[j >> 1][4 * (j & 1) + e]));
         }
-        uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[0], y[1], 1.0f, 0);
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], 1.0f, 1);
-        w = bb ? 0u : w;
-        const int cb = cbl * 32 + 16 * h;   // the block's first column in the tile
-        *reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(smem) + (rbl * 16 + lr) * kFp4Pad + (cb >> 1) +
-                                     2 * lg) = (uint16_t)w;
-        if (lg == 0 && row < m && col0 + cb < d) {
-          a.bscales[(int64_t)row * bpr + (col0 + cb) / kFp4Block] = (uint8_t)sc;
-          if (bb && gt == gt) atomicOr(a.flags, (unsigned)GIFT_FLAG_NONFINITE);
+        r[k] = mb;
+      }
+      quad_transpose(r);
+      const uint32_t mb = umax32(umax32(r[0], r[1]), umax32(r[2], r[3]));
+      float sig;
+      if (gt != gt) sig = __builtin_nanf("");
+      else if (gt == 0.0f) sig = 0.0f;
+      else sig = (float)((double)__uint_as_float(mb) / (6.0 * (double)gt));
+      const uint32_t sc = enc_e4m3(sig);
+      const float S = dec_e4m3(sc) * gt;
+      const float rb_ = S != S ? S : (S > 0.0f ? 1.0f / S : 0.0f);
+      risky = risky || mb >= 0x7F800000u || !(__builtin_fabsf(rb_) < __builtin_inff());
+      const int j = 4 * g4 + lg, i = j >> 1;
+      const int row = row0 + (i % 3) * 16 + lr, col = col0 + (wave + 8 * (i / 3)) * 32 + 16 * (j & 1);
+      if (j < 2 * NSUB && row < m && col < d) {
+        a.bscales[(int64_t)row * bpr + col / kFp4Block] = (uint8_t)sc;
+        if (S != S && gt == gt) atomicOr(a.flags, (unsigned)GIFT_FLAG_NONFINITE);
+      }
+      uint32_t bq[4] = {__float_as_uint(rb_), __float_as_uint(rb_), __float_as_uint(rb_), __float_as_uint(rb_)};
+      quad_transpose(bq);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) rbs[g4][k] = __uint_as_float(bq[k]);
+    }
+    auto codes = [&](auto fix) {
+#pragma unroll
+      for (int i = 0; i < NSUB; ++i) {
+        if (!live[i / 3]) continue;
+        const int rbl = SUB_RB(i), cbl = SUB_CB(i);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int j = 2 * i + h;
+          const float rb_ = rbs[j >> 2][j & 3];
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float t = x[i][4 * h + e] * rb_;
+            y[e] = (!decltype(fix)::value || t == t) ? t : 0.0f;
+          }
+          uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[0], y[1], 1.0f, 0);
+          w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], 1.0f, 1);
+          const int cb = cbl * 32 + 16 * h;   // the block's first column in the tile
+          *reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(smem) + (rbl * 16 + lr) * kFp4Pad + (cb >> 1) +
+                                       2 * lg) = (uint16_t)w;
         }
       }
-    }
+    };
+    if (__any(risky)) codes(std::true_type{});
+    else codes(std::false_type{});
   } else {
   // Per tensor with a finite amax and no non-finite element in the wave's
   // sub-tiles (the usual case, one uniform test): one scale pair for every
