@@ -260,6 +260,39 @@ def main():
 
     t_other = _event_ms(torch, unit_other, args.steps)
     del bsets
+
+    # the same unit with the FP4 payload (E2M1 codes, an E4M3 scale per 16
+    # elements of a row, one fp32 tensor scale), over its own rotating sets
+    c4s, b4s, t4s = (torch.empty(R, m, d // 2, dtype=torch.uint8, device=dev),
+                     torch.empty(R, m, d // 16, dtype=torch.uint8, device=dev),
+                     torch.empty(R, dtype=torch.float32, device=dev))
+    for r in range(1, R):
+        L.encode_fp4(case.W[r], codes=c4s[r], bscales=b4s[r], tscale=t4s[r:r + 1])
+    fsets = [(c4s.clone(), b4s.clone(), t4s.clone()) for _ in sets]
+    del c4s, b4s, t4s
+    fturn = [0]
+
+    def fp4_part(i, e, dcd):
+        W, _, _, out = sets[i % len(sets)]
+        c4, b4, t4 = fsets[i % len(sets)]
+        if e:
+            L.encode_fp4(W, codes=c4[0], bscales=b4[0], tscale=t4[0:1])
+        if dcd:
+            L.decode_reduce_fp4(c4, b4, t4, out=out)
+
+    def fp4_unit():
+        fp4_part(fturn[0], True, True)
+        fturn[0] += 1
+
+    t_fp4 = _event_ms(torch, fp4_unit, args.steps)
+    t_fp4_enc = batch_ms(lambda i: fp4_part(i, True, False))
+    t_fp4_dec = batch_ms(lambda i: fp4_part(i, False, True))
+    torch.cuda.synchronize()
+    assert L.flags() == 0
+    del fsets
+    pay4 = m * d // 2 + m * d // 16 + 4
+    enc4_bytes = 4.0 * m * d + u_bytes + pay4
+    dec4_bytes = R * pay4 + u_bytes + 4.0 * m * d
     csrc = torch.ones(64 << 20, dtype=torch.float32, device=dev)
     cdst = torch.empty_like(csrc)
     t_copy = _event_ms(torch, lambda: torch.neg(csrc, out=cdst), 10)
@@ -274,6 +307,13 @@ def main():
         ("block128" if other == fw.SCALE_BLOCK128 else "tensor"): {
             "ms_per_step": round(t_other, 5), "GB_s_of_grad": round(grad_bytes / (t_other * 1e-3) / 1e9, 1),
             "cache": f"cold ({args.sets} rotating buffer sets)"},
+        "fp4": {"ms_per_step": round(t_fp4, 5), "GB_s_of_grad": round(grad_bytes / (t_fp4 * 1e-3) / 1e9, 1),
+                "unit_frac": round((enc4_bytes + dec4_bytes) / (t_fp4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "encode_ms": round(t_fp4_enc, 5), "decode_ms": round(t_fp4_dec, 5),
+                "decode_frac": round(dec4_bytes / (t_fp4_dec * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "alg_bytes_encode": int(enc4_bytes), "alg_bytes_decode": int(dec4_bytes),
+                "work": "E2M1 codes with E4M3 scales per 16 elements of a row; encode of replica 0, "
+                        "decode-reduce of the 8 payloads", "cache": f"cold ({args.sets} rotating buffer sets)"},
         "copy_ceiling": {"kernel": "torch.neg, 64 Mi fp32 (256 MiB read + 256 MiB written)",
                          "GB_s": round(copy_gbs, 1), "frac_of_peak": round(copy_gbs / HBM_PEAK_GBS, 4),
                          "unit_frac_of_copy": round((enc_bytes + dec_bytes) / (ms_per_step * 1e-3) / 1e9 / copy_gbs,

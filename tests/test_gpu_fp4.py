@@ -111,11 +111,11 @@ def test_fp4_encode_stage_isolated(fw, kind, shape, ef):
 def test_fp4_decode_reduce(fw, kind, shape, R):
     """The mean of R FP4 payloads mapped back: Euclidean within the fp32
     rounding of the sum; rank-32 with the oracle's factor in the layer state
-    and the oracle's inverse transform (at 4 and 8 replicas the persistent
-    decode, which streams the payloads block by block; otherwise the
-    multi-kernel route).  d = 1008 (not a multiple of 32) takes the
+    and the oracle's inverse transform (at 4, 8 and 16 replicas the
+    persistent decode, which streams the payloads block by block; otherwise
+    the multi-kernel route).  d = 1008 (not a multiple of 32) takes the
     16-codes-per-lane decoder."""
-    if shape == (1536, 6144) and R not in (4, 8):
+    if shape == (1536, 6144) and R not in (4, 8, 16):
         pytest.skip("the full layer is checked on the persistent decode's replica counts")
     m, d = shape
     print(f"[fp4 decode {kind} {shape} R={R}]", flush=True)
