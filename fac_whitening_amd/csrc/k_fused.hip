@@ -515,7 +515,8 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
     // Units (row block rb, replica r), rb-major; a unit is the block's
     // 16 x 768 codes of one replica: the 16-byte chunk at byte 16 t and the
     // 8-byte chunk at 8192 + 8 t of thread t (768 = 48 x 16: a 16-byte
-    // chunk never crosses a row).  kPipeDepth units in flight.
+    // chunk never crosses a row).  kPipeDepth units in flight (FP8), twice
+    // as many of the half-size FP4 units.
     constexpr int NU = 3 * RC;
     constexpr bool PT = SC == 0;
     const int fA = 16 * tid, rA = fA / TC, cA = fA % TC;
@@ -554,7 +555,9 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
     // the projection operands first (loads complete in order)
     load_uops(a.ub, d, cbg0, uo);
     using UnitT = typename pick_t<FMT == 2, Unit4, Unit>::type;
-    UnitT buf[kPipeDepth];
+    // FP4 units are half the bytes: twice as many in flight
+    constexpr int PD = FMT == 2 ? 2 * kPipeDepth : kPipeDepth;
+    UnitT buf[PD];
     auto issue = [&](int u, UnitT& U) {
       const int rb = u / RC, r = u % RC;
       const bool in = u < NU;
@@ -573,14 +576,14 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
       }
     };
 #pragma unroll
-    for (int u = 0; u < kPipeDepth; ++u) issue(u, buf[u]);
+    for (int u = 0; u < PD; ++u) issue(u, buf[u]);
     if constexpr (!PT) __syncthreads();   // the staged scales are visible
     float accA[16], accB[8];
     const float ir = a.invR;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int rb = u / RC, r = u % RC;
-      UnitT& U = buf[u % kPipeDepth];
+      UnitT& U = buf[u % PD];
       {
         float sa, sb, va[16], vb[8];
         if constexpr (FMT == 2) {
@@ -605,7 +608,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
 #pragma unroll
         for (int k = 0; k < 8; ++k) accB[k] = r == 0 ? sb * vb[k] : accB[k] + sb * vb[k];
       }
-      issue(u + kPipeDepth, U);   // past the last unit: an empty buffer resource, no memory traffic
+      issue(u + PD, U);   // past the last unit: an empty buffer resource, no memory traffic
       if (r == RC - 1) {
         // the block's mean into its rows of the tile, then its projection
         float* da = smem + (16 * rb + rA) * kTilePad + cA;
