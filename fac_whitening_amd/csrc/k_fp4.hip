@@ -220,6 +220,65 @@ __global__ void __launch_bounds__(256) k_dequant_sum_fp4(const uint8_t* __restri
   }
 }
 
+// The same with a compile-time replica count RC: the RC replicas' codes and
+// scale bytes of a row are all in flight together (not replica 0 alone,
+// then groups of four), and the tensor scales are read once per band.  The
+// sums are formed in the same order, so the results are identical.
+template <int V, int RC>
+__global__ void __launch_bounds__(256) k_dequant_sum_fp4_rc(const uint8_t* __restrict__ codes, int64_t code_stride,
+                                                            const uint8_t* __restrict__ bscales, int64_t bscale_stride,
+                                                            const float* __restrict__ tscales, int m, int d,
+                                                            float* __restrict__ out, int64_t ldo, float invR) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = blockIdx.x * (64 * V) + lane * V;
+  const int r0 = blockIdx.y * kDq4Rows;
+  const int r1 = min(m, r0 + kDq4Rows);
+  if (col >= d) return;   // d is a multiple of V: a lane's codes are all in range
+  float ts[RC];
+#pragma unroll
+  for (int r = 0; r < RC; ++r) ts[r] = tscales[r];
+  for (int row = r0 + wave; row < r1; row += 4) {
+    const uint8_t* cp = codes + (int64_t)row * (d >> 1) + (col >> 1);
+    const uint8_t* sp = bscales + (int64_t)row * (d / kFp4Block) + col / kFp4Block;
+    Fp4Vec<V> c[RC];
+#pragma unroll
+    for (int r = 0; r < RC; ++r) c[r] = load_fp4<V>(cp + (int64_t)r * code_stride, sp + (int64_t)r * bscale_stride);
+    float a[V];
+    acc_fp4<V, true>(c[0], ts[0], a);
+#pragma unroll
+    for (int r = 1; r < RC; ++r) acc_fp4<V, false>(c[r], ts[r], a);
+    float* o = out + (int64_t)row * ldo + col;
+#pragma unroll
+    for (int k = 0; k < V / 4; ++k)
+      *reinterpret_cast<float4*>(o + 4 * k) =
+          make_float4(a[4 * k] * invR, a[4 * k + 1] * invR, a[4 * k + 2] * invR, a[4 * k + 3] * invR);
+  }
+}
+
+template <int V>
+static void launch_dq4(const uint8_t* codes, int64_t code_stride, const uint8_t* bscales, int64_t bscale_stride,
+                       const float* tscales, int R, int m, int d, float* out, int64_t ldo, float invR,
+                       hipStream_t s) {
+  dim3 grid((unsigned)cdiv(d, 64 * V), (unsigned)cdiv(m, kDq4Rows));
+  switch (R) {
+    case 4:
+      hipLaunchKernelGGL((k_dequant_sum_fp4_rc<V, 4>), grid, dim3(256), 0, s, codes, code_stride, bscales,
+                         bscale_stride, tscales, m, d, out, ldo, invR);
+      break;
+    case 8:
+      hipLaunchKernelGGL((k_dequant_sum_fp4_rc<V, 8>), grid, dim3(256), 0, s, codes, code_stride, bscales,
+                         bscale_stride, tscales, m, d, out, ldo, invR);
+      break;
+    case 16:
+      hipLaunchKernelGGL((k_dequant_sum_fp4_rc<V, 16>), grid, dim3(256), 0, s, codes, code_stride, bscales,
+                         bscale_stride, tscales, m, d, out, ldo, invR);
+      break;
+    default:
+      hipLaunchKernelGGL(k_dequant_sum_fp4<V>, grid, dim3(256), 0, s, codes, code_stride, bscales, bscale_stride,
+                         tscales, R, m, d, out, ldo, invR);
+  }
+}
+
 hipError_t launch_dequant_sum_fp4(const uint8_t* codes, int64_t code_stride, const uint8_t* bscales,
                                   int64_t bscale_stride, const float* tscales, int R, int m, int d, float* out,
                                   int64_t ldo, hipStream_t s) {
@@ -228,15 +287,10 @@ hipError_t launch_dequant_sum_fp4(const uint8_t* codes, int64_t code_stride, con
   const float invR = 1.0f / (float)R;
   // 16-byte loads need 16-byte aligned code rows in every replica
   const bool v32 = d % 32 == 0 && (reinterpret_cast<uintptr_t>(codes) & 15u) == 0 && (R == 1 || code_stride % 16 == 0);
-  if (v32) {
-    dim3 grid((unsigned)cdiv(d, 64 * 32), (unsigned)cdiv(m, kDq4Rows));
-    hipLaunchKernelGGL(k_dequant_sum_fp4<32>, grid, dim3(256), 0, s, codes, code_stride, bscales, bscale_stride,
-                       tscales, R, m, d, out, ldo, invR);
-  } else {
-    dim3 grid((unsigned)cdiv(d, 64 * 16), (unsigned)cdiv(m, kDq4Rows));
-    hipLaunchKernelGGL(k_dequant_sum_fp4<16>, grid, dim3(256), 0, s, codes, code_stride, bscales, bscale_stride,
-                       tscales, R, m, d, out, ldo, invR);
-  }
+  if (v32)
+    launch_dq4<32>(codes, code_stride, bscales, bscale_stride, tscales, R, m, d, out, ldo, invR, s);
+  else
+    launch_dq4<16>(codes, code_stride, bscales, bscale_stride, tscales, R, m, d, out, ldo, invR, s);
   return hipGetLastError();
 }
 
