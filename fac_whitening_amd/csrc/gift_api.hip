@@ -637,9 +637,9 @@ static gift_status encode_impl(gift_layer_t L, const float* d_W, int64_t ldw, in
   // FP4 takes the amax per tensor; its block amax is taken by the quantiser
   const int amax_scaling = fp4 ? GIFT_SCALE_TENSOR : scaling;
   const int64_t nb = nblk(m, d, amax_scaling);
-  // the fused kernels take FP8 and, without error feedback, FP4 (rank-k and
-  // Euclidean transforms)
-  const bool fused_fp4 = fp4 && !d_resid && (g.transform == GIFT_LOWRANK || g.transform == GIFT_EUCLID);
+  // the fused kernels take FP8 and FP4 (FP4: rank-k and Euclidean
+  // transforms)
+  const bool fused_fp4 = fp4 && (g.transform == GIFT_LOWRANK || g.transform == GIFT_EUCLID);
   if (fused_ok(g, ldw) && (!fp4 || fused_fp4)) {
     gift::FusedArgs a{};
     a.mode = 0;

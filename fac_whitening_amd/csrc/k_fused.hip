@@ -1218,11 +1218,13 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
     // NaN products are set to +0 first, the encoder's code for NaN and
     // the zero codes of a NaN block scale.  Four codes per lane and block
     // go into the tile memory (rows of 384 bytes, the even column in the
-    // low nibble).
+    // low nibble).  With error feedback the S_b are spread the same way
+    // and the new residual fp32(U~ - S_b dec(q)) is formed from the codes
+    // (the difference rounded once) and stored.
     const float gt = sss[0];
     const int bpr = d / kFp4Block;
     constexpr int NG = (2 * NSUB + 3) / 4;
-    float rbs[NG][4];
+    float rbs[NG][4], sbs[EF ? NG : 1][4];
     bool risky = false;
 #pragma unroll
     for (int g4 = 0; g4 < NG; ++g4) {
@@ -1257,6 +1259,12 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
       quad_transpose(bq);
 #pragma unroll
       for (int k = 0; k < 4; ++k) rbs[g4][k] = __uint_as_float(bq[k]);
+      if constexpr (EF) {
+        uint32_t bs[4] = {__float_as_uint(S), __float_as_uint(S), __float_as_uint(S), __float_as_uint(S)};
+        quad_transpose(bs);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) sbs[g4][k] = __uint_as_float(bs[k]);
+      }
     }
     auto codes = [&](auto fix) {
 #pragma unroll
@@ -1278,6 +1286,17 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
           const int cb = cbl * 32 + 16 * h;   // the block's first column in the tile
           *reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(smem) + (rbl * 16 + lr) * kFp4Pad + (cb >> 1) +
                                        2 * lg) = (uint16_t)w;
+          if constexpr (EF) {
+            const float sb = sbs[j >> 2][j & 3];
+            const auto d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+            const auto d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+            const float dv[4] = {d0[0], d0[1], d1[0], d1[1]};
+            int32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = __float_as_int(__builtin_fmaf(-sb, dv[e], x[i][4 * h + e]));
+            const int row = row0 + rbl * 16 + lr, c = col0 + cb + 4 * lg;
+            __builtin_amdgcn_raw_buffer_store_b128(o, rr, (row < m && c < d) ? (row * d + c) * 4 : kOff, 0, kNT);
+          }
         }
       }
     };
@@ -1449,11 +1468,15 @@ static hipError_t launch_encode(const FusedArgs& a, int grid, hipStream_t s) {
 hipError_t launch_fused(const FusedArgs& a, int grid, hipStream_t s) {
   hipError_t e;
   if (a.fmt == 2) {
-    // FP4 (tensor amax, 16-element block scales): the encode without error
-    // feedback; the rank-k decode at 4, 8 or 16 replicas
+    // FP4 (tensor amax, 16-element block scales): the encode, with or
+    // without error feedback; the rank-k decode at 4, 8 or 16 replicas
     if (a.mode == 0) {
-      if (a.resid) return hipErrorInvalidValue;
-      e = a.lr ? persistent_launch(k_rank_encode<2, 0>, grid, a, s) : persistent_launch(k_euclid_encode<2, 0>, grid, a, s);
+      if (a.resid)
+        e = a.lr ? persistent_launch(k_rank_encode_ef<2, 0>, grid, a, s)
+                 : persistent_launch(k_euclid_encode_ef<2, 0>, grid, a, s);
+      else
+        e = a.lr ? persistent_launch(k_rank_encode<2, 0>, grid, a, s)
+                 : persistent_launch(k_euclid_encode<2, 0>, grid, a, s);
     } else {
       if (!a.lr || (a.R != 4 && a.R != 8 && a.R != 16)) return hipErrorInvalidValue;
       e = a.R == 4   ? persistent_launch(k_rank_decode<2, 4, 0>, grid, a, s)
@@ -1537,6 +1560,7 @@ int fused_resident_groups() {
 #undef GIFT_GRP
       // the FP4 payload
       reinterpret_cast<const void*>(k_rank_encode<2, 0>), reinterpret_cast<const void*>(k_euclid_encode<2, 0>),
+      reinterpret_cast<const void*>(k_rank_encode_ef<2, 0>), reinterpret_cast<const void*>(k_euclid_encode_ef<2, 0>),
       reinterpret_cast<const void*>(k_rank_decode<2, 4, 0>), reinterpret_cast<const void*>(k_rank_decode<2, 8, 0>),
       reinterpret_cast<const void*>(k_rank_decode<2, 16, 0>)
   };

@@ -186,9 +186,10 @@ def test_fp4_nonfinite(fw):
     L.close()
 
 
+@pytest.mark.parametrize("ef", [False, True])
 @pytest.mark.parametrize("kind", ["euclid", "lowrank"])
 @pytest.mark.parametrize("share", ["finite", "zero"])
-def test_fp4_nonfinite_under_shared_amax(fw, kind, share):
+def test_fp4_nonfinite_under_shared_amax(fw, kind, share, ef):
     """Inf, -Inf and NaN elements at 1536 x 6144 (the persistent encode)
     under a finite shared amax (1.5x the finite local one) or a zero one:
     codes, block scales and tensor scale bit for bit against the oracle on
@@ -196,9 +197,10 @@ def test_fp4_nonfinite_under_shared_amax(fw, kind, share):
     a NaN block takes the NaN scale and zero codes; under a zero amax every
     code is a signed zero (an Inf times the zero reciprocal gives +0).  The
     flag is raised exactly where a finite tensor scale meets a NaN block
-    scale."""
+    scale.  With error feedback (from a zero residual) the new residual
+    matches too, NaN where the block scale is NaN."""
     m, d = 1536, 6144
-    print(f"[fp4 non-finite {kind} shared amax {share}]", flush=True)
+    print(f"[fp4 non-finite {kind} shared amax {share} ef={ef}]", flush=True)
     rng = np.random.default_rng(91)
     L = _layer(fw, kind, m, d, seed=5)
     w = _grad(m, d, rng)
@@ -209,9 +211,12 @@ def test_fp4_nonfinite_under_shared_amax(fw, kind, share):
     w[48, 767] = np.inf                       # the last column of a tile
     amax_in = torch.tensor([1.5 * finite_amax if share == "finite" else 0.0], dtype=torch.float32, device=DEV)
     wh = torch.empty(m, d, device=DEV)
-    codes, bsc, tsc = L.encode_fp4(torch.from_numpy(w).to(DEV), amax_in=amax_in, whitened=wh)
+    resid = torch.zeros(m, d, device=DEV) if ef else None
+    codes, bsc, tsc = L.encode_fp4(torch.from_numpy(w).to(DEV), amax_in=amax_in, whitened=wh, resid=resid)
     torch.cuda.synchronize()
-    ref = G.quantize_fp4(wh.cpu().numpy(), amax_in=amax_in.cpu().numpy())
+    ref = G.error_feedback_fp4(wh.cpu().numpy(), np.zeros((m, d), np.float32), amax_in=amax_in.cpu().numpy())
+    if ef:
+        assert _same(resid.cpu().numpy(), ref["residual"])
     assert np.array_equal(codes.cpu().numpy(), fp4.pack(ref["codes"]))
     assert np.array_equal(bsc.cpu().numpy(), ref["bscales"])
     assert tsc.item() == ref["tscale"]
