@@ -560,9 +560,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
     UnitT buf[PD];
     auto issue = [&](int u, UnitT& U) {
       const int rb = u / RC, r = u % RC;
-      // FP4 runs R <= RC replicas on the RC-replica stream: the units of
-      // replicas R .. RC - 1 read nothing and add nothing
-      const bool in = u < NU && (FMT != 2 || r < a.R);
+      const bool in = u < NU;
       if constexpr (FMT == 2) {
         const auto q = make_rsrc(a.qcodes + (in ? (int64_t)r * a.code_stride : 0), in ? (int64_t)m * d / 2 : 0);
         const auto qs = make_rsrc(a.qbscales + (in ? (int64_t)r * a.bscale_stride : 0),
@@ -586,7 +584,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
     for (int u = 0; u < NU; ++u) {
       const int rb = u / RC, r = u % RC;
       UnitT& U = buf[u % PD];
-      if (FMT != 2 || r < a.R) {
+      {
         float sa, sb, va[16], vb[8];
         if constexpr (FMT == 2) {
           // S_b = fp32(dec(sc_b) g_r); the E2M1 codes converted exactly by
@@ -1471,8 +1469,7 @@ hipError_t launch_fused(const FusedArgs& a, int grid, hipStream_t s) {
   hipError_t e;
   if (a.fmt == 2) {
     // FP4 (tensor amax, 16-element block scales): the encode, with or
-    // without error feedback; the rank-k decode of up to 16 replicas (on
-    // the 4-, 8- or 16-replica stream)
+    // without error feedback; the rank-k decode at 4, 8 or 16 replicas
     if (a.mode == 0) {
       if (a.resid)
         e = a.lr ? persistent_launch(k_rank_encode_ef<2, 0>, grid, a, s)
@@ -1481,9 +1478,9 @@ hipError_t launch_fused(const FusedArgs& a, int grid, hipStream_t s) {
         e = a.lr ? persistent_launch(k_rank_encode<2, 0>, grid, a, s)
                  : persistent_launch(k_euclid_encode<2, 0>, grid, a, s);
     } else {
-      if (!a.lr || a.R < 1 || a.R > 16) return hipErrorInvalidValue;
-      e = a.R <= 4   ? persistent_launch(k_rank_decode<2, 4, 0>, grid, a, s)
-          : a.R <= 8 ? persistent_launch(k_rank_decode<2, 8, 0>, grid, a, s)
+      if (!a.lr || (a.R != 4 && a.R != 8 && a.R != 16)) return hipErrorInvalidValue;
+      e = a.R == 4   ? persistent_launch(k_rank_decode<2, 4, 0>, grid, a, s)
+          : a.R == 8 ? persistent_launch(k_rank_decode<2, 8, 0>, grid, a, s)
                      : persistent_launch(k_rank_decode<2, 16, 0>, grid, a, s);
     }
   } else if (a.mode == 0) {
