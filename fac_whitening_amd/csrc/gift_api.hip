@@ -856,8 +856,8 @@ gift_status gift_decode_reduce_fp4(gift_layer_t L, const uint8_t* d_codes, int64
   if (!L->ready) return GIFT_ERR_NOT_READY;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* work = static_cast<char*>(d_work);
-  // the fused rank-k decode streams 4, 8 or 16 replicas' FP4 payloads
-  if (g.transform == GIFT_LOWRANK && (R == 4 || R == 8 || R == 16) && fused_ok(g, ldo)) {
+  // the fused rank-k decode streams 4 or 8 replicas' FP4 payloads
+  if (g.transform == GIFT_LOWRANK && (R == 4 || R == 8) && fused_ok(g, ldo)) {
     gift::FusedArgs a{};
     a.mode = 1;
     a.m = m;

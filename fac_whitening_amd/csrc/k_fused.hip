@@ -407,10 +407,10 @@ __device__ __forceinline__ void fused_body(const FusedArgs& a, const int g, cons
   if (tid == 0) s_bad = 0;
   // PIPE: the projection of each 16-row block runs as soon as the block is
   // in (the rank-k encode; the rank-k decode with a compile-time replica
-  // count of at most 8 streams the replicas block by block: at 16 FP8
-  // payloads the unrolled stream no longer fits the registers, 16 FP4
-  // payloads, with half the code bytes per unit, still do)
-  constexpr bool PIPE = LR && (ENC || (RC > 0 && (RC <= 8 || (FMT == 2 && RC <= 16))));
+  // count of at most 8 streams the replicas block by block: at 16 the
+  // unrolled stream no longer fits the registers, and its unit buffers
+  // would go to scratch memory)
+  constexpr bool PIPE = LR && (ENC || (RC > 0 && RC <= 8));
 
   float x[NSUB][8];
   bool live[3];
@@ -1469,7 +1469,7 @@ hipError_t launch_fused(const FusedArgs& a, int grid, hipStream_t s) {
   hipError_t e;
   if (a.fmt == 2) {
     // FP4 (tensor amax, 16-element block scales): the encode, with or
-    // without error feedback; the rank-k decode at 4, 8 or 16 replicas
+    // without error feedback; the rank-k decode at 4 or 8 replicas
     if (a.mode == 0) {
       if (a.resid)
         e = a.lr ? persistent_launch(k_rank_encode_ef<2, 0>, grid, a, s)
@@ -1478,10 +1478,9 @@ hipError_t launch_fused(const FusedArgs& a, int grid, hipStream_t s) {
         e = a.lr ? persistent_launch(k_rank_encode<2, 0>, grid, a, s)
                  : persistent_launch(k_euclid_encode<2, 0>, grid, a, s);
     } else {
-      if (!a.lr || (a.R != 4 && a.R != 8 && a.R != 16)) return hipErrorInvalidValue;
-      e = a.R == 4   ? persistent_launch(k_rank_decode<2, 4, 0>, grid, a, s)
-          : a.R == 8 ? persistent_launch(k_rank_decode<2, 8, 0>, grid, a, s)
-                     : persistent_launch(k_rank_decode<2, 16, 0>, grid, a, s);
+      if (!a.lr || (a.R != 4 && a.R != 8)) return hipErrorInvalidValue;
+      e = a.R == 4 ? persistent_launch(k_rank_decode<2, 4, 0>, grid, a, s)
+                   : persistent_launch(k_rank_decode<2, 8, 0>, grid, a, s);
     }
   } else if (a.mode == 0) {
     e = a.scaling == 0 ? launch_encode<0>(a, grid, s) : launch_encode<1>(a, grid, s);
@@ -1561,8 +1560,7 @@ int fused_resident_groups() {
       // the FP4 payload
       reinterpret_cast<const void*>(k_rank_encode<2, 0>), reinterpret_cast<const void*>(k_euclid_encode<2, 0>),
       reinterpret_cast<const void*>(k_rank_encode_ef<2, 0>), reinterpret_cast<const void*>(k_euclid_encode_ef<2, 0>),
-      reinterpret_cast<const void*>(k_rank_decode<2, 4, 0>), reinterpret_cast<const void*>(k_rank_decode<2, 8, 0>),
-      reinterpret_cast<const void*>(k_rank_decode<2, 16, 0>)
+      reinterpret_cast<const void*>(k_rank_decode<2, 4, 0>), reinterpret_cast<const void*>(k_rank_decode<2, 8, 0>)
   };
   int per_cu = 1 << 30;
   for (const void* k : kernels) {

@@ -268,7 +268,7 @@ size_t gift_payload_bytes(int32_t d_out, int32_t d_in, int32_t scaling);
  *   scale 0x7F (NaN), codes 0 and GIFT_FLAG_NONFINITE.
  * Requires d_in % 16 == 0.  Routes: the rank-k and Euclidean encodes (with
  * or without d_resid) run as one persistent launch where the layer's route
- * allows it (gift_layer_route), and so does the rank-k decode of 4, 8 or 16
+ * allows it (gift_layer_route), and so does the rank-k decode of 4 or 8
  * replicas; everything else takes the multi-kernel route.  Codes, scales
  * and amax are the same on both routes; decoded tensors agree to within
  * fp32 rounding.

@@ -112,9 +112,9 @@ def test_fp4_encode_stage_isolated(fw, kind, shape, ef):
 def test_fp4_decode_reduce(fw, kind, shape, R):
     """The mean of R FP4 payloads mapped back: Euclidean within the fp32
     rounding of the sum; rank-32 with the oracle's factor in the layer state
-    and the oracle's inverse transform (at 4, 8 and 16 replicas the
-    persistent decode, which streams the payloads block by block; otherwise
-    the multi-kernel route).  d = 1008 (not a multiple of 32) takes the
+    and the oracle's inverse transform (at 4 and 8 replicas the persistent
+    decode, which streams the payloads block by block; otherwise the
+    multi-kernel route, which the full layer also takes at 16).  d = 1008 (not a multiple of 32) takes the
     16-codes-per-lane decoder on the multi-kernel route and, on the
     persistent one, a last column tile whose final 32-column sub-tile is
     half inside."""
