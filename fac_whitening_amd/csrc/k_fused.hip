@@ -53,9 +53,6 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSpinLimit = 1 << 20;
 
-__device__ __forceinline__ unsigned ld_dev(const unsigned* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ unsigned long long ld_dev64(const unsigned long long* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
