@@ -227,6 +227,39 @@ def test_fp4_nonfinite_under_shared_amax(fw, kind, share, ef):
     L.close()
 
 
+@pytest.mark.parametrize("kind", ["euclid", "lowrank"])
+def test_fp4_strided_gradient_and_output(fw, kind):
+    """W read at a row stride wider than d_in, and the decoded tensor written
+    at one: the same codes, scales, residual and decoded values as with
+    dense rows (the persistent kernels at 1536 x 6144, 8 replicas)."""
+    m, d, R = 1536, 6144, 8
+    print(f"[fp4 strided {kind}]", flush=True)
+    rng = np.random.default_rng(23)
+    L = _layer(fw, kind, m, d, seed=9)
+    wide = torch.zeros(m, d + 96, device=DEV)
+    codes = torch.empty(R, m, d // 2, dtype=torch.uint8, device=DEV)
+    bsc = torch.empty(R, m, d // 16, dtype=torch.uint8, device=DEV)
+    tsc = torch.empty(R, device=DEV)
+    for r in range(R):
+        W = torch.from_numpy(_grad(m, d, rng, heavy=r == 3)).to(DEV)
+        wide[:, 32:32 + d] = W
+        ra, rb = torch.zeros(m, d, device=DEV), torch.zeros(m, d, device=DEV)
+        c1, b1, t1 = L.encode_fp4(W, resid=ra)
+        c2, b2, t2 = L.encode_fp4(wide[:, 32:32 + d], resid=rb)
+        torch.cuda.synchronize()
+        assert torch.equal(c1, c2) and torch.equal(b1, b2) and torch.equal(t1, t2), r
+        assert torch.equal(ra, rb), r
+        codes[r], bsc[r], tsc[r:r + 1] = c1, b1, t1
+    dense = L.decode_reduce_fp4(codes, bsc, tsc)
+    outw = torch.full((m, d + 64), 7.0, device=DEV)
+    L.decode_reduce_fp4(codes, bsc, tsc, out=outw[:, 16:16 + d])
+    torch.cuda.synchronize()
+    assert torch.equal(dense, outw[:, 16:16 + d])
+    assert bool((outw[:, :16] == 7.0).all()) and bool((outw[:, 16 + d:] == 7.0).all())
+    assert L.flags() == 0
+    L.close()
+
+
 def test_fp4_argument_checks(fw):
     """d_in not a multiple of 16 and E2M1 through the FP8 call are refused
     before anything is enqueued."""
