@@ -22,6 +22,7 @@ namespace gift {
 
 // Small-buffer layout (fp64 elements).
 constexpr int kSmTrace = 0;            // [0] tr(A)
+constexpr int kSmSolved = 1;           // [1] 1: the tridiagonal solver wrote the factor
 constexpr int kSmM = 64;               // [LP*LP] l x l matrix (R^-1 or V_k)
 constexpr int kSmTheta = kSmM + 64 * 64;  // [LP] Ritz values (sorted)
 
@@ -392,6 +393,57 @@ __global__ void __launch_bounds__(256) k_right_small(const double* __restrict__ 
   for (int c = 0; c < CPT; ++c) out[(int64_t)i * NC + g * CPT + c] = (TO)acc[c];
 }
 
+// Outputs of the Rayleigh-Ritz step, shared by both solvers: order[t] is the
+// t-th largest Ritz value's index, theta(a) its value, vec(r, a) component r
+// of its eigenvector.  V_k into small[kSmM] as [LP][32], the sorted Ritz
+// values into small[kSmTheta], and the coefficient vectors (c_enc, c_dec,
+// rho^-1/2, rho^1/2, lambda, rho) into coef.  Called by every thread after
+// a barrier that made order, theta and vec visible.
+template <int LP, typename TF, typename VF>
+__device__ __forceinline__ void store_factor(int l, int k, int d, float damping_rel, const int* order, TF theta,
+                                             VF vec, double* __restrict__ small, float* __restrict__ coef,
+                                             uint32_t* __restrict__ flags) {
+  const int tid = threadIdx.x;
+  for (int o = tid; o < LP * 32; o += 256) {
+    int a = o / 32, t = o % 32;
+    small[kSmM + o] = (a < l && t < k) ? vec(a, order[t]) : 0.0;
+  }
+  if (tid < LP) small[kSmTheta + tid] = tid < l ? theta(order[tid]) : 0.0;
+  __syncthreads();
+  if (tid == 0) {
+    double tr = small[kSmTrace];
+    double lam = (double)damping_rel * tr / (double)d;
+    double sum = 0.0;
+    for (int t = 0; t < k; ++t) sum += theta(order[t]);
+    double rho;
+    if (k < d) {
+      rho = (tr - sum) / (double)(d - k);
+      rho = (rho > 0.0 ? rho : 0.0) + lam;
+    } else {
+      rho = lam > 0.0 ? lam : 1.0;
+    }
+    double rm = 1.0 / sqrt(rho), rp = sqrt(rho);
+    bool bad = !(rho > 0.0) || !isfinite(rm);
+    for (int t = 0; t < 32; ++t) {
+      double ce = 0.0, cd = 0.0;
+      if (t < k) {
+        double th = theta(order[t]);
+        double lt = (th > 0.0 ? th : 0.0) + lam;
+        if (!(lt > 0.0)) bad = true;
+        ce = 1.0 / sqrt(lt) - rm;
+        cd = sqrt(lt) - rp;
+      }
+      coef[t] = (float)ce;
+      coef[32 + t] = (float)cd;
+    }
+    coef[64] = (float)rm;
+    coef[65] = (float)rp;
+    coef[66] = (float)lam;
+    coef[67] = (float)rho;
+    if (bad) atomicOr(flags, (uint32_t)GIFT_FLAG_NONFINITE);
+  }
+}
+
 // Jacobi rotation annihilating B[p][q] (Golub & Van Loan, Alg. 8.5.1): with
 // d = aqq - app and a = 2 apq, t = tan(theta) = sg a / (|d| + sqrt(d^2 + a^2))
 // (sg = sign(d), t = sign(a) at d = 0: |t| = 1 there, either root
@@ -424,7 +476,11 @@ __device__ __forceinline__ void jacobi_rot(double app, double aqq, double apq, d
 template <int LP>
 __global__ void __launch_bounds__(256) k_jacobi_coef(const double* __restrict__ B0, int l, int k, int d,
                                                      float damping_rel, double* __restrict__ small,
-                                                     float* __restrict__ coef, uint32_t* __restrict__ flags) {
+                                                     float* __restrict__ coef, uint32_t* __restrict__ flags,
+                                                     int after_tridiagonal) {
+  // behind the tridiagonal solver, this kernel only runs when that solver
+  // met a cluster of Ritz values and left the factor to it
+  if (after_tridiagonal && small[kSmSolved] == 1.0) return;
   constexpr int NP = LP / 2;
   __shared__ double B[LP][LP + 1];
   __shared__ double V[LP][LP + 1];
@@ -557,8 +613,7 @@ __global__ void __launch_bounds__(256) k_jacobi_coef(const double* __restrict__ 
     __syncthreads();
     if (done) break;
   }
-  // sort Ritz values descending (stable) -- one thread, l <= 64
-  if (tid == 0) {
+  if (tid == 0) {   // sort Ritz values descending (stable) -- one thread, l <= 64
     for (int a = 0; a < l; ++a) order[a] = a;
     for (int a = 1; a < l; ++a) {
       int v = order[a];
@@ -571,45 +626,332 @@ __global__ void __launch_bounds__(256) k_jacobi_coef(const double* __restrict__ 
     }
   }
   __syncthreads();
-  // V_k into small[kSmM] as [LP][32]
-  for (int o = tid; o < LP * 32; o += 256) {
-    int a = o / 32, t = o % 32;
-    small[kSmM + o] = (a < l && t < k) ? V[a][order[t]] : 0.0;
+  store_factor<LP>(l, k, d, damping_rel, order, [&](int a) { return B[a][a]; },
+                   [&](int r, int a) { return V[r][a]; }, small, coef, flags);
+}
+
+// Rayleigh-Ritz step by a tridiagonal reduction (used for l <= 48; the
+// Jacobi kernel above stays as the solver for clustered spectra and for
+// larger l).  One workgroup of 256 threads:
+//  1. Householder reduction of the symmetric B to tridiagonal T = H^T B H
+//     (Golub & Van Loan, Alg. 8.3.1): step j reflects column j below the
+//     diagonal onto its first entry with v = x - alpha e1, alpha =
+//     -sign(x1) |x|, and updates the trailing block S <- S - v w^T - w v^T
+//     with p = beta S v, w = p - (beta/2)(p^T v) v, beta = 2 / v^T v.
+//  2. T is split where a coupling is below eps (|d_i| + |d_i+1|); the
+//     eigenvalues of each unreduced block come from bisection on Sturm counts
+//     (the sign changes of the leading principal minors of T - s I, GvL
+//     8.4.1), five evaluation points per step on five lanes of a wave (the
+//     interval shrinks six-fold per step).
+//  3. If two neighbouring eigenvalues of one block, both among the k largest,
+//     are closer than 1e-6 of |T|, the eigenvectors below would not be
+//     reliably orthogonal: the kernel leaves the step to the Jacobi kernel
+//     (small[kSmSolved] = 0).
+//  4. Each eigenvector of T from one twisted factorisation at its eigenvalue
+//     (Dhillon and Parlett's twisted factorisation of T - lambda I: the
+//     forward LDL^T and backward UDU^T pivots D+ and D-, the twist index r
+//     minimising |D+_r + D-_r - (d_r - lambda)|, then z_r = 1 and the two
+//     one-sided recurrences), normalised.
+//  5. The eigenvectors of B are H z (the reflections applied in reverse).
+// Every sum runs in a fixed order, so the result is deterministic.
+template <int LP>
+__global__ void __launch_bounds__(256) k_tridiag_coef(const double* __restrict__ B0, int l, int k, int d,
+                                                      float damping_rel, double* __restrict__ small,
+                                                      float* __restrict__ coef, uint32_t* __restrict__ flags) {
+  static_assert(LP <= 48, "slots: 12 per wave, five lanes each");
+  __shared__ double Bm[LP][LP + 1];
+  __shared__ double HV[LP][LP];          // HV[j][i]: component i of the reflection vector of step j
+  __shared__ double Zc[LP][LP + 1];      // Zc[i][g]: component i of eigenvector g
+  __shared__ double Fw[3][LP][LP];       // per eigenvector g: D+ [0][i][g], L [1][i][g], U [2][i][g]
+  __shared__ double dd[LP], ee[LP], e2[LP], hb[LP], vv[LP], pv[LP], wv[LP], th[LP];
+  __shared__ int blk0[LP], blk1[LP], rk[LP], order[LP];
+  __shared__ double s_tn, s_pivmin;
+  __shared__ int s_cluster;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = l;
+  const double eps = 0x1p-52;
+  for (int o = tid; o < LP * LP; o += 256) {
+    const int a = o / LP, b = o % LP;
+    Bm[a][b] = (a < n && b < n) ? 0.5 * (B0[a * LP + b] + B0[b * LP + a]) : 0.0;
+    Zc[a][b] = 0.0;
+    HV[a][b] = 0.0;
   }
-  if (tid < LP) small[kSmTheta + tid] = tid < l ? B[order[tid]][order[tid]] : 0.0;
+  if (tid < LP) {
+    dd[tid] = 0.0;
+    ee[tid] = 0.0;
+    e2[tid] = 0.0;
+  }
   __syncthreads();
-  if (tid == 0) {
-    double tr = small[kSmTrace];
-    double lam = (double)damping_rel * tr / (double)d;
-    double sum = 0.0;
-    for (int t = 0; t < k; ++t) sum += B[order[t]][order[t]];
-    double rho;
-    if (k < d) {
-      rho = (tr - sum) / (double)(d - k);
-      rho = (rho > 0.0 ? rho : 0.0) + lam;
-    } else {
-      rho = lam > 0.0 ? lam : 1.0;
-    }
-    double rm = 1.0 / sqrt(rho), rp = sqrt(rho);
-    bool bad = !(rho > 0.0) || !isfinite(rm);
-    for (int t = 0; t < 32; ++t) {
-      double ce = 0.0, cd = 0.0;
-      if (t < k) {
-        double th = B[order[t]][order[t]];
-        double lt = (th > 0.0 ? th : 0.0) + lam;
-        if (!(lt > 0.0)) bad = true;
-        ce = 1.0 / sqrt(lt) - rm;
-        cd = sqrt(lt) - rp;
+  // 1. Householder reduction
+  for (int j = 0; j + 2 < n; ++j) {
+    const int m = n - j - 1;   // rows j + 1 .. n - 1
+    if (wave == 0) {
+      const double x = lane < m ? Bm[j + 1 + lane][j] : 0.0;
+      double sq = x * x;
+      for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
+      const double sig = __shfl(sq, 0, 64), x0 = __shfl(x, 0, 64);
+      double beta = 0.0, alpha = x0, v = 0.0;
+      if (sig > 0.0) {
+        alpha = -copysign(sqrt(sig), x0);
+        const double v0 = x0 - alpha;
+        v = lane == 0 ? v0 : x;
+        beta = 2.0 / (sig - x0 * x0 + v0 * v0);
       }
-      coef[t] = (float)ce;
-      coef[32 + t] = (float)cd;
+      if (lane < m) {
+        HV[j][j + 1 + lane] = v;
+        vv[lane] = v;
+      }
+      if (lane == 0) {
+        hb[j] = beta;
+        ee[j] = alpha;
+        dd[j] = Bm[j][j];
+      }
     }
-    coef[64] = (float)rm;
-    coef[65] = (float)rp;
-    coef[66] = (float)lam;
-    coef[67] = (float)rho;
-    if (bad) atomicOr(flags, (uint32_t)GIFT_FLAG_NONFINITE);
+    __syncthreads();
+    {   // p = beta S v: four lanes per row, their partial sums added in a fixed order
+      const int r = tid >> 2, sub = tid & 3;
+      double acc = 0.0;
+      if (r < m)
+        for (int c = sub; c < m; c += 4) acc += Bm[j + 1 + r][j + 1 + c] * vv[c];
+      const int base = lane & ~3;
+      const double q0 = __shfl(acc, base, 64), q1 = __shfl(acc, base + 1, 64), q2 = __shfl(acc, base + 2, 64),
+                   q3 = __shfl(acc, base + 3, 64);
+      if (r < m && sub == 0) pv[r] = hb[j] * ((q0 + q1) + (q2 + q3));
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const double pr = lane < m ? pv[lane] : 0.0, vr = lane < m ? vv[lane] : 0.0;
+      double t = pr * vr;
+      for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
+      const double K = 0.5 * hb[j] * __shfl(t, 0, 64);
+      if (lane < m) wv[lane] = pr - K * vr;
+    }
+    __syncthreads();
+    for (int o = tid; o < m * m; o += 256) {
+      const int r = o / m, c = o % m;
+      Bm[j + 1 + r][j + 1 + c] -= vv[r] * wv[c] + wv[r] * vv[c];
+    }
+    __syncthreads();
   }
+  // 2. the last diagonal and coupling entries, the norm, the split
+  if (tid == 0) {
+    if (n >= 2) {
+      dd[n - 2] = Bm[n - 2][n - 2];
+      ee[n - 2] = Bm[n - 1][n - 2];
+    }
+    dd[n - 1] = Bm[n - 1][n - 1];
+    double tn = 0.0, me2 = 1.0;
+    for (int i = 0; i < n; ++i) {
+      const double r = fabs(dd[i]) + (i > 0 ? fabs(ee[i - 1]) : 0.0) + (i + 1 < n ? fabs(ee[i]) : 0.0);
+      tn = r > tn ? r : tn;
+    }
+    for (int i = 0; i + 1 < n; ++i) {
+      if (fabs(ee[i]) <= eps * (fabs(dd[i]) + fabs(dd[i + 1]))) ee[i] = 0.0;
+      e2[i] = ee[i] * ee[i];
+      me2 = e2[i] > me2 ? e2[i] : me2;
+    }
+    s_tn = tn > 0.0 ? tn : 0x1p-1022;
+    s_pivmin = 0x1p-1022 * me2;
+    s_cluster = 0;
+  }
+  __syncthreads();
+  const double tn = s_tn, pivmin = s_pivmin;
+  // eigenvalue slot g: its unreduced block [blk0, blk1)
+  if (tid < n) {
+    int a = tid, b = tid + 1;
+    while (a > 0 && ee[a - 1] != 0.0) --a;
+    while (b < n && ee[b - 1] != 0.0) ++b;
+    blk0[tid] = a;
+    blk1[tid] = b;
+  }
+  __syncthreads();
+  // bisection: slot g on lanes 5 (g % 12) .. + 4 of wave g / 12.  The
+  // Sturm count is taken as the sign changes of the sequence of leading
+  // principal minors of T - s I, p_i = (d_i - s) p_i-1 - e_i-1^2 p_i-2 (one
+  // fma on the critical path per term, no division), on T scaled by a power
+  // of two to |T| < 1, the pair (p_i-1, p_i) rescaled by a power of two every
+  // eight terms; a zero term takes the sign opposite to the one before it.
+  // The diagonal and the squared couplings sit in registers.
+  {
+    const int g = 12 * wave + lane / 5, sp = lane % 5;
+    int tex;
+    (void)frexp(tn, &tex);
+    double dr[LP], er[LP];
+#pragma unroll
+    for (int i = 0; i < LP; ++i) {
+      dr[i] = ldexp(dd[i], -tex);
+      er[i] = ldexp(e2[i], -2 * tex);
+    }
+    if (lane < 60 && g < n) {
+      const int a = blk0[g], b = blk1[g], idx = b - 1 - g;   // ascending index of the (g - a)-th largest
+      double lam;
+      if (b - a == 1) {
+        lam = dd[g];
+      } else {
+        double lo = dd[a], hi = dd[a];
+        for (int i = a; i < b; ++i) {
+          const double r = (i > a ? fabs(ee[i - 1]) : 0.0) + (i + 1 < b ? fabs(ee[i]) : 0.0);
+          lo = fmin(lo, dd[i] - r);
+          hi = fmax(hi, dd[i] + r);
+        }
+        lo -= 2.0 * eps * tn;
+        hi += 2.0 * eps * tn;
+        const int base = lane - sp;
+        for (int it = 0; it < 64; ++it) {
+          const double w = hi - lo;
+          const double pt = lo + w * (double)(sp + 1) * (1.0 / 6.0);
+          const double ps = ldexp(pt, -tex);
+          int cnt = 0;
+          double p0 = 1.0, p1 = 1.0;
+          if (a == 0 && b == LP) {   // one unreduced block over all LP rows: no per-term test
+#pragma unroll
+            for (int i = 0; i < LP; ++i) {
+              double pn = dr[i] - ps;
+              if (i > 0) pn = fma(pn, p1, -er[i > 0 ? i - 1 : 0] * p0);
+              if (pn == 0.0) pn = -copysign(0x1p-1000, p1);
+              cnt += (int)((__double_as_longlong(pn) ^ __double_as_longlong(p1)) >> 63) & 1;
+              p0 = p1;
+              p1 = pn;
+              if ((i & 7) == 7) {
+                int ex;
+                (void)frexp(p1, &ex);
+                p1 = ldexp(p1, -ex);
+                p0 = ldexp(p0, -ex);
+              }
+            }
+          } else {
+#pragma unroll
+          for (int i = 0; i < LP; ++i) {
+            if (i >= a && i < b) {
+              double pn = dr[i] - ps;
+              if (i > a) pn = fma(pn, p1, -er[i > 0 ? i - 1 : 0] * p0);
+              if (pn == 0.0) pn = -copysign(0x1p-1000, p1);
+              cnt += (pn < 0.0) != (p1 < 0.0);
+              p0 = p1;
+              p1 = pn;
+              if ((i & 7) == 7) {
+                int ex;
+                (void)frexp(p1, &ex);
+                p1 = ldexp(p1, -ex);
+                p0 = ldexp(p0, -ex);
+              }
+            }
+          }
+          }
+          double nlo = lo, nhi = hi;
+#pragma unroll
+          for (int t = 0; t < 5; ++t) {
+            const int ct = __shfl(cnt, base + t, 64);
+            const double ptt = lo + w * (double)(t + 1) * (1.0 / 6.0);
+            if (ct <= idx) nlo = ptt;
+          }
+#pragma unroll
+          for (int t = 4; t >= 0; --t) {
+            const int ct = __shfl(cnt, base + t, 64);
+            const double ptt = lo + w * (double)(t + 1) * (1.0 / 6.0);
+            if (ct > idx) nhi = ptt;
+          }
+          const bool done = (nlo == lo && nhi == hi) || nhi - nlo <= 2.0 * eps * fmax(fabs(nlo), fabs(nhi));
+          lo = nlo;
+          hi = nhi;
+          if (done) break;
+        }
+        lam = 0.5 * (lo + hi);
+      }
+      if (sp == 0) th[g] = lam;
+    }
+  }
+  __syncthreads();
+  // ranks (descending, ties to the lower slot) and the cluster test
+  if (tid < n) {
+    int r = 0;
+    for (int h = 0; h < n; ++h) r += (th[h] > th[tid]) || (th[h] == th[tid] && h < tid);
+    rk[tid] = r;
+    order[r] = tid;
+  }
+  __syncthreads();
+  if (tid + 1 < n && blk1[tid] > tid + 1 && rk[tid] < k && rk[tid + 1] < k &&
+      fabs(th[tid] - th[tid + 1]) <= 1e-6 * tn)
+    s_cluster = 1;
+  __syncthreads();
+  if (s_cluster) {
+    if (tid == 0) small[kSmSolved] = 0.0;
+    return;
+  }
+  // 4. eigenvectors of T, one thread each
+  if (tid < n) {
+    const int g = tid, a = blk0[g], b = blk1[g];
+    const double lam = th[g];
+    if (b - a == 1) {
+      Zc[g][g] = 1.0;
+    } else {
+      double dp = dd[a] - lam;
+      if (fabs(dp) < pivmin) dp = pivmin;
+      Fw[0][a][g] = dp;
+      for (int i = a; i + 1 < b; ++i) {
+        const double L = ee[i] / dp;
+        dp = dd[i + 1] - lam - L * ee[i];
+        if (fabs(dp) < pivmin) dp = pivmin;
+        Fw[1][i][g] = L;
+        Fw[0][i + 1][g] = dp;
+      }
+      double dm = dd[b - 1] - lam;
+      if (fabs(dm) < pivmin) dm = pivmin;
+      int r = b - 1;
+      double best = fabs(Fw[0][b - 1][g] + dm - (dd[b - 1] - lam));
+      for (int i = b - 2; i >= a; --i) {
+        const double U = ee[i] / dm;
+        dm = dd[i] - lam - U * ee[i];
+        if (fabs(dm) < pivmin) dm = pivmin;
+        Fw[2][i][g] = U;
+        const double gam = fabs(Fw[0][i][g] + dm - (dd[i] - lam));
+        if (gam < best) {
+          best = gam;
+          r = i;
+        }
+      }
+      double z = 1.0, nrm = 1.0;
+      Zc[r][g] = 1.0;
+      for (int i = r - 1; i >= a; --i) {
+        z = -Fw[1][i][g] * z;
+        Zc[i][g] = z;
+        nrm += z * z;
+      }
+      z = 1.0;
+      for (int i = r; i + 1 < b; ++i) {
+        z = -Fw[2][i][g] * z;
+        Zc[i + 1][g] = z;
+        nrm += z * z;
+      }
+      const double sc = 1.0 / sqrt(nrm);
+      for (int i = a; i < b; ++i) Zc[i][g] *= sc;
+    }
+  }
+  __syncthreads();
+  // 5. back-transformation: thread g applies the reflections, last first,
+  // to column g held in registers
+  if (tid < n) {
+    double z[LP];
+#pragma unroll
+    for (int i = 0; i < LP; ++i) z[i] = Zc[i][tid];
+#pragma unroll
+    for (int j = LP - 3; j >= 0; --j) {
+      if (j + 2 < n) {
+        double acc = 0.0;
+#pragma unroll
+        for (int i = j + 1; i < LP; ++i) acc += HV[j][i] * z[i];
+        const double sj = hb[j] * acc;
+#pragma unroll
+        for (int i = j + 1; i < LP; ++i) z[i] -= sj * HV[j][i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < LP; ++i) Zc[i][tid] = z[i];
+  }
+  __syncthreads();
+  store_factor<LP>(l, k, d, damping_rel, order, [&](int a) { return th[a]; }, [&](int r, int a) { return Zc[r][a]; },
+                   small, coef, flags);
+  if (tid == 0) small[kSmSolved] = 1.0;
 }
 
 template <int LP>
@@ -680,7 +1022,10 @@ static hipError_t refresh_lowrank_lp(const float* A, int d, int k, int l, int q,
   orth(Y, Q, 2);                      // Q = orth(Y)
   product(Q, Z);                      // Z = A Q (fp64: the Rayleigh-Ritz matrix and the Ritz values)
   gram(Q, Z);
-  hipLaunchKernelGGL((k_jacobi_coef<LP>), dim3(1), dim3(256), 0, s, gsum, l, k, d, damping_rel, small, coef, flags);
+  if constexpr (LP <= 48)
+    hipLaunchKernelGGL((k_tridiag_coef<LP>), dim3(1), dim3(256), 0, s, gsum, l, k, d, damping_rel, small, coef, flags);
+  hipLaunchKernelGGL((k_jacobi_coef<LP>), dim3(1), dim3(256), 0, s, gsum, l, k, d, damping_rel, small, coef, flags,
+                     LP <= 48 ? 1 : 0);
   hipLaunchKernelGGL((k_right_small<LP, 32, float>), dim3((unsigned)cdiv((int64_t)d * 4, 256)), dim3(256), 0, s, Q,
                      d, small, 32, U);
   return hipGetLastError();

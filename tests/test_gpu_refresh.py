@@ -53,3 +53,52 @@ def test_refresh_metric_layer(fw):
     err = rel_fro(whit[:rows].cpu().numpy(), ref)
     print(f"  whitened rel err {err:.3e}", flush=True)
     assert err <= 1e-5
+
+
+def _factor_from_activations(fw, x, d, seed):
+    L = fw.Layer(64, d, "lowrank", device=DEV)
+    L.accumulate_stats(x, commit=True)
+    om = torch.from_numpy(np.random.default_rng(seed).standard_normal((d, 48)).astype(np.float32)).to(DEV)
+    L.refresh(om)
+    torch.cuda.synchronize()
+    assert L.flags() == 0
+    b = L.buffers()
+    return L, b["A"].double().cpu().numpy(), om.cpu().numpy(), b["U"].double().cpu().numpy(), \
+        b["coef"].cpu().numpy().astype(np.float64)
+
+
+def test_refresh_repeated_eigenvalues(fw):
+    """Spectra with repeated Ritz values, where the eigenvectors of the
+    Rayleigh-Ritz step are not unique (the tridiagonal solver hands such
+    spectra to the Jacobi solver).  A = 4 I (activations 32 I over 256
+    tokens): every coefficient against the oracle, c_enc = c_dec = 0 up to
+    rounding, U orthonormal.  A with eigenvalues 4 and 1 on 128-dimensional
+    subspaces: U orthonormal, its residual in the eigenspace of 4 no larger
+    than the oracle's, the coefficients against the oracle."""
+    d = 256
+    print("[refresh, repeated eigenvalues]", flush=True)
+    x = 32.0 * torch.eye(d, device=DEV)
+    L, A, om, U, coef = _factor_from_activations(fw, x, d, 1)
+    assert np.array_equal(A, 4.0 * np.eye(d))
+    fac = G.lowrank_factor(A, om, 32, 4, G.damping(A))
+    assert abs(coef[67] / fac["rho"] - 1) <= 1e-6 and abs(coef[64] * np.sqrt(fac["rho"]) - 1) <= 1e-6
+    assert np.max(np.abs(coef[:32])) <= 1e-6 * coef[64] and np.max(np.abs(coef[32:64])) <= 1e-6 * coef[65]
+    assert np.max(np.abs(U.T @ U - np.eye(32))) <= 1e-5
+    L.close()
+    rng = np.random.default_rng(2)
+    Q = np.linalg.qr(rng.standard_normal((d, d)))[0]
+    lam = np.concatenate([np.full(d // 2, 4.0), np.ones(d // 2)])
+    xs = np.ascontiguousarray((np.sqrt(d) * np.sqrt(lam)[:, None] * Q.T).astype(np.float32))   # x^T x / d = Q diag(lam) Q^T
+    L, A, om, U, coef = _factor_from_activations(fw, torch.from_numpy(xs).to(DEV), d, 3)
+    fac = G.lowrank_factor(A, om, 32, 4, G.damping(A))
+    assert np.max(np.abs(U.T @ U - np.eye(32))) <= 1e-5
+    # four iterations leave (1/4)^5 of the other eigenspace in the basis:
+    # the residual is the oracle's own, not zero
+    resid = np.linalg.norm(A @ U - U * fac["theta"]) / np.linalg.norm(A @ U)
+    Uo = fac["U"]
+    resid_o = np.linalg.norm(A @ Uo - Uo * fac["theta"]) / np.linalg.norm(A @ Uo)
+    print(f"  eigenspace residual {resid:.3e} (oracle {resid_o:.3e})", flush=True)
+    assert resid <= 1.05 * resid_o + 1e-6
+    assert abs(coef[67] / fac["rho"] - 1) <= 1e-6
+    assert np.max(np.abs(coef[:32] - fac["c_enc"]) / np.abs(fac["c_enc"])) <= 1e-5
+    L.close()
