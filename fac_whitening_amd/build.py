@@ -24,6 +24,13 @@ FLAGS = [
 ]
 
 
+# per-source additions: the tridiagonal reduction in k_refresh.hip is fully
+# unrolled over its steps (a row of the matrix per lane in registers, indexed
+# by compile-time columns), past the compiler's default size limit for a
+# requested unroll
+EXTRA = {"k_refresh.hip": ["-mllvm", "-pragma-unroll-threshold=1000000"]}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
@@ -36,7 +43,8 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     for src in sources():
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
         objs.append(obj)
-        cmd = ["hipcc", *[f for f in FLAGS if f != "-shared"], "-c", src, "-o", obj]
+        cmd = ["hipcc", *[f for f in FLAGS if f != "-shared"], *EXTRA.get(os.path.basename(src), []), "-c", src,
+               "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

@@ -630,6 +630,43 @@ __global__ void __launch_bounds__(256) k_jacobi_coef(const double* __restrict__ 
                    [&](int r, int a) { return V[r][a]; }, small, coef, flags);
 }
 
+// Sum over the 64 lanes of a wave, the same value in every lane: rotations
+// inside each 16-lane row (DPP row_ror 8, 4, 2, 1), then the row swaps
+// (v_permlane16_swap, v_permlane32_swap), each on the two 32-bit halves;
+// lane 0's total is broadcast (the lanes' rounding orders differ, so one
+// lane decides).
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double x) {
+  const long long b = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)b, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+__device__ __forceinline__ double pair_d(unsigned lo0, unsigned hi0, unsigned lo1, unsigned hi1) {
+  return __longlong_as_double(((long long)hi0 << 32) | lo0) + __longlong_as_double(((long long)hi1 << 32) | lo1);
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+  v += dpp_d<0x128>(v);
+  v += dpp_d<0x124>(v);
+  v += dpp_d<0x122>(v);
+  v += dpp_d<0x121>(v);
+  {
+    const long long b = __double_as_longlong(v);
+    const auto pl = __builtin_amdgcn_permlane16_swap((unsigned)b, (unsigned)b, false, false);
+    const auto ph = __builtin_amdgcn_permlane16_swap((unsigned)(b >> 32), (unsigned)(b >> 32), false, false);
+    v = pair_d(pl[0], ph[0], pl[1], ph[1]);
+  }
+  {
+    const long long b = __double_as_longlong(v);
+    const auto pl = __builtin_amdgcn_permlane32_swap((unsigned)b, (unsigned)b, false, false);
+    const auto ph = __builtin_amdgcn_permlane32_swap((unsigned)(b >> 32), (unsigned)(b >> 32), false, false);
+    v = pair_d(pl[0], ph[0], pl[1], ph[1]);
+  }
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)b, 0), hi = __builtin_amdgcn_readlane((int)(b >> 32), 0);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
 // Rayleigh-Ritz step by a tridiagonal reduction (used for l <= 48; the
 // Jacobi kernel above stays as the solver for clustered spectra and for
 // larger l).  One workgroup of 256 threads:
@@ -668,6 +705,10 @@ __global__ void __launch_bounds__(256) k_tridiag_coef(const double* __restrict__
   __shared__ double s_tn, s_pivmin;
   __shared__ int s_cluster;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // scaled copies of the diagonal and squared couplings for the bisection,
+  // in the eigenvector work area (free until then)
+  auto hv_dr = [&](int i) -> double& { return Fw[0][i][0]; };
+  auto hv_er = [&](int i) -> double& { return Fw[0][i][1]; };
   const int n = l;
   const double eps = 0x1p-52;
   for (int o = tid; o < LP * LP; o += 256) {
@@ -682,57 +723,67 @@ __global__ void __launch_bounds__(256) k_tridiag_coef(const double* __restrict__
     e2[tid] = 0.0;
   }
   __syncthreads();
-  // 1. Householder reduction
-  for (int j = 0; j + 2 < n; ++j) {
-    const int m = n - j - 1;   // rows j + 1 .. n - 1
-    if (wave == 0) {
-      const double x = lane < m ? Bm[j + 1 + lane][j] : 0.0;
-      double sq = x * x;
-      for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
-      const double sig = __shfl(sq, 0, 64), x0 = __shfl(x, 0, 64);
-      double beta = 0.0, alpha = x0, v = 0.0;
-      if (sig > 0.0) {
-        alpha = -copysign(sqrt(sig), x0);
-        const double v0 = x0 - alpha;
-        v = lane == 0 ? v0 : x;
-        beta = 2.0 / (sig - x0 * x0 + v0 * v0);
+  // 1. Householder reduction by wave 0: lane r holds row r of the matrix in
+  // registers (compile-time column indices, the steps unrolled); by symmetry
+  // step j's column below the diagonal is row j, which lane j publishes in
+  // LDS.  The wave's LDS accesses complete in program order, so the steps
+  // need no barrier.
+  if (wave == 0) {
+    double row[LP];
+    const int rl = lane < LP ? lane : LP - 1;   // lanes past LP carry a copy and change nothing
+#pragma unroll
+    for (int c = 0; c < LP; ++c) row[c] = Bm[rl][c];
+#pragma unroll
+    for (int j = 0; j + 2 < LP; ++j) {
+      if (j + 2 < n) {
+        if (lane == j) {
+#pragma unroll
+          for (int c = 0; c < LP; ++c) pv[c] = row[c];
+        }
+        __builtin_amdgcn_wave_barrier();
+        const bool act = lane > j && lane < n;   // rows j + 1 .. n - 1
+        const double x = act ? pv[lane] : 0.0;
+        const double sig = wave_sum_d(x * x), x0 = pv[j + 1];
+        double beta = 0.0, alpha = x0, v = 0.0;
+        if (sig > 0.0) {
+          alpha = -copysign(sqrt(sig), x0);
+          const double v0 = x0 - alpha;
+          v = act ? (lane == j + 1 ? v0 : x) : 0.0;
+          beta = 2.0 / (sig - x0 * x0 + v0 * v0);
+        }
+        if (lane < LP) {
+          vv[lane] = v;   // zero outside rows j + 1 .. n - 1
+          HV[j][lane] = v;
+        }
+        if (lane == 0) {
+          hb[j] = beta;
+          ee[j] = alpha;
+          dd[j] = pv[j];
+        }
+        __builtin_amdgcn_wave_barrier();
+        // p = beta S v, w = p - (beta/2)(p^T v) v (v_c and w_c read as LDS
+        // broadcasts)
+        double acc = 0.0;
+#pragma unroll
+        for (int c = j + 1; c < LP; ++c) acc += row[c] * vv[c];
+        const double pr = act ? beta * acc : 0.0;
+        const double K = 0.5 * beta * wave_sum_d(pr * v);
+        const double wr = act ? pr - K * v : 0.0;
+        if (lane < LP) wv[lane] = wr;
+        __builtin_amdgcn_wave_barrier();
+        // S <- S - v w^T - w v^T (rows outside the block have v = w = 0)
+#pragma unroll
+        for (int c = j + 1; c < LP; ++c) row[c] -= v * wv[c] + wr * vv[c];
+        __builtin_amdgcn_wave_barrier();
       }
-      if (lane < m) {
-        HV[j][j + 1 + lane] = v;
-        vv[lane] = v;
-      }
-      if (lane == 0) {
-        hb[j] = beta;
-        ee[j] = alpha;
-        dd[j] = Bm[j][j];
-      }
     }
-    __syncthreads();
-    {   // p = beta S v: four lanes per row, their partial sums added in a fixed order
-      const int r = tid >> 2, sub = tid & 3;
-      double acc = 0.0;
-      if (r < m)
-        for (int c = sub; c < m; c += 4) acc += Bm[j + 1 + r][j + 1 + c] * vv[c];
-      const int base = lane & ~3;
-      const double q0 = __shfl(acc, base, 64), q1 = __shfl(acc, base + 1, 64), q2 = __shfl(acc, base + 2, 64),
-                   q3 = __shfl(acc, base + 3, 64);
-      if (r < m && sub == 0) pv[r] = hb[j] * ((q0 + q1) + (q2 + q3));
+    // the trailing 2 x 2 block for the entries below
+    if (lane < LP) {
+#pragma unroll
+      for (int c = 0; c < LP; ++c) Bm[lane][c] = row[c];
     }
-    __syncthreads();
-    if (wave == 0) {
-      const double pr = lane < m ? pv[lane] : 0.0, vr = lane < m ? vv[lane] : 0.0;
-      double t = pr * vr;
-      for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
-      const double K = 0.5 * hb[j] * __shfl(t, 0, 64);
-      if (lane < m) wv[lane] = pr - K * vr;
-    }
-    __syncthreads();
-    for (int o = tid; o < m * m; o += 256) {
-      const int r = o / m, c = o % m;
-      Bm[j + 1 + r][j + 1 + c] -= vv[r] * wv[c] + wv[r] * vv[c];
-    }
-    __syncthreads();
   }
+  __syncthreads();
   // 2. the last diagonal and coupling entries, the norm, the split
   if (tid == 0) {
     if (n >= 2) {
@@ -771,17 +822,17 @@ __global__ void __launch_bounds__(256) k_tridiag_coef(const double* __restrict__
   // fma on the critical path per term, no division), on T scaled by a power
   // of two to |T| < 1, the pair (p_i-1, p_i) rescaled by a power of two every
   // eight terms; a zero term takes the sign opposite to the one before it.
-  // The diagonal and the squared couplings sit in registers.
+  // The scaled diagonal and squared couplings are read as LDS broadcasts
+  // (their addresses are fixed, so the reads run ahead of the recurrence).
+  int tex;
+  (void)frexp(tn, &tex);
+  if (tid < LP) {
+    hv_dr(tid) = ldexp(dd[tid], -tex);
+    hv_er(tid) = ldexp(e2[tid], -2 * tex);
+  }
+  __syncthreads();
   {
     const int g = 12 * wave + lane / 5, sp = lane % 5;
-    int tex;
-    (void)frexp(tn, &tex);
-    double dr[LP], er[LP];
-#pragma unroll
-    for (int i = 0; i < LP; ++i) {
-      dr[i] = ldexp(dd[i], -tex);
-      er[i] = ldexp(e2[i], -2 * tex);
-    }
     if (lane < 60 && g < n) {
       const int a = blk0[g], b = blk1[g], idx = b - 1 - g;   // ascending index of the (g - a)-th largest
       double lam;
@@ -804,12 +855,14 @@ __global__ void __launch_bounds__(256) k_tridiag_coef(const double* __restrict__
           int cnt = 0;
           double p0 = 1.0, p1 = 1.0;
           if (a == 0 && b == LP) {   // one unreduced block over all LP rows: no per-term test
+            // (a zero term in the middle gives the same count whatever sign
+            // it is given; only a zero last term, s an eigenvalue of T, can
+            // move the count by one, which the bracketing tolerates)
 #pragma unroll
             for (int i = 0; i < LP; ++i) {
-              double pn = dr[i] - ps;
-              if (i > 0) pn = fma(pn, p1, -er[i > 0 ? i - 1 : 0] * p0);
-              if (pn == 0.0) pn = -copysign(0x1p-1000, p1);
-              cnt += (int)((__double_as_longlong(pn) ^ __double_as_longlong(p1)) >> 63) & 1;
+              double pn = hv_dr(i) - ps;
+              if (i > 0) pn = fma(pn, p1, -hv_er(i > 0 ? i - 1 : 0) * p0);
+              cnt += (int)((uint32_t)(__double2hiint(pn) ^ __double2hiint(p1)) >> 31);
               p0 = p1;
               p1 = pn;
               if ((i & 7) == 7) {
@@ -823,8 +876,8 @@ __global__ void __launch_bounds__(256) k_tridiag_coef(const double* __restrict__
 #pragma unroll
           for (int i = 0; i < LP; ++i) {
             if (i >= a && i < b) {
-              double pn = dr[i] - ps;
-              if (i > a) pn = fma(pn, p1, -er[i > 0 ? i - 1 : 0] * p0);
+              double pn = hv_dr(i) - ps;
+              if (i > a) pn = fma(pn, p1, -hv_er(i > 0 ? i - 1 : 0) * p0);
               if (pn == 0.0) pn = -copysign(0x1p-1000, p1);
               cnt += (pn < 0.0) != (p1 < 0.0);
               p0 = p1;
@@ -851,7 +904,8 @@ __global__ void __launch_bounds__(256) k_tridiag_coef(const double* __restrict__
             const double ptt = lo + w * (double)(t + 1) * (1.0 / 6.0);
             if (ct > idx) nhi = ptt;
           }
-          const bool done = (nlo == lo && nhi == hi) || nhi - nlo <= 2.0 * eps * fmax(fabs(nlo), fabs(nhi));
+          // absolute tolerance 4 eps |T| (the k largest are far above it)
+          const bool done = (nlo == lo && nhi == hi) || nhi - nlo <= 4.0 * eps * tn;
           lo = nlo;
           hi = nhi;
           if (done) break;
@@ -888,8 +942,13 @@ __global__ void __launch_bounds__(256) k_tridiag_coef(const double* __restrict__
       double dp = dd[a] - lam;
       if (fabs(dp) < pivmin) dp = pivmin;
       Fw[0][a][g] = dp;
+      // the divisions by a refined hardware reciprocal (one Newton step)
+      auto rcp = [](double x) {
+        const double r = __builtin_amdgcn_rcp(x);
+        return fma(r, fma(-x, r, 1.0), r);
+      };
       for (int i = a; i + 1 < b; ++i) {
-        const double L = ee[i] / dp;
+        const double L = ee[i] * rcp(dp);
         dp = dd[i + 1] - lam - L * ee[i];
         if (fabs(dp) < pivmin) dp = pivmin;
         Fw[1][i][g] = L;
@@ -900,7 +959,7 @@ __global__ void __launch_bounds__(256) k_tridiag_coef(const double* __restrict__
       int r = b - 1;
       double best = fabs(Fw[0][b - 1][g] + dm - (dd[b - 1] - lam));
       for (int i = b - 2; i >= a; --i) {
-        const double U = ee[i] / dm;
+        const double U = ee[i] * rcp(dm);
         dm = dd[i] - lam - U * ee[i];
         if (fabs(dm) < pivmin) dm = pivmin;
         Fw[2][i][g] = U;

@@ -35,7 +35,9 @@ HOT = ["k_rank_encode<0, 0>", "k_rank_encode<0, 1>", "k_rank_decode<0, 8, 0>", "
        "k_rank_encode<2, 0>", "k_euclid_encode<2, 0>", "k_rank_encode_ef<2, 0>", "k_euclid_encode_ef<2, 0>",
        "k_rank_decode<2, 4, 0>", "k_rank_decode<2, 8, 0>", "k_quantize_fp4", "k_dequant_sum_fp4",
        "k_bucket_amax", "k_bucket_quantize", "k_bucket_dequant_sum", "k_project", "k_lr_apply", "k_quantize",
-       "k_dequant_sum", "k_aq<48>", "k_aq32<48>"]
+       "k_dequant_sum", "k_aq<48>", "k_aq32<48>",
+       # register-resident Householder rows: fully unrolled (a per-file unroll threshold in the build)
+       "k_tridiag_coef<48>"]
 
 
 def _tool(name):
