@@ -700,7 +700,7 @@ __global__ void __launch_bounds__(256) k_tridiag_coef(const double* __restrict__
   __shared__ double HV[LP][LP];          // HV[j][i]: component i of the reflection vector of step j
   __shared__ double Zc[LP][LP + 1];      // Zc[i][g]: component i of eigenvector g
   __shared__ double Fw[3][LP][LP];       // per eigenvector g: D+ [0][i][g], L [1][i][g], U [2][i][g]
-  __shared__ double dd[LP], ee[LP], e2[LP], hb[LP], vv[LP], pv[LP], wv[LP], th[LP];
+  __shared__ double dd[LP], ee[LP], e2[LP], hb[LP], vv[LP], wv[LP], th[LP];
   __shared__ int blk0[LP], blk1[LP], rk[LP], order[LP];
   __shared__ double s_tn, s_pivmin;
   __shared__ int s_cluster;
@@ -725,9 +725,9 @@ __global__ void __launch_bounds__(256) k_tridiag_coef(const double* __restrict__
   __syncthreads();
   // 1. Householder reduction by wave 0: lane r holds row r of the matrix in
   // registers (compile-time column indices, the steps unrolled); by symmetry
-  // step j's column below the diagonal is row j, which lane j publishes in
-  // LDS.  The wave's LDS accesses complete in program order, so the steps
-  // need no barrier.
+  // step j's column below the diagonal is entry j of each lane's row.  The
+  // wave's LDS accesses complete in program order, so the steps need no
+  // barrier.
   if (wave == 0) {
     double row[LP];
     const int rl = lane < LP ? lane : LP - 1;   // lanes past LP carry a copy and change nothing
@@ -736,14 +736,13 @@ __global__ void __launch_bounds__(256) k_tridiag_coef(const double* __restrict__
 #pragma unroll
     for (int j = 0; j + 2 < LP; ++j) {
       if (j + 2 < n) {
-        if (lane == j) {
-#pragma unroll
-          for (int c = 0; c < LP; ++c) pv[c] = row[c];
-        }
-        __builtin_amdgcn_wave_barrier();
         const bool act = lane > j && lane < n;   // rows j + 1 .. n - 1
-        const double x = act ? pv[lane] : 0.0;
-        const double sig = wave_sum_d(x * x), x0 = pv[j + 1];
+        const double cj = row[j];
+        const double x = act ? cj : 0.0;
+        const double sig = wave_sum_d(x * x);
+        const long long cb = __double_as_longlong(cj);
+        const int x0l = __builtin_amdgcn_readlane((int)cb, j + 1), x0h = __builtin_amdgcn_readlane((int)(cb >> 32), j + 1);
+        const double x0 = __longlong_as_double(((long long)x0h << 32) | (unsigned)x0l);
         double beta = 0.0, alpha = x0, v = 0.0;
         if (sig > 0.0) {
           alpha = -copysign(sqrt(sig), x0);
@@ -755,17 +754,18 @@ __global__ void __launch_bounds__(256) k_tridiag_coef(const double* __restrict__
           vv[lane] = v;   // zero outside rows j + 1 .. n - 1
           HV[j][lane] = v;
         }
-        if (lane == 0) {
+        if (lane == j) {
           hb[j] = beta;
           ee[j] = alpha;
-          dd[j] = pv[j];
+          dd[j] = cj;
         }
         __builtin_amdgcn_wave_barrier();
         // p = beta S v, w = p - (beta/2)(p^T v) v (v_c and w_c read as LDS
         // broadcasts)
-        double acc = 0.0;
+        double a4[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-        for (int c = j + 1; c < LP; ++c) acc += row[c] * vv[c];
+        for (int c = j + 1; c < LP; ++c) a4[(c - j - 1) & 3] += row[c] * vv[c];
+        const double acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
         const double pr = act ? beta * acc : 0.0;
         const double K = 0.5 * beta * wave_sum_d(pr * v);
         const double wr = act ? pr - K * v : 0.0;
