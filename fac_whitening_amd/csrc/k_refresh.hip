@@ -702,7 +702,7 @@ __global__ void __launch_bounds__(256) k_tridiag_coef(const double* __restrict__
   __shared__ double Fw[3][LP][LP];       // per eigenvector g: D+ [0][i][g], L [1][i][g], U [2][i][g]
   __shared__ double dd[LP], ee[LP], e2[LP], hb[LP], vv[LP], wv[LP], th[LP];
   __shared__ int blk0[LP], blk1[LP], rk[LP], order[LP];
-  __shared__ double s_tn, s_pivmin;
+  __shared__ double s_tn, s_pivmin, s_glo, s_ghi;
   __shared__ int s_cluster;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // scaled copies of the diagonal and squared couplings for the bisection,
@@ -784,38 +784,63 @@ __global__ void __launch_bounds__(256) k_tridiag_coef(const double* __restrict__
     }
   }
   __syncthreads();
-  // 2. the last diagonal and coupling entries, the norm, the split
+  // 2. the last diagonal and coupling entries; then by wave 0, lane i for
+  // row i: the norm |T| (largest absolute row sum), the split, the squared
+  // couplings and a Gershgorin interval of the split T (the union of its
+  // blocks' intervals, so it holds every block's eigenvalues)
   if (tid == 0) {
     if (n >= 2) {
       dd[n - 2] = Bm[n - 2][n - 2];
       ee[n - 2] = Bm[n - 1][n - 2];
     }
     dd[n - 1] = Bm[n - 1][n - 1];
-    double tn = 0.0, me2 = 1.0;
-    for (int i = 0; i < n; ++i) {
-      const double r = fabs(dd[i]) + (i > 0 ? fabs(ee[i - 1]) : 0.0) + (i + 1 < n ? fabs(ee[i]) : 0.0);
-      tn = r > tn ? r : tn;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const bool in = lane < n, cpl = lane + 1 < n;
+    // each lane reads and writes only its own coupling; its left neighbour's
+    // comes by a shuffle, before and after the split
+    const double di = in ? dd[lane] : 0.0, dn = cpl ? dd[lane + 1] : 0.0;
+    double er = cpl ? ee[lane] : 0.0;
+    const double el = __shfl_up(er, 1, 64);
+    double tn = fabs(di) + (lane > 0 ? fabs(el) : 0.0) + fabs(er);
+    if (cpl && fabs(er) <= eps * (fabs(di) + fabs(dn))) er = 0.0;
+    double me2 = er * er;
+    if (cpl) {
+      ee[lane] = er;
+      e2[lane] = er * er;
     }
-    for (int i = 0; i + 1 < n; ++i) {
-      if (fabs(ee[i]) <= eps * (fabs(dd[i]) + fabs(dd[i + 1]))) ee[i] = 0.0;
-      e2[i] = ee[i] * ee[i];
-      me2 = e2[i] > me2 ? e2[i] : me2;
+    const double els = __shfl_up(er, 1, 64);
+    const double r = (lane > 0 ? fabs(els) : 0.0) + fabs(er);
+    double lo = in ? di - r : 0.0, hi = in ? di + r : 0.0;
+    lo = in ? lo : __shfl(lo, 0, 64);
+    hi = in ? hi : __shfl(hi, 0, 64);
+    for (int o = 32; o > 0; o >>= 1) {
+      tn = fmax(tn, __shfl_xor(tn, o, 64));
+      me2 = fmax(me2, __shfl_xor(me2, o, 64));
+      lo = fmin(lo, __shfl_xor(lo, o, 64));
+      hi = fmax(hi, __shfl_xor(hi, o, 64));
     }
-    s_tn = tn > 0.0 ? tn : 0x1p-1022;
-    s_pivmin = 0x1p-1022 * me2;
-    s_cluster = 0;
+    if (lane == 0) {
+      s_tn = tn > 0.0 ? tn : 0x1p-1022;
+      s_pivmin = 0x1p-1022 * fmax(me2, 1.0);
+      s_glo = lo;
+      s_ghi = hi;
+      s_cluster = 0;
+    }
   }
   __syncthreads();
   const double tn = s_tn, pivmin = s_pivmin;
-  // eigenvalue slot g: its unreduced block [blk0, blk1)
-  if (tid < n) {
-    int a = tid, b = tid + 1;
-    while (a > 0 && ee[a - 1] != 0.0) --a;
-    while (b < n && ee[b - 1] != 0.0) ++b;
-    blk0[tid] = a;
-    blk1[tid] = b;
+  // eigenvalue slot g: its unreduced block [blk0, blk1), from the mask of
+  // zero couplings (bit i: rows i and i + 1 decoupled)
+  {
+    const unsigned long long zm = __ballot(lane + 1 < n && ee[lane < LP ? lane : 0] == 0.0);
+    if (tid < n) {
+      const unsigned long long below = zm & ((1ull << tid) - 1ull), above = zm >> tid;
+      blk0[tid] = below ? 64 - __clzll((long long)below) : 0;
+      blk1[tid] = above ? tid + __ffsll((long long)above) : n;
+    }
   }
-  __syncthreads();
   // bisection: slot g on lanes 5 (g % 12) .. + 4 of wave g / 12.  The
   // Sturm count is taken as the sign changes of the sequence of leading
   // principal minors of T - s I, p_i = (d_i - s) p_i-1 - e_i-1^2 p_i-2 (one
@@ -839,14 +864,7 @@ __global__ void __launch_bounds__(256) k_tridiag_coef(const double* __restrict__
       if (b - a == 1) {
         lam = dd[g];
       } else {
-        double lo = dd[a], hi = dd[a];
-        for (int i = a; i < b; ++i) {
-          const double r = (i > a ? fabs(ee[i - 1]) : 0.0) + (i + 1 < b ? fabs(ee[i]) : 0.0);
-          lo = fmin(lo, dd[i] - r);
-          hi = fmax(hi, dd[i] + r);
-        }
-        lo -= 2.0 * eps * tn;
-        hi += 2.0 * eps * tn;
+        double lo = s_glo - 2.0 * eps * tn, hi = s_ghi + 2.0 * eps * tn;
         const int base = lane - sp;
         for (int it = 0; it < 64; ++it) {
           const double w = hi - lo;
@@ -919,7 +937,9 @@ __global__ void __launch_bounds__(256) k_tridiag_coef(const double* __restrict__
   // ranks (descending, ties to the lower slot) and the cluster test
   if (tid < n) {
     int r = 0;
-    for (int h = 0; h < n; ++h) r += (th[h] > th[tid]) || (th[h] == th[tid] && h < tid);
+    const double t = th[tid];
+#pragma unroll
+    for (int h = 0; h < LP; ++h) r += h < n && ((th[h] > t) || (th[h] == t && h < tid));
     rk[tid] = r;
     order[r] = tid;
   }
