@@ -681,9 +681,11 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 //     8.4.1), five evaluation points per step on five lanes of a wave (the
 //     interval shrinks six-fold per step).
 //  3. If two neighbouring eigenvalues of one block, both among the k largest,
-//     are closer than 1e-6 of |T|, the eigenvectors below would not be
-//     reliably orthogonal: the kernel leaves the step to the Jacobi kernel
-//     (small[kSmSolved] = 0).
+//     are closer than 1e-8 of |T|, the eigenvectors below would not be
+//     reliably orthogonal (a computed vector's angle to the true one is
+//     about its residual, O(eps |T|), over the gap to the next eigenvalue,
+//     here kept below the factor's fp32 rounding): the kernel leaves the
+//     step to the Jacobi kernel (small[kSmSolved] = 0).
 //  4. Each eigenvector of T from one twisted factorisation at its eigenvalue
 //     (Dhillon and Parlett's twisted factorisation of T - lambda I: the
 //     forward LDL^T and backward UDU^T pivots D+ and D-, the twist index r
@@ -945,7 +947,7 @@ __global__ void __launch_bounds__(256) k_tridiag_coef(const double* __restrict__
   }
   __syncthreads();
   if (tid + 1 < n && blk1[tid] > tid + 1 && rk[tid] < k && rk[tid + 1] < k &&
-      fabs(th[tid] - th[tid + 1]) <= 1e-6 * tn)
+      fabs(th[tid] - th[tid + 1]) <= 1e-8 * tn)
     s_cluster = 1;
   __syncthreads();
   if (s_cluster) {
