@@ -102,3 +102,36 @@ def test_refresh_repeated_eigenvalues(fw):
     assert abs(coef[67] / fac["rho"] - 1) <= 1e-6
     assert np.max(np.abs(coef[:32] - fac["c_enc"]) / np.abs(fac["c_enc"])) <= 1e-5
     L.close()
+
+
+def test_refresh_graded_spectrum_with_close_pairs(fw):
+    """A spectrum graded over three decades (the k largest eigenvalues
+    10^(-3 i / 31)) with two neighbouring pairs 3e-7 and 2.5e-7 of the largest
+    apart, 1e-4 and 2e-4 of their own size: close for a test on |T| alone,
+    well separated for the tridiagonal solver's eigenvectors.  The rest of
+    the spectrum lies below 1e-5.  U orthonormal, its residual no larger than
+    the oracle's (to the fp32 storage of U), rho and the coefficients
+    against the oracle at the tolerance of the other refresh tests."""
+    d = 256
+    print("[refresh, graded spectrum with close pairs]", flush=True)
+    rng = np.random.default_rng(4)
+    lam = np.concatenate([10.0 ** (-3.0 * np.arange(32) / 31), 1e-5 * rng.uniform(0.5, 1.0, d - 32)])
+    lam[27] = lam[26] * (1 - 1e-4)
+    lam[31] = lam[30] * (1 - 2e-4)
+    Q = np.linalg.qr(rng.standard_normal((d, d)))[0]
+    xs = np.ascontiguousarray((np.sqrt(d) * np.sqrt(lam)[:, None] * Q.T).astype(np.float32))
+    L, A, om, U, coef = _factor_from_activations(fw, torch.from_numpy(xs).to(DEV), d, 5)
+    fac = G.lowrank_factor(A, om, 32, 4, G.damping(A))
+    orth = np.max(np.abs(U.T @ U - np.eye(32)))
+    resid = np.linalg.norm(A @ U - U * fac["theta"]) / np.linalg.norm(A @ U)
+    Uo = fac["U"]
+    resid_o = np.linalg.norm(A @ Uo - Uo * fac["theta"]) / np.linalg.norm(A @ Uo)
+    e_enc = np.max(np.abs(coef[:32] - fac["c_enc"]) / np.abs(fac["c_enc"]))
+    e_dec = np.max(np.abs(coef[32:64] - fac["c_dec"]) / np.abs(fac["c_dec"]))
+    print(f"  orthogonality {orth:.2e}, residual {resid:.3e} (oracle {resid_o:.3e}), "
+          f"c_enc {e_enc:.2e}, c_dec {e_dec:.2e}", flush=True)
+    assert orth <= 1e-5
+    assert resid <= 1.05 * resid_o + 1e-6
+    assert abs(coef[67] / fac["rho"] - 1) <= 1e-6
+    assert e_enc <= 1e-5 and e_dec <= 1e-5
+    L.close()
