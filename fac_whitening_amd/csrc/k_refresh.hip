@@ -1018,10 +1018,10 @@ __global__ void __launch_bounds__(256) k_tridiag_coef(const double* __restrict__
 #pragma unroll
     for (int j = LP - 3; j >= 0; --j) {
       if (j + 2 < n) {
-        double acc = 0.0;
+        double a4[4] = {0.0, 0.0, 0.0, 0.0};   // four chains
 #pragma unroll
-        for (int i = j + 1; i < LP; ++i) acc += HV[j][i] * z[i];
-        const double sj = hb[j] * acc;
+        for (int i = j + 1; i < LP; ++i) a4[(i - j - 1) & 3] += HV[j][i] * z[i];
+        const double sj = hb[j] * ((a4[0] + a4[1]) + (a4[2] + a4[3]));
 #pragma unroll
         for (int i = j + 1; i < LP; ++i) z[i] -= sj * HV[j][i];
       }
